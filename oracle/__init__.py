@@ -1,0 +1,165 @@
+"""FP64 CPU oracle for the Gated DeltaNet recurrent-state path.
+
+TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the
+benchmark's CPU-baseline leg are the only callers; the GPU library and its
+Python binding never import this package.  The arithmetic lives in
+``oracle.c`` (plain C, double precision, token by token); this module only
+marshals NumPy arrays into it.  See the header of ``oracle.c`` for the pages
+and readings each function follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3}
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        subprocess.run(
+            ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+             "-Wall", "-o", tmp, _SRC, "-lm", "-lpthread"],
+            check=True,
+        )
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.oracle_round_bf16.restype = f64
+        lib.oracle_round_bf16.argtypes = [f64]
+        lib.oracle_round_bf16_array.restype = None
+        lib.oracle_round_bf16_array.argtypes = [P, P, i64]
+        lib.oracle_decode.restype = i32
+        lib.oracle_decode.argtypes = [i32, i32, i32, i32, i32, i64, i32, f64, i32,
+                                      P, P, P, P, P, P, P, P, P, i32]
+        lib.oracle_sequences.restype = i32
+        lib.oracle_sequences.argtypes = [i32, P, i32, i32, i32, i32, i64, i32, f64, i32,
+                                         P, P, P, P, P, P, P, P, P, i32]
+        lib.oracle_frontend.restype = i32
+        lib.oracle_frontend.argtypes = [i32, P, i32, i32, i32, i32, i32, f64,
+                                        P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_version.restype = i32
+        _lib = lib
+    return _lib
+
+
+def _f64(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _i32(a):
+    return None if a is None else np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _rule(rule):
+    return RULES[rule] if isinstance(rule, str) else int(rule)
+
+
+def default_threads() -> int:
+    return len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+
+
+def round_bf16(x):
+    """Nearest BF16 value of each element (ties to even), as float64."""
+    x = _f64(x)
+    out = np.empty_like(x)
+    _load().oracle_round_bf16_array(_p(x), _p(out), x.size)
+    return out
+
+
+def decode(q, k, v, g, beta, pool, read_slot=None, write_slot=None, *, rule="gated_delta",
+           scale=1.0, round_state=False, n_threads=None):
+    """One decode token for B requests.
+
+    q, k: [B, Hqk, dk]; v: [B, Hv, dv]; g, beta: [B, Hv]; pool: [n_slots, Hv,
+    dk, dv] (a float64 copy is updated and returned).  Returns
+    ``(o [B, Hv, dv], pool_after, code)``; code 1 means a request was skipped
+    because one of its slots was out of range.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    pool = _f64(pool).copy()
+    B, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    rs, ws = _i32(read_slot), _i32(write_slot)
+    o = np.zeros((B, Hv, dv), np.float64)
+    code = _load().oracle_decode(B, Hqk, Hv, dk, dv, pool.shape[0], _rule(rule), float(scale),
+                                 int(bool(round_state)), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                 _p(pool), _p(rs), _p(ws), _p(o),
+                                 n_threads or default_threads())
+    if code < 0:
+        raise ValueError("oracle_decode rejected its arguments")
+    return o, pool, code
+
+
+def sequences(cu_seqlens, q, k, v, g, beta, pool, read_slot=None, write_slot=None, *,
+              rule="gated_delta", scale=1.0, round_state=False, n_threads=None):
+    """Token-by-token recurrence over variable-length sequences.
+
+    cu_seqlens: [n_seq+1]; q, k: [N, Hqk, dk]; v: [N, Hv, dv]; g, beta:
+    [N, Hv]; pool: [n_slots, Hv, dk, dv].  Returns ``(o, pool_after, code)``.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    pool = _f64(pool).copy()
+    cu = _i32(cu_seqlens)
+    n_seq = cu.shape[0] - 1
+    N, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    rs, ws = _i32(read_slot), _i32(write_slot)
+    o = np.zeros((N, Hv, dv), np.float64)
+    code = _load().oracle_sequences(n_seq, _p(cu), Hqk, Hv, dk, dv, pool.shape[0], _rule(rule),
+                                    float(scale), int(bool(round_state)), _p(q), _p(k), _p(v),
+                                    _p(g), _p(beta), _p(pool), _p(rs), _p(ws), _p(o),
+                                    n_threads or default_threads())
+    if code < 0:
+        raise ValueError("oracle_sequences rejected its arguments")
+    return o, pool, code
+
+
+def frontend(cu_seqlens, q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw, *, Hqk, Hv, eps=1e-6):
+    """Causal depthwise conv + SiLU, L2 norm of q/k per head, gates.
+
+    q_raw, k_raw: [N, Hqk*dk]; v_raw: [N, Hv*dv]; w*: [channels, K];
+    a_raw, b_raw: [N, Hv].  Returns (q, k, v, g, beta) with q, k as
+    [N, Hqk, dk], v as [N, Hv, dv], g and beta as [N, Hv].
+    """
+    q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw = map(
+        _f64, (q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw))
+    cu = _i32(cu_seqlens)
+    N = q_raw.shape[0]
+    dk = q_raw.shape[1] // Hqk
+    dv = v_raw.shape[1] // Hv
+    K = wq.shape[1]
+    qo, ko, vo = np.zeros_like(q_raw), np.zeros_like(k_raw), np.zeros_like(v_raw)
+    g = np.zeros((N, Hv), np.float64)
+    beta = np.zeros((N, Hv), np.float64)
+    code = _load().oracle_frontend(cu.shape[0] - 1, _p(cu), Hqk, Hv, dk, dv, K, float(eps),
+                                   _p(q_raw), _p(k_raw), _p(v_raw), _p(wq), _p(wk), _p(wv),
+                                   _p(a_raw), _p(b_raw), _p(qo), _p(ko), _p(vo), _p(g), _p(beta))
+    if code != 0:
+        raise ValueError("oracle_frontend rejected its arguments")
+    return qo.reshape(N, Hqk, dk), ko.reshape(N, Hqk, dk), vo.reshape(N, Hv, dv), g, beta
