@@ -1,0 +1,215 @@
+/*
+ * gdn.h -- C ABI of an MI355X (gfx950) library for the Gated DeltaNet
+ * recurrent-state hot path: one-token decode over a batch of slot-indexed
+ * states, a fused causal-conv/SiLU/L2-norm/gate front-end, a chunked prefill
+ * over variable-length sequences, and a single launch that mixes the two.
+ *
+ * The operation (web pages, by title and section):
+ *  - "Gated DeltaNet" glossary entry, Technical definition: at each step the
+ *    per-head state is decayed by a gate, corrected by a rank-one delta-rule
+ *    term, and read out by the query.
+ *  - "Seven Architectures Replacing KV Cache With Bounded Mutable State",
+ *    Gated DeltaNet-2 section: S_t = a_t (I - beta_t k_t k_t^T) S_{t-1}
+ *    + beta_t k_t v_t^T once the gates are tied to scalars, with S of size
+ *    d_k x d_v; Kimi Linear section: the same update in residual form
+ *    S_t = a S + beta k (v - a S^T k)^T.
+ *  - Same article, ONNX LinearAttention / FlashInfer section: update_rule in
+ *    {linear, gated, delta, gated_delta} (default gated_delta), optional
+ *    past_state / present_state of shape (B, H_kv, d_k, d_v), grouped heads.
+ *  - "Recurrent state" glossary entry, Engineering details / Why it matters:
+ *    slots for the state, BF16 storage with FP32 compute, and separate read
+ *    (checkpoint) and write (live) slots for prefix caching.
+ *  - "Gated DeltaNet" glossary entry, Engineering details: Conv1D fused with
+ *    the layer.
+ *
+ * Conventions shared by every call:
+ *  - Every tensor argument is a DEVICE pointer to contiguous row-major memory
+ *    that the caller owns; the library never allocates, frees or
+ *    synchronises, keeps no global mutable state, and reads argument structs
+ *    only during the call.  All work is enqueued on `stream` (a hipStream_t;
+ *    NULL = the null stream).
+ *  - State tensors hold M = S with rows indexed by the key dimension:
+ *    pool[n_slots][H_v][d_k][d_v]; the output is o = scale * M_t^T q_t, read
+ *    after the token's update.  State head h uses q/k head
+ *    h / (H_v / H_qk) (contiguous groups); H_v must be a multiple of H_qk.
+ *  - Gates: g is the log of the decay (a = exp(g), g <= 0 normally) and beta
+ *    the write strength, one FP32 value per (token, state head).
+ *      linear:      M <- M + k v^T                    (g, beta ignored)
+ *      gated:       M <- a M + k v^T                  (beta ignored)
+ *      delta:       M <- (I - beta k k^T) M + beta k v^T  (g ignored)
+ *      gated_delta: M <- a (I - beta k k^T) M + beta k v^T
+ *  - Slots: past = pool[read_slot[r]], present = pool[write_slot[r]].  A read
+ *    index of -1 means a zero initial state, a write index of -1 means the
+ *    new state is not stored; a NULL index array means slot r for request r
+ *    (then n_slots must cover the batch).  An index outside [-1, n_slots)
+ *    makes the kernel skip that request (neither o nor the state is written
+ *    for it) and set GDN_DEVICE_BAD_SLOT in *status when status is non-NULL.
+ *  - Caller contract: write indices >= 0 are unique within a call, and no
+ *    request's write index equals another request's read index (a request
+ *    may read and write the same slot).  gdn_validate_slots checks this on
+ *    host copies.  Violations give undefined results, never out-of-bounds
+ *    accesses.
+ *  - Synchronous errors (bad pointer, shape, dtype, rule, workspace) return
+ *    a non-zero gdn_status and launch nothing; a failed launch returns
+ *    GDN_ERR_LAUNCH.
+ *  - Supported sizes: d_k, d_v in {16, 32, 64, 128}; chunk = 64; conv_k = 4.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum gdn_rule {
+  GDN_RULE_LINEAR = 0,
+  GDN_RULE_GATED = 1,
+  GDN_RULE_DELTA = 2,
+  GDN_RULE_GATED_DELTA = 3
+} gdn_rule;
+
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL = 1,        /* a required pointer is NULL */
+  GDN_ERR_SHAPE = 2,       /* a size is negative, zero where it must not be, or inconsistent */
+  GDN_ERR_DTYPE = 3,       /* unknown dtype code */
+  GDN_ERR_RULE = 4,        /* unknown update rule */
+  GDN_ERR_UNSUPPORTED = 5, /* a valid but unsupported size (d, chunk, conv width, head ratio) */
+  GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than gdn_prefill_workspace_size */
+  GDN_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
+  GDN_ERR_SLOTS = 8        /* gdn_validate_slots found a range error or a hazard */
+} gdn_status;
+
+/* bit set in the optional device status word when a request was skipped */
+#define GDN_DEVICE_BAD_SLOT 1u
+
+/* Decode: one token for each of B requests (the per-token recurrence of the
+ * "Gated DeltaNet" glossary entry, Technical definition; the residual /
+ * rearranged read-out of its Engineering details). */
+typedef struct gdn_decode_args {
+  int32_t B;           /* requests (>= 0; 0 launches nothing) */
+  int32_t H_qk;        /* q/k heads */
+  int32_t H_v;         /* state heads (the H_kv of the state shape), multiple of H_qk */
+  int32_t d_k, d_v;    /* state tile is d_k x d_v */
+  int32_t rule;        /* gdn_rule */
+  int32_t state_dtype; /* gdn_dtype of state_pool: BF16 storage with FP32 compute, or FP32 */
+  int32_t act_dtype;   /* gdn_dtype of q, k, v and o */
+  int64_t n_slots;     /* pool capacity in slots */
+  float scale;         /* read-out scale (1.0 for none) */
+  int32_t reserved0;   /* must be 0 */
+  const void *q;       /* [B, H_qk, d_k] act_dtype; normalised by the caller */
+  const void *k;       /* [B, H_qk, d_k] act_dtype */
+  const void *v;       /* [B, H_v, d_v] act_dtype */
+  const float *g;      /* [B, H_v] log-decay (unused by linear and delta; may be NULL then) */
+  const float *beta;   /* [B, H_v] write strength (unused by linear and gated; may be NULL then) */
+  void *state_pool;    /* [n_slots, H_v, d_k, d_v] state_dtype, read and written in place */
+  const int32_t *read_slot;  /* [B] or NULL */
+  const int32_t *write_slot; /* [B] or NULL */
+  void *o;             /* [B, H_v, d_v] act_dtype */
+  uint32_t *status;    /* optional device word; bits are OR-ed in, never cleared */
+} gdn_decode_args;
+
+/* Prefill: the same recurrence over n_seq variable-length sequences packed
+ * along the token axis, evaluated chunk by chunk (chunk = 64 tokens).  With
+ * use_frontend = 1 the inputs are raw projections: each channel goes through
+ * a causal depthwise conv of width conv_k (tap j multiplies x[t-conv_k+1+j],
+ * zero before a sequence's first token) and SiLU; q and k are then scaled to
+ * unit L2 norm per (token, head) as y / sqrt(sum y^2 + eps); g =
+ * -softplus(a_raw), beta = sigmoid(b_raw).  With use_frontend = 0, q/k/v and
+ * g/beta are used as given. */
+typedef struct gdn_prefill_args {
+  int32_t n_seq;       /* sequences (>= 0) */
+  int32_t H_qk, H_v, d_k, d_v;
+  int32_t rule, state_dtype, act_dtype;
+  int32_t use_frontend; /* 0 or 1 */
+  int32_t conv_k;      /* conv width; 4 (ignored when use_frontend = 0) */
+  int32_t chunk;       /* 64 */
+  int32_t reserved0;   /* must be 0 */
+  int64_t n_tokens;    /* total tokens = cu_seqlens[n_seq] */
+  int64_t n_slots;
+  float scale;         /* read-out scale */
+  float eps;           /* L2-norm epsilon (front-end only), e.g. 1e-6 */
+  const int32_t *cu_seqlens; /* [n_seq + 1] device, non-decreasing, cu[0] = 0, cu[n_seq] = n_tokens */
+  const void *q;       /* [n_tokens, H_qk * d_k] act_dtype (raw or final) */
+  const void *k;       /* [n_tokens, H_qk * d_k] act_dtype */
+  const void *v;       /* [n_tokens, H_v * d_v] act_dtype */
+  const float *g;      /* [n_tokens, H_v] log-decay when use_frontend = 0 */
+  const float *beta;   /* [n_tokens, H_v] write strength when use_frontend = 0 */
+  const float *a_raw;  /* [n_tokens, H_v] when use_frontend = 1: g = -softplus(a_raw) */
+  const float *b_raw;  /* [n_tokens, H_v] when use_frontend = 1: beta = sigmoid(b_raw) */
+  const float *conv_wq;  /* [H_qk * d_k, conv_k] when use_frontend = 1 */
+  const float *conv_wk;  /* [H_qk * d_k, conv_k] */
+  const float *conv_wv;  /* [H_v * d_v, conv_k] */
+  void *state_pool;    /* [n_slots, H_v, d_k, d_v] state_dtype */
+  const int32_t *read_slot;  /* [n_seq] or NULL: initial state (-1 = zero, a fresh request) */
+  const int32_t *write_slot; /* [n_seq] or NULL: final state (-1 = not stored) */
+  void *o;             /* [n_tokens, H_v, d_v] act_dtype */
+  void *workspace;     /* device scratch of gdn_prefill_workspace_size() bytes (may be NULL if 0) */
+  size_t workspace_bytes;
+  uint32_t *status;    /* optional device word */
+} gdn_prefill_args;
+
+/* Bytes of one slot (all H_v heads of one request, one layer).  The ONNX
+ * LinearAttention section of "Seven Architectures ..." sizes 64 heads of
+ * 128 x 128 at 16 bits as 2 MB per request. */
+size_t gdn_state_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t state_dtype);
+
+/* Workspace that gdn_prefill / gdn_mixed need for these arguments (host-only
+ * arithmetic on the sizes; no pointer is read). */
+size_t gdn_prefill_workspace_size(const gdn_prefill_args *args);
+
+/* "linear" | "gated" | "delta" | "gated_delta"; NULL or "" gives the default
+ * gated_delta (ONNX LinearAttention section).  Host-only. */
+gdn_status gdn_parse_rule(const char *name, int32_t *out_rule);
+
+/* One decode token for B requests: gather each request's state from its read
+ * slot, decay, apply the rank-one delta update in FP32, read out
+ * o = scale * M_t^T q_t, store the state (rounded to nearest-even BF16 when
+ * state_dtype is BF16) into its write slot. */
+gdn_status gdn_decode(const gdn_decode_args *args, void *stream);
+
+/* The front-end alone, for checking it in isolation (use_frontend must be 1):
+ * q_out, k_out [n_tokens, H_qk, d_k] and v_out [n_tokens, H_v, d_v] in
+ * act_dtype; g_out, beta_out [n_tokens, H_v] FP32.  No recurrence is run. */
+gdn_status gdn_frontend(const gdn_prefill_args *args, void *q_out, void *k_out, void *v_out,
+                        float *g_out, float *beta_out, void *stream);
+
+/* Chunked prefill: initial state from read_slot[s], outputs for every token,
+ * final state (FP32 across chunks, rounded once when stored as BF16) into
+ * write_slot[s]. */
+gdn_status gdn_prefill(const gdn_prefill_args *args, void *stream);
+
+/* A decode batch and a prefill batch in ONE kernel launch (each half has its
+ * own rule and slot arrays; they may share a pool).  The halves' results are
+ * those of gdn_decode and gdn_prefill called separately; either half may be
+ * empty (B = 0 or n_seq = 0).  The caller contract on slots applies across
+ * both halves. */
+gdn_status gdn_mixed(const gdn_decode_args *decode, const gdn_prefill_args *prefill,
+                     void *stream);
+
+/* Host-side check of the slot contract on host copies of the index arrays
+ * (NULL = identity): every index in [-1, n_slots), write indices >= 0
+ * unique, no write index equal to another request's read index.  Returns
+ * GDN_OK or GDN_ERR_SLOTS. */
+gdn_status gdn_validate_slots(const int32_t *host_read, const int32_t *host_write, int32_t n,
+                              int64_t n_slots);
+
+const char *gdn_status_string(int32_t status);
+int32_t gdn_abi_version(void);
+/* sizeof of the argument structs as compiled into the library, so that a
+ * binding can check its own layout */
+size_t gdn_sizeof_decode_args(void);
+size_t gdn_sizeof_prefill_args(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,11 @@
+"""MI355X (gfx950) Gated DeltaNet recurrent-state hot path.
+
+The compute lives in the HIP library ``libgdn.so`` (C ABI: include/gdn.h);
+``gdn`` is its thin ctypes binding and ``synthetic`` makes seeded inputs.
+Importing the package loads nothing; the first binding call loads the
+library and raises if it has not been built.
+"""
+from .gdn import (DecodeArgs, GdnError, PrefillArgs, gdn_abi_version, gdn_decode,  # noqa: F401
+                  gdn_frontend, gdn_mixed, gdn_parse_rule, gdn_prefill, gdn_state_bytes,
+                  gdn_status_string, gdn_validate_slots, load_library, make_decode_args,
+                  make_prefill_args)

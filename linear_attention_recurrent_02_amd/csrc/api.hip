@@ -1,0 +1,177 @@
+// api.hip -- the extern "C" entry points declared in include/gdn.h:
+// argument validation (host only, before any HIP call) and dispatch.
+#include <string.h>
+
+#include <new>
+
+#include "internal.h"
+
+namespace {
+
+bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool valid_dtype(int32_t t) { return t == GDN_F32 || t == GDN_BF16; }
+bool valid_rule(int32_t r) { return r >= GDN_RULE_LINEAR && r <= GDN_RULE_GATED_DELTA; }
+
+gdn_status check_heads(int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v) {
+  if (H_qk <= 0 || H_v <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
+  if (H_v % H_qk != 0) return GDN_ERR_UNSUPPORTED;  // q/k heads must group evenly
+  if (!supported_d(d_k) || !supported_d(d_v)) return GDN_ERR_UNSUPPORTED;
+  return GDN_OK;
+}
+
+gdn_status check_decode(const gdn_decode_args *a) {
+  if (!a) return GDN_ERR_NULL;
+  if (a->B < 0 || a->n_slots < 0) return GDN_ERR_SHAPE;
+  if (!valid_rule(a->rule)) return GDN_ERR_RULE;
+  if (!valid_dtype(a->state_dtype) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
+  if (a->reserved0 != 0) return GDN_ERR_UNSUPPORTED;
+  gdn_status st = check_heads(a->H_qk, a->H_v, a->d_k, a->d_v);
+  if (st != GDN_OK) return st;
+  if ((int64_t)a->B * a->H_v > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;  // grid size
+  if (a->B == 0) return GDN_OK;
+  if (!a->q || !a->k || !a->v || !a->state_pool || !a->o) return GDN_ERR_NULL;
+  if ((a->rule & gdn::kRuleDecay) && !a->g) return GDN_ERR_NULL;
+  if ((a->rule & gdn::kRuleErase) && !a->beta) return GDN_ERR_NULL;
+  if ((!a->read_slot || !a->write_slot) && a->n_slots < a->B) return GDN_ERR_SHAPE;
+  return GDN_OK;
+}
+
+// need_state: the recurrence runs (pool, outputs, slots, workspace are used);
+// false for the stand-alone front-end, which reads only the inputs.
+gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
+  if (!a) return GDN_ERR_NULL;
+  if (a->n_seq < 0 || a->n_tokens < 0 || a->n_slots < 0) return GDN_ERR_SHAPE;
+  if (!valid_rule(a->rule)) return GDN_ERR_RULE;
+  if (!valid_dtype(a->state_dtype) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
+  if (a->reserved0 != 0) return GDN_ERR_UNSUPPORTED;
+  if (a->use_frontend != 0 && a->use_frontend != 1) return GDN_ERR_UNSUPPORTED;
+  gdn_status st = check_heads(a->H_qk, a->H_v, a->d_k, a->d_v);
+  if (st != GDN_OK) return st;
+  if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;
+  if (a->use_frontend && a->conv_k != 4) return GDN_ERR_UNSUPPORTED;
+  if (a->use_frontend && !(a->eps >= 0.0f)) return GDN_ERR_SHAPE;
+  if ((int64_t)a->n_seq * a->H_v > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;
+  if (a->n_tokens > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;  // token index fits int32
+  if (a->n_seq == 0) return a->n_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;
+  if (!a->cu_seqlens) return GDN_ERR_NULL;
+  if (need_state && !a->state_pool) return GDN_ERR_NULL;
+  if (a->n_tokens > 0 && (!a->q || !a->k || !a->v)) return GDN_ERR_NULL;
+  if (need_state && a->n_tokens > 0 && !a->o) return GDN_ERR_NULL;
+  if (a->n_tokens > 0) {
+    if (a->use_frontend) {
+      if (!a->conv_wq || !a->conv_wk || !a->conv_wv) return GDN_ERR_NULL;
+      if ((a->rule & gdn::kRuleDecay) && !a->a_raw) return GDN_ERR_NULL;
+      if ((a->rule & gdn::kRuleErase) && !a->b_raw) return GDN_ERR_NULL;
+    } else {
+      if ((a->rule & gdn::kRuleDecay) && !a->g) return GDN_ERR_NULL;
+      if ((a->rule & gdn::kRuleErase) && !a->beta) return GDN_ERR_NULL;
+    }
+  }
+  if (!need_state) return GDN_OK;
+  if ((!a->read_slot || !a->write_slot) && a->n_slots < a->n_seq) return GDN_ERR_SHAPE;
+  const size_t need = gdn::prefill_workspace_bytes(*a);
+  if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return GDN_ERR_WORKSPACE;
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t gdn_state_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t state_dtype) {
+  if (H_v <= 0 || d_k <= 0 || d_v <= 0 || !valid_dtype(state_dtype)) return 0;
+  return (size_t)H_v * (size_t)d_k * (size_t)d_v * (state_dtype == GDN_BF16 ? 2u : 4u);
+}
+
+size_t gdn_prefill_workspace_size(const gdn_prefill_args *args) {
+  return args ? gdn::prefill_workspace_bytes(*args) : 0;
+}
+
+gdn_status gdn_parse_rule(const char *name, int32_t *out_rule) {
+  if (!out_rule) return GDN_ERR_NULL;
+  if (!name || !*name || !strcmp(name, "gated_delta")) { *out_rule = GDN_RULE_GATED_DELTA; return GDN_OK; }
+  if (!strcmp(name, "linear")) { *out_rule = GDN_RULE_LINEAR; return GDN_OK; }
+  if (!strcmp(name, "gated")) { *out_rule = GDN_RULE_GATED; return GDN_OK; }
+  if (!strcmp(name, "delta")) { *out_rule = GDN_RULE_DELTA; return GDN_OK; }
+  return GDN_ERR_RULE;
+}
+
+gdn_status gdn_decode(const gdn_decode_args *args, void *stream) {
+  gdn_status st = check_decode(args);
+  if (st != GDN_OK || args->B == 0) return st;
+  return gdn::launch_decode(*args, static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_frontend(const gdn_prefill_args *args, void *q_out, void *k_out, void *v_out,
+                        float *g_out, float *beta_out, void *stream) {
+  gdn_status st = check_prefill(args, false);
+  if (st != GDN_OK) return st;
+  if (!args->use_frontend) return GDN_ERR_UNSUPPORTED;
+  if (args->n_seq == 0 || args->n_tokens == 0) return GDN_OK;
+  if (!q_out || !k_out || !v_out || !g_out || !beta_out) return GDN_ERR_NULL;
+  if (!args->a_raw || !args->b_raw) return GDN_ERR_NULL;
+  return gdn::launch_frontend(*args, q_out, k_out, v_out, g_out, beta_out,
+                              static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_prefill(const gdn_prefill_args *args, void *stream) {
+  gdn_status st = check_prefill(args, true);
+  if (st != GDN_OK || args->n_seq == 0) return st;
+  return gdn::launch_prefill(*args, static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_mixed(const gdn_decode_args *decode, const gdn_prefill_args *prefill,
+                     void *stream) {
+  gdn_status st = check_decode(decode);
+  if (st != GDN_OK) return st;
+  st = check_prefill(prefill, true);
+  if (st != GDN_OK) return st;
+  if (decode->B == 0 && prefill->n_seq == 0) return GDN_OK;
+  return gdn::launch_mixed(*decode, *prefill, static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_validate_slots(const int32_t *host_read, const int32_t *host_write, int32_t n,
+                              int64_t n_slots) {
+  if (n < 0 || n_slots < 0) return GDN_ERR_SHAPE;
+  if ((!host_read || !host_write) && n_slots < n) return GDN_ERR_SLOTS;
+  // per slot: which request writes it (-1 none), and a count of its readers
+  int32_t *writer = new (std::nothrow) int32_t[n_slots > 0 ? n_slots : 1];
+  if (!writer) return GDN_ERR_SHAPE;
+  for (int64_t s = 0; s < n_slots; ++s) writer[s] = -1;
+  gdn_status st = GDN_OK;
+  for (int32_t r = 0; r < n && st == GDN_OK; ++r) {
+    const int64_t rs = host_read ? host_read[r] : r, ws = host_write ? host_write[r] : r;
+    if (rs < -1 || rs >= n_slots || ws < -1 || ws >= n_slots) st = GDN_ERR_SLOTS;
+    else if (ws >= 0) {
+      if (writer[ws] != -1) st = GDN_ERR_SLOTS;  // two requests write one slot
+      else writer[ws] = r;
+    }
+  }
+  for (int32_t r = 0; r < n && st == GDN_OK; ++r) {
+    const int64_t rs = host_read ? host_read[r] : r;
+    if (rs >= 0 && writer[rs] != -1 && writer[rs] != r) st = GDN_ERR_SLOTS;  // read-after-write hazard
+  }
+  delete[] writer;
+  return st;
+}
+
+const char *gdn_status_string(int32_t status) {
+  switch (status) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL: return "a required pointer is NULL";
+    case GDN_ERR_SHAPE: return "invalid or inconsistent sizes";
+    case GDN_ERR_DTYPE: return "unknown dtype";
+    case GDN_ERR_RULE: return "unknown update rule";
+    case GDN_ERR_UNSUPPORTED: return "unsupported size or option";
+    case GDN_ERR_WORKSPACE: return "workspace missing or too small";
+    case GDN_ERR_LAUNCH: return "kernel launch failed";
+    case GDN_ERR_SLOTS: return "slot index out of range or slot hazard";
+  }
+  return "unknown status";
+}
+
+int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
+size_t gdn_sizeof_decode_args(void) { return sizeof(gdn_decode_args); }
+size_t gdn_sizeof_prefill_args(void) { return sizeof(gdn_prefill_args); }
+
+}  // extern "C"

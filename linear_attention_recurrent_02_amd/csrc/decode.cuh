@@ -1,0 +1,333 @@
+// decode.cuh -- the decode state-update tile: one (request, state head) pair.
+//
+// Per tile the state M (d_k x d_v, rows = key index) is read once from its
+// read slot, kept in registers, updated and written once to its write slot:
+//
+//   u = M^T k,  w = M^T q,  kq = k . q        (reductions over the d_k rows)
+//   delta = bw * (v - c * a * u)             (c = 1 for the delta rules)
+//   o     = scale * (a * w + kq * delta)     (= scale * M'^T q)
+//   M'    = a * M + k delta^T
+//
+// This is the residual form of the update given in the Kimi Linear section of
+// "Seven Architectures Replacing KV Cache With Bounded Mutable State" with a
+// scalar decay (which the Gated DeltaNet-2 section says is Gated DeltaNet),
+// and the read-out is the rearrangement in the "Gated DeltaNet" glossary
+// entry, Engineering details: the decayed old state read by the query plus,
+// for the current token, a per-head scalar (k . q) times a small vector.  The
+// read-out therefore never waits for the new state.
+//
+// Work split (gfx950, wave64): every column j of the update is independent
+// given k, q and v, so a lane owns VEC consecutive columns (one 16-byte
+// vector per row) and RPT consecutive rows; LPR lanes cover one row, so each
+// wave-wide load instruction moves whole contiguous 256-byte rows.  The only
+// cross-lane work is the sum over rows: a butterfly across the lanes of a
+// wave that share columns, then NW partials through LDS.
+#pragma once
+
+#include "device.h"
+#include "internal.h"
+
+// Tuning knobs (compile-time): workgroup size cap for the decode tile, and
+// whether the state stream uses non-temporal loads/stores (each state byte is
+// touched exactly once per call, so there is nothing to keep in cache).
+#ifndef GDN_DECODE_MAX_THREADS
+#define GDN_DECODE_MAX_THREADS 256
+#endif
+// Software pipelining of the persistent loop (next tile's loads in flight
+// during this tile's reduction and store).  Off by default: on MI355X the
+// extra registers cost more occupancy than the overlap gains (measured
+// 196 us vs 191 us per B=512 layer).
+#ifndef GDN_DECODE_PIPELINE
+#define GDN_DECODE_PIPELINE 0
+#endif
+#ifndef GDN_DECODE_NONTEMPORAL
+#define GDN_DECODE_NONTEMPORAL 1
+#endif
+
+namespace gdn {
+
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 stream_load(const uint4 *p) {
+#if GDN_DECODE_NONTEMPORAL
+  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+#else
+  return *p;
+#endif
+}
+__device__ __forceinline__ void stream_store(uint4 *p, const uint4 &v) {
+#if GDN_DECODE_NONTEMPORAL
+  u32x4_t w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
+#else
+  *p = v;
+#endif
+}
+
+struct DecodeParams {
+  int32_t B, H_qk, H_v, group;  // group = H_v / H_qk
+  int64_t n_slots;
+  float scale;
+  int32_t rule;
+  const void *q, *k, *v;
+  const float *g, *beta;
+  void *pool;
+  const int32_t *read_slot, *write_slot;
+  void *o;
+  uint32_t *status;
+};
+
+template <bool SB, int DK, int DV, int NT>
+struct DecodeShape {
+  static constexpr int VEC = Elem<SB>::kPer16B;  // state elements per 16-byte vector
+  static constexpr int LPR = DV / VEC;           // lanes per state row
+  static_assert(DV % VEC == 0 && LPR >= 1 && LPR <= 64 && (64 % LPR) == 0, "bad d_v");
+  static constexpr int RG = NT / LPR;            // row groups in the workgroup
+  static constexpr int RPT = (DK + RG - 1) / RG; // rows per thread
+  static constexpr int NW = NT / 64;             // waves
+  static constexpr int LDS_FLOATS = (NW + 1) * (2 * DV + 1);
+  // every row group owns rows (true unless the tile is tiny)
+  static constexpr bool ALL_LIVE = RG * RPT == DK;
+};
+
+// Registers of one (request, state head) tile between its two phases.  When
+// the thread's runs of k, q (RPT rows) and v (VEC columns) are whole 16-byte
+// vectors they are kept packed as loaded (half the registers for BF16) and
+// unpacked in phase 2.
+template <bool SB, bool AB, int DK, int DV, int NT>
+struct DecodeTileRegs {
+  using S = DecodeShape<SB, DK, DV, NT>;
+  static constexpr int AV = Elem<AB>::kPer16B;  // activation elements per 16 bytes
+  static constexpr bool PACKED =
+      S::ALL_LIVE && DK % S::RPT == 0 && S::RPT % AV == 0 && S::VEC % AV == 0;
+  static constexpr int KN = PACKED ? S::RPT / AV : 1;
+  static constexpr int VN = PACKED ? S::VEC / AV : 1;
+  uint4 m[S::RPT];                  // the packed state rows of this thread
+  uint4 kp[KN], qp[KN], vp[VN];     // packed k, q, v (PACKED)
+  float kr[PACKED ? 1 : S::RPT], qr[PACKED ? 1 : S::RPT], vv[PACKED ? 1 : S::VEC];
+  float a, bw;                      // decay and write strength
+  int64_t r, ws;                    // request, write slot
+  int h;
+  bool valid;                       // false: a bad slot (the tile is skipped)
+};
+
+// Phase 1 of a tile: resolve the slots (a1) and issue every load -- this
+// token's q, k, v first, then the state tile -- without waiting for any of
+// them, so the caller can overlap them with the previous tile's phase 2.  All
+// NT threads of the workgroup call it with the same (r, h).
+template <bool SB, bool AB, int DK, int DV, int NT>
+__device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t r, int h,
+                                                 DecodeTileRegs<SB, AB, DK, DV, NT> &t) {
+  using S = DecodeShape<SB, DK, DV, NT>;
+  constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT;
+  constexpr bool ALL_LIVE = S::ALL_LIVE;
+  using SE = Elem<SB>;
+  const int tid = threadIdx.x;
+  const int cv = tid % LPR;  // column vector: columns [cv*VEC, cv*VEC + VEC)
+  const int row0 = (tid / LPR) * RPT;  // rows [row0, row0 + RPT)
+
+  t.r = r;
+  t.h = h;
+  const int64_t rs = p.read_slot ? (int64_t)p.read_slot[r] : r;
+  t.ws = p.write_slot ? (int64_t)p.write_slot[r] : r;
+  t.valid = !(rs < -1 || rs >= p.n_slots || t.ws < -1 || t.ws >= p.n_slots);
+  if (!t.valid) {
+    if (tid == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+    return;
+  }
+  const int hq = h / p.group;
+  constexpr int64_t TILE = (int64_t)DK * DV;
+
+  // this token's q, k (rows of this thread), v (its columns); issued before
+  // the state tile: loads return in order, so waiting for these leaves the
+  // state loads in flight
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT>;
+  using AT = typename Elem<AB>::T;
+  if constexpr (Regs::PACKED) {
+    const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.k) +
+                                                      (r * p.H_qk + hq) * DK + row0);
+    const uint4 *qp = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.q) +
+                                                      (r * p.H_qk + hq) * DK + row0);
+    const uint4 *vp = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.v) +
+                                                      (r * p.H_v + h) * DV + cv * VEC);
+#pragma unroll
+    for (int j = 0; j < Regs::KN; ++j) { t.kp[j] = kp[j]; t.qp[j] = qp[j]; }
+#pragma unroll
+    for (int j = 0; j < Regs::VN; ++j) t.vp[j] = vp[j];
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const bool ok = row0 + i < DK;
+      t.kr[i] = ok ? Elem<AB>::load1(p.k, (r * p.H_qk + hq) * DK + row0 + i) : 0.f;
+      t.qr[i] = ok ? Elem<AB>::load1(p.q, (r * p.H_qk + hq) * DK + row0 + i) : 0.f;
+    }
+    load_run<AB, VEC>(p.v, (r * p.H_v + h) * DV + cv * VEC, t.vv);
+  }
+
+  // the state tile: RPT 16-byte vectors per thread (a1)
+  if (rs >= 0) {
+    const uint4 *src = reinterpret_cast<const uint4 *>(
+        static_cast<const typename SE::T *>(p.pool) + ((rs * p.H_v + h) * TILE));
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      if (ALL_LIVE || row0 + i < DK) t.m[i] = stream_load(src + (int64_t)(row0 + i) * LPR + cv);
+      else t.m[i] = make_uint4(0u, 0u, 0u, 0u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) t.m[i] = make_uint4(0u, 0u, 0u, 0u);
+  }
+  const bool decay = (p.rule & kRuleDecay) != 0;
+  const bool erase = (p.rule & kRuleErase) != 0;
+  t.a = decay ? expf(p.g[r * p.H_v + h]) : 1.0f;
+  t.bw = erase ? p.beta[r * p.H_v + h] : 1.0f;
+}
+
+// Phase 2 of a tile: the reductions over rows, the read-out (a4), the update
+// and the store to the write slot (a5).  `red` is LDS of
+// DecodeShape::LDS_FLOATS floats.  For NW > 1 it has three barriers (the last
+// lets the caller reuse `red`); a skipped tile has none, uniformly.
+template <bool SB, bool AB, int DK, int DV, int NT>
+__device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
+                                                   DecodeTileRegs<SB, AB, DK, DV, NT> &t,
+                                                   float *red) {
+  using S = DecodeShape<SB, DK, DV, NT>;
+  constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT, NW = S::NW;
+  constexpr bool ALL_LIVE = S::ALL_LIVE;
+  using SE = Elem<SB>;
+  if (!t.valid) return;
+  const int tid = threadIdx.x;
+  const int cv = tid % LPR;
+  const int row0 = (tid / LPR) * RPT;
+  const bool rows_live = ALL_LIVE || row0 < DK;
+  const bool erase = (p.rule & kRuleErase) != 0;
+  const float a = t.a;
+  const int64_t r = t.r;
+  const int h = t.h;
+  constexpr int64_t TILE = (int64_t)DK * DV;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT>;
+  float kr[RPT], qr[RPT], vv[VEC];
+  if constexpr (Regs::PACKED) {
+#pragma unroll
+    for (int j = 0; j < Regs::KN; ++j) {
+      Elem<AB>::unpack(t.kp[j], kr + j * Regs::AV);
+      Elem<AB>::unpack(t.qp[j], qr + j * Regs::AV);
+    }
+#pragma unroll
+    for (int j = 0; j < Regs::VN; ++j) Elem<AB>::unpack(t.vp[j], vv + j * Regs::AV);
+  } else {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) { kr[i] = t.kr[i]; qr[i] = t.qr[i]; }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) vv[e] = t.vv[e];
+  }
+
+  // ---- partial reductions over this thread's rows ----
+  float u[VEC], w[VEC];
+  float kq = 0.f;
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) u[e] = w[e] = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    float f[VEC];
+    SE::unpack(t.m[i], f);
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      u[e] = fmaf(f[e], kr[i], u[e]);
+      w[e] = fmaf(f[e], qr[i], w[e]);
+    }
+    kq = fmaf(kr[i], qr[i], kq);
+  }
+  // butterfly over the lanes of this wave that share column vector cv
+#pragma unroll
+  for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      u[e] += __shfl_xor(u[e], off);
+      w[e] += __shfl_xor(w[e], off);
+    }
+    kq += __shfl_xor(kq, off);
+  }
+  const int lane = tid & 63, wave = tid >> 6;
+  if constexpr (NW > 1) {
+    // two levels through LDS: each wave's totals, then thread j sums value j
+    // over the waves, then every thread reads back only what it needs
+    constexpr int NV = 2 * DV + 1;  // u[0..DV), w[0..DV), kq
+    float *mine = red + wave * NV;
+    if (lane < LPR) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        mine[cv * VEC + e] = u[e];
+        mine[DV + cv * VEC + e] = w[e];
+      }
+      if (lane == 0) mine[2 * DV] = kq;
+    }
+    __syncthreads();
+    float *tot = red + NW * NV;
+    for (int j = tid; j < NV; j += NT) {
+      float sum = 0.f;
+#pragma unroll
+      for (int wv = 0; wv < NW; ++wv) sum += red[wv * NV + j];
+      tot[j] = sum;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) u[e] = tot[cv * VEC + e];
+    if (tid < LPR) {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) w[e] = tot[DV + cv * VEC + e];
+      kq = tot[2 * DV];
+    }
+  }
+  // keep the tile packed across the reduction instead of holding it unpacked
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) opaque(t.m[i]);
+
+  // ---- delta, read-out (a4) ----
+  float d[VEC];
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) d[e] = erase ? t.bw * (vv[e] - a * u[e]) : vv[e];
+  if (tid < LPR) {
+    float o[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) o[e] = p.scale * fmaf(a, w[e], kq * d[e]);
+    store_run<AB, VEC>(p.o, (r * p.H_v + h) * DV + cv * VEC, o);
+  }
+
+  // ---- update and scatter to the write slot (a5) ----
+  if (t.ws >= 0 && rows_live) {
+    uint4 *dst = reinterpret_cast<uint4 *>(static_cast<typename SE::T *>(p.pool) +
+                                           ((t.ws * p.H_v + h) * TILE));
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      if (!ALL_LIVE && row0 + i >= DK) continue;
+      float f[VEC];
+      SE::unpack(t.m[i], f);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) f[e] = fmaf(kr[i], d[e], a * f[e]);
+      stream_store(dst + (int64_t)(row0 + i) * LPR + cv, SE::pack(f));
+    }
+  }
+  if constexpr (NW > 1) __syncthreads();  // `red` may be reused by the next tile
+}
+
+// One whole tile (both phases, no overlap).
+template <bool SB, bool AB, int DK, int DV, int NT>
+__device__ __forceinline__ void decode_tile(const DecodeParams &p, int64_t r, int h, float *red) {
+  DecodeTileRegs<SB, AB, DK, DV, NT> t;
+  decode_tile_load<SB, AB, DK, DV, NT>(p, r, h, t);
+  decode_tile_finish<SB, AB, DK, DV, NT>(p, t, red);
+}
+
+// Threads per workgroup for a (state dtype, d_k, d_v) instance: enough lanes
+// for every row group to own at least one row, at most 256.
+template <bool SB, int DK, int DV>
+constexpr int decode_threads() {
+  constexpr int lpr = DV / Elem<SB>::kPer16B;
+  constexpr int full = lpr * DK;  // one row per thread
+  constexpr int cap = GDN_DECODE_MAX_THREADS;
+  return full >= cap ? cap : (full <= 64 ? 64 : full);
+}
+
+}  // namespace gdn

@@ -1,0 +1,23 @@
+// internal.h -- launchers behind the C ABI.  Arguments have been validated by
+// the API layer before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// rule bits: bit 0 = the state decays by a = exp(g), bit 1 = delta-rule erase
+// with write strength beta (linear = 0, gated = 1, delta = 2, gated_delta = 3)
+constexpr int kRuleDecay = 1;
+constexpr int kRuleErase = 2;
+
+gdn_status launch_decode(const gdn_decode_args &a, hipStream_t stream);
+gdn_status launch_frontend(const gdn_prefill_args &a, void *q_out, void *k_out, void *v_out,
+                           float *g_out, float *beta_out, hipStream_t stream);
+gdn_status launch_prefill(const gdn_prefill_args &a, hipStream_t stream);
+gdn_status launch_mixed(const gdn_decode_args &d, const gdn_prefill_args &p, hipStream_t stream);
+size_t prefill_workspace_bytes(const gdn_prefill_args &a);
+
+}  // namespace gdn

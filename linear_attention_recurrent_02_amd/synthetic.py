@@ -96,10 +96,12 @@ def state_pool(wl: int, layer: int, n_slots: int, H_v: int, d_k: int, d_v: int,
         gen = torch.Generator(device="cuda")
         gen.manual_seed(1_000_003 * (int(wl) + 1) + 7919 * int(layer) + 17)
         out = torch.empty(shape, dtype=state_dtype, device="cuda")
-        flat = out.view(n_slots, -1)
-        for s in range(n_slots):  # slot by slot keeps the float32 temporary small
-            flat[s] = (torch.randn(flat.shape[1], generator=gen, device="cuda",
-                                   dtype=torch.float32) * std).to(state_dtype)
+        flat = out.view(-1)
+        step = 1 << 26  # float32 temporary of at most 256 MiB
+        for s in range(0, flat.numel(), step):
+            e = min(flat.numel(), s + step)
+            flat[s:e] = (torch.randn(e - s, generator=gen, device="cuda", dtype=torch.float32)
+                         * std).to(state_dtype)
         return out
     a = rng(wl, layer, _S_STATE).standard_normal(shape) * std
     return _cast(a, state_dtype)
