@@ -42,3 +42,18 @@ def scaled_err(x, r, lead: int) -> float:
 def tol(*dtypes) -> float:
     """1e-4 when every tensor that feeds the compared value is FP32, else 2e-2."""
     return TOL_BF16 if any(d == torch.bfloat16 for d in dtypes) else TOL_F32
+
+
+def seq_err(x, r, cu) -> float:
+    """Scaled max error per (sequence, head) slice of a [N, H, d] prefill output:
+    max over sequences s and heads h of max|x - r| / max|r| over the tokens of s."""
+    x = np.asarray(x, np.float64)
+    r = np.asarray(r, np.float64)
+    assert x.shape == r.shape, (x.shape, r.shape)
+    cu = np.asarray(cu, np.int64)
+    worst = 0.0
+    for s in range(len(cu) - 1):
+        a, b = cu[s], cu[s + 1]
+        if b > a:
+            worst = max(worst, scaled_err(x[a:b].transpose(1, 0, 2), r[a:b].transpose(1, 0, 2), 1))
+    return worst
