@@ -68,6 +68,8 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
     }
   }
   if (!need_state) return GDN_OK;
+  // FP32 activations keep FP32 MFMA operands in LDS, which fits d_k, d_v <= 64
+  if (a->act_dtype == GDN_F32 && (a->d_k > 64 || a->d_v > 64)) return GDN_ERR_UNSUPPORTED;
   if ((!a->read_slot || !a->write_slot) && a->n_slots < a->n_seq) return GDN_ERR_SHAPE;
   const size_t need = gdn::prefill_workspace_bytes(*a);
   if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return GDN_ERR_WORKSPACE;

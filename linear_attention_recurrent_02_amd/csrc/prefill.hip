@@ -459,16 +459,8 @@ size_t prefill_workspace_bytes(const gdn_prefill_args &a) {
   return fe_workspace(a).bytes;
 }
 
-static gdn_status prefill_supported(const gdn_prefill_args &a) {
-  // FP32 activations keep FP32 operands in LDS: the tile has to fit in the
-  // 160 KiB of LDS (d_k, d_v <= 64)
-  if (a.act_dtype == GDN_F32 && (a.d_k > 64 || a.d_v > 64)) return GDN_ERR_UNSUPPORTED;
-  return GDN_OK;
-}
-
 gdn_status launch_prefill(const gdn_prefill_args &a, hipStream_t stream) {
-  gdn_status st = prefill_supported(a);
-  if (st != GDN_OK) return st;
+  gdn_status st = GDN_OK;
   const void *q = a.q, *k = a.k, *v = a.v;
   const float *g = a.g, *beta = a.beta;
   if (a.use_frontend && a.n_tokens > 0) {

@@ -115,12 +115,34 @@ def _prefill_args(**over):
     (dict(rule=9), RULE), (dict(act_dtype=3), DTYPE), (dict(n_seq=-1), SHAPE),
     (dict(n_seq=0), SHAPE), (dict(eps=-1.0), SHAPE), (dict(cu_seqlens=None), NULL),
     (dict(conv_wk=None), NULL), (dict(a_raw=None), NULL), (dict(state_pool=None), NULL),
-    (dict(H_v=6), UNSUP), (dict(d_v=96), UNSUP), (dict(n_slots=1), SHAPE),
+    (dict(H_v=5), UNSUP), (dict(d_v=96), UNSUP), (dict(n_slots=1), SHAPE),
+    (dict(), WORKSPACE),  # the fused front-end needs gdn_prefill_workspace_size() bytes
 ])
 def test_prefill_validation(over, code):
     lib = gdn.load_library()
     a = _prefill_args(**over)
     assert lib.gdn_prefill(ctypes.byref(a), None) == code
+
+
+def test_prefill_workspace_size():
+    lib = gdn.load_library()
+    a = _prefill_args()
+    need = lib.gdn_prefill_workspace_size(ctypes.byref(a))
+    # q, k, v of 100 tokens in BF16 plus g, beta in FP32, 256-byte aligned segments
+    assert need >= 100 * (2 * 2 * 128 + 4 * 128) * 2 + 2 * 100 * 4 * 4
+    a.workspace, a.workspace_bytes = FAKE, need - 1
+    assert lib.gdn_prefill(ctypes.byref(a), None) == WORKSPACE
+    a.use_frontend = 0
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(a)) == 0
+
+
+def test_prefill_fp32_needs_small_heads():
+    lib = gdn.load_library()
+    # FP32 activations keep FP32 MFMA operands in LDS: d_k, d_v <= 64 only
+    a = _prefill_args(act_dtype=0, use_frontend=0)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == UNSUP
+    a = _prefill_args(act_dtype=0, use_frontend=0, d_k=64, d_v=128)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == UNSUP
 
 
 def test_prefill_conv_width_ignored_without_frontend_and_empty_batch():
