@@ -129,6 +129,86 @@ def run_decode(args, torch, gdn, syn):
     return res, layers
 
 
+PREFILL_FLOPS_PER_TOKEN_HEAD = None  # computed from the chunk algebra below
+
+
+def prefill_useful_flops(lengths, H_v, d_k, d_v, C=64):
+    """Useful flops of the chunked recurrence (per chunk of n tokens and head):
+    K K^T and Q K^T (lower triangle incl. diagonal), the triangular solve,
+    U = T R, K M, Q M, (L o Q K^T) U and K~^T U."""
+    total = 0
+    for T in lengths:
+        full, tail = divmod(int(T), C)
+        for n in [C] * full + ([tail] if tail else []):
+            tri = n * (n + 1) // 2
+            f = 2 * tri * d_k * 2            # K K^T, Q K^T
+            f += n * n * n // 3              # (I + A)^-1, forward substitution
+            f += 2 * tri * d_v               # U = T R (T lower triangular)
+            f += 2 * 2 * n * d_k * d_v       # K M, Q M
+            f += 2 * tri * d_v               # (L o Q K^T) U
+            f += 2 * n * d_k * d_v           # K~^T U
+            total += f
+    return total * H_v
+
+
+def run_prefill(args, torch, gdn, syn):
+    """Chunked prefill of 8 ragged sequences (1024..8192 tokens, seeded) with
+    the fused front-end, H_qk=16, H_v=32, d=128, BF16, fresh requests whose
+    final states go to 8 checkpoint slots of a 64-slot pool."""
+    import numpy as np
+    wl = syn.WORKLOADS["prefill_varlen"]
+    Hqk, Hv, d = wl["H_qk"], wl["H_v"], wl["d_k"]
+    lengths = syn.seq_lengths(wl["index"], 0, wl["n_seq"], wl["min_len"], wl["max_len"])
+    cu = syn.cu_from_lengths(lengths).cuda()
+    N = int(lengths.sum())
+    x = {k: v.cuda() for k, v in syn.frontend_inputs(wl["index"], 0, N, Hqk, Hv, d, d, 4).items()}
+    pool = torch.zeros((wl["n_slots"], Hv, d, d), dtype=torch.bfloat16, device="cuda")
+    rs = torch.full((len(lengths),), -1, dtype=torch.int32, device="cuda")
+    ws = torch.from_numpy(np.random.default_rng(3).permutation(wl["n_slots"])[:len(lengths)]
+                          .astype(np.int32)).cuda()
+    a, o, keep = gdn.make_prefill_args(cu, x["q_raw"], x["k_raw"], x["v_raw"], pool, rs, ws,
+                                       H_qk=Hqk, H_v=Hv, a_raw=x["a_raw"], b_raw=x["b_raw"],
+                                       conv_wq=x["conv_wq"], conv_wk=x["conv_wk"],
+                                       conv_wv=x["conv_wv"])
+    lib = gdn.load_library()
+    s = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def step():
+        code = lib.gdn_prefill(ctypes.byref(a), s())
+        if code:
+            raise gdn.GdnError("gdn_prefill", code)
+
+    def fe_only():
+        gdn.gdn_frontend(cu, x["q_raw"], x["k_raw"], x["v_raw"], H_qk=Hqk, H_v=Hv,
+                         conv_wq=x["conv_wq"], conv_wk=x["conv_wk"], conv_wv=x["conv_wv"],
+                         a_raw=x["a_raw"], b_raw=x["b_raw"])
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(step, args.prefill_reps)
+    ms_fe = timed(fe_only, args.prefill_reps)
+    flops = prefill_useful_flops(lengths, Hv, d, d)
+    algo_bytes = N * ((2 * Hqk * d + Hv * d) * 2 + Hv * d * 2 + 2 * Hv * 4) + len(lengths) * Hv * d * d * 2
+    return dict(workload="prefill_varlen", tokens=N, lengths=[int(v) for v in lengths],
+                ms=round(ms, 3), tokens_per_s=round(N / (ms / 1e3), 1),
+                frontend_ms=round(ms_fe, 3),
+                useful_tflops=round(flops / (ms / 1e3) / 1e12, 2),
+                mfma_frac=round(flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                algorithmic_GBps=round(algo_bytes / (ms / 1e3) / 1e9, 1),
+                hbm_frac=round(algo_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                longest_chain_chunks=int((max(lengths) + 63) // 64))
+
+
 def run_cpu_baseline(args, torch, layers, syn):
     """The FP64 oracle on layers 0 and L-1 at full batch (every request-head),
     timed on this host's cores; tokens/s extrapolated to all layers."""
@@ -164,6 +244,8 @@ def main():
     ap.add_argument("--layers", type=int, default=48)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--prefill-reps", type=int, default=10)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a device copy of known size (for counter calibration)")
     args = ap.parse_args()
@@ -205,6 +287,12 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(args, torch, layers, syn)
+    prefill = None
+    if not args.no_prefill:
+        del layers[:]
+        torch.cuda.empty_cache()
+        prefill = run_prefill(args, torch, gdn, syn)
+        log(f"prefill: {prefill}")
     out = {
         "metric": METRIC,
         "value": round(dec["tokens_per_s"], 1),
@@ -227,6 +315,7 @@ def main():
         "hbm_frac": round(dec["total_GBps"] / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "prefill": prefill,
     }
     print(json.dumps(out), flush=True)
 

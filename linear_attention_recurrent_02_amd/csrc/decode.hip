@@ -9,10 +9,6 @@
 
 namespace gdn {
 
-// Slot ordering is used when the batch's order and the slot bitmap fit in a
-// few KiB of LDS; larger batches or pools run in request order.
-constexpr int kOrderMaxB = 4096;
-constexpr int64_t kOrderMaxSlots = 32768;
 
 template <bool SB, bool AB, int DK, int DV>
 __global__ __launch_bounds__(GDN_DECODE_MAX_THREADS) void decode_kernel(DecodeParams p,

@@ -20,4 +20,9 @@ gdn_status launch_prefill(const gdn_prefill_args &a, hipStream_t stream);
 gdn_status launch_mixed(const gdn_decode_args &d, const gdn_prefill_args &p, hipStream_t stream);
 size_t prefill_workspace_bytes(const gdn_prefill_args &a);
 
+struct PrefillParams;
+// Kernel parameters of a prefill call; runs the front-end kernel into the
+// workspace first when the inputs are raw.
+gdn_status prepare_prefill(const gdn_prefill_args &a, hipStream_t stream, PrefillParams *out);
+
 }  // namespace gdn

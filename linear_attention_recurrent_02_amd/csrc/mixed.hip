@@ -1,8 +1,148 @@
-// mixed.hip -- placeholder until the single-launch mixed batch is built.
-#include "internal.h"
+// mixed.hip -- one launch for a decode batch and a prefill batch.
+//
+// Mixed batches are where the pages' GDN v3 kernels gained the most (2.14x
+// on Ironwood; "Gated DeltaNet" glossary entry, How to read it).  Here the
+// grid's first blocks are the prefill chains -- the long poles, one per
+// (sequence, state head), dispatched first -- and the remaining blocks are
+// persistent decode workers that stream the decode tiles in write-slot
+// order on the CUs the chains leave free.  Each block runs exactly the device
+// code of gdn_prefill or gdn_decode, so the results equal the two calls made
+// separately.  A block holds the prefill chain's LDS, so one block fits per
+// CU; a decode worker therefore keeps two tiles in flight (the next tile's
+// loads are issued before the current tile is reduced and stored).
+//
+// Both halves must describe the same layer shape (heads, d_k, d_v, state and
+// activation dtypes).  With raw prefill inputs the front-end kernel runs
+// first, then the single mixed launch.
+#include <algorithm>
+
+#include "decode.cuh"
+#include "order.cuh"
+#include "prefill_chain.cuh"
 
 namespace gdn {
-gdn_status launch_mixed(const gdn_decode_args &, const gdn_prefill_args &, hipStream_t) {
+
+DecodeParams make_decode_params(const gdn_decode_args &a);
+
+template <bool SB, bool AB, int DK, int DV, bool F32>
+struct MixedLayout {
+  static constexpr int NT = 256;
+  static constexpr size_t PREFILL = PrefillLayout<DK, DV, F32>::BYTES;
+  static constexpr size_t RED = sizeof(float) * DecodeShape<SB, DK, DV, NT>::LDS_FLOATS;
+  static constexpr size_t ORDER = slot_order_lds_bytes(kOrderMaxB, kOrderMaxSlots, NT);
+  static constexpr size_t DECODE = RED + ORDER;
+  static constexpr size_t BYTES = PREFILL > DECODE ? PREFILL : DECODE;
+};
+
+template <bool SB, bool AB, int DK, int DV, bool F32>
+__global__ __launch_bounds__(256) void mixed_kernel(DecodeParams dp, PrefillParams pp,
+                                                    int n_chains, int prefill_blocks,
+                                                    int ordered) {
+  using L = MixedLayout<SB, AB, DK, DV, F32>;
+  constexpr int NT = L::NT;
+  __shared__ __align__(16) char smem[L::BYTES];
+  if ((int)blockIdx.x < prefill_blocks) {
+    const int chain = chain_of_block(blockIdx.x);
+    if (chain < n_chains) prefill_chain<SB, AB, DK, DV, F32>(pp, chain, smem);
+    return;
+  }
+  // decode worker
+  float *red = reinterpret_cast<float *>(smem);
+  int *order = reinterpret_cast<int *>(smem + L::RED);
+  if (ordered) build_slot_order<NT>(dp.write_slot, dp.B, dp.n_slots, order);
+  const int64_t n_tiles = (int64_t)dp.B * dp.H_v;
+  const int64_t workers = (int64_t)gridDim.x - prefill_blocks;
+  int64_t t = (int64_t)blockIdx.x - prefill_blocks;
+  if (t >= n_tiles) return;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT>;
+  auto load = [&](int64_t tile, Regs &dst) {
+    const int pos = (int)(tile / dp.H_v);
+    decode_tile_load<SB, AB, DK, DV, NT>(dp, ordered ? order[pos] : pos, (int)(tile % dp.H_v), dst);
+  };
+  Regs cur, nxt;
+  load(t, cur);
+  for (;;) {
+    const int64_t tn = t + workers;
+    const bool more = tn < n_tiles;
+    if (more) load(tn, nxt);
+    decode_tile_finish<SB, AB, DK, DV, NT>(dp, cur, red);
+    if (!more) break;
+    cur = nxt;
+    t = tn;
+  }
+}
+
+template <bool SB, bool AB, int DK, int DV>
+static gdn_status launch_mixed_t(const DecodeParams &dp, const PrefillParams &pp, hipStream_t s) {
+  constexpr bool F32 = !AB;
+  using L = MixedLayout<SB, AB, DK, DV, F32>;
+  if constexpr (L::BYTES > 160 * 1024) {
+    return GDN_ERR_UNSUPPORTED;
+  } else {
+    const int n_chains = pp.n_seq * pp.H_v;
+    const int prefill_blocks = (n_chains + 15) / 16 * 16;
+    const int64_t tiles = (int64_t)dp.B * dp.H_v;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return GDN_ERR_LAUNCH;
+    // decode workers on the CUs the chains leave free (at least a quarter of the chip)
+    const int64_t free_cus = std::max<int64_t>(cus - n_chains, std::max(1, cus / 4));
+    const int64_t workers = tiles > 0 ? std::min<int64_t>(tiles, free_cus) : 0;
+    const int ordered =
+        dp.write_slot != nullptr && dp.B <= kOrderMaxB && dp.n_slots <= kOrderMaxSlots ? 1 : 0;
+    const int64_t grid = (n_chains > 0 ? prefill_blocks : 0) + workers;
+    if (grid == 0) return GDN_OK;
+    hipLaunchKernelGGL((mixed_kernel<SB, AB, DK, DV, F32>), dim3((unsigned)grid), dim3(L::NT), 0, s,
+                       dp, pp, n_chains, n_chains > 0 ? prefill_blocks : 0, ordered);
+    return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+  }
+}
+
+template <bool SB, bool AB, int DK>
+static gdn_status mixed_dv(const DecodeParams &dp, const PrefillParams &pp, int dv, hipStream_t s) {
+  switch (dv) {
+    case 16: return launch_mixed_t<SB, AB, DK, 16>(dp, pp, s);
+    case 32: return launch_mixed_t<SB, AB, DK, 32>(dp, pp, s);
+    case 64: return launch_mixed_t<SB, AB, DK, 64>(dp, pp, s);
+    case 128: return launch_mixed_t<SB, AB, DK, 128>(dp, pp, s);
+  }
   return GDN_ERR_UNSUPPORTED;
 }
+
+template <bool SB, bool AB>
+static gdn_status mixed_dk(const DecodeParams &dp, const PrefillParams &pp, int dk, int dv,
+                           hipStream_t s) {
+  switch (dk) {
+    case 16: return mixed_dv<SB, AB, 16>(dp, pp, dv, s);
+    case 32: return mixed_dv<SB, AB, 32>(dp, pp, dv, s);
+    case 64: return mixed_dv<SB, AB, 64>(dp, pp, dv, s);
+    case 128: return mixed_dv<SB, AB, 128>(dp, pp, dv, s);
+  }
+  return GDN_ERR_UNSUPPORTED;
+}
+
+gdn_status launch_mixed(const gdn_decode_args &d, const gdn_prefill_args &p, hipStream_t stream) {
+  if (d.B > 0 && p.n_seq > 0 &&
+      (d.H_qk != p.H_qk || d.H_v != p.H_v || d.d_k != p.d_k || d.d_v != p.d_v ||
+       d.state_dtype != p.state_dtype || d.act_dtype != p.act_dtype))
+    return GDN_ERR_UNSUPPORTED;
+  // shapes come from whichever half is present
+  const gdn_prefill_args &shape = p;
+  const int dk = d.B > 0 ? d.d_k : shape.d_k, dv = d.B > 0 ? d.d_v : shape.d_v;
+  const int sdt = d.B > 0 ? d.state_dtype : shape.state_dtype;
+  const int adt = d.B > 0 ? d.act_dtype : shape.act_dtype;
+  PrefillParams pp = {};
+  if (p.n_seq > 0) {
+    const gdn_status st = prepare_prefill(p, stream, &pp);
+    if (st != GDN_OK) return st;
+  }
+  const DecodeParams dp = d.B > 0 ? make_decode_params(d) : DecodeParams{};
+  const bool sb = sdt == GDN_BF16, ab = adt == GDN_BF16;
+  if (sb && ab) return mixed_dk<true, true>(dp, pp, dk, dv, stream);
+  if (sb && !ab) return mixed_dk<true, false>(dp, pp, dk, dv, stream);
+  if (!sb && ab) return mixed_dk<false, true>(dp, pp, dk, dv, stream);
+  return mixed_dk<false, false>(dp, pp, dk, dv, stream);
+}
+
 }  // namespace gdn

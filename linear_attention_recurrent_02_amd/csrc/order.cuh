@@ -17,6 +17,11 @@
 
 namespace gdn {
 
+// Slot ordering is used when the batch's order and the slot bitmap fit in a
+// few KiB of LDS; larger batches or pools run in request order.
+constexpr int kOrderMaxB = 4096;
+constexpr int64_t kOrderMaxSlots = 32768;
+
 // Exclusive prefix sum of x over the NT threads of the workgroup (thread
 // order); `total` receives the sum over all threads.  `wsum` is LDS of at
 // least NT/64 ints.  Contains two barriers; every thread must call it.

@@ -1,393 +1,24 @@
-// prefill.hip -- the chunked-prefill chain kernel (one workgroup per
-// (sequence, state head)) and the gdn_prefill launcher: front-end kernel into
-// the workspace when the inputs are raw, then the chains.  The algebra and
-// the LDS layout are described in prefill.cuh.
+// prefill.hip -- the chunked-prefill kernel (one workgroup per (sequence,
+// state head) chain, the chain itself in prefill_chain.cuh) and the
+// gdn_prefill launcher: the front-end kernel into the workspace when the
+// inputs are raw, then the chains.
 #include <algorithm>
 
-#include "prefill.cuh"
+#include "prefill_chain.cuh"
 
 namespace gdn {
 
-template <typename OT>
-__device__ __forceinline__ void put4(OT *p, const float *x) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) put(p + e, x[e]);
-}
-
-// Chain c of blockIdx b: inside each group of 16 blocks, chains 2m and 2m+1
-// (the two state heads that share a q/k head when H_v = 2 H_qk) go to blocks
-// m and m + 8, which the dispatcher places on the same XCD (blocks are dealt
-// to the 8 XCDs round-robin), so their shared q/k rows meet in one L2.
-__device__ __forceinline__ int chain_of_block(int b) {
-  const int w = b & 15;
-  return (b & ~15) + 2 * (w & 7) + (w >> 3);
-}
-
 template <bool SB, bool AB, int DK, int DV, bool F32>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, int n_chains) {
-  using L = PrefillLayout<DK, DV, F32>;
-  using OT = typename L::OT;
-  constexpr int C = L::C;
-  constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF;
-  constexpr int NKB = L::DKP / 32;  // MFMA K-steps over d_k
-  constexpr int DKB = DK / 16;      // 16-row blocks of d_k
-  constexpr int DVB = DV / 16;      // 16-column blocks of d_v
-  using MS = TileSplit<DKB, DVB>;  // tiles of the state (d_k x d_v)
-  using OS = TileSplit<4, DVB>;    // tiles of a 64 x d_v product
-  constexpr int MPW = MS::PER, OPW = OS::PER;
-  __shared__ __align__(16) char smem[L::BYTES];
-  OT *Kh = reinterpret_cast<OT *>(smem + L::KH);
-  OT *Qh = reinterpret_cast<OT *>(smem + L::QH);
-  OT *Kt = reinterpret_cast<OT *>(smem + L::KT);
-  OT *Mt = reinterpret_cast<OT *>(smem + L::MT);
-  OT *Sq = reinterpret_cast<OT *>(smem + L::SQ);
-  OT *Rt = reinterpret_cast<OT *>(smem + L::RT);  // R, then U, transposed
-  float *Af = reinterpret_cast<float *>(smem + L::RT);  // shares bytes with Rt
-  float *Tf = reinterpret_cast<float *>(smem + L::TF);
-  float *Gs = reinterpret_cast<float *>(smem + L::GATES);
-  float *gam = Gs + C, *bet = Gs + 2 * C, *eGn = Gs + 3 * C;
-  float *XS = reinterpret_cast<float *>(smem + L::XS);
-
+  __shared__ __align__(16) char smem[PrefillLayout<DK, DV, F32>::BYTES];
   const int chain = chain_of_block(blockIdx.x);
-  if (chain >= n_chains) return;
-  const int seq = chain / p.H_v, h = chain % p.H_v, hq = h / p.group;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int col = lane & 15, rq = 4 * (lane >> 4);  // accumulator layout: rows rq..rq+3, column col
-  const int64_t t_begin = p.cu[seq], t_end = p.cu[seq + 1];
-  const int64_t rs = p.read_slot ? (int64_t)p.read_slot[seq] : seq;
-  const int64_t ws = p.write_slot ? (int64_t)p.write_slot[seq] : seq;
-  if (rs < -1 || rs >= p.n_slots || ws < -1 || ws >= p.n_slots) {
-    if (tid == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
-    return;
-  }
-  const bool decay = (p.rule & kRuleDecay) != 0;
-  const bool erase = (p.rule & kRuleErase) != 0;
-
-  // padded K columns (d_k < 32 only) stay zero for the whole chain
-  if constexpr (L::DKP > DK) {
-    constexpr int PADC = L::DKP - DK;
-    for (int i = tid; i < (2 * C + DV) * PADC; i += 256) {
-      const int row = i / PADC, c = DK + i % PADC;
-      if (row < C) put(Kh + row * LDK + c, 0.f);
-      else if (row < 2 * C) put(Qh + (row - C) * LDK + c, 0.f);
-      else put(Mt + (row - 2 * C) * LDK + c, 0.f);
-    }
-  }
-
-  // ---- initial state (a8): read slot -> FP32 accumulators and Mt ----
-  f32x4_t macc[MPW];
-  const int64_t state_base = (rs * p.H_v + h) * (int64_t)DK * DV;
-  const bool mvalid = MS::valid(wave), ovalid = OS::valid(wave);
-#pragma unroll
-  for (int j = 0; j < MPW; ++j) {
-    float x[4] = {0.f, 0.f, 0.f, 0.f};
-    if (mvalid) {
-      const int d = 16 * MS::x(wave, j) + rq, c = 16 * MS::y(wave, j) + col;
-      if (rs >= 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = Elem<SB>::load1(p.pool, state_base + (int64_t)(d + e) * DV + c);
-      }
-      put4(Mt + c * LDK + d, x);
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) macc[j][e] = x[e];
-  }
-  __syncthreads();
-
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += C) {
-    const int n = (int)std::min<int64_t>(C, t_end - t0);
-
-    // ---- 1: K and Q rows of the chunk (zero past the end), gates, G ----
-    for (int idx = tid; idx < C * (DK / 8); idx += 256) {
-      const int r = idx / (DK / 8), d = (idx % (DK / 8)) * 8;
-      float kx[8], qx[8];
-      if (r < n) {
-        const int64_t off = ((t0 + r) * p.H_qk + hq) * DK + d;
-        load_run<AB, 8>(p.k, off, kx);
-        load_run<AB, 8>(p.q, off, qx);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kx[e] = qx[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        put(Kh + r * LDK + d + e, kx[e]);
-        put(Qh + r * LDK + d + e, qx[e]);
-      }
-    }
-    if (wave == 0) {
-      const int r = lane;
-      const bool valid = r < n;
-      const float gv = (valid && decay) ? p.g[(t0 + r) * p.H_v + h] : 0.f;
-      const float bv = valid ? (erase ? p.beta[(t0 + r) * p.H_v + h] : 1.f) : 0.f;
-      float G = gv;  // inclusive prefix sum over the 64 lanes
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(G, off);
-        if (lane >= off) G += y;
-      }
-      const float G_last = __shfl(G, 63);
-      Gs[r] = G;
-      gam[r] = expf(G);
-      bet[r] = bv;
-      eGn[r] = expf(G_last - G);
-    }
-    __syncthreads();
-
-    // ---- 2: S = K K^T and P = Q K^T, row block `wave` (a6) ----
-    f32x4_t sacc[4], pacc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sacc[cb][e] = pacc[cb][e] = 0.f;
-    }
-#pragma unroll 1
-    for (int kk = 0; kk < NKB; ++kk) {
-      const Frag<F32> fk = load_frag<F32>(Kh, LDK, 16 * wave, 32 * kk);
-      const Frag<F32> fq = load_frag<F32>(Qh, LDK, 16 * wave, 32 * kk);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const Frag<F32> fb = load_frag<F32>(Kh, LDK, 16 * cb, 32 * kk);
-        if (erase) sacc[cb] = mma<F32>(sacc[cb], fk, fb);
-        pacc[cb] = mma<F32>(pacc[cb], fq, fb);
-      }
-    }
-    // ---- 3: A = strict_lower(beta_r e^{G_r-G_s} S), Sq = lower(e^{G_r-G_s} P), Kt ----
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 16 * wave + rq + e, s = 16 * cb + col;
-        const float dec = s <= r ? expf(Gs[r] - Gs[s]) : 0.f;
-        Af[r * LDF + s] = (erase && s < r) ? bet[r] * dec * sacc[cb][e] : 0.f;
-        put(Sq + r * LDC + s, dec * pacc[cb][e]);
-      }
-    }
-    for (int idx = tid; idx < DK * C; idx += 256) {
-      const int d = idx / C, s = idx % C;
-      put(Kt + d * LDC + s, eGn[s] * get(Kh + s * LDK + d));
-    }
-    __syncthreads();
-
-    // ---- 4: T = (I + A)^-1 (FP32, blocked forward substitution) ----
-    if (erase) {
-      if (wave == 0) {
-        // the four 16 x 16 diagonal blocks: lane -> (block, column)
-        const int bb = lane >> 4, c = lane & 15;
-        float tc[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = r == c ? 1.f : 0.f;
-          const float *arow = Af + (16 * bb + r) * LDF + 16 * bb;
-#pragma unroll
-          for (int s = 0; s < r; ++s) x = fmaf(-arow[s], tc[s], x);
-          tc[r] = x;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tf[(16 * bb + r) * LDF + 16 * bb + c] = tc[r];
-      } else {
-        // zero the strictly upper blocks
-        for (int i = tid - 64; i < 6 * 256; i += 192) {
-          const int blk = i >> 8, e = i & 255;
-          const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-          const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-          Tf[(16 * bi + (e >> 4)) * LDF + 16 * bj + (e & 15)] = 0.f;
-        }
-      }
-      __syncthreads();
-      // off-diagonal blocks by levels: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
-#pragma unroll
-      for (int lv = 1; lv < 4; ++lv) {
-        const bool act = wave < 4 - lv;
-        const int bj = wave, bi = wave + lv;
-        float *xs = XS + wave * 16 * 17;
-        if (act) {
-          float x[4] = {0.f, 0.f, 0.f, 0.f};
-          for (int kb = bj; kb < bi; ++kb) {
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-              const float tv = Tf[(16 * kb + m) * LDF + 16 * bj + col];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                x[e] = fmaf(Af[(16 * bi + rq + e) * LDF + 16 * kb + m], tv, x[e]);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) xs[(rq + e) * 17 + col] = x[e];
-        }
-        __syncthreads();
-        if (act) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float y = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m)
-              y = fmaf(Tf[(16 * bi + rq + e) * LDF + 16 * bi + m], xs[m * 17 + col], y);
-            Tf[(16 * bi + rq + e) * LDF + 16 * bj + col] = -y;
-          }
-        }
-        __syncthreads();
-      }
-    }
-
-    // ---- 5: Q M, K M (a7); R = beta (V - gamma K M) -> Rt ----
-    f32x4_t qm[OPW], ur[OPW];
-#pragma unroll
-    for (int j = 0; j < OPW; ++j) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qm[j][e] = ur[j][e] = 0.f;
-    }
-    if (ovalid) {
-#pragma unroll 1
-      for (int kk = 0; kk < NKB; ++kk) {
-        Frag<F32> fm[OS::YN], fq[OS::XN], fk[OS::XN];
-#pragma unroll
-        for (int yi = 0; yi < OS::YN; ++yi)
-          fm[yi] = load_frag<F32>(Mt, LDK, 16 * OS::y(wave, yi), 32 * kk);
-#pragma unroll
-        for (int xi = 0; xi < OS::XN; ++xi) {
-          fq[xi] = load_frag<F32>(Qh, LDK, 16 * OS::x(wave, xi * OS::YN), 32 * kk);
-          if (erase) fk[xi] = load_frag<F32>(Kh, LDK, 16 * OS::x(wave, xi * OS::YN), 32 * kk);
-        }
-#pragma unroll
-        for (int j = 0; j < OPW; ++j) {
-          const int xi = j / OS::YN, yi = j % OS::YN;
-          qm[j] = mma<F32>(qm[j], fq[xi], fm[yi]);
-          if (erase) ur[j] = mma<F32>(ur[j], fk[xi], fm[yi]);  // K M for now
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < OPW; ++j) {
-        const int r0 = 16 * OS::x(wave, j) + rq, c = 16 * OS::y(wave, j) + col;
-        float x[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = r0 + e;
-          const float vv = r < n ? Elem<AB>::load1(p.v, ((t0 + r) * p.H_v + h) * DV + c) : 0.f;
-          x[e] = erase ? bet[r] * (vv - gam[r] * ur[j][e]) : vv;
-          ur[j][e] = x[e];
-        }
-        put4(Rt + c * LDC + r0, x);
-      }
-    }
-    __syncthreads();
-
-    // ---- 6: U = T R (delta rules; otherwise U = R already in Rt) ----
-    if (erase) {
-      if (ovalid) {
-#pragma unroll
-        for (int j = 0; j < OPW; ++j) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ur[j][e] = 0.f;
-        }
-#pragma unroll 1
-        for (int kk = 0; kk < 2; ++kk) {
-          Frag<F32> fr[OS::YN], ft[OS::XN];
-#pragma unroll
-          for (int yi = 0; yi < OS::YN; ++yi)
-            fr[yi] = load_frag<F32>(Rt, LDC, 16 * OS::y(wave, yi), 32 * kk);
-#pragma unroll
-          for (int xi = 0; xi < OS::XN; ++xi)
-            ft[xi] = load_frag<F32>(Tf, LDF, 16 * OS::x(wave, xi * OS::YN), 32 * kk);
-#pragma unroll
-          for (int j = 0; j < OPW; ++j) {
-            if (32 * kk > 16 * OS::x(wave, j) + 15) continue;  // T is lower triangular
-            ur[j] = mma<F32>(ur[j], ft[j / OS::YN], fr[j % OS::YN]);
-          }
-        }
-      }
-      __syncthreads();  // every wave has read R
-      if (ovalid) {
-#pragma unroll
-        for (int j = 0; j < OPW; ++j) {
-          float x[4] = {ur[j][0], ur[j][1], ur[j][2], ur[j][3]};
-          put4(Rt + (16 * OS::y(wave, j) + col) * LDC + 16 * OS::x(wave, j) + rq, x);
-        }
-      }
-      __syncthreads();
-    }
-
-    // ---- 7: O = gamma Q M + Sq U (a7), scaled, to HBM ----
-    if (ovalid) {
-#pragma unroll
-      for (int j = 0; j < OPW; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qm[j][e] *= gam[16 * OS::x(wave, j) + rq + e];
-      }
-#pragma unroll 1
-      for (int kk = 0; kk < 2; ++kk) {
-        Frag<F32> fu[OS::YN], fs[OS::XN];
-#pragma unroll
-        for (int yi = 0; yi < OS::YN; ++yi)
-          fu[yi] = load_frag<F32>(Rt, LDC, 16 * OS::y(wave, yi), 32 * kk);
-#pragma unroll
-        for (int xi = 0; xi < OS::XN; ++xi)
-          fs[xi] = load_frag<F32>(Sq, LDC, 16 * OS::x(wave, xi * OS::YN), 32 * kk);
-#pragma unroll
-        for (int j = 0; j < OPW; ++j) {
-          if (32 * kk > 16 * OS::x(wave, j) + 15) continue;  // Sq is lower triangular
-          qm[j] = mma<F32>(qm[j], fs[j / OS::YN], fu[j % OS::YN]);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < OPW; ++j) {
-        const int c = 16 * OS::y(wave, j) + col;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * OS::x(wave, j) + rq + e;
-          if (r < n) Elem<AB>::store1(p.o, ((t0 + r) * p.H_v + h) * DV + c, p.scale * qm[j][e]);
-        }
-      }
-    }
-
-    // ---- 8: M <- gamma_last M + Kt U (FP32 accumulators), refresh Mt ----
-    if (mvalid) {
-      const float gl = gam[C - 1];
-#pragma unroll
-      for (int j = 0; j < MPW; ++j) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) macc[j][e] *= gl;
-      }
-#pragma unroll 1
-      for (int kk = 0; kk < 2; ++kk) {
-        Frag<F32> fu[MS::YN], fk[MS::XN];
-#pragma unroll
-        for (int yi = 0; yi < MS::YN; ++yi)
-          fu[yi] = load_frag<F32>(Rt, LDC, 16 * MS::y(wave, yi), 32 * kk);
-#pragma unroll
-        for (int xi = 0; xi < MS::XN; ++xi)
-          fk[xi] = load_frag<F32>(Kt, LDC, 16 * MS::x(wave, xi * MS::YN), 32 * kk);
-#pragma unroll
-        for (int j = 0; j < MPW; ++j) macc[j] = mma<F32>(macc[j], fk[j / MS::YN], fu[j % MS::YN]);
-      }
-    }
-    __syncthreads();  // all reads of Mt, Kt, Rt, Sq for this chunk are done
-    if (mvalid) {
-#pragma unroll
-      for (int j = 0; j < MPW; ++j) {
-        float x[4] = {macc[j][0], macc[j][1], macc[j][2], macc[j][3]};
-        put4(Mt + (16 * MS::y(wave, j) + col) * LDK + 16 * MS::x(wave, j) + rq, x);
-      }
-    }
-    __syncthreads();
-  }
-
-  // ---- final state (a8): FP32 -> state dtype (RNE for BF16) -> write slot ----
-  if (ws >= 0 && mvalid) {
-    const int64_t out_base = (ws * p.H_v + h) * (int64_t)DK * DV;
-#pragma unroll
-    for (int j = 0; j < MPW; ++j) {
-      const int d = 16 * MS::x(wave, j) + rq, c = 16 * MS::y(wave, j) + col;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) Elem<SB>::store1(p.pool, out_base + (int64_t)(d + e) * DV + c, macc[j][e]);
-    }
-  }
+  if (chain < n_chains) prefill_chain<SB, AB, DK, DV, F32>(p, chain, smem);
 }
 
 // ---- launcher --------------------------------------------------------------
 
-static PrefillParams make_prefill_params(const gdn_prefill_args &a, const void *q, const void *k,
-                                         const void *v, const float *g, const float *beta) {
+PrefillParams make_prefill_params(const gdn_prefill_args &a, const void *q, const void *k,
+                                  const void *v, const float *g, const float *beta) {
   PrefillParams p;
   p.n_seq = a.n_seq; p.H_qk = a.H_qk; p.H_v = a.H_v; p.group = a.H_v / a.H_qk;
   p.n_slots = a.n_slots; p.scale = a.scale; p.rule = a.rule; p.cu = a.cu_seqlens;
@@ -459,22 +90,28 @@ size_t prefill_workspace_bytes(const gdn_prefill_args &a) {
   return fe_workspace(a).bytes;
 }
 
-gdn_status launch_prefill(const gdn_prefill_args &a, hipStream_t stream) {
-  gdn_status st = GDN_OK;
+gdn_status prepare_prefill(const gdn_prefill_args &a, hipStream_t stream, PrefillParams *out) {
   const void *q = a.q, *k = a.k, *v = a.v;
   const float *g = a.g, *beta = a.beta;
   if (a.use_frontend && a.n_tokens > 0) {
     const FeWorkspace w = fe_workspace(a);
     char *base = static_cast<char *>(a.workspace);
-    st = launch_frontend(a, base + w.q, base + w.k, base + w.v,
-                         reinterpret_cast<float *>(base + w.g),
-                         reinterpret_cast<float *>(base + w.beta), stream);
+    const gdn_status st = launch_frontend(a, base + w.q, base + w.k, base + w.v,
+                                          reinterpret_cast<float *>(base + w.g),
+                                          reinterpret_cast<float *>(base + w.beta), stream);
     if (st != GDN_OK) return st;
     q = base + w.q; k = base + w.k; v = base + w.v;
     g = reinterpret_cast<const float *>(base + w.g);
     beta = reinterpret_cast<const float *>(base + w.beta);
   }
-  const PrefillParams p = make_prefill_params(a, q, k, v, g, beta);
+  *out = make_prefill_params(a, q, k, v, g, beta);
+  return GDN_OK;
+}
+
+gdn_status launch_prefill(const gdn_prefill_args &a, hipStream_t stream) {
+  PrefillParams p;
+  const gdn_status st = prepare_prefill(a, stream, &p);
+  if (st != GDN_OK) return st;
   const bool sb = a.state_dtype == GDN_BF16, ab = a.act_dtype == GDN_BF16;
   if (sb && ab) return chains_dk<true, true>(p, a.d_k, a.d_v, stream);
   if (sb && !ab) return chains_dk<true, false>(p, a.d_k, a.d_v, stream);

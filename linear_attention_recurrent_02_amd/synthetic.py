@@ -151,3 +151,23 @@ def frontend_inputs(wl: int, layer: int, n_tok: int, H_qk: int, H_v: int, d_k: i
     return dict(q_raw=_cast(q, act_dtype), k_raw=_cast(k, act_dtype), v_raw=_cast(v, act_dtype),
                 conv_wq=_cast(wq, f32), conv_wk=_cast(wk, f32), conv_wv=_cast(wv, f32),
                 a_raw=_cast(a_raw, f32), b_raw=_cast(b_raw, f32))
+
+
+def mixed_slots(wl: int, n_decode: int, n_prefill: int, n_slots: int, frac: float = 0.25):
+    """Slots for a mixed batch sharing one pool: every request writes a distinct
+    slot; a seeded `frac` of all requests read a prefix-cache checkpoint slot
+    (distinct from every write slot); the other decode requests update in
+    place and the other prefills start fresh (read -1).  Returns int32 tensors
+    (dec_read, dec_write, pre_read, pre_write)."""
+    n = n_decode + n_prefill
+    r = rng(wl, 0, _S_SLOTS)
+    perm = r.permutation(n_slots).astype(np.int32)
+    n_ckpt = int(round(frac * n))
+    if n + n_ckpt > n_slots:
+        raise ValueError("pool too small for distinct write and checkpoint slots")
+    write = perm[:n].copy()
+    ckpt_req = np.sort(r.choice(n, size=n_ckpt, replace=False))
+    read = np.concatenate([write[:n_decode], np.full(n_prefill, -1, np.int32)])
+    read[ckpt_req] = perm[n:n + n_ckpt]
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32))
+    return t(read[:n_decode]), t(write[:n_decode]), t(read[n_decode:]), t(write[n_decode:])
