@@ -44,11 +44,12 @@ __device__ __forceinline__ int seq_of(const int32_t *cu, int n_seq, int64_t t) {
 
 __device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
 
-// conv + SiLU of channels [c0, c0+NC) of one head for token t (raw row stride
-// ld elements); seq_start is the first token of t's sequence.
+// conv + SiLU of NC consecutive channels of one head for token t (raw row
+// stride ld elements, channel offset c0); w holds the NC channels' 4 taps
+// (LDS, channel-major); seq_start is the first token of t's sequence.
 template <bool AB, int NC>
 __device__ __forceinline__ void conv_silu_run(const void *raw, int64_t ld, int64_t c0, int64_t t,
-                                              int64_t seq_start, const float *w, float *y) {
+                                              int64_t seq_start, const float4 *w, float *y) {
 #pragma unroll
   for (int c = 0; c < NC; ++c) y[c] = 0.f;
 #pragma unroll
@@ -58,29 +59,49 @@ __device__ __forceinline__ void conv_silu_run(const void *raw, int64_t ld, int64
     float x[NC];
     load_run<AB, NC>(raw, src * ld + c0, x);
 #pragma unroll
-    for (int c = 0; c < NC; ++c) y[c] = fmaf(w[(c0 + c) * 4 + j], x[c], y[c]);
+    for (int c = 0; c < NC; ++c) {
+      const float4 wc = w[c];
+      const float wj = j == 0 ? wc.x : (j == 1 ? wc.y : (j == 2 ? wc.z : wc.w));
+      y[c] = fmaf(wj, x[c], y[c]);
+    }
   }
 #pragma unroll
   for (int c = 0; c < NC; ++c) y[c] = silu(y[c]);
 }
 
+// LDS: the head's conv weights (d x 4 floats) and, for up to kFeCuLds
+// sequences, the sequence offsets (binary search in LDS, not global memory)
+constexpr int kFeCuLds = 2048;
+
 template <bool AB, int DK, int DV>
 __global__ __launch_bounds__(256) void frontend_kernel(FrontendParams p) {
+  constexpr int DMAX = DK > DV ? DK : DV;
+  __shared__ float4 w_lds[DMAX];
+  __shared__ int32_t cu_lds[kFeCuLds + 1];
   const int tid = threadIdx.x;
   const int64_t t = (int64_t)blockIdx.x * 64 + (tid >> 2);
   const int quarter = tid & 3;
   const int job = blockIdx.y;  // [0, H_qk): q head, [H_qk, 2 H_qk): k head, then v heads
+  const bool is_qk = job < 2 * p.H_qk;
+  const bool is_q = job < p.H_qk;
+  const int D = is_qk ? DK : DV;
+  const int hd = is_qk ? (is_q ? job : job - p.H_qk) : job - 2 * p.H_qk;
+  const float *wsrc = (is_qk ? (is_q ? p.wq : p.wk) : p.wv) + (int64_t)hd * D * 4;
+  for (int c = tid; c < D; c += 256) w_lds[c] = reinterpret_cast<const float4 *>(wsrc)[c];
+  const bool cu_in_lds = p.n_seq <= kFeCuLds;
+  if (cu_in_lds)
+    for (int i = tid; i <= p.n_seq; i += 256) cu_lds[i] = p.cu[i];
+  __syncthreads();
   const bool live = t < p.n_tokens;
   const int64_t tt = live ? t : p.n_tokens - 1;  // keep every lane in the shuffles
-  const int64_t s0 = p.cu[seq_of(p.cu, p.n_seq, tt)];
-  if (job < 2 * p.H_qk) {
-    const bool is_q = job < p.H_qk;
-    const int hd = is_q ? job : job - p.H_qk;
+  const int32_t *cu = cu_in_lds ? cu_lds : p.cu;
+  const int64_t s0 = cu[seq_of(cu, p.n_seq, tt)];
+  if (is_qk) {
     constexpr int NC = DK / 4;
     const int64_t ld = (int64_t)p.H_qk * DK;
     const int64_t c0 = (int64_t)hd * DK + quarter * NC;
     float y[NC];
-    conv_silu_run<AB, NC>(is_q ? p.q_raw : p.k_raw, ld, c0, tt, s0, is_q ? p.wq : p.wk, y);
+    conv_silu_run<AB, NC>(is_q ? p.q_raw : p.k_raw, ld, c0, tt, s0, w_lds + quarter * NC, y);
     float ss = 0.f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) ss = fmaf(y[c], y[c], ss);
@@ -91,16 +112,15 @@ __global__ __launch_bounds__(256) void frontend_kernel(FrontendParams p) {
     for (int c = 0; c < NC; ++c) y[c] *= inv;
     if (live) store_run<AB, NC>(is_q ? p.q_out : p.k_out, tt * ld + c0, y);
   } else {
-    const int hv = job - 2 * p.H_qk;
     constexpr int NC = DV / 4;
     const int64_t ld = (int64_t)p.H_v * DV;
-    const int64_t c0 = (int64_t)hv * DV + quarter * NC;
+    const int64_t c0 = (int64_t)hd * DV + quarter * NC;
     float y[NC];
-    conv_silu_run<AB, NC>(p.v_raw, ld, c0, tt, s0, p.wv, y);
+    conv_silu_run<AB, NC>(p.v_raw, ld, c0, tt, s0, w_lds + quarter * NC, y);
     if (live) {
       store_run<AB, NC>(p.v_out, tt * ld + c0, y);
       if (quarter == 0) {
-        const int64_t gi = tt * p.H_v + hv;
+        const int64_t gi = tt * p.H_v + hd;
         // g = -softplus(a) computed as -(max(a,0) + log1p(exp(-|a|))); beta = sigmoid(b)
         if (p.a_raw) {
           const float a = p.a_raw[gi];

@@ -76,7 +76,9 @@ struct PrefillLayout {
   static constexpr size_t KT = QH + (size_t)C * LDK * sizeof(OT);
   static constexpr size_t MT = KT + (size_t)DK * LDC * sizeof(OT);
   static constexpr size_t SQ = MT + (size_t)DV * LDK * sizeof(OT);
-  static constexpr size_t RT = SQ + (size_t)C * LDC * sizeof(OT);
+  static constexpr int LDV = DV + PADE;   // Vh / Oh rows (64 tokens x d_v)
+  static constexpr size_t VH = SQ + (size_t)C * LDC * sizeof(OT);  // V, then O, row-major
+  static constexpr size_t RT = VH + (size_t)C * LDV * sizeof(OT);
   static constexpr size_t RT_BYTES = (size_t)DV * LDC * sizeof(OT);
   static constexpr size_t AF_BYTES = (size_t)C * LDF * 4;
   // Af (only live while T is formed) shares its bytes with Rt/Ut
@@ -156,6 +158,9 @@ struct TileSplit {
   }
   __device__ static __forceinline__ bool valid(int w) { return BY_Y || BY_X || w < NX * NY; }
 };
+
+// 2^x on the hardware transcendental unit (v_exp_f32)
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // store a float into an operand buffer
 __device__ __forceinline__ void put(uint16_t *p, float x) { *p = f32_to_bf16(x); }

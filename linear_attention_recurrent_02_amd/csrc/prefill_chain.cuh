@@ -1,6 +1,11 @@
 // prefill_chain.cuh -- one (sequence, state head) chain of the chunked
 // prefill, as a device function shared by the prefill kernel and the mixed
 // launcher.  The algebra and the LDS layout are described in prefill.cuh.
+//
+// Latency: every global input of chunk c+1 (K and Q rows, V rows, gates) is
+// loaded into registers while chunk c computes, and written to LDS at the
+// end of chunk c, so no chunk waits on a global-memory round trip.  The
+// workgroup barriers wait only on LDS (lgkmcnt), not on these loads.
 #pragma once
 
 #include <algorithm>
@@ -14,7 +19,30 @@ __device__ __forceinline__ void put4(OT *p, const float *x) {
 #pragma unroll
   for (int e = 0; e < 4; ++e) put(p + e, x[e]);
 }
-
+// four consecutive operand elements as floats
+__device__ __forceinline__ void get4(const uint16_t *p, float *x) {
+  const uint2 u = *reinterpret_cast<const uint2 *>(p);
+  x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
+}
+__device__ __forceinline__ void get4(const float *p, float *x) {
+  const float4 v = *reinterpret_cast<const float4 *>(p);
+  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+}
+// eight consecutive operand elements <-> floats
+__device__ __forceinline__ void get8(const uint16_t *p, float *x) {
+  Elem<true>::unpack(*reinterpret_cast<const uint4 *>(p), x);
+}
+__device__ __forceinline__ void get8(const float *p, float *x) {
+  const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ __forceinline__ void put8(uint16_t *p, const float *x) {
+  *reinterpret_cast<uint4 *>(p) = Elem<true>::pack(x);
+}
+__device__ __forceinline__ void put8(float *p, const float *x) {
+  reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
+  reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
+}
 // Chain c of blockIdx b: inside each group of 16 blocks, chains 2m and 2m+1
 // (the two state heads that share a q/k head when H_v = 2 H_qk) go to blocks
 // m and m + 8, which the dispatcher places on the same XCD (blocks are dealt
@@ -30,23 +58,30 @@ template <bool SB, bool AB, int DK, int DV, bool F32>
 __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain, char *smem) {
   using L = PrefillLayout<DK, DV, F32>;
   using OT = typename L::OT;
+  using AT = typename Elem<AB>::T;
+  static_assert(sizeof(AT) == sizeof(OT), "operands are staged in the activation dtype");
   constexpr int C = L::C;
-  constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF;
+  constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF, LDV = L::LDV;
   constexpr int NKB = L::DKP / 32;  // MFMA K-steps over d_k
   constexpr int DKB = DK / 16;      // 16-row blocks of d_k
   constexpr int DVB = DV / 16;      // 16-column blocks of d_v
   using MS = TileSplit<DKB, DVB>;  // tiles of the state (d_k x d_v)
   using OS = TileSplit<4, DVB>;    // tiles of a 64 x d_v product
   constexpr int MPW = MS::PER, OPW = OS::PER;
+  constexpr int EW = 8 * (int)sizeof(AT) / 16;  // 16-byte vectors per 8 elements
+  constexpr int KQ_GROUPS = C * (DK / 8), KQ_PER = (KQ_GROUPS + 255) / 256;
+  constexpr int V_GROUPS = C * (DV / 8), V_PER = (V_GROUPS + 255) / 256;
+  constexpr float LOG2E = 1.4426950408889634f;
   OT *Kh = reinterpret_cast<OT *>(smem + L::KH);
   OT *Qh = reinterpret_cast<OT *>(smem + L::QH);
   OT *Kt = reinterpret_cast<OT *>(smem + L::KT);
   OT *Mt = reinterpret_cast<OT *>(smem + L::MT);
   OT *Sq = reinterpret_cast<OT *>(smem + L::SQ);
+  OT *Vh = reinterpret_cast<OT *>(smem + L::VH);  // V rows, then the chunk's O rows
   OT *Rt = reinterpret_cast<OT *>(smem + L::RT);  // R, then U, transposed
   float *Af = reinterpret_cast<float *>(smem + L::RT);  // shares bytes with Rt
   float *Tf = reinterpret_cast<float *>(smem + L::TF);
-  float *Gs = reinterpret_cast<float *>(smem + L::GATES);
+  float *Gs = reinterpret_cast<float *>(smem + L::GATES);  // cumulative log2 decay
   float *gam = Gs + C, *bet = Gs + 2 * C, *eGn = Gs + 3 * C;
   float *XS = reinterpret_cast<float *>(smem + L::XS);
 
@@ -62,6 +97,75 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   }
   const bool decay = (p.rule & kRuleDecay) != 0;
   const bool erase = (p.rule & kRuleErase) != 0;
+
+  // ---- prefetch of one chunk's inputs into registers, and their staging ----
+  uint4 pk[KQ_PER][EW], pq[KQ_PER][EW], pv[V_PER][EW];
+  float pg = 0.f, pb = 0.f;  // wave 0: gate inputs of token `lane`
+  auto fetch = [&](int64_t t0, int n) {
+#pragma unroll
+    for (int i = 0; i < KQ_PER; ++i) {
+      const int gi = tid + 256 * i;
+      const int r = gi / (DK / 8), d = (gi % (DK / 8)) * 8;
+      const bool ok = gi < KQ_GROUPS && r < n;
+      const int64_t off = ((t0 + r) * p.H_qk + hq) * DK + d;
+      const uint4 *sk = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.k) + off);
+      const uint4 *sq = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.q) + off);
+#pragma unroll
+      for (int e = 0; e < EW; ++e) {
+        pk[i][e] = ok ? sk[e] : make_uint4(0u, 0u, 0u, 0u);
+        pq[i][e] = ok ? sq[e] : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+      const int gi = tid + 256 * i;
+      const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
+      const bool ok = gi < V_GROUPS && r < n;
+      const uint4 *sv = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.v) +
+                                                        ((t0 + r) * p.H_v + h) * DV + c);
+#pragma unroll
+      for (int e = 0; e < EW; ++e) pv[i][e] = ok ? sv[e] : make_uint4(0u, 0u, 0u, 0u);
+    }
+    if (wave == 0) {
+      const bool valid = lane < n;
+      pg = (valid && decay) ? p.g[(t0 + lane) * p.H_v + h] : 0.f;
+      pb = valid ? (erase ? p.beta[(t0 + lane) * p.H_v + h] : 1.f) : 0.f;
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < KQ_PER; ++i) {
+      const int gi = tid + 256 * i;
+      if (gi >= KQ_GROUPS) continue;
+      const int r = gi / (DK / 8), d = (gi % (DK / 8)) * 8;
+      uint4 *dk = reinterpret_cast<uint4 *>(Kh + r * LDK + d);
+      uint4 *dq = reinterpret_cast<uint4 *>(Qh + r * LDK + d);
+#pragma unroll
+      for (int e = 0; e < EW; ++e) { dk[e] = pk[i][e]; dq[e] = pq[i][e]; }
+    }
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+      const int gi = tid + 256 * i;
+      if (gi >= V_GROUPS) continue;
+      const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
+      uint4 *dv = reinterpret_cast<uint4 *>(Vh + r * LDV + c);
+#pragma unroll
+      for (int e = 0; e < EW; ++e) dv[e] = pv[i][e];
+    }
+    if (wave == 0) {
+      float G = pg * LOG2E;  // inclusive prefix sum of log2 decays over the 64 lanes
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(G, off);
+        if (lane >= off) G += y;
+      }
+      const float G_last = __shfl(G, 63);
+      Gs[lane] = G;
+      gam[lane] = fast_exp2(G);
+      bet[lane] = pb;
+      eGn[lane] = fast_exp2(G_last - G);
+    }
+  };
 
   // padded K columns (d_k < 32 only) stay zero for the whole chain
   if constexpr (L::DKP > DK) {
@@ -92,47 +196,17 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
     for (int e = 0; e < 4; ++e) macc[j][e] = x[e];
   }
+  if (t_begin < t_end) {
+    fetch(t_begin, (int)std::min<int64_t>(C, t_end - t_begin));
+    stage();
+  }
   __syncthreads();
 
   for (int64_t t0 = t_begin; t0 < t_end; t0 += C) {
     const int n = (int)std::min<int64_t>(C, t_end - t0);
-
-    // ---- 1: K and Q rows of the chunk (zero past the end), gates, G ----
-    for (int idx = tid; idx < C * (DK / 8); idx += 256) {
-      const int r = idx / (DK / 8), d = (idx % (DK / 8)) * 8;
-      float kx[8], qx[8];
-      if (r < n) {
-        const int64_t off = ((t0 + r) * p.H_qk + hq) * DK + d;
-        load_run<AB, 8>(p.k, off, kx);
-        load_run<AB, 8>(p.q, off, qx);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) kx[e] = qx[e] = 0.f;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        put(Kh + r * LDK + d + e, kx[e]);
-        put(Qh + r * LDK + d + e, qx[e]);
-      }
-    }
-    if (wave == 0) {
-      const int r = lane;
-      const bool valid = r < n;
-      const float gv = (valid && decay) ? p.g[(t0 + r) * p.H_v + h] : 0.f;
-      const float bv = valid ? (erase ? p.beta[(t0 + r) * p.H_v + h] : 1.f) : 0.f;
-      float G = gv;  // inclusive prefix sum over the 64 lanes
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(G, off);
-        if (lane >= off) G += y;
-      }
-      const float G_last = __shfl(G, 63);
-      Gs[r] = G;
-      gam[r] = expf(G);
-      bet[r] = bv;
-      eGn[r] = expf(G_last - G);
-    }
-    __syncthreads();
+    const int64_t t1 = t0 + C;
+    const bool more = t1 < t_end;
+    if (more) fetch(t1, (int)std::min<int64_t>(C, t_end - t1));  // in flight until staged
 
     // ---- 2: S = K K^T and P = Q K^T, row block `wave` (a6) ----
     f32x4_t sacc[4], pacc[4];
@@ -153,19 +227,42 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       }
     }
     // ---- 3: A = strict_lower(beta_r e^{G_r-G_s} S), Sq = lower(e^{G_r-G_s} P), Kt ----
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
+    {
+      float Gr[4], br[4], Gc[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * wave + rq + e, s = 16 * cb + col;
-        const float dec = s <= r ? expf(Gs[r] - Gs[s]) : 0.f;
-        Af[r * LDF + s] = (erase && s < r) ? bet[r] * dec * sacc[cb][e] : 0.f;
-        put(Sq + r * LDC + s, dec * pacc[cb][e]);
+        Gr[e] = Gs[16 * wave + rq + e];
+        br[e] = bet[16 * wave + rq + e];
+      }
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) Gc[cb] = Gs[16 * cb + col];
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * wave + rq + e, s = 16 * cb + col;
+          const float dec = s <= r ? fast_exp2(Gr[e] - Gc[cb]) : 0.f;
+          Af[r * LDF + s] = (erase && s < r) ? br[e] * dec * sacc[cb][e] : 0.f;
+          put(Sq + r * LDC + s, dec * pacc[cb][e]);
+        }
       }
     }
-    for (int idx = tid; idx < DK * C; idx += 256) {
-      const int d = idx / C, s = idx % C;
-      put(Kt + d * LDC + s, eGn[s] * get(Kh + s * LDK + d));
+    // Kt[d][s] = exp(G_last - G_s) K[s][d], by 8 x 8 blocks
+    for (int blk = tid; blk < (C / 8) * (DK / 8); blk += 256) {
+      const int sb = blk % (C / 8), db = blk / (C / 8);
+      float x[8][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) get8(Kh + (8 * sb + i) * LDK + 8 * db, x[i]);
+      float sc[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sc[i] = eGn[8 * sb + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) y[i] = sc[i] * x[i][j];
+        put8(Kt + (8 * db + j) * LDC + 8 * sb, y);
+      }
     }
     __syncthreads();
 
@@ -195,36 +292,36 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         }
       }
       __syncthreads();
-      // off-diagonal blocks by levels: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj
+      // off-diagonal blocks by levels: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, each 16 x 16
+      // x 16 product as four v_mfma_f32_16x16x4f32 (lane l: A[l%16][k0 + l/16],
+      // B[k0 + l/16][l%16]; result rows 4(l/16)..+3, column l%16)
+      const int lr = lane & 15, lk = lane >> 4;
 #pragma unroll
       for (int lv = 1; lv < 4; ++lv) {
         const bool act = wave < 4 - lv;
         const int bj = wave, bi = wave + lv;
         float *xs = XS + wave * 16 * 17;
         if (act) {
-          float x[4] = {0.f, 0.f, 0.f, 0.f};
+          f32x4_t x = {0.f, 0.f, 0.f, 0.f};
           for (int kb = bj; kb < bi; ++kb) {
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-              const float tv = Tf[(16 * kb + m) * LDF + 16 * bj + col];
-#pragma unroll
-              for (int e = 0; e < 4; ++e)
-                x[e] = fmaf(Af[(16 * bi + rq + e) * LDF + 16 * kb + m], tv, x[e]);
-            }
+            for (int k0 = 0; k0 < 16; k0 += 4)
+              x = __builtin_amdgcn_mfma_f32_16x16x4f32(Af[(16 * bi + lr) * LDF + 16 * kb + k0 + lk],
+                                                       Tf[(16 * kb + k0 + lk) * LDF + 16 * bj + lr],
+                                                       x, 0, 0, 0);
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) xs[(rq + e) * 17 + col] = x[e];
         }
         __syncthreads();
         if (act) {
+          f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            float y = 0.f;
+          for (int k0 = 0; k0 < 16; k0 += 4)
+            y = __builtin_amdgcn_mfma_f32_16x16x4f32(Tf[(16 * bi + lr) * LDF + 16 * bi + k0 + lk],
+                                                     xs[(k0 + lk) * 17 + lr], y, 0, 0, 0);
 #pragma unroll
-            for (int m = 0; m < 16; ++m)
-              y = fmaf(Tf[(16 * bi + rq + e) * LDF + 16 * bi + m], xs[m * 17 + col], y);
-            Tf[(16 * bi + rq + e) * LDF + 16 * bj + col] = -y;
-          }
+          for (int e = 0; e < 4; ++e) Tf[(16 * bi + rq + e) * LDF + 16 * bj + col] = -y[e];
         }
         __syncthreads();
       }
@@ -259,12 +356,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
       for (int j = 0; j < OPW; ++j) {
         const int r0 = 16 * OS::x(wave, j) + rq, c = 16 * OS::y(wave, j) + col;
-        float x[4];
+        float vv[4], x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vv[e] = get(Vh + (r0 + e) * LDV + c);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = r0 + e;
-          const float vv = r < n ? Elem<AB>::load1(p.v, ((t0 + r) * p.H_v + h) * DV + c) : 0.f;
-          x[e] = erase ? bet[r] * (vv - gam[r] * ur[j][e]) : vv;
+          x[e] = erase ? bet[r] * (vv[e] - gam[r] * ur[j][e]) : vv[e];
           ur[j][e] = x[e];
         }
         put4(Rt + c * LDC + r0, x);
@@ -329,14 +427,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           qm[j] = mma<F32>(qm[j], fs[j / OS::YN], fu[j % OS::YN]);
         }
       }
+      // O into the V rows' LDS (V was consumed in step 5); written to HBM as whole
+      // rows after the next barrier
 #pragma unroll
       for (int j = 0; j < OPW; ++j) {
         const int c = 16 * OS::y(wave, j) + col;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * OS::x(wave, j) + rq + e;
-          if (r < n) Elem<AB>::store1(p.o, ((t0 + r) * p.H_v + h) * DV + c, p.scale * qm[j][e]);
-        }
+        for (int e = 0; e < 4; ++e)
+          put(Vh + (16 * OS::x(wave, j) + rq + e) * LDV + c, p.scale * qm[j][e]);
       }
     }
 
@@ -361,7 +459,19 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         for (int j = 0; j < MPW; ++j) macc[j] = mma<F32>(macc[j], fk[j / MS::YN], fu[j % MS::YN]);
       }
     }
-    __syncthreads();  // all reads of Mt, Kt, Rt, Sq for this chunk are done
+    __syncthreads();  // all reads of this chunk's LDS operands are done; O is in Vh
+#pragma unroll
+    for (int i = 0; i < V_PER; ++i) {
+      const int gi = tid + 256 * i;
+      const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
+      if (gi < V_GROUPS && r < n) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(Vh + r * LDV + c);
+        uint4 *dst = reinterpret_cast<uint4 *>(static_cast<AT *>(p.o) + ((t0 + r) * p.H_v + h) * DV + c);
+#pragma unroll
+        for (int e = 0; e < EW; ++e) dst[e] = src[e];
+      }
+    }
+    __syncthreads();  // O rows read out of Vh before the next chunk's V lands there
     if (mvalid) {
 #pragma unroll
       for (int j = 0; j < MPW; ++j) {
@@ -369,6 +479,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         put4(Mt + (16 * MS::y(wave, j) + col) * LDK + 16 * MS::x(wave, j) + rq, x);
       }
     }
+    if (more) stage();  // next chunk's K, Q, V and gates into LDS
     __syncthreads();
   }
 
