@@ -209,6 +209,57 @@ def run_prefill(args, torch, gdn, syn):
                 longest_chain_chunks=int((max(lengths) + 63) // 64))
 
 
+def run_mixed(args, torch, gdn, syn):
+    """448 decode requests plus 4 prefills of 8192 tokens (fused front-end) on
+    one 1024-slot BF16 pool, 25% of requests reading a checkpoint slot, decode
+    rule gated_delta: one gdn_mixed call vs gdn_decode + gdn_prefill."""
+    wl = syn.WORKLOADS["mixed"]
+    Hqk, Hv, d = wl["H_qk"], wl["H_v"], wl["d_k"]
+    nd, npf, L = wl["n_decode"], wl["n_prefill"], wl["prefill_len"]
+    q, k, v, g, beta = (t.cuda() for t in syn.token_inputs(wl["index"], 1, nd, Hqk, Hv, d, d))
+    pool = syn.state_pool(wl["index"], 0, wl["n_slots"], Hv, d, d, torch.bfloat16, on_device=True)
+    drs, dws, prs, pws = (t.cuda() for t in syn.mixed_slots(wl["index"], nd, npf, wl["n_slots"]))
+    cu = syn.cu_from_lengths([L] * npf).cuda()
+    x = {kk: vv.cuda() for kk, vv in syn.frontend_inputs(wl["index"], 2, L * npf, Hqk, Hv, d, d, 4).items()}
+    da, do, dkeep = gdn.make_decode_args(q, k, v, g, beta, pool, drs, dws)
+    pa, po, pkeep = gdn.make_prefill_args(cu, x["q_raw"], x["k_raw"], x["v_raw"], pool, prs, pws,
+                                          H_qk=Hqk, H_v=Hv, a_raw=x["a_raw"], b_raw=x["b_raw"],
+                                          conv_wq=x["conv_wq"], conv_wk=x["conv_wk"],
+                                          conv_wv=x["conv_wv"])
+    lib = gdn.load_library()
+    s = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def mixed():
+        code = lib.gdn_mixed(ctypes.byref(da), ctypes.byref(pa), s())
+        if code:
+            raise gdn.GdnError("gdn_mixed", code)
+
+    def separate():
+        for fn, a in ((lib.gdn_decode, da), (lib.gdn_prefill, pa)):
+            code = fn(ctypes.byref(a), s())
+            if code:
+                raise gdn.GdnError("separate", code)
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms_mixed = timed(mixed, args.prefill_reps)
+    ms_sep = timed(separate, args.prefill_reps)
+    tokens = nd + npf * L
+    return dict(workload="mixed", decode_requests=nd, prefill_tokens=npf * L,
+                ms=round(ms_mixed, 3), tokens_per_s=round(tokens / (ms_mixed / 1e3), 1),
+                separate_ms=round(ms_sep, 3), speedup_vs_separate=round(ms_sep / ms_mixed, 3))
+
+
 def run_cpu_baseline(args, torch, layers, syn):
     """The FP64 oracle on layers 0 and L-1 at full batch (every request-head),
     timed on this host's cores; tokens/s extrapolated to all layers."""
@@ -293,6 +344,11 @@ def main():
         torch.cuda.empty_cache()
         prefill = run_prefill(args, torch, gdn, syn)
         log(f"prefill: {prefill}")
+    mixed = None
+    if not args.no_prefill:
+        torch.cuda.empty_cache()
+        mixed = run_mixed(args, torch, gdn, syn)
+        log(f"mixed: {mixed}")
     out = {
         "metric": METRIC,
         "value": round(dec["tokens_per_s"], 1),
@@ -316,6 +372,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "prefill": prefill,
+        "mixed": mixed,
     }
     print(json.dumps(out), flush=True)
 
