@@ -191,7 +191,7 @@ def oracle_frontend(cu, x, Hqk, Hv):
 @pytest.mark.parametrize("dk,dv", [(128, 128), (16, 64), (64, 16)])
 def test_frontend(adt, dk, dv):
     say("frontend", adt, dk, dv)
-    lengths = [1, 2, 5, 70, 131]
+    lengths = [1, 2, 0, 5, 70, 0, 131]  # starts inside 64-token runs, empty sequences, ragged end
     Hqk, Hv = 2, 4
     cu, x = frontend_case(301, lengths, Hqk, Hv, dk, dv, adt)
     q, k, v, g, beta = gdn_frontend(dev(cu), dev(x["q_raw"]), dev(x["k_raw"]), dev(x["v_raw"]),
