@@ -20,17 +20,21 @@
 // beta = 0, g = 0), so they add nothing and gamma_last is the last real
 // token's.
 //
-// Every matrix product runs on MFMA with operands read from LDS as fragments
-// of 8 K-consecutive elements (K-contiguous layouts: the right-hand operand
-// of each product is stored transposed).  With BF16 activations (F32 =
-// false) the operands are BF16 and each product is one
-// v_mfma_f32_16x16x32_bf16 per 32-wide K slab, FP32 accumulate -- measured at
-// ~6e-3 scaled error over 8192 tokens against the FP64 oracle, inside the 2e-2
-// bar.  With FP32 activations (F32 = true) the operands stay FP32 and each
-// slab is eight v_mfma_f32_16x16x4f32, for the 1e-4 bar.  The state M is FP32
-// in accumulator registers in both.  T is formed in FP32 on the vector ALUs by
-// blocked forward substitution (16 x 16 diagonal blocks, then three levels of
-// off-diagonal blocks).
+// Every product runs on MFMA with FP32 accumulation.  The recurrence is
+// independent per state column (a column of M only ever meets the same column
+// of V, R, U and O), so each wave owns a slice of d_v columns and keeps its
+// columns of M, of K M and Q M, of R, U and O in its own accumulator
+// registers: the M-dependent half of a chunk needs no LDS round trip and no
+// barrier.  An accumulator tile serves directly as the right-hand operand of
+// the next product through a permuted K order (see bfrag); the left-hand
+// operands Q, K, T, L o P and the scaled K^T are chunk-local, formed once per
+// chunk in LDS.  With BF16 activations (F32 = false) operands are BF16, one
+// v_mfma_f32_16x16x32_bf16 per 32-wide K slab -- measured at ~6e-3 scaled
+// error over 8192 tokens against the FP64 oracle, inside the 2e-2 bar.  With
+// FP32 activations (F32 = true) they stay FP32, eight v_mfma_f32_16x16x4f32
+// per slab, for the 1e-4 bar.  T is formed in FP32 by blocked forward
+// substitution (16 x 16 diagonal blocks, then three levels of off-diagonal
+// blocks on FP32 MFMA).
 #pragma once
 
 #include <math.h>
@@ -68,21 +72,17 @@ struct PrefillLayout {
   static constexpr int C = 64;
   static constexpr int DKP = DK < 32 ? 32 : DK;  // MFMA K-steps are 32 wide
   static constexpr int PADE = 16 / (int)sizeof(OT);
-  static constexpr int LDK = DKP + PADE;  // Kh, Qh (token rows), Mt (column rows)
-  static constexpr int LDC = C + PADE;    // Kt, Sq, Rt (rows of 64 tokens)
+  static constexpr int LDK = DKP + PADE;  // Kh, Qh (token rows)
+  static constexpr int LDC = C + PADE;    // Kt, Sq (rows of 64 tokens)
   static constexpr int LDF = C + 4;       // Af, Tf (float)
+  static constexpr int LDV = DV + PADE;   // Vh / Oh rows (64 tokens x d_v)
   static constexpr size_t KH = 0;
   static constexpr size_t QH = KH + (size_t)C * LDK * sizeof(OT);
   static constexpr size_t KT = QH + (size_t)C * LDK * sizeof(OT);
-  static constexpr size_t MT = KT + (size_t)DK * LDC * sizeof(OT);
-  static constexpr size_t SQ = MT + (size_t)DV * LDK * sizeof(OT);
-  static constexpr int LDV = DV + PADE;   // Vh / Oh rows (64 tokens x d_v)
+  static constexpr size_t SQ = KT + (size_t)DK * LDC * sizeof(OT);
   static constexpr size_t VH = SQ + (size_t)C * LDC * sizeof(OT);  // V, then O, row-major
-  static constexpr size_t RT = VH + (size_t)C * LDV * sizeof(OT);
-  static constexpr size_t RT_BYTES = (size_t)DV * LDC * sizeof(OT);
-  static constexpr size_t AF_BYTES = (size_t)C * LDF * 4;
-  // Af (only live while T is formed) shares its bytes with Rt/Ut
-  static constexpr size_t TF = RT + (RT_BYTES > AF_BYTES ? RT_BYTES : AF_BYTES);
+  static constexpr size_t AF = VH + (size_t)C * LDV * sizeof(OT);
+  static constexpr size_t TF = AF + (size_t)C * LDF * 4;
   static constexpr size_t GATES = TF + (size_t)C * LDF * 4;  // G, gamma, beta, eGn
   static constexpr size_t XS = GATES + 4 * C * 4;            // 4 x 16 x 17 floats
   static constexpr size_t BYTES = XS + 4 * 16 * 17 * 4;
@@ -140,24 +140,63 @@ __device__ __forceinline__ f32x4_t mma(f32x4_t c, const Frag<F32> &a, const Frag
   return c;
 }
 
-// Split of an NX x NY grid of 16 x 16 tiles over the 4 waves: by columns when
-// there are at least 4 column blocks (each wave then shares its column
-// fragments across all rows), else by rows, else one tile per wave.
-template <int NX, int NY>
-struct TileSplit {
-  static constexpr int BY_Y = NY >= 4, BY_X = !BY_Y && NX >= 4;
-  static constexpr int PER = BY_Y ? NX * (NY / 4) : (BY_X ? (NX / 4) * NY : 1);
-  static constexpr int XN = BY_Y ? NX : (BY_X ? NX / 4 : 1);  // rows per wave
-  static constexpr int YN = BY_Y ? NY / 4 : (BY_X ? NY : 1);  // columns per wave
-  // tile j of wave w -> (x, y); valid() false for waves without a tile
-  __device__ static __forceinline__ int x(int w, int j) {
-    return BY_Y ? j / YN : (BY_X ? w * XN + j / YN : w / NY);
+// ---- accumulator tiles as right-hand operands ------------------------------
+//
+// An FP32 accumulator tile of a 16 x 16 product holds, in lane l = 16 g + n,
+// rows 4g .. 4g+3 of column n.  Two stacked tiles (rows 0-15 = lo, 16-31 =
+// hi) give lane (g, n) the eight values B[k][n] for k in {4g..4g+3} and
+// {16+4g..16+4g+3}.  Feeding those as the lane's eight K-elements of a
+// 32-wide slab, with the left-hand operand's elements taken at the same k
+// (load_afrag), sums over all 32 k exactly once: the K order inside a slab is
+// permuted, the product is not.  So the output of one product becomes the
+// right-hand operand of the next without leaving the wave's registers.
+
+template <bool F32>
+__device__ __forceinline__ Frag<F32> bfrag(const f32x4_t &lo, const f32x4_t &hi) {
+  Frag<F32> f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (F32) {
+      f.v[i] = lo[i];
+      f.v[4 + i] = hi[i];
+    } else {
+      f.v[i] = (__bf16)lo[i];  // round to nearest even
+      f.v[4 + i] = (__bf16)hi[i];
+    }
   }
-  __device__ static __forceinline__ int y(int w, int j) {
-    return BY_Y ? w * YN + j % YN : (BY_X ? j % YN : w % NY);
+  return f;
+}
+
+// Left-hand fragment matching bfrag's K order: lane (g, m) holds row r0 + m
+// at columns k0 + 4g + {0..3} and k0 + 16 + 4g + {0..3}.
+template <bool F32>
+__device__ __forceinline__ Frag<F32> load_afrag(const uint16_t *base, int ld, int r0, int k0) {
+  static_assert(!F32, "FP32 fragments come from float buffers");
+  const int l = threadIdx.x & 63;
+  const uint16_t *row = base + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+  uint4 u;
+  const uint2 a = *reinterpret_cast<const uint2 *>(row);
+  const uint2 b = *reinterpret_cast<const uint2 *>(row + 16);
+  u.x = a.x; u.y = a.y; u.z = b.x; u.w = b.y;
+  Frag<false> f;
+  f.v = __builtin_bit_cast(bf16x8_t, u);
+  return f;
+}
+template <bool F32>
+__device__ __forceinline__ Frag<F32> load_afrag(const float *base, int ld, int r0, int k0) {
+  const int l = threadIdx.x & 63;
+  const float *row = base + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
+  const float4 x0 = *reinterpret_cast<const float4 *>(row);
+  const float4 x1 = *reinterpret_cast<const float4 *>(row + 16);
+  const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+  Frag<F32> f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if constexpr (F32) f.v[j] = x[j];
+    else f.v[j] = (__bf16)x[j];  // round to nearest even
   }
-  __device__ static __forceinline__ bool valid(int w) { return BY_Y || BY_X || w < NX * NY; }
-};
+  return f;
+}
 
 // 2^x on the hardware transcendental unit (v_exp_f32)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }

@@ -6,6 +6,10 @@
 // loaded into registers while chunk c computes, and written to LDS at the
 // end of chunk c, so no chunk waits on a global-memory round trip.  The
 // workgroup barriers wait only on LDS (lgkmcnt), not on these loads.
+//
+// Work split: the chunk-local half (S, P, A, L o P, the scaled K^T, T) is
+// shared by the 4 waves through LDS; the M-dependent half runs per wave on
+// the wave's own d_v columns (NA column blocks of 16), entirely in registers.
 #pragma once
 
 #include <algorithm>
@@ -14,11 +18,6 @@
 
 namespace gdn {
 
-template <typename OT>
-__device__ __forceinline__ void put4(OT *p, const float *x) {
-#pragma unroll
-  for (int e = 0; e < 4; ++e) put(p + e, x[e]);
-}
 // four consecutive operand elements as floats
 __device__ __forceinline__ void get4(const uint16_t *p, float *x) {
   const uint2 u = *reinterpret_cast<const uint2 *>(p);
@@ -65,9 +64,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   constexpr int NKB = L::DKP / 32;  // MFMA K-steps over d_k
   constexpr int DKB = DK / 16;      // 16-row blocks of d_k
   constexpr int DVB = DV / 16;      // 16-column blocks of d_v
-  using MS = TileSplit<DKB, DVB>;  // tiles of the state (d_k x d_v)
-  using OS = TileSplit<4, DVB>;    // tiles of a 64 x d_v product
-  constexpr int MPW = MS::PER, OPW = OS::PER;
+  constexpr int NA = DVB >= 4 ? DVB / 4 : 1;  // d_v blocks per wave
   constexpr int EW = 8 * (int)sizeof(AT) / 16;  // 16-byte vectors per 8 elements
   constexpr int KQ_GROUPS = C * (DK / 8), KQ_PER = (KQ_GROUPS + 255) / 256;
   constexpr int V_GROUPS = C * (DV / 8), V_PER = (V_GROUPS + 255) / 256;
@@ -75,11 +72,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   OT *Kh = reinterpret_cast<OT *>(smem + L::KH);
   OT *Qh = reinterpret_cast<OT *>(smem + L::QH);
   OT *Kt = reinterpret_cast<OT *>(smem + L::KT);
-  OT *Mt = reinterpret_cast<OT *>(smem + L::MT);
   OT *Sq = reinterpret_cast<OT *>(smem + L::SQ);
   OT *Vh = reinterpret_cast<OT *>(smem + L::VH);  // V rows, then the chunk's O rows
-  OT *Rt = reinterpret_cast<OT *>(smem + L::RT);  // R, then U, transposed
-  float *Af = reinterpret_cast<float *>(smem + L::RT);  // shares bytes with Rt
+  float *Af = reinterpret_cast<float *>(smem + L::AF);
   float *Tf = reinterpret_cast<float *>(smem + L::TF);
   float *Gs = reinterpret_cast<float *>(smem + L::GATES);  // cumulative log2 decay
   float *gam = Gs + C, *bet = Gs + 2 * C, *eGn = Gs + 3 * C;
@@ -170,31 +165,32 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   // padded K columns (d_k < 32 only) stay zero for the whole chain
   if constexpr (L::DKP > DK) {
     constexpr int PADC = L::DKP - DK;
-    for (int i = tid; i < (2 * C + DV) * PADC; i += 256) {
+    for (int i = tid; i < 2 * C * PADC; i += 256) {
       const int row = i / PADC, c = DK + i % PADC;
       if (row < C) put(Kh + row * LDK + c, 0.f);
-      else if (row < 2 * C) put(Qh + (row - C) * LDK + c, 0.f);
-      else put(Mt + (row - 2 * C) * LDK + c, 0.f);
+      else put(Qh + (row - C) * LDK + c, 0.f);
     }
   }
 
-  // ---- initial state (a8): read slot -> FP32 accumulators and Mt ----
-  f32x4_t macc[MPW];
+  // ---- initial state (a8): read slot -> FP32 accumulators ----
+  // macc[b][ia]: rows 16b.. of d_k, columns 16 (wave NA + ia).. of d_v, in the
+  // accumulator layout (lane (g, n): rows 4g..4g+3 of column n)
+  const bool mwave = DVB >= 4 || wave < DVB;  // waves that own d_v columns
+  f32x4_t macc[DKB][NA];
   const int64_t state_base = (rs * p.H_v + h) * (int64_t)DK * DV;
-  const bool mvalid = MS::valid(wave), ovalid = OS::valid(wave);
 #pragma unroll
-  for (int j = 0; j < MPW; ++j) {
-    float x[4] = {0.f, 0.f, 0.f, 0.f};
-    if (mvalid) {
-      const int d = 16 * MS::x(wave, j) + rq, c = 16 * MS::y(wave, j) + col;
-      if (rs >= 0) {
+  for (int b = 0; b < DKB; ++b) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[e] = Elem<SB>::load1(p.pool, state_base + (int64_t)(d + e) * DV + c);
+    for (int ia = 0; ia < NA; ++ia) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) macc[b][ia][e] = 0.f;
+      if (mwave && rs >= 0) {
+        const int d = 16 * b + rq, c = 16 * (wave * NA + ia) + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          macc[b][ia][e] = Elem<SB>::load1(p.pool, state_base + (int64_t)(d + e) * DV + c);
       }
-      put4(Mt + c * LDK + d, x);
     }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) macc[j][e] = x[e];
   }
   if (t_begin < t_end) {
     fetch(t_begin, (int)std::min<int64_t>(C, t_end - t_begin));
@@ -327,136 +323,127 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       }
     }
 
-    // ---- 5: Q M, K M (a7); R = beta (V - gamma K M) -> Rt ----
-    f32x4_t qm[OPW], ur[OPW];
+    // ---- 5-8: the wave's d_v columns, in registers ----
+    if (mwave) {
+      // accumulator tile pair k-slab s of M: d_k blocks 2s, 2s+1 (zero past d_k)
+      auto mfrag = [&](int s2, int ia) {
+        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+        return bfrag<F32>(macc[2 * s2][ia], 2 * s2 + 1 < DKB ? macc[2 * s2 + 1][ia] : z);
+      };
+      // 5: Q M and K M (a7), all 64 rows x the wave's columns
+      f32x4_t qm[4][NA], um[4][NA];
 #pragma unroll
-    for (int j = 0; j < OPW; ++j) {
+      for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) qm[j][e] = ur[j][e] = 0.f;
-    }
-    if (ovalid) {
-#pragma unroll 1
-      for (int kk = 0; kk < NKB; ++kk) {
-        Frag<F32> fm[OS::YN], fq[OS::XN], fk[OS::XN];
+        for (int ia = 0; ia < NA; ++ia) {
 #pragma unroll
-        for (int yi = 0; yi < OS::YN; ++yi)
-          fm[yi] = load_frag<F32>(Mt, LDK, 16 * OS::y(wave, yi), 32 * kk);
-#pragma unroll
-        for (int xi = 0; xi < OS::XN; ++xi) {
-          fq[xi] = load_frag<F32>(Qh, LDK, 16 * OS::x(wave, xi * OS::YN), 32 * kk);
-          if (erase) fk[xi] = load_frag<F32>(Kh, LDK, 16 * OS::x(wave, xi * OS::YN), 32 * kk);
-        }
-#pragma unroll
-        for (int j = 0; j < OPW; ++j) {
-          const int xi = j / OS::YN, yi = j % OS::YN;
-          qm[j] = mma<F32>(qm[j], fq[xi], fm[yi]);
-          if (erase) ur[j] = mma<F32>(ur[j], fk[xi], fm[yi]);  // K M for now
+          for (int e = 0; e < 4; ++e) qm[tb][ia][e] = um[tb][ia][e] = 0.f;
         }
       }
 #pragma unroll
-      for (int j = 0; j < OPW; ++j) {
-        const int r0 = 16 * OS::x(wave, j) + rq, c = 16 * OS::y(wave, j) + col;
-        float vv[4], x[4];
+      for (int s2 = 0; s2 < NKB; ++s2) {
+        Frag<F32> fm[NA];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) vv[e] = get(Vh + (r0 + e) * LDV + c);
+        for (int ia = 0; ia < NA; ++ia) fm[ia] = mfrag(s2, ia);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = r0 + e;
-          x[e] = erase ? bet[r] * (vv[e] - gam[r] * ur[j][e]) : vv[e];
-          ur[j][e] = x[e];
-        }
-        put4(Rt + c * LDC + r0, x);
-      }
-    }
-    __syncthreads();
-
-    // ---- 6: U = T R (delta rules; otherwise U = R already in Rt) ----
-    if (erase) {
-      if (ovalid) {
+        for (int tb = 0; tb < 4; ++tb) {
+          const Frag<F32> fq = load_afrag<F32>(Qh, LDK, 16 * tb, 32 * s2);
 #pragma unroll
-        for (int j = 0; j < OPW; ++j) {
+          for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], fq, fm[ia]);
+          if (erase) {
+            const Frag<F32> fk = load_afrag<F32>(Kh, LDK, 16 * tb, 32 * s2);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) ur[j][e] = 0.f;
-        }
-#pragma unroll 1
-        for (int kk = 0; kk < 2; ++kk) {
-          Frag<F32> fr[OS::YN], ft[OS::XN];
-#pragma unroll
-          for (int yi = 0; yi < OS::YN; ++yi)
-            fr[yi] = load_frag<F32>(Rt, LDC, 16 * OS::y(wave, yi), 32 * kk);
-#pragma unroll
-          for (int xi = 0; xi < OS::XN; ++xi)
-            ft[xi] = load_frag<F32>(Tf, LDF, 16 * OS::x(wave, xi * OS::YN), 32 * kk);
-#pragma unroll
-          for (int j = 0; j < OPW; ++j) {
-            if (32 * kk > 16 * OS::x(wave, j) + 15) continue;  // T is lower triangular
-            ur[j] = mma<F32>(ur[j], ft[j / OS::YN], fr[j % OS::YN]);
+            for (int ia = 0; ia < NA; ++ia) um[tb][ia] = mma<F32>(um[tb][ia], fk, fm[ia]);
           }
         }
       }
-      __syncthreads();  // every wave has read R
-      if (ovalid) {
+      // R = beta (V - gamma K M) for the delta rules, else R = V; um holds R
 #pragma unroll
-        for (int j = 0; j < OPW; ++j) {
-          float x[4] = {ur[j][0], ur[j][1], ur[j][2], ur[j][3]};
-          put4(Rt + (16 * OS::y(wave, j) + col) * LDC + 16 * OS::x(wave, j) + rq, x);
+      for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * tb + rq + e;
+          const float br = bet[r], gr = gam[r];
+#pragma unroll
+          for (int ia = 0; ia < NA; ++ia) {
+            const float vv = get(Vh + r * LDV + 16 * (wave * NA + ia) + col);
+            um[tb][ia][e] = erase ? br * (vv - gr * um[tb][ia][e]) : vv;
+          }
         }
       }
-      __syncthreads();
-    }
-
-    // ---- 7: O = gamma Q M + Sq U (a7), scaled, to HBM ----
-    if (ovalid) {
+      // 6: U = T R (delta rules; T is lower triangular, so row block tb needs
+      // only the slabs s2 <= tb / 2)
+      if (erase) {
+        f32x4_t uu[4][NA];
 #pragma unroll
-      for (int j = 0; j < OPW; ++j) {
+        for (int tb = 0; tb < 4; ++tb) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) qm[j][e] *= gam[16 * OS::x(wave, j) + rq + e];
-      }
-#pragma unroll 1
-      for (int kk = 0; kk < 2; ++kk) {
-        Frag<F32> fu[OS::YN], fs[OS::XN];
+          for (int ia = 0; ia < NA; ++ia) {
 #pragma unroll
-        for (int yi = 0; yi < OS::YN; ++yi)
-          fu[yi] = load_frag<F32>(Rt, LDC, 16 * OS::y(wave, yi), 32 * kk);
+            for (int e = 0; e < 4; ++e) uu[tb][ia][e] = 0.f;
+          }
+        }
 #pragma unroll
-        for (int xi = 0; xi < OS::XN; ++xi)
-          fs[xi] = load_frag<F32>(Sq, LDC, 16 * OS::x(wave, xi * OS::YN), 32 * kk);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          Frag<F32> fr[NA];
 #pragma unroll
-        for (int j = 0; j < OPW; ++j) {
-          if (32 * kk > 16 * OS::x(wave, j) + 15) continue;  // Sq is lower triangular
-          qm[j] = mma<F32>(qm[j], fs[j / OS::YN], fu[j % OS::YN]);
+          for (int ia = 0; ia < NA; ++ia) fr[ia] = bfrag<F32>(um[2 * s2][ia], um[2 * s2 + 1][ia]);
+#pragma unroll
+          for (int tb = 2 * s2; tb < 4; ++tb) {
+            const Frag<F32> ft = load_afrag<F32>(Tf, LDF, 16 * tb, 32 * s2);
+#pragma unroll
+            for (int ia = 0; ia < NA; ++ia) uu[tb][ia] = mma<F32>(uu[tb][ia], ft, fr[ia]);
+          }
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+          for (int ia = 0; ia < NA; ++ia) um[tb][ia] = uu[tb][ia];
         }
       }
-      // O into the V rows' LDS (V was consumed in step 5); written to HBM as whole
-      // rows after the next barrier
+      // 7: O = gamma Q M + (L o P) U (a7), scaled, into the wave's columns of
+      // the V rows' LDS (this wave's V columns were consumed above)
+      Frag<F32> fu[2][NA];
 #pragma unroll
-      for (int j = 0; j < OPW; ++j) {
-        const int c = 16 * OS::y(wave, j) + col;
+      for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          put(Vh + (16 * OS::x(wave, j) + rq + e) * LDV + c, p.scale * qm[j][e]);
+        for (int ia = 0; ia < NA; ++ia) fu[s2][ia] = bfrag<F32>(um[2 * s2][ia], um[2 * s2 + 1][ia]);
       }
-    }
-
-    // ---- 8: M <- gamma_last M + Kt U (FP32 accumulators), refresh Mt ----
-    if (mvalid) {
+#pragma unroll
+      for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int ia = 0; ia < NA; ++ia) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) qm[tb][ia][e] *= gam[16 * tb + rq + e];
+        }
+#pragma unroll
+        for (int s2 = 0; s2 <= tb / 2; ++s2) {
+          const Frag<F32> fs = load_afrag<F32>(Sq, LDC, 16 * tb, 32 * s2);
+#pragma unroll
+          for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], fs, fu[s2][ia]);
+        }
+#pragma unroll
+        for (int ia = 0; ia < NA; ++ia) {
+          const int c = 16 * (wave * NA + ia) + col;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) put(Vh + (16 * tb + rq + e) * LDV + c, p.scale * qm[tb][ia][e]);
+        }
+      }
+      // 8: M <- gamma_last M + Kt U
       const float gl = gam[C - 1];
 #pragma unroll
-      for (int j = 0; j < MPW; ++j) {
+      for (int b = 0; b < DKB; ++b) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) macc[j][e] *= gl;
-      }
-#pragma unroll 1
-      for (int kk = 0; kk < 2; ++kk) {
-        Frag<F32> fu[MS::YN], fk[MS::XN];
+        for (int ia = 0; ia < NA; ++ia) {
 #pragma unroll
-        for (int yi = 0; yi < MS::YN; ++yi)
-          fu[yi] = load_frag<F32>(Rt, LDC, 16 * MS::y(wave, yi), 32 * kk);
+          for (int e = 0; e < 4; ++e) macc[b][ia][e] *= gl;
+        }
 #pragma unroll
-        for (int xi = 0; xi < MS::XN; ++xi)
-          fk[xi] = load_frag<F32>(Kt, LDC, 16 * MS::x(wave, xi * MS::YN), 32 * kk);
+        for (int s2 = 0; s2 < 2; ++s2) {
+          const Frag<F32> fk = load_afrag<F32>(Kt, LDC, 16 * b, 32 * s2);
 #pragma unroll
-        for (int j = 0; j < MPW; ++j) macc[j] = mma<F32>(macc[j], fk[j / MS::YN], fu[j % MS::YN]);
+          for (int ia = 0; ia < NA; ++ia) macc[b][ia] = mma<F32>(macc[b][ia], fk, fu[s2][ia]);
+        }
       }
     }
     __syncthreads();  // all reads of this chunk's LDS operands are done; O is in Vh
@@ -472,25 +459,22 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       }
     }
     __syncthreads();  // O rows read out of Vh before the next chunk's V lands there
-    if (mvalid) {
-#pragma unroll
-      for (int j = 0; j < MPW; ++j) {
-        float x[4] = {macc[j][0], macc[j][1], macc[j][2], macc[j][3]};
-        put4(Mt + (16 * MS::y(wave, j) + col) * LDK + 16 * MS::x(wave, j) + rq, x);
-      }
-    }
     if (more) stage();  // next chunk's K, Q, V and gates into LDS
     __syncthreads();
   }
 
   // ---- final state (a8): FP32 -> state dtype (RNE for BF16) -> write slot ----
-  if (ws >= 0 && mvalid) {
+  if (ws >= 0 && mwave) {
     const int64_t out_base = (ws * p.H_v + h) * (int64_t)DK * DV;
 #pragma unroll
-    for (int j = 0; j < MPW; ++j) {
-      const int d = 16 * MS::x(wave, j) + rq, c = 16 * MS::y(wave, j) + col;
+    for (int b = 0; b < DKB; ++b) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) Elem<SB>::store1(p.pool, out_base + (int64_t)(d + e) * DV + c, macc[j][e]);
+      for (int ia = 0; ia < NA; ++ia) {
+        const int d = 16 * b + rq, c = 16 * (wave * NA + ia) + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Elem<SB>::store1(p.pool, out_base + (int64_t)(d + e) * DV + c, macc[b][ia][e]);
+      }
     }
   }
 }
