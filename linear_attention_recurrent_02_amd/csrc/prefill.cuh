@@ -9,9 +9,9 @@
 // DeltaNet-2 section says is Gated DeltaNet):
 //
 //   S = K K^T,  P = Q K^T                                    (intra-chunk)
-//   A[r,s] = beta_r exp(G_r - G_s) S[r,s]  (s < r),  T = (I + A)^-1
+//   A[r,s] = beta_r exp(G_r - G_s) S[r,s]  (s < r)
 //   R = diag(beta) (V - diag(gamma) K M)                      (needs M)
-//   U = T R                        (= the per-token residual writes u_r)
+//   U = (I + A)^-1 R               (= the per-token residual writes u_r)
 //   O = diag(gamma) Q M + (L o P) U,  L[r,s] = exp(G_r - G_s) (s <= r)
 //   M <- gamma_last M + (diag(exp(G_last - G)) K)^T U
 //
@@ -32,9 +32,11 @@
 // v_mfma_f32_16x16x32_bf16 per 32-wide K slab -- measured at ~6e-3 scaled
 // error over 8192 tokens against the FP64 oracle, inside the 2e-2 bar.  With
 // FP32 activations (F32 = true) they stay FP32, eight v_mfma_f32_16x16x4f32
-// per slab, for the 1e-4 bar.  T is formed in FP32 by blocked forward
-// substitution (16 x 16 diagonal blocks, then three levels of off-diagonal
-// blocks on FP32 MFMA).
+// per slab, for the 1e-4 bar.  U = (I + A)^-1 R is solved by block forward
+// substitution over the four 16-row blocks, each wave on its own columns:
+// U_i = T_ii (R_i - sum_{j<i} A_ij U_j), with T_ii = (I + A_ii)^-1 formed in
+// FP32 on the vector ALUs (every wave forms all four, so no wave waits on
+// another) and the 16-wide products on MFMA.
 #pragma once
 
 #include <math.h>
@@ -82,10 +84,11 @@ struct PrefillLayout {
   static constexpr size_t SQ = KT + (size_t)DK * LDC * sizeof(OT);
   static constexpr size_t VH = SQ + (size_t)C * LDC * sizeof(OT);  // V, then O, row-major
   static constexpr size_t AF = VH + (size_t)C * LDV * sizeof(OT);
-  static constexpr size_t TF = AF + (size_t)C * LDF * 4;
-  static constexpr size_t GATES = TF + (size_t)C * LDF * 4;  // G, gamma, beta, eGn
-  static constexpr size_t XS = GATES + 4 * C * 4;            // 4 x 16 x 17 floats
-  static constexpr size_t BYTES = XS + 4 * 16 * 17 * 4;
+  static constexpr int LDT = 20;  // T_ii rows (float); 16-byte aligned rows
+  static constexpr size_t TW = AF + (size_t)C * LDF * 4;  // per wave: 4 blocks T_ii
+  static constexpr size_t TW_WAVE = (size_t)C * LDT;      // floats per wave
+  static constexpr size_t GATES = TW + 4 * TW_WAVE * 4;   // G, gamma, beta, eGn
+  static constexpr size_t BYTES = GATES + 4 * C * 4;
 };
 
 // ---- MFMA fragments -------------------------------------------------------
@@ -196,6 +199,57 @@ __device__ __forceinline__ Frag<F32> load_afrag(const float *base, int ld, int r
     else f.v[j] = (__bf16)x[j];  // round to nearest even
   }
   return f;
+}
+
+// ---- 16-wide K products -----------------------------------------------------
+//
+// One accumulator tile is exactly the right-hand operand of a K = 16 product
+// (v_mfma_f32_16x16x16_bf16: lane (g, n) holds B[4g + j][n]; FP32: four
+// v_mfma_f32_16x16x4f32, instruction j taking k = 4g + j); the left-hand
+// operand's lane (g, m) holds row m at columns 4g .. 4g+3.
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+template <bool F32> struct Frag16;
+template <> struct Frag16<false> { s16x4_t v; };
+template <> struct Frag16<true> { float v[4]; };
+
+template <bool F32>
+__device__ __forceinline__ Frag16<F32> bfrag16(const f32x4_t &x) {
+  Frag16<F32> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (F32) f.v[j] = x[j];
+    else f.v[j] = __builtin_bit_cast(short, (__bf16)x[j]);  // round to nearest even
+  }
+  return f;
+}
+
+// rows r0 .. r0+15, columns k0 .. k0+15 of a row-major float matrix, times sgn
+template <bool F32>
+__device__ __forceinline__ Frag16<F32> load_afrag16(const float *base, int ld, int r0, int k0,
+                                                    float sgn) {
+  const int l = threadIdx.x & 63;
+  const float4 x = *reinterpret_cast<const float4 *>(base + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4));
+  const float y[4] = {sgn * x.x, sgn * x.y, sgn * x.z, sgn * x.w};
+  Frag16<F32> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (F32) f.v[j] = y[j];
+    else f.v[j] = __builtin_bit_cast(short, (__bf16)y[j]);
+  }
+  return f;
+}
+
+template <bool F32>
+__device__ __forceinline__ f32x4_t mma16(f32x4_t c, const Frag16<F32> &a, const Frag16<F32> &b) {
+  if constexpr (F32) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], c, 0, 0, 0);
+  } else {
+    c = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.v, b.v, c, 0, 0, 0);
+  }
+  return c;
 }
 
 // 2^x on the hardware transcendental unit (v_exp_f32)

@@ -75,10 +75,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   OT *Sq = reinterpret_cast<OT *>(smem + L::SQ);
   OT *Vh = reinterpret_cast<OT *>(smem + L::VH);  // V rows, then the chunk's O rows
   float *Af = reinterpret_cast<float *>(smem + L::AF);
-  float *Tf = reinterpret_cast<float *>(smem + L::TF);
+  float *Tw = reinterpret_cast<float *>(smem + L::TW) + (threadIdx.x >> 6) * L::TW_WAVE;  // this wave's T_ii
   float *Gs = reinterpret_cast<float *>(smem + L::GATES);  // cumulative log2 decay
   float *gam = Gs + C, *bet = Gs + 2 * C, *eGn = Gs + 3 * C;
-  float *XS = reinterpret_cast<float *>(smem + L::XS);
 
   const int seq = chain / p.H_v, h = chain % p.H_v, hq = h / p.group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -262,10 +261,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     }
     __syncthreads();
 
-    // ---- 4: T = (I + A)^-1 (FP32, blocked forward substitution) ----
-    if (erase) {
-      if (wave == 0) {
-        // the four 16 x 16 diagonal blocks: lane -> (block, column)
+    // ---- 5-8: the wave's d_v columns, in registers ----
+    if (mwave) {
+      // T_bb = (I + A_bb)^-1 for the four diagonal 16 x 16 blocks, by forward
+      // substitution: lane (bb, c) forms column c of T_bb; into this wave's Tw
+      if (erase) {
         const int bb = lane >> 4, c = lane & 15;
         float tc[16];
 #pragma unroll
@@ -273,58 +273,12 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           float x = r == c ? 1.f : 0.f;
           const float *arow = Af + (16 * bb + r) * LDF + 16 * bb;
 #pragma unroll
-          for (int s = 0; s < r; ++s) x = fmaf(-arow[s], tc[s], x);
+          for (int s2 = 0; s2 < r; ++s2) x = fmaf(-arow[s2], tc[s2], x);
           tc[r] = x;
         }
 #pragma unroll
-        for (int r = 0; r < 16; ++r) Tf[(16 * bb + r) * LDF + 16 * bb + c] = tc[r];
-      } else {
-        // zero the strictly upper blocks
-        for (int i = tid - 64; i < 6 * 256; i += 192) {
-          const int blk = i >> 8, e = i & 255;
-          const int bi = blk < 3 ? 0 : (blk < 5 ? 1 : 2);
-          const int bj = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-          Tf[(16 * bi + (e >> 4)) * LDF + 16 * bj + (e & 15)] = 0.f;
-        }
+        for (int r = 0; r < 16; ++r) Tw[(16 * bb + r) * L::LDT + c] = tc[r];
       }
-      __syncthreads();
-      // off-diagonal blocks by levels: T_ij = -T_ii sum_{k=j}^{i-1} A_ik T_kj, each 16 x 16
-      // x 16 product as four v_mfma_f32_16x16x4f32 (lane l: A[l%16][k0 + l/16],
-      // B[k0 + l/16][l%16]; result rows 4(l/16)..+3, column l%16)
-      const int lr = lane & 15, lk = lane >> 4;
-#pragma unroll
-      for (int lv = 1; lv < 4; ++lv) {
-        const bool act = wave < 4 - lv;
-        const int bj = wave, bi = wave + lv;
-        float *xs = XS + wave * 16 * 17;
-        if (act) {
-          f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-          for (int kb = bj; kb < bi; ++kb) {
-#pragma unroll
-            for (int k0 = 0; k0 < 16; k0 += 4)
-              x = __builtin_amdgcn_mfma_f32_16x16x4f32(Af[(16 * bi + lr) * LDF + 16 * kb + k0 + lk],
-                                                       Tf[(16 * kb + k0 + lk) * LDF + 16 * bj + lr],
-                                                       x, 0, 0, 0);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) xs[(rq + e) * 17 + col] = x[e];
-        }
-        __syncthreads();
-        if (act) {
-          f32x4_t y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k0 = 0; k0 < 16; k0 += 4)
-            y = __builtin_amdgcn_mfma_f32_16x16x4f32(Tf[(16 * bi + lr) * LDF + 16 * bi + k0 + lk],
-                                                     xs[(k0 + lk) * 17 + lr], y, 0, 0, 0);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) Tf[(16 * bi + rq + e) * LDF + 16 * bj + col] = -y[e];
-        }
-        __syncthreads();
-      }
-    }
-
-    // ---- 5-8: the wave's d_v columns, in registers ----
-    if (mwave) {
       // accumulator tile pair k-slab s of M: d_k blocks 2s, 2s+1 (zero past d_k)
       auto mfrag = [&](int s2, int ia) {
         const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
@@ -371,28 +325,26 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           }
         }
       }
-      // 6: U = T R (delta rules; T is lower triangular, so row block tb needs
-      // only the slabs s2 <= tb / 2)
+      // 6: U = (I + A)^-1 R (delta rules), block forward substitution:
+      // U_i = T_ii (R_i - sum_{j<i} A_ij U_j), 16-row blocks i = 0..3
       if (erase) {
         f32x4_t uu[4][NA];
 #pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
+        for (int i = 0; i < 4; ++i) {
+          f32x4_t x[NA];
+#pragma unroll
+          for (int ia = 0; ia < NA; ++ia) x[ia] = um[i][ia];
+#pragma unroll
+          for (int j = 0; j < i; ++j) {
+            const Frag16<F32> fa = load_afrag16<F32>(Af, LDF, 16 * i, 16 * j, -1.f);
+#pragma unroll
+            for (int ia = 0; ia < NA; ++ia) x[ia] = mma16<F32>(x[ia], fa, bfrag16<F32>(uu[j][ia]));
+          }
+          const Frag16<F32> ft = load_afrag16<F32>(Tw, L::LDT, 16 * i, 0, 1.f);
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) uu[tb][ia][e] = 0.f;
-          }
-        }
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          Frag<F32> fr[NA];
-#pragma unroll
-          for (int ia = 0; ia < NA; ++ia) fr[ia] = bfrag<F32>(um[2 * s2][ia], um[2 * s2 + 1][ia]);
-#pragma unroll
-          for (int tb = 2 * s2; tb < 4; ++tb) {
-            const Frag<F32> ft = load_afrag<F32>(Tf, LDF, 16 * tb, 32 * s2);
-#pragma unroll
-            for (int ia = 0; ia < NA; ++ia) uu[tb][ia] = mma<F32>(uu[tb][ia], ft, fr[ia]);
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            uu[i][ia] = mma16<F32>(z, ft, bfrag16<F32>(x[ia]));
           }
         }
 #pragma unroll
