@@ -27,8 +27,7 @@
 // registers: the M-dependent half of a chunk needs no LDS round trip and no
 // barrier.  An accumulator tile serves directly as the right-hand operand of
 // the next product through a permuted K order (see bfrag); the left-hand
-// operands Q, K, T, L o P and the scaled K^T are chunk-local, formed once per
-// chunk in LDS.  With BF16 activations (F32 = false) operands are BF16, one
+// operands (Q, K, K^T, A, T_ii, L o P) are chunk-local and read from LDS.  With BF16 activations (F32 = false) operands are BF16, one
 // v_mfma_f32_16x16x32_bf16 per 32-wide K slab -- measured at ~6e-3 scaled
 // error over 8192 tokens against the FP64 oracle, inside the 2e-2 bar.  With
 // FP32 activations (F32 = true) they stay FP32, eight v_mfma_f32_16x16x4f32
@@ -75,13 +74,12 @@ struct PrefillLayout {
   static constexpr int DKP = DK < 32 ? 32 : DK;  // MFMA K-steps are 32 wide
   static constexpr int PADE = 16 / (int)sizeof(OT);
   static constexpr int LDK = DKP + PADE;  // Kh, Qh (token rows)
-  static constexpr int LDC = C + PADE;    // Kt, Sq (rows of 64 tokens)
+  static constexpr int LDC = C + PADE;    // Sq (rows of 64 tokens)
   static constexpr int LDF = C + 4;       // Af, Tf (float)
   static constexpr int LDV = DV + PADE;   // Vh / Oh rows (64 tokens x d_v)
   static constexpr size_t KH = 0;
   static constexpr size_t QH = KH + (size_t)C * LDK * sizeof(OT);
-  static constexpr size_t KT = QH + (size_t)C * LDK * sizeof(OT);
-  static constexpr size_t SQ = KT + (size_t)DK * LDC * sizeof(OT);
+  static constexpr size_t SQ = QH + (size_t)C * LDK * sizeof(OT);
   static constexpr size_t VH = SQ + (size_t)C * LDC * sizeof(OT);  // V, then O, row-major
   static constexpr size_t AF = VH + (size_t)C * LDV * sizeof(OT);
   static constexpr int LDT = 20;  // T_ii rows (float); 16-byte aligned rows
@@ -197,6 +195,42 @@ __device__ __forceinline__ Frag<F32> load_afrag(const float *base, int ld, int r
   for (int j = 0; j < 8; ++j) {
     if constexpr (F32) f.v[j] = x[j];
     else f.v[j] = (__bf16)x[j];  // round to nearest even
+  }
+  return f;
+}
+
+// The same fragment of a transposed operand: lane (g, m) holds column r0 + m
+// of a row-major matrix at rows k0 + 4g + {0..3} and k0 + 16 + 4g + {0..3},
+// i.e. A[m][k] = base[k][r0 + m] -- one element per read, down the column.
+template <bool F32>
+__device__ __forceinline__ Frag<F32> load_afrag_t(const uint16_t *base, int ld, int r0, int k0) {
+  static_assert(!F32, "FP32 fragments come from float buffers");
+  const int l = threadIdx.x & 63;
+  const uint16_t *c = base + (k0 + 4 * (l >> 4)) * ld + r0 + (l & 15);
+  uint16_t x[8];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    x[j] = c[j * ld];
+    x[4 + j] = c[(16 + j) * ld];
+  }
+  Frag<false> f;
+  f.v = __builtin_bit_cast(bf16x8_t, x);
+  return f;
+}
+template <bool F32>
+__device__ __forceinline__ Frag<F32> load_afrag_t(const float *base, int ld, int r0, int k0) {
+  const int l = threadIdx.x & 63;
+  const float *c = base + (k0 + 4 * (l >> 4)) * ld + r0 + (l & 15);
+  Frag<F32> f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (F32) {
+      f.v[j] = c[j * ld];
+      f.v[4 + j] = c[(16 + j) * ld];
+    } else {
+      f.v[j] = (__bf16)c[j * ld];
+      f.v[4 + j] = (__bf16)c[(16 + j) * ld];
+    }
   }
   return f;
 }

@@ -18,30 +18,6 @@
 
 namespace gdn {
 
-// four consecutive operand elements as floats
-__device__ __forceinline__ void get4(const uint16_t *p, float *x) {
-  const uint2 u = *reinterpret_cast<const uint2 *>(p);
-  x[0] = bf16_lo(u.x); x[1] = bf16_hi(u.x); x[2] = bf16_lo(u.y); x[3] = bf16_hi(u.y);
-}
-__device__ __forceinline__ void get4(const float *p, float *x) {
-  const float4 v = *reinterpret_cast<const float4 *>(p);
-  x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-}
-// eight consecutive operand elements <-> floats
-__device__ __forceinline__ void get8(const uint16_t *p, float *x) {
-  Elem<true>::unpack(*reinterpret_cast<const uint4 *>(p), x);
-}
-__device__ __forceinline__ void get8(const float *p, float *x) {
-  const float4 a = reinterpret_cast<const float4 *>(p)[0], b = reinterpret_cast<const float4 *>(p)[1];
-  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-}
-__device__ __forceinline__ void put8(uint16_t *p, const float *x) {
-  *reinterpret_cast<uint4 *>(p) = Elem<true>::pack(x);
-}
-__device__ __forceinline__ void put8(float *p, const float *x) {
-  reinterpret_cast<float4 *>(p)[0] = make_float4(x[0], x[1], x[2], x[3]);
-  reinterpret_cast<float4 *>(p)[1] = make_float4(x[4], x[5], x[6], x[7]);
-}
 // Chain c of blockIdx b: inside each group of 16 blocks, chains 2m and 2m+1
 // (the two state heads that share a q/k head when H_v = 2 H_qk) go to blocks
 // m and m + 8, which the dispatcher places on the same XCD (blocks are dealt
@@ -71,7 +47,6 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   constexpr float LOG2E = 1.4426950408889634f;
   OT *Kh = reinterpret_cast<OT *>(smem + L::KH);
   OT *Qh = reinterpret_cast<OT *>(smem + L::QH);
-  OT *Kt = reinterpret_cast<OT *>(smem + L::KT);
   OT *Sq = reinterpret_cast<OT *>(smem + L::SQ);
   OT *Vh = reinterpret_cast<OT *>(smem + L::VH);  // V rows, then the chunk's O rows
   float *Af = reinterpret_cast<float *>(smem + L::AF);
@@ -183,7 +158,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     for (int ia = 0; ia < NA; ++ia) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) macc[b][ia][e] = 0.f;
-      if (mwave && rs >= 0) {
+    }
+  }
+  if (mwave && rs >= 0) {  // one branch around all the loads, so they overlap
+#pragma unroll
+    for (int b = 0; b < DKB; ++b) {
+#pragma unroll
+      for (int ia = 0; ia < NA; ++ia) {
         const int d = 16 * b + rq, c = 16 * (wave * NA + ia) + col;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -203,14 +184,26 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     const bool more = t1 < t_end;
     if (more) fetch(t1, (int)std::min<int64_t>(C, t_end - t1));  // in flight until staged
 
-    // ---- 2: S = K K^T and P = Q K^T, row block `wave` (a6) ----
+    // ---- 2 and 5: S = K K^T, P = Q K^T for row block `wave` (a6), and Q M,
+    // K M (a7) for the wave's d_v columns.  All of them read only this chunk's
+    // K and Q rows and the state, so they share one pass over the d_k slabs
+    // and their MFMAs interleave. ----
     f32x4_t sacc[4], pacc[4];
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) sacc[cb][e] = pacc[cb][e] = 0.f;
     }
-#pragma unroll 1
+    f32x4_t qm[4][NA], um[4][NA];
+#pragma unroll
+    for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+      for (int ia = 0; ia < NA; ++ia) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) qm[tb][ia][e] = um[tb][ia][e] = 0.f;
+      }
+    }
+#pragma unroll
     for (int kk = 0; kk < NKB; ++kk) {
       const Frag<F32> fk = load_frag<F32>(Kh, LDK, 16 * wave, 32 * kk);
       const Frag<F32> fq = load_frag<F32>(Qh, LDK, 16 * wave, 32 * kk);
@@ -220,8 +213,28 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         if (erase) sacc[cb] = mma<F32>(sacc[cb], fk, fb);
         pacc[cb] = mma<F32>(pacc[cb], fq, fb);
       }
+      if (mwave) {
+        // the state's accumulator tile pair for d_k blocks 2kk, 2kk+1 (zero past d_k)
+        Frag<F32> fm[NA];
+#pragma unroll
+        for (int ia = 0; ia < NA; ++ia) {
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          fm[ia] = bfrag<F32>(macc[2 * kk][ia], 2 * kk + 1 < DKB ? macc[2 * kk + 1][ia] : z);
+        }
+#pragma unroll
+        for (int tb = 0; tb < 4; ++tb) {
+          const Frag<F32> aq = load_afrag<F32>(Qh, LDK, 16 * tb, 32 * kk);
+#pragma unroll
+          for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], aq, fm[ia]);
+          if (erase) {
+            const Frag<F32> ak = load_afrag<F32>(Kh, LDK, 16 * tb, 32 * kk);
+#pragma unroll
+            for (int ia = 0; ia < NA; ++ia) um[tb][ia] = mma<F32>(um[tb][ia], ak, fm[ia]);
+          }
+        }
+      }
     }
-    // ---- 3: A = strict_lower(beta_r e^{G_r-G_s} S), Sq = lower(e^{G_r-G_s} P), Kt ----
+    // ---- 3: A = strict_lower(beta_r e^{G_r-G_s} S), Sq = lower(e^{G_r-G_s} P) ----
     {
       float Gr[4], br[4], Gc[4];
 #pragma unroll
@@ -240,23 +253,6 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           Af[r * LDF + s] = (erase && s < r) ? br[e] * dec * sacc[cb][e] : 0.f;
           put(Sq + r * LDC + s, dec * pacc[cb][e]);
         }
-      }
-    }
-    // Kt[d][s] = exp(G_last - G_s) K[s][d], by 8 x 8 blocks
-    for (int blk = tid; blk < (C / 8) * (DK / 8); blk += 256) {
-      const int sb = blk % (C / 8), db = blk / (C / 8);
-      float x[8][8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) get8(Kh + (8 * sb + i) * LDK + 8 * db, x[i]);
-      float sc[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) sc[i] = eGn[8 * sb + i];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float y[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) y[i] = sc[i] * x[i][j];
-        put8(Kt + (8 * db + j) * LDC + 8 * sb, y);
       }
     }
     __syncthreads();
@@ -278,38 +274,6 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) Tw[(16 * bb + r) * L::LDT + c] = tc[r];
-      }
-      // accumulator tile pair k-slab s of M: d_k blocks 2s, 2s+1 (zero past d_k)
-      auto mfrag = [&](int s2, int ia) {
-        const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-        return bfrag<F32>(macc[2 * s2][ia], 2 * s2 + 1 < DKB ? macc[2 * s2 + 1][ia] : z);
-      };
-      // 5: Q M and K M (a7), all 64 rows x the wave's columns
-      f32x4_t qm[4][NA], um[4][NA];
-#pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-        for (int ia = 0; ia < NA; ++ia) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) qm[tb][ia][e] = um[tb][ia][e] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < NKB; ++s2) {
-        Frag<F32> fm[NA];
-#pragma unroll
-        for (int ia = 0; ia < NA; ++ia) fm[ia] = mfrag(s2, ia);
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const Frag<F32> fq = load_afrag<F32>(Qh, LDK, 16 * tb, 32 * s2);
-#pragma unroll
-          for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], fq, fm[ia]);
-          if (erase) {
-            const Frag<F32> fk = load_afrag<F32>(Kh, LDK, 16 * tb, 32 * s2);
-#pragma unroll
-            for (int ia = 0; ia < NA; ++ia) um[tb][ia] = mma<F32>(um[tb][ia], fk, fm[ia]);
-          }
-        }
       }
       // R = beta (V - gamma K M) for the delta rules, else R = V; um holds R
 #pragma unroll
@@ -381,7 +345,22 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           for (int e = 0; e < 4; ++e) put(Vh + (16 * tb + rq + e) * LDV + c, p.scale * qm[tb][ia][e]);
         }
       }
-      // 8: M <- gamma_last M + Kt U
+      // 8: M <- gamma_last M + K^T diag(exp(G_last - G)) U: the decay weights
+      // scale U's rows; K^T's fragments are read down the columns of the K rows
+      Frag<F32> fe[2][NA];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+#pragma unroll
+        for (int ia = 0; ia < NA; ++ia) {
+          f32x4_t lo = um[2 * s2][ia], hi = um[2 * s2 + 1][ia];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] *= eGn[32 * s2 + rq + e];
+            hi[e] *= eGn[32 * s2 + 16 + rq + e];
+          }
+          fe[s2][ia] = bfrag<F32>(lo, hi);
+        }
+      }
       const float gl = gam[C - 1];
 #pragma unroll
       for (int b = 0; b < DKB; ++b) {
@@ -392,9 +371,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         }
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
-          const Frag<F32> fk = load_afrag<F32>(Kt, LDC, 16 * b, 32 * s2);
+          const Frag<F32> fk = load_afrag_t<F32>(Kh, LDK, 16 * b, 32 * s2);
 #pragma unroll
-          for (int ia = 0; ia < NA; ++ia) macc[b][ia] = mma<F32>(macc[b][ia], fk, fu[s2][ia]);
+          for (int ia = 0; ia < NA; ++ia) macc[b][ia] = mma<F32>(macc[b][ia], fk, fe[s2][ia]);
         }
       }
     }
