@@ -28,6 +28,16 @@ CXXFLAGS = [
 ]
 
 
+# Per-source extra flags.  The chunked-prefill sources keep their MFMA
+# accumulators in ordinary VGPRs (the "VGPR form" of MFMA): the chain
+# post-processes every accumulator tile on the vector ALUs, and with AGPR
+# accumulators each of those touches costs an extra register move.
+PER_SOURCE = {
+    "prefill.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "mixed.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
         if cand and os.path.exists(cand):
@@ -54,7 +64,8 @@ def build(jobs: int | None = None, extra: list[str] | None = None, verbose: bool
     objs = [os.path.join(BUILD, os.path.basename(s)[:-4] + ".o") for s in srcs]
     jobs = jobs or min(8, len(srcs), os.cpu_count() or 1)
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        futs = [ex.submit(_compile, s, o, extra or []) for s, o in zip(srcs, objs)]
+        futs = [ex.submit(_compile, s, o, PER_SOURCE.get(os.path.basename(s), []) + (extra or []))
+                for s, o in zip(srcs, objs)]
         for f in futs:
             f.result()
     tmp = LIB + ".tmp"

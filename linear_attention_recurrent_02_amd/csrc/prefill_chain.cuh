@@ -289,32 +289,23 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           }
         }
       }
-      // 6: U = (I + A)^-1 R (delta rules), block forward substitution:
-      // U_i = T_ii (R_i - sum_{j<i} A_ij U_j), 16-row blocks i = 0..3
+      // 6: U = (I + A)^-1 R (delta rules), block forward substitution in
+      // place: um[i] <- T_ii (R_i - sum_{j<i} A_ij U_j), 16-row blocks i = 0..3
       if (erase) {
-        f32x4_t uu[4][NA];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f32x4_t x[NA];
-#pragma unroll
-          for (int ia = 0; ia < NA; ++ia) x[ia] = um[i][ia];
 #pragma unroll
           for (int j = 0; j < i; ++j) {
             const Frag16<F32> fa = load_afrag16<F32>(Af, LDF, 16 * i, 16 * j, -1.f);
 #pragma unroll
-            for (int ia = 0; ia < NA; ++ia) x[ia] = mma16<F32>(x[ia], fa, bfrag16<F32>(uu[j][ia]));
+            for (int ia = 0; ia < NA; ++ia) um[i][ia] = mma16<F32>(um[i][ia], fa, bfrag16<F32>(um[j][ia]));
           }
           const Frag16<F32> ft = load_afrag16<F32>(Tw, L::LDT, 16 * i, 0, 1.f);
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia) {
             const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            uu[i][ia] = mma16<F32>(z, ft, bfrag16<F32>(x[ia]));
+            um[i][ia] = mma16<F32>(z, ft, bfrag16<F32>(um[i][ia]));
           }
-        }
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-          for (int ia = 0; ia < NA; ++ia) um[tb][ia] = uu[tb][ia];
         }
       }
       // 7: O = gamma Q M + (L o P) U (a7), scaled, into the wave's columns of
