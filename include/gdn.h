@@ -87,8 +87,12 @@ typedef enum gdn_status {
   GDN_ERR_SLOTS = 8        /* gdn_validate_slots found a range error or a hazard */
 } gdn_status;
 
-/* bit set in the optional device status word when a request was skipped */
+/* bits set in the optional device status word: a request (decode) or
+ * sequence (prefill) was skipped because of a slot index outside
+ * [-1, n_slots), or a prefill sequence whose offsets lie outside
+ * [0, n_tokens] or decrease */
 #define GDN_DEVICE_BAD_SLOT 1u
+#define GDN_DEVICE_BAD_SEQ 2u
 
 /* Decode: one token for each of B requests (the per-token recurrence of the
  * "Gated DeltaNet" glossary entry, Technical definition; the residual /
@@ -136,7 +140,9 @@ typedef struct gdn_prefill_args {
   int64_t n_slots;
   float scale;         /* read-out scale */
   float eps;           /* L2-norm epsilon (front-end only), e.g. 1e-6 */
-  const int32_t *cu_seqlens; /* [n_seq + 1] device, non-decreasing, cu[0] = 0, cu[n_seq] = n_tokens */
+  const int32_t *cu_seqlens; /* [n_seq + 1] device, non-decreasing, cu[0] = 0, cu[n_seq] = n_tokens;
+                                a sequence s with cu[s] < 0, cu[s+1] < cu[s] or cu[s+1] > n_tokens is
+                                skipped (no o, no state) and sets GDN_DEVICE_BAD_SEQ */
   const void *q;       /* [n_tokens, H_qk * d_k] act_dtype (raw or final) */
   const void *k;       /* [n_tokens, H_qk * d_k] act_dtype */
   const void *v;       /* [n_tokens, H_v * d_v] act_dtype */

@@ -123,7 +123,7 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
   for (int j = s + 1; j < p.n_seq; ++j) {
     const int64_t c = p.cu[j];
     if (c >= te) break;
-    resets |= 1ull << (c - ts);
+    if (c >= ts) resets |= 1ull << (c - ts);  // (offsets below ts only if they decrease)
   }
 
   // x1, x2, x3 = the previous three tokens of this piece (0 before the sequence)

@@ -52,7 +52,7 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 struct PrefillParams {
   int32_t n_seq, H_qk, H_v, group;
-  int64_t n_slots;
+  int64_t n_tokens, n_slots;
   float scale;
   int32_t rule;
   const int32_t *cu;

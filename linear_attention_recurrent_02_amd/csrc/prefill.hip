@@ -21,7 +21,7 @@ PrefillParams make_prefill_params(const gdn_prefill_args &a, const void *q, cons
                                   const void *v, const float *g, const float *beta) {
   PrefillParams p;
   p.n_seq = a.n_seq; p.H_qk = a.H_qk; p.H_v = a.H_v; p.group = a.H_v / a.H_qk;
-  p.n_slots = a.n_slots; p.scale = a.scale; p.rule = a.rule; p.cu = a.cu_seqlens;
+  p.n_tokens = a.n_tokens; p.n_slots = a.n_slots; p.scale = a.scale; p.rule = a.rule; p.cu = a.cu_seqlens;
   p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
   p.pool = a.state_pool; p.read_slot = a.read_slot; p.write_slot = a.write_slot;
   p.o = a.o; p.status = a.status;

@@ -64,6 +64,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     if (tid == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
     return;
   }
+  if (t_begin < 0 || t_end < t_begin || t_end > p.n_tokens) {  // offsets break the contract
+    if (tid == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SEQ);
+    return;
+  }
   const bool decay = (p.rule & kRuleDecay) != 0;
   const bool erase = (p.rule & kRuleErase) != 0;
 

@@ -20,6 +20,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3}
 F32, BF16 = 0, 1
 DEVICE_BAD_SLOT = 1
+DEVICE_BAD_SEQ = 2
 
 _P = ctypes.c_void_p
 _I32 = ctypes.c_int32

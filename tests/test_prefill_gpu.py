@@ -170,6 +170,33 @@ def test_prefill_bad_slot_status():
     assert seq_err(f64(o[:40]), ro[:40], [0, 40]) < 1e-4
 
 
+@pytest.mark.parametrize("bad_cu", [[0, 40, 120], [0, 60, 40]])
+def test_prefill_bad_offsets_status(bad_cu):
+    """A sequence whose offsets break the cu_seqlens contract (ending past
+    n_tokens, or decreasing) is skipped and flags GDN_DEVICE_BAD_SEQ; the other
+    sequence is computed as usual.  The kernel's own offset check keeps every
+    access inside the token arrays."""
+    say("prefill bad offsets", bad_cu)
+    case = prefill_case(208, [40, 40], 1, 2, 32, 32, 4, torch.float32, torch.float32, std=0.3)
+    cu, q, k, v, g, beta, pool, rs, ws = case
+    bad = torch.tensor(bad_cu, dtype=torch.int32)
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dpool = dev(pool)
+    o = torch.full((80, 2, 32), 5.0, device=DEV)
+    gdn_prefill(dev(bad), dev(q), dev(k), dev(v), dpool, dev(rs), dev(ws), o, H_qk=1, H_v=2,
+                g=dev(g), beta=dev(beta), status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 2
+    first = bad_cu[1] if bad_cu[1] <= 80 else 80
+    ro, rpool, code = oracle.sequences(np.array([0, first]), f64(q[:first]), f64(k[:first]),
+                                       f64(v[:first]), f64(g[:first]), f64(beta[:first]),
+                                       f64(pool), rs[:1].numpy(), ws[:1].numpy())
+    assert code == 0
+    assert seq_err(f64(o[:first]), ro, [0, first]) < 1e-4
+    assert torch.all(o[first:].cpu() == 5.0)  # the skipped sequence wrote nothing
+    assert scaled_err(f64(dpool)[ws[1]], f64(pool)[ws[1]], 2) == 0  # nor its state
+
+
 # --------------------------------------------------------------------------
 # front-end
 
