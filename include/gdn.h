@@ -24,7 +24,10 @@
  *
  * Conventions shared by every call:
  *  - Every tensor argument is a DEVICE pointer to contiguous row-major memory
- *    that the caller owns; the library never allocates, frees or
+ *    that the caller owns, aligned to its element size; q, k, v, o, the
+ *    state pool, the front-end's raw inputs, conv weights and outputs, and
+ *    the workspace are read and written as 16-byte vectors and must be
+ *    16-byte aligned (GDN_ERR_ALIGN otherwise); the library never allocates, frees or
  *    synchronises, keeps no global mutable state, and reads argument structs
  *    only during the call.  All work is enqueued on `stream` (a hipStream_t;
  *    NULL = the null stream).
@@ -84,7 +87,8 @@ typedef enum gdn_status {
   GDN_ERR_UNSUPPORTED = 5, /* a valid but unsupported size (d, chunk, conv width, head ratio) */
   GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than gdn_prefill_workspace_size */
   GDN_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
-  GDN_ERR_SLOTS = 8        /* gdn_validate_slots found a range error or a hazard */
+  GDN_ERR_SLOTS = 8,       /* gdn_validate_slots found a range error or a hazard */
+  GDN_ERR_ALIGN = 9        /* a tensor pointer that is read as 16-byte vectors is not 16-byte aligned */
 } gdn_status;
 
 /* bits set in the optional device status word: a request (decode) or

@@ -11,6 +11,8 @@ namespace {
 bool supported_d(int32_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool valid_dtype(int32_t t) { return t == GDN_F32 || t == GDN_BF16; }
 bool valid_rule(int32_t r) { return r >= GDN_RULE_LINEAR && r <= GDN_RULE_GATED_DELTA; }
+// pointers the kernels access as 16-byte vectors (NULL passes: absence is checked separately)
+bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 gdn_status check_heads(int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v) {
   if (H_qk <= 0 || H_v <= 0 || d_k <= 0 || d_v <= 0) return GDN_ERR_SHAPE;
@@ -33,6 +35,8 @@ gdn_status check_decode(const gdn_decode_args *a) {
   if ((a->rule & gdn::kRuleDecay) && !a->g) return GDN_ERR_NULL;
   if ((a->rule & gdn::kRuleErase) && !a->beta) return GDN_ERR_NULL;
   if ((!a->read_slot || !a->write_slot) && a->n_slots < a->B) return GDN_ERR_SHAPE;
+  if (!al16(a->q) || !al16(a->k) || !al16(a->v) || !al16(a->o) || !al16(a->state_pool))
+    return GDN_ERR_ALIGN;
   return GDN_OK;
 }
 
@@ -67,7 +71,11 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
       if ((a->rule & gdn::kRuleErase) && !a->beta) return GDN_ERR_NULL;
     }
   }
+  if (!al16(a->q) || !al16(a->k) || !al16(a->v)) return GDN_ERR_ALIGN;
+  if (a->use_frontend && (!al16(a->conv_wq) || !al16(a->conv_wk) || !al16(a->conv_wv)))
+    return GDN_ERR_ALIGN;
   if (!need_state) return GDN_OK;
+  if (!al16(a->o) || !al16(a->state_pool) || !al16(a->workspace)) return GDN_ERR_ALIGN;
   // FP32 activations keep FP32 MFMA operands in LDS, which fits d_k, d_v <= 64
   if (a->act_dtype == GDN_F32 && (a->d_k > 64 || a->d_v > 64)) return GDN_ERR_UNSUPPORTED;
   if ((!a->read_slot || !a->write_slot) && a->n_slots < a->n_seq) return GDN_ERR_SHAPE;
@@ -111,6 +119,7 @@ gdn_status gdn_frontend(const gdn_prefill_args *args, void *q_out, void *k_out, 
   if (!args->use_frontend) return GDN_ERR_UNSUPPORTED;
   if (args->n_seq == 0 || args->n_tokens == 0) return GDN_OK;
   if (!q_out || !k_out || !v_out || !g_out || !beta_out) return GDN_ERR_NULL;
+  if (!al16(q_out) || !al16(k_out) || !al16(v_out)) return GDN_ERR_ALIGN;
   if (!args->a_raw || !args->b_raw) return GDN_ERR_NULL;
   return gdn::launch_frontend(*args, q_out, k_out, v_out, g_out, beta_out,
                               static_cast<hipStream_t>(stream));
@@ -168,6 +177,7 @@ const char *gdn_status_string(int32_t status) {
     case GDN_ERR_WORKSPACE: return "workspace missing or too small";
     case GDN_ERR_LAUNCH: return "kernel launch failed";
     case GDN_ERR_SLOTS: return "slot index out of range or slot hazard";
+    case GDN_ERR_ALIGN: return "a vector-accessed tensor is not 16-byte aligned";
   }
   return "unknown status";
 }

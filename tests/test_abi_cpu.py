@@ -11,7 +11,7 @@ import linear_attention_recurrent_02_amd as gdn
 from linear_attention_recurrent_02_amd import gdn as B
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-OK, NULL, SHAPE, DTYPE, RULE, UNSUP, WORKSPACE, LAUNCH, SLOTS = range(9)
+OK, NULL, SHAPE, DTYPE, RULE, UNSUP, WORKSPACE, LAUNCH, SLOTS, ALIGN = range(10)
 FAKE = 0x10000  # never dereferenced: these calls fail validation before any device work
 
 
@@ -52,8 +52,8 @@ def test_parse_rule():
 
 
 def test_status_strings():
-    for c in range(9):
-        assert gdn.gdn_status_string(c)
+    for c in range(10):
+        assert gdn.gdn_status_string(c) != "unknown status"
     assert gdn.gdn_status_string(99) == "unknown status"
 
 
@@ -81,6 +81,8 @@ def _call_decode(a):
     (dict(q=None), NULL), (dict(state_pool=None), NULL), (dict(o=None), NULL),
     (dict(g=None), NULL), (dict(beta=None), NULL),
     (dict(n_slots=3), SHAPE),  # identity slots need n_slots >= B
+    (dict(q=FAKE + 2), ALIGN), (dict(v=FAKE + 8), ALIGN), (dict(o=FAKE + 4), ALIGN),
+    (dict(state_pool=FAKE + 2), ALIGN),
 ])
 def test_decode_validation(over, code):
     assert _call_decode(_decode_args(**over)) == code
@@ -117,6 +119,9 @@ def _prefill_args(**over):
     (dict(conv_wk=None), NULL), (dict(a_raw=None), NULL), (dict(state_pool=None), NULL),
     (dict(H_v=5), UNSUP), (dict(d_v=96), UNSUP), (dict(n_slots=1), SHAPE),
     (dict(), WORKSPACE),  # the fused front-end needs gdn_prefill_workspace_size() bytes
+    (dict(q=FAKE + 2), ALIGN), (dict(v=FAKE + 8), ALIGN), (dict(conv_wv=FAKE + 4), ALIGN),
+    (dict(o=FAKE + 2), ALIGN), (dict(state_pool=FAKE + 8), ALIGN),
+    (dict(workspace=FAKE + 8, workspace_bytes=1 << 40), ALIGN),
 ])
 def test_prefill_validation(over, code):
     lib = gdn.load_library()
