@@ -226,3 +226,17 @@ def test_decode_b512_full_size_sampled():
     assert scaled_err(f64(o.cpu()[sel]), ro, 2) < 2e-2
     after = pool[ws[sample].long().to(DEV)].cpu()
     assert scaled_err(f64(after), rpool, 2) < 2e-2
+
+
+@pytest.mark.parametrize("B,n_slots", [(4200, 8400), (64, 40000)])
+def test_decode_request_order_fallback(B, n_slots):
+    """Batches larger than the slot-order table (B > 4096) or pools larger than
+    its bitmap (n_slots > 32768) are walked in request order; results are the
+    same as ever (small heads keep the oracle quick)."""
+    say("decode order fallback", B, n_slots)
+    case = make_case(9, B, 1, 2, 16, 16, n_slots, torch.bfloat16, torch.float32)
+    o, dpool, ro, rpool, code = run_both(case, "gated_delta")
+    assert code == 0
+    ws = case[7].numpy()
+    assert scaled_err(f64(o), ro, 2) < tol(torch.bfloat16)
+    assert scaled_err(f64(dpool.cpu())[ws], rpool[ws], 2) < tol(torch.bfloat16)

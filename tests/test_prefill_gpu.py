@@ -170,6 +170,21 @@ def test_prefill_bad_slot_status():
     assert seq_err(f64(o[:40]), ro[:40], [0, 40]) < 1e-4
 
 
+def test_prefill_many_short_sequences():
+    """300 sequences of 0..150 tokens (chain count not a multiple of the
+    16-chain block groups, many one-chunk and empty sequences), gated_delta,
+    BF16 state in a 600-slot pool."""
+    say("prefill many short sequences")
+    lengths = np.random.default_rng(11).integers(0, 151, size=300)
+    lengths[::37] = 0
+    case = prefill_case(209, lengths, 1, 2, 32, 32, 600, torch.bfloat16, torch.bfloat16,
+                        fresh=range(0, 300, 5))
+    o, dpool, ro, rpool = run_prefill_both(case, "gated_delta")
+    cu, ws = case[0], case[8].numpy()
+    assert seq_err(f64(o), ro, cu) < 2e-2
+    assert scaled_err(f64(dpool.cpu())[ws], rpool[ws], 2) < 2e-2
+
+
 @pytest.mark.parametrize("bad_cu", [[0, 40, 120], [0, 60, 40]])
 def test_prefill_bad_offsets_status(bad_cu):
     """A sequence whose offsets break the cu_seqlens contract (ending past
