@@ -28,6 +28,18 @@ __device__ __forceinline__ void opaque(uint4 &v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
 
+// 16-byte loads and stores marked non-temporal (streamed once: no reason to
+// keep the line in the caches).
+typedef unsigned int nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_load16(const void *p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(static_cast<const nt_u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_store16(void *p, const uint4 &v) {
+  nt_u32x4 w = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(w, static_cast<nt_u32x4 *>(p));
+}
+
 // Element type of a tensor: BF16 (stored as uint16) or FP32.
 template <bool BF16> struct Elem;
 template <> struct Elem<true> {

@@ -9,9 +9,10 @@
 //
 // HBM-bound elementwise work, laid out so that every raw byte is read once
 // and every load and store is a whole-row stream.  A thread owns one 16-byte
-// piece of a row (8 BF16 or 4 FP32 channels) and walks a run of consecutive
-// tokens, keeping the three previous tokens of its channels in registers, so
-// the conv window costs no re-reads.  The threads of a workgroup cover a
+// piece of a row (8 BF16 or 4 FP32 channels) and walks a contiguous range of
+// 64-token runs, keeping the three previous tokens of its channels in
+// registers, so the conv window costs no re-reads.  The grid is sized so that
+// every workgroup is resident at once and the ranges are balanced.  The threads of a workgroup cover a
 // contiguous span of a row (q, k or v; several row groups per workgroup when
 // the row is shorter than 256 pieces), so each token's loads and stores are
 // contiguous across lanes.  A head's pieces sit in neighbouring lanes of one
@@ -19,14 +20,19 @@
 // loads of its next 8 tokens in flight while it computes.
 #include <math.h>
 
+#include <algorithm>
+#include <type_traits>
+
 #include "device.h"
 #include "internal.h"
 
 namespace gdn {
 
 constexpr int kFeThreads = 256;
-constexpr int kFeRun = 64;    // consecutive tokens per row group
+constexpr int kFeRun = 64;    // tokens per run (one 64-bit mask of sequence starts)
+constexpr int kFeCuLds = 4096;  // sequence offsets kept in LDS (more: read from global memory)
 constexpr int kFeDepth = 8;   // tokens loaded ahead per thread
+constexpr int kFeBlocksPerCU = 3;  // resident workgroups per CU the grid aims at
 static_assert(kFeRun <= 64, "sequence starts in a run are a 64-bit mask");
 static_assert(kFeRun % kFeDepth == 0, "a whole run is a whole number of ring turns");
 
@@ -50,6 +56,7 @@ struct FrontendParams {
   FeTensor t[3];      // q, k, v
   int32_t y0[4];      // first blockIdx.y of q, k, v; y0[3] = total
   int32_t x_blocks[3];  // blockIdx.x extent of each tensor (row groups differ)
+  int32_t runs_per[3];  // 64-token runs per row group
   const float *a_raw, *b_raw;
   float *g_out, *beta_out;
 };
@@ -80,7 +87,8 @@ __device__ __forceinline__ float silu_fast(float x) {
 }
 
 template <bool AB, int D, bool NORM, bool GATES>
-__device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &T, int chunk) {
+__device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &T, int chunk,
+                                       int runs_per, const int32_t *cu) {
   using E = Elem<AB>;
   constexpr int CH = E::kPer16B;  // channels per piece
   constexpr int PPH = D / CH;     // pieces per head (power of two, at most 32)
@@ -91,14 +99,15 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
   const int piece = chunk * lpr + lane;
   // whole heads are active or not: lpr and pieces are multiples of PPH
   if (piece >= T.pieces) return;
-  const int64_t ts = ((int64_t)blockIdx.x * R + rg) * kFeRun;
-  const int64_t te = min(ts + (int64_t)kFeRun, p.n_tokens);
+  const int64_t ts = ((int64_t)blockIdx.x * R + rg) * runs_per * kFeRun;
+  const int64_t te = min(ts + (int64_t)runs_per * kFeRun, p.n_tokens);
   if (ts >= te) return;
 
   const int64_t row_bytes = (int64_t)T.pieces * 16;
   const char *src = static_cast<const char *>(T.raw) + (int64_t)piece * 16;
   char *dst = static_cast<char *>(T.out) + (int64_t)piece * 16;
-  auto ld = [&](int64_t t) { return *reinterpret_cast<const uint4 *>(src + t * row_bytes); };
+  // every raw byte is read once and every output byte written once: stream them
+  auto ld = [&](int64_t t) { return nt_load16(src + t * row_bytes); };
 
   // first the loads that do not depend on the sequence bounds: the ring of
   // the next kFeDepth tokens, the three tokens before ts and the conv taps
@@ -115,16 +124,21 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
 #pragma unroll
   for (int c = 0; c < CH; ++c) w[c] = wsrc[c];
 
-  // bit i of `resets` is set when token ts + i opens a sequence (it equals a
-  // sequence offset cu[j], j >= 1); the conv window is cleared there
-  const int s = seq_of(p.cu, p.n_seq, ts);
-  const int64_t s_start = p.cu[s];
-  uint64_t resets = 0;
-  for (int j = s + 1; j < p.n_seq; ++j) {
-    const int64_t c = p.cu[j];
-    if (c >= te) break;
-    if (c >= ts) resets |= 1ull << (c - ts);  // (offsets below ts only if they decrease)
-  }
+  // the sequence holding ts, and the offsets of the sequences that follow
+  int s = seq_of(cu, p.n_seq, ts);
+  const int64_t s_start = cu[s];
+  // bit i of the mask is set when token r0 + i opens a sequence (equals an
+  // offset cu[j], j >= 1): the conv window is cleared there
+  auto starts_mask = [&](int64_t r0, int64_t r1) {
+    while (s + 1 < p.n_seq && cu[s + 1] < r0) ++s;  // a start at r0 itself stays ahead
+    uint64_t m = 0;
+    for (int j = s + 1; j < p.n_seq; ++j) {
+      const int64_t c = cu[j];
+      if (c >= r1) break;
+      if (c >= r0) m |= 1ull << (c - r0);  // (offsets below r0 only if they decrease)
+    }
+    return m;
+  };
 
   // x1, x2, x3 = the previous three tokens of this piece (0 before the sequence)
   float x1[CH], x2[CH], x3[CH];
@@ -133,9 +147,10 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
   if (ts - 3 < s_start) h3 = make_uint4(0, 0, 0, 0);
   E::unpack(h1, x1); E::unpack(h2, x2); E::unpack(h3, x3);
 
-  // one token: conv + SiLU (+ L2 norm) of x0 given the window, then slide it
-  auto step = [&](const float (&x0)[CH], int64_t t, float (&y)[CH]) {
-    if ((resets >> (t - ts)) & 1ull) {
+  // one token: conv + SiLU (+ L2 norm) of x0 given the window, then slide it;
+  // `check` = the run holds a sequence start (bit i of resets clears the window)
+  auto step = [&](const float (&x0)[CH], bool check, uint64_t resets, int i, float (&y)[CH]) {
+    if (check && ((resets >> i) & 1ull)) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
     }
@@ -157,30 +172,47 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
     }
   };
 
-  if (te - ts == kFeRun) {
-    // a whole run: token t comes from ring slot (t - ts) % kFeDepth, which is
-    // then refilled with token t + kFeDepth (clamped to the run, so every step
-    // issues one load and one store and the waits stay kFeDepth deep)
-    for (int64_t b0 = ts; b0 < te; b0 += kFeDepth) {
+  // whole runs: token t comes from ring slot (t - ts) % kFeDepth, which is
+  // then refilled with token t + kFeDepth (clamped to the range, so every step
+  // issues one load and one store and the waits stay kFeDepth deep)
+  // (runs without a sequence start -- nearly all -- skip the per-token check)
+  auto whole_run = [&](int64_t r0, uint64_t resets, auto check_tag) {
+    constexpr bool check = decltype(check_tag)::value;
+#pragma unroll 1
+    for (int b0 = 0; b0 < kFeRun; b0 += kFeDepth) {
 #pragma unroll
       for (int u = 0; u < kFeDepth; ++u) {
-        const int64_t t = b0 + u;
+        const int64_t t = r0 + b0 + u;
         float x0[CH], y[CH];
         E::unpack(ring[u], x0);
         // refill the slot only after it has been unpacked, so the load can
         // land in the slot's own registers (no copies, no early waits)
         ring[u] = ld(ordered_after(x0, min(t + kFeDepth, tl)));
-        step(x0, t, y);
-        *reinterpret_cast<uint4 *>(dst + t * row_bytes) = E::pack(y);
+        step(x0, check, resets, b0 + u, y);
+        nt_store16(dst + t * row_bytes, E::pack(y));
       }
     }
-  } else {
-    // the ragged last run of the tensor: plain loads, one token at a time
-    for (int64_t t = ts; t < te; ++t) {
-      float x0[CH], y[CH];
-      E::unpack(ld(t), x0);
-      step(x0, t, y);
-      *reinterpret_cast<uint4 *>(dst + t * row_bytes) = E::pack(y);
+  };
+  int64_t r0 = ts;
+  for (; r0 + kFeRun <= te; r0 += kFeRun) {
+    const uint64_t resets = starts_mask(r0, r0 + kFeRun);
+    if (resets == 0) whole_run(r0, resets, std::false_type{});
+    else whole_run(r0, resets, std::true_type{});
+  }
+  if (r0 < te) {
+    // the ragged last run of the tensor: the same steps, stores guarded
+    const uint64_t resets = starts_mask(r0, te);
+#pragma unroll 1
+    for (int b0 = 0; b0 < kFeRun; b0 += kFeDepth) {
+#pragma unroll
+      for (int u = 0; u < kFeDepth; ++u) {
+        const int64_t t = r0 + b0 + u;
+        float x0[CH], y[CH];
+        E::unpack(ring[u], x0);
+        ring[u] = ld(min(t + kFeDepth, tl));
+        step(x0, true, resets, b0 + u, y);
+        if (t < te) nt_store16(dst + t * row_bytes, E::pack(y));
+      }
     }
   }
 
@@ -206,13 +238,22 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
 
 template <bool AB, int DK, int DV>
 __global__ __launch_bounds__(kFeThreads) void frontend_kernel(FrontendParams p) {
+  __shared__ int32_t cu_lds[kFeCuLds + 1];
+  const bool in_lds = p.n_seq <= kFeCuLds;
+  if (in_lds)
+    for (int i = threadIdx.x; i <= p.n_seq; i += kFeThreads) cu_lds[i] = p.cu[i];
+  __syncthreads();
+  const int32_t *cu = in_lds ? cu_lds : p.cu;
   const int y = blockIdx.y;
   if (y < p.y0[1]) {
-    if ((int)blockIdx.x < p.x_blocks[0]) fe_run<AB, DK, true, false>(p, p.t[0], y - p.y0[0]);
+    if ((int)blockIdx.x < p.x_blocks[0])
+      fe_run<AB, DK, true, false>(p, p.t[0], y - p.y0[0], p.runs_per[0], cu);
   } else if (y < p.y0[2]) {
-    if ((int)blockIdx.x < p.x_blocks[1]) fe_run<AB, DK, true, false>(p, p.t[1], y - p.y0[1]);
+    if ((int)blockIdx.x < p.x_blocks[1])
+      fe_run<AB, DK, true, false>(p, p.t[1], y - p.y0[1], p.runs_per[1], cu);
   } else {
-    if ((int)blockIdx.x < p.x_blocks[2]) fe_run<AB, DV, false, true>(p, p.t[2], y - p.y0[2]);
+    if ((int)blockIdx.x < p.x_blocks[2])
+      fe_run<AB, DV, false, true>(p, p.t[2], y - p.y0[2], p.runs_per[2], cu);
   }
 }
 
@@ -243,13 +284,24 @@ gdn_status launch_frontend(const gdn_prefill_args &a, void *q_out, void *k_out, 
   p.t[1] = make_tensor(a.k, k_out, a.conv_wk, a.H_qk, a.d_k, ab);
   p.t[2] = make_tensor(a.v, v_out, a.conv_wv, a.H_v, a.d_v, ab);
   p.a_raw = a.a_raw; p.b_raw = a.b_raw; p.g_out = g_out; p.beta_out = beta_out;
-  int xmax = 0;
   p.y0[0] = 0;
+  for (int i = 0; i < 3; ++i) p.y0[i + 1] = p.y0[i] + p.t[i].chunks;
+  // about kFeBlocksPerCU workgroups per CU in all (each resident at once), the
+  // runs of a tensor dealt out as equal contiguous ranges
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return GDN_ERR_LAUNCH;
+  const int64_t runs = (a.n_tokens + kFeRun - 1) / kFeRun;
+  const int64_t x_target = std::max<int64_t>(1, (int64_t)cus * kFeBlocksPerCU / p.y0[3]);
+  int xmax = 0;
   for (int i = 0; i < 3; ++i) {
-    const int64_t tokens_per_block = (int64_t)(kFeThreads >> p.t[i].lpr_log2) * kFeRun;
+    const int64_t R = kFeThreads >> p.t[i].lpr_log2;  // row groups per workgroup
+    const int64_t ranges = std::max<int64_t>(1, std::min<int64_t>(runs, x_target * R));
+    p.runs_per[i] = (int)((runs + ranges - 1) / ranges);
+    const int64_t tokens_per_block = R * p.runs_per[i] * kFeRun;
     p.x_blocks[i] = (int)((a.n_tokens + tokens_per_block - 1) / tokens_per_block);
     xmax = p.x_blocks[i] > xmax ? p.x_blocks[i] : xmax;
-    p.y0[i + 1] = p.y0[i] + p.t[i].chunks;
   }
   const dim3 grid((unsigned)xmax, (unsigned)p.y0[3]);
   const dim3 block(kFeThreads);

@@ -250,6 +250,28 @@ def test_frontend(adt, dk, dv):
     np.testing.assert_allclose(f64(beta), rb, rtol=1e-5, atol=1e-6)
 
 
+def test_frontend_full_heads_long_ranges():
+    """H_qk=16, H_v=32, d=128 BF16 over 17,000 tokens: each workgroup then walks
+    several 64-token runs, and sequence starts fall on run boundaries (64, 8384),
+    next to empty sequences and one-token ones."""
+    say("frontend long ranges")
+    lengths = [64, 0, 8192, 128, 63, 1, 8552]
+    Hqk, Hv, d = 16, 32, 128
+    cu, x = frontend_case(304, lengths, Hqk, Hv, d, d, torch.bfloat16)
+    q, k, v, g, beta = gdn_frontend(dev(cu), dev(x["q_raw"]), dev(x["k_raw"]), dev(x["v_raw"]),
+                                    H_qk=Hqk, H_v=Hv, conv_wq=dev(x["conv_wq"]),
+                                    conv_wk=dev(x["conv_wk"]), conv_wv=dev(x["conv_wv"]),
+                                    a_raw=dev(x["a_raw"]), b_raw=dev(x["b_raw"]))
+    torch.cuda.synchronize()
+    rq, rk, rv, rg, rb = oracle_frontend(cu, x, Hqk, Hv)
+    t = tol(torch.bfloat16)
+    assert scaled_err(f64(q), rq, 2) < t
+    assert scaled_err(f64(k), rk, 2) < t
+    assert scaled_err(f64(v), rv, 2) < t
+    np.testing.assert_allclose(f64(g), rg, rtol=1e-5, atol=1e-6)
+    np.testing.assert_allclose(f64(beta), rb, rtol=1e-5, atol=1e-6)
+
+
 @pytest.mark.parametrize("rule", ["gated_delta", "delta"])
 def test_prefill_with_frontend(rule):
     """Raw projections through the fused front-end then the chunked recurrence,
