@@ -49,6 +49,7 @@ namespace gdn {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 struct PrefillParams {
   int32_t n_seq, H_qk, H_v, group;
@@ -201,20 +202,22 @@ __device__ __forceinline__ Frag<F32> load_afrag(const float *base, int ld, int r
 
 // The same fragment of a transposed operand: lane (g, m) holds column r0 + m
 // of a row-major matrix at rows k0 + 4g + {0..3} and k0 + 16 + 4g + {0..3},
-// i.e. A[m][k] = base[k][r0 + m] -- one element per read, down the column.
+// i.e. A[m][k] = base[k][r0 + m].  BF16: two ds_read_b64_tr_b16 per fragment.
+// That gfx950 load transposes inside each 16-lane group: result lane i,
+// element j is element i % 4 of the 8 bytes addressed by lane 4j + i / 4
+// (checked on the hardware with index-valued LDS).  So lane (g, s) points at
+// row k0 + 4g + s / 4, columns r0 + 4 (s % 4) .. +3 -- 8 contiguous bytes.
 template <bool F32>
 __device__ __forceinline__ Frag<F32> load_afrag_t(const uint16_t *base, int ld, int r0, int k0) {
   static_assert(!F32, "FP32 fragments come from float buffers");
-  const int l = threadIdx.x & 63;
-  const uint16_t *c = base + (k0 + 4 * (l >> 4)) * ld + r0 + (l & 15);
-  uint16_t x[8];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    x[j] = c[j * ld];
-    x[4 + j] = c[(16 + j) * ld];
-  }
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
+  const uint16_t *a = base + (k0 + 4 * g + (s >> 2)) * ld + r0 + 4 * (s & 3);
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a));
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 16 * ld));
+  const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
   Frag<false> f;
-  f.v = __builtin_bit_cast(bf16x8_t, x);
+  f.v = __builtin_bit_cast(bf16x8_t, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
   return f;
 }
 template <bool F32>
@@ -241,8 +244,6 @@ __device__ __forceinline__ Frag<F32> load_afrag_t(const float *base, int ld, int
 // (v_mfma_f32_16x16x16_bf16: lane (g, n) holds B[4g + j][n]; FP32: four
 // v_mfma_f32_16x16x4f32, instruction j taking k = 4g + j); the left-hand
 // operand's lane (g, m) holds row m at columns 4g .. 4g+3.
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
 
 template <bool F32> struct Frag16;
 template <> struct Frag16<false> { s16x4_t v; };
