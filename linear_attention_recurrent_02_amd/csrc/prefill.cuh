@@ -220,6 +220,23 @@ __device__ __forceinline__ Frag<F32> load_afrag_t(const uint16_t *base, int ld, 
   f.v = __builtin_bit_cast(bf16x8_t, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
   return f;
 }
+// Four consecutive rows of one column, in the accumulator layout: lane (g, n)
+// gets base[(r0 + 4g + e) * ld + c0 + n], e = 0..3 -- one transposing load
+// (lane (g, s) points at row r0 + 4g + s / 4, columns c0 + 4 (s % 4) .. +3).
+__device__ __forceinline__ void load_col4(const uint16_t *base, int ld, int r0, int c0, float *x) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(base + (r0 + 4 * g + (s >> 2)) * ld + c0 + 4 * (s & 3)));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = bf16_to_f32((uint16_t)v[e]);
+}
+__device__ __forceinline__ void load_col4(const float *base, int ld, int r0, int c0, float *x) {
+  const int l = threadIdx.x & 63;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = base[(r0 + 4 * (l >> 4) + e) * ld + c0 + (l & 15)];
+}
+
 template <bool F32>
 __device__ __forceinline__ Frag<F32> load_afrag_t(const float *base, int ld, int r0, int k0) {
   const int l = threadIdx.x & 63;

@@ -282,15 +282,16 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       // R = beta (V - gamma K M) for the delta rules, else R = V; um holds R
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
+        float vv[NA][4];
+#pragma unroll
+        for (int ia = 0; ia < NA; ++ia) load_col4(Vh, LDV, 16 * tb, 16 * (wave * NA + ia), vv[ia]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 16 * tb + rq + e;
           const float br = bet[r], gr = gam[r];
 #pragma unroll
-          for (int ia = 0; ia < NA; ++ia) {
-            const float vv = get(Vh + r * LDV + 16 * (wave * NA + ia) + col);
-            um[tb][ia][e] = erase ? br * (vv - gr * um[tb][ia][e]) : vv;
-          }
+          for (int ia = 0; ia < NA; ++ia)
+            um[tb][ia][e] = erase ? br * (vv[ia][e] - gr * um[tb][ia][e]) : vv[ia][e];
         }
       }
       // 6: U = (I + A)^-1 R (delta rules), block forward substitution in
