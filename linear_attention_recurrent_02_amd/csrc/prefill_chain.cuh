@@ -214,8 +214,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb) {
         const Frag<F32> fb = load_frag<F32>(Kh, LDK, 16 * cb, 32 * kk);
-        if (erase) sacc[cb] = mma<F32>(sacc[cb], fk, fb);
-        pacc[cb] = mma<F32>(pacc[cb], fq, fb);
+        sacc[cb] = mma<F32>(sacc[cb], fk, fb);  // (unused without erase: no branch here,
+        pacc[cb] = mma<F32>(pacc[cb], fq, fb);  //  so the loads and MFMAs interleave)
       }
       if (mwave) {
         // the state's accumulator tile pair for d_k blocks 2kk, 2kk+1 (zero past d_k)
@@ -230,11 +230,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           const Frag<F32> aq = load_afrag<F32>(Qh, LDK, 16 * tb, 32 * kk);
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], aq, fm[ia]);
-          if (erase) {
-            const Frag<F32> ak = load_afrag<F32>(Kh, LDK, 16 * tb, 32 * kk);
+          const Frag<F32> ak = load_afrag<F32>(Kh, LDK, 16 * tb, 32 * kk);
 #pragma unroll
-            for (int ia = 0; ia < NA; ++ia) um[tb][ia] = mma<F32>(um[tb][ia], ak, fm[ia]);
-          }
+          for (int ia = 0; ia < NA; ++ia) um[tb][ia] = mma<F32>(um[tb][ia], ak, fm[ia]);
         }
       }
     }
