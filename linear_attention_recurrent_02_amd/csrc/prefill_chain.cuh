@@ -186,7 +186,6 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     const int n = (int)std::min<int64_t>(C, t_end - t0);
     const int64_t t1 = t0 + C;
     const bool more = t1 < t_end;
-    if (more) fetch(t1, (int)std::min<int64_t>(C, t_end - t1));  // in flight until staged
 
     // ---- 2 and 5: S = K K^T, P = Q K^T for row block `wave` (a6), and Q M,
     // K M (a7) for the wave's d_v columns.  All of them read only this chunk's
@@ -217,23 +216,36 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         sacc[cb] = mma<F32>(sacc[cb], fk, fb);  // (unused without erase: no branch here,
         pacc[cb] = mma<F32>(pacc[cb], fq, fb);  //  so the loads and MFMAs interleave)
       }
-      if (mwave) {
-        // the state's accumulator tile pair for d_k blocks 2kk, 2kk+1 (zero past d_k)
-        Frag<F32> fm[NA];
+    }
+    // Q M and K M with the A fragments double-buffered by hand: the load of
+    // fragment f+1 is issued before the MFMAs of fragment f (scheduling
+    // barriers keep the compiler from moving it back next to its use)
+    if (mwave) {
+      constexpr int NF = NKB * 8;  // (slab, row block, q or k)
+      Frag<F32> fa[2];
+      Frag<F32> fm[NA];
+      fa[0] = load_afrag<F32>(Qh, LDK, 0, 0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        const int kk = f >> 3, tb = (f >> 1) & 3, isk = f & 1;
+        if (f + 1 < NF) {
+          const int kn = (f + 1) >> 3, tn = ((f + 1) >> 1) & 3, kn_isk = (f + 1) & 1;
+          fa[(f + 1) & 1] = load_afrag<F32>(kn_isk ? Kh : Qh, LDK, 16 * tn, 32 * kn);
+        }
+        if ((f & 7) == 0) {
+#pragma unroll
+          for (int ia = 0; ia < NA; ++ia) {
+            const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+            fm[ia] = bfrag<F32>(macc[2 * kk][ia], 2 * kk + 1 < DKB ? macc[2 * kk + 1][ia] : z);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
-          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-          fm[ia] = bfrag<F32>(macc[2 * kk][ia], 2 * kk + 1 < DKB ? macc[2 * kk + 1][ia] : z);
+          if (isk) um[tb][ia] = mma<F32>(um[tb][ia], fa[f & 1], fm[ia]);
+          else qm[tb][ia] = mma<F32>(qm[tb][ia], fa[f & 1], fm[ia]);
         }
-#pragma unroll
-        for (int tb = 0; tb < 4; ++tb) {
-          const Frag<F32> aq = load_afrag<F32>(Qh, LDK, 16 * tb, 32 * kk);
-#pragma unroll
-          for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], aq, fm[ia]);
-          const Frag<F32> ak = load_afrag<F32>(Kh, LDK, 16 * tb, 32 * kk);
-#pragma unroll
-          for (int ia = 0; ia < NA; ++ia) um[tb][ia] = mma<F32>(um[tb][ia], ak, fm[ia]);
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // ---- 3: A = strict_lower(beta_r e^{G_r-G_s} S), Sq = lower(e^{G_r-G_s} P) ----
@@ -258,6 +270,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       }
     }
     __syncthreads();
+    // the next chunk's inputs, in flight through the rest of this chunk (issued
+    // only now so the prefetch registers are free during the MFMA pass above)
+    if (more) fetch(t1, (int)std::min<int64_t>(C, t_end - t1));
 
     // ---- 5-8: the wave's d_v columns, in registers ----
     if (mwave) {
