@@ -206,15 +206,29 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         for (int e = 0; e < 4; ++e) qm[tb][ia][e] = um[tb][ia][e] = 0.f;
       }
     }
+    // S and P (S unused without erase: no branch, straight-line code), the
+    // fragments of step f + 1 loaded during step f's MFMAs
+    {
+      constexpr int NF = NKB * 4;  // (slab, column block)
+      Frag<F32> fk[2], fq[2], fb[2];
+      fk[0] = load_frag<F32>(Kh, LDK, 16 * wave, 0);
+      fq[0] = load_frag<F32>(Qh, LDK, 16 * wave, 0);
+      fb[0] = load_frag<F32>(Kh, LDK, 0, 0);
 #pragma unroll
-    for (int kk = 0; kk < NKB; ++kk) {
-      const Frag<F32> fk = load_frag<F32>(Kh, LDK, 16 * wave, 32 * kk);
-      const Frag<F32> fq = load_frag<F32>(Qh, LDK, 16 * wave, 32 * kk);
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-        const Frag<F32> fb = load_frag<F32>(Kh, LDK, 16 * cb, 32 * kk);
-        sacc[cb] = mma<F32>(sacc[cb], fk, fb);  // (unused without erase: no branch here,
-        pacc[cb] = mma<F32>(pacc[cb], fq, fb);  //  so the loads and MFMAs interleave)
+      for (int f = 0; f < NF; ++f) {
+        const int kk = f >> 2, cb = f & 3;
+        if (f + 1 < NF) {
+          const int kn = (f + 1) >> 2;
+          if (((f + 1) & 3) == 0) {
+            fk[kn & 1] = load_frag<F32>(Kh, LDK, 16 * wave, 32 * kn);
+            fq[kn & 1] = load_frag<F32>(Qh, LDK, 16 * wave, 32 * kn);
+          }
+          fb[(f + 1) & 1] = load_frag<F32>(Kh, LDK, 16 * ((f + 1) & 3), 32 * kn);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        sacc[cb] = mma<F32>(sacc[cb], fk[kk & 1], fb[f & 1]);
+        pacc[cb] = mma<F32>(pacc[cb], fq[kk & 1], fb[f & 1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // Q M and K M with the A fragments double-buffered by hand: the load of
@@ -310,19 +324,29 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       // 6: U = (I + A)^-1 R (delta rules), block forward substitution in
       // place: um[i] <- T_ii (R_i - sum_{j<i} A_ij U_j), 16-row blocks i = 0..3
       if (erase) {
+        // every A_ij and T_ii fragment is loaded up front (none depends on U),
+        // so the serial chain below waits only on its own MFMAs
+        Frag16<F32> fa[6], ft[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 1, n = 0; i < 4; ++i) {
 #pragma unroll
-          for (int j = 0; j < i; ++j) {
-            const Frag16<F32> fa = load_afrag16<F32>(Af, LDF, 16 * i, 16 * j, -1.f);
+          for (int j = 0; j < i; ++j, ++n) fa[n] = load_afrag16<F32>(Af, LDF, 16 * i, 16 * j, -1.f);
+        }
 #pragma unroll
-            for (int ia = 0; ia < NA; ++ia) um[i][ia] = mma16<F32>(um[i][ia], fa, bfrag16<F32>(um[j][ia]));
+        for (int i = 0; i < 4; ++i) ft[i] = load_afrag16<F32>(Tw, L::LDT, 16 * i, 0, 1.f);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0, n = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < i; ++j, ++n) {
+#pragma unroll
+            for (int ia = 0; ia < NA; ++ia)
+              um[i][ia] = mma16<F32>(um[i][ia], fa[n], bfrag16<F32>(um[j][ia]));
           }
-          const Frag16<F32> ft = load_afrag16<F32>(Tw, L::LDT, 16 * i, 0, 1.f);
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia) {
             const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-            um[i][ia] = mma16<F32>(z, ft, bfrag16<F32>(um[i][ia]));
+            um[i][ia] = mma16<F32>(z, ft[i], bfrag16<F32>(um[i][ia]));
           }
         }
       }
@@ -334,18 +358,25 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) fu[s2][ia] = bfrag<F32>(um[2 * s2][ia], um[2 * s2 + 1][ia]);
       }
+      // the six (L o P) fragments below the diagonal, loaded together
+      Frag<F32> fs[6];
 #pragma unroll
-      for (int tb = 0; tb < 4; ++tb) {
+      for (int tb = 0, n = 0; tb < 4; ++tb) {
+#pragma unroll
+        for (int s2 = 0; s2 <= tb / 2; ++s2, ++n) fs[n] = load_afrag<F32>(Sq, LDC, 16 * tb, 32 * s2);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int tb = 0, n = 0; tb < 4; ++tb) {
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) qm[tb][ia][e] *= gam[16 * tb + rq + e];
         }
 #pragma unroll
-        for (int s2 = 0; s2 <= tb / 2; ++s2) {
-          const Frag<F32> fs = load_afrag<F32>(Sq, LDC, 16 * tb, 32 * s2);
+        for (int s2 = 0; s2 <= tb / 2; ++s2, ++n) {
 #pragma unroll
-          for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], fs, fu[s2][ia]);
+          for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], fs[n], fu[s2][ia]);
         }
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
@@ -378,11 +409,20 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
           for (int e = 0; e < 4; ++e) macc[b][ia][e] *= gl;
         }
+      }
+      // K^T fragments double-buffered: the next one loads during this one's MFMAs
+      {
+        constexpr int NF = DKB * 2;  // (d_k block, token slab)
+        Frag<F32> fk[2];
+        fk[0] = load_afrag_t<F32>(Kh, LDK, 0, 0);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          const Frag<F32> fk = load_afrag_t<F32>(Kh, LDK, 16 * b, 32 * s2);
+        for (int f = 0; f < NF; ++f) {
+          if (f + 1 < NF) fk[(f + 1) & 1] = load_afrag_t<F32>(Kh, LDK, 16 * ((f + 1) >> 1), 32 * ((f + 1) & 1));
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int ia = 0; ia < NA; ++ia) macc[b][ia] = mma<F32>(macc[b][ia], fk, fe[s2][ia]);
+          for (int ia = 0; ia < NA; ++ia)
+            macc[f >> 1][ia] = mma<F32>(macc[f >> 1][ia], fk[f & 1], fe[f & 1][ia]);
+          __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
