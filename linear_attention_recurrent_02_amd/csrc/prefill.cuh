@@ -16,9 +16,10 @@
 //   M <- gamma_last M + (diag(exp(G_last - G)) K)^T U
 //
 // linear / gated have no erase: A = 0, T = I, R = V.  linear / delta have no
-// decay: G = 0.  Rows past the end of a ragged tail chunk are zero (k, q, v,
-// beta = 0, g = 0), so they add nothing and gamma_last is the last real
-// token's.
+// decay: G = 0.  Rows past the end of a ragged tail chunk repeat the last
+// token's k, q, v but carry beta = 0 (R = beta V under the plain rules) and
+// g = 0: their rows of A, R and U vanish, so they add nothing, and gamma_last
+// is the last real token's.
 //
 // Every product runs on MFMA with FP32 accumulation.  The recurrence is
 // independent per state column (a column of M only ever meets the same column
@@ -50,6 +51,7 @@ namespace gdn {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));  // 16 raw bytes
 
 struct PrefillParams {
   int32_t n_seq, H_qk, H_v, group;
@@ -306,6 +308,26 @@ __device__ __forceinline__ f32x4_t mma16(f32x4_t c, const Frag16<F32> &a, const 
 
 // 2^x on the hardware transcendental unit (v_exp_f32)
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// one DPP move of a float: lanes of the rows in ROWS read the lane CTRL
+// selects; every other lane reads 0
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, without LDS: shifts by
+// 1, 2, 4, 8 inside each 16-lane row, then lane 15's total is broadcast into
+// rows 1 and 3 and lane 31's into rows 2 and 3.
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+  x += dpp_move<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_move<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_move<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_move<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_move<0x142, 0xa>(x);  // row_bcast:15
+  x += dpp_move<0x143, 0xc>(x);  // row_bcast:31
+  return x;
+}
 
 // store a float into an operand buffer
 __device__ __forceinline__ void put(uint16_t *p, float x) { *p = f32_to_bf16(x); }

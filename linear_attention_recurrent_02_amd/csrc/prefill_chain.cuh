@@ -72,71 +72,102 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   const bool erase = (p.rule & kRuleErase) != 0;
 
   // ---- prefetch of one chunk's inputs into registers, and their staging ----
-  uint4 pk[KQ_PER][EW], pq[KQ_PER][EW], pv[V_PER][EW];
+  // The loads are unconditional: a row past the sequence's end re-reads its
+  // last token.  Such padded rows are harmless because their beta factor is
+  // zero: their rows of A and U vanish, so they reach neither M nor a stored
+  // O row.  (Held as vector values, so they stay in registers.)
+  u32x4_t pk[KQ_PER][EW], pq[KQ_PER][EW], pv[V_PER][EW];
   float pg = 0.f, pb = 0.f;  // wave 0: gate inputs of token `lane`
-  auto fetch = [&](int64_t t0, int n) {
+  bool p_valid = false;       // wave 0: token `lane` lies inside the sequence
+  auto fetch = [&](int64_t t0) {
+    const int64_t last = t_end - 1;
 #pragma unroll
     for (int i = 0; i < KQ_PER; ++i) {
       const int gi = tid + 256 * i;
       const int r = gi / (DK / 8), d = (gi % (DK / 8)) * 8;
-      const bool ok = gi < KQ_GROUPS && r < n;
-      const int64_t off = ((t0 + r) * p.H_qk + hq) * DK + d;
-      const uint4 *sk = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.k) + off);
-      const uint4 *sq = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.q) + off);
+      const int64_t off = (std::min(t0 + r, last) * p.H_qk + hq) * DK + d;
+      const u32x4_t *sk = reinterpret_cast<const u32x4_t *>(static_cast<const AT *>(p.k) + off);
+      const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(static_cast<const AT *>(p.q) + off);
 #pragma unroll
-      for (int e = 0; e < EW; ++e) {
-        pk[i][e] = ok ? sk[e] : make_uint4(0u, 0u, 0u, 0u);
-        pq[i][e] = ok ? sq[e] : make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int e = 0; e < EW; ++e) { pk[i][e] = sk[e]; pq[i][e] = sq[e]; }
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
       const int gi = tid + 256 * i;
       const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
-      const bool ok = gi < V_GROUPS && r < n;
-      const uint4 *sv = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.v) +
-                                                        ((t0 + r) * p.H_v + h) * DV + c);
+      const u32x4_t *sv = reinterpret_cast<const u32x4_t *>(
+          static_cast<const AT *>(p.v) + (std::min(t0 + r, last) * p.H_v + h) * DV + c);
 #pragma unroll
-      for (int e = 0; e < EW; ++e) pv[i][e] = ok ? sv[e] : make_uint4(0u, 0u, 0u, 0u);
+      for (int e = 0; e < EW; ++e) pv[i][e] = sv[e];
     }
     if (wave == 0) {
-      const bool valid = lane < n;
-      pg = (valid && decay) ? p.g[(t0 + lane) * p.H_v + h] : 0.f;
-      pb = valid ? (erase ? p.beta[(t0 + lane) * p.H_v + h] : 1.f) : 0.f;
+      // raw values only: any arithmetic on them here would wait for the whole
+      // fetch (loads retire in order); stage() masks them.  g and beta may be
+      // NULL under the rules that do not use them.
+      const int64_t gt = std::min(t0 + lane, last) * p.H_v + h;
+      if (decay) pg = p.g[gt];
+      if (erase) pb = p.beta[gt];
+      p_valid = t0 + lane <= last;
     }
   };
   auto stage = [&]() {
 #pragma unroll
     for (int i = 0; i < KQ_PER; ++i) {
       const int gi = tid + 256 * i;
-      if (gi >= KQ_GROUPS) continue;
+      if (KQ_GROUPS % 256 != 0 && gi >= KQ_GROUPS) continue;
       const int r = gi / (DK / 8), d = (gi % (DK / 8)) * 8;
-      uint4 *dk = reinterpret_cast<uint4 *>(Kh + r * LDK + d);
-      uint4 *dq = reinterpret_cast<uint4 *>(Qh + r * LDK + d);
+      u32x4_t *dk = reinterpret_cast<u32x4_t *>(Kh + r * LDK + d);
+      u32x4_t *dq = reinterpret_cast<u32x4_t *>(Qh + r * LDK + d);
 #pragma unroll
       for (int e = 0; e < EW; ++e) { dk[e] = pk[i][e]; dq[e] = pq[i][e]; }
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
       const int gi = tid + 256 * i;
-      if (gi >= V_GROUPS) continue;
+      if (V_GROUPS % 256 != 0 && gi >= V_GROUPS) continue;
       const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
-      uint4 *dv = reinterpret_cast<uint4 *>(Vh + r * LDV + c);
+      u32x4_t *dv = reinterpret_cast<u32x4_t *>(Vh + r * LDV + c);
 #pragma unroll
       for (int e = 0; e < EW; ++e) dv[e] = pv[i][e];
     }
     if (wave == 0) {
-      float G = pg * LOG2E;  // inclusive prefix sum of log2 decays over the 64 lanes
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(G, off);
-        if (lane >= off) G += y;
-      }
-      const float G_last = __shfl(G, 63);
+      // inclusive prefix sum of the log2 decays over the chunk's 64 tokens
+      const float G = wave_inclusive_sum(p_valid && decay ? pg * LOG2E : 0.f);
+      const float G_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), 63));
       Gs[lane] = G;
       gam[lane] = fast_exp2(G);
-      bet[lane] = pb;
+      bet[lane] = p_valid ? (erase ? pb : 1.f) : 0.f;  // the plain rules take R = beta V
       eGn[lane] = fast_exp2(G_last - G);
+    }
+  };
+
+  // O rows r0 + rq .. r0 + rq + 3 of column c0 + col, held by this lane in
+  // the accumulator layout, scaled and stored (only rows inside the chunk).
+  // BF16: each lane swaps halves with its neighbour column (lane ^ 1), so a
+  // lane stores two rows of a column pair as 4-byte words.
+  AT *const o_head = static_cast<AT *>(p.o) + (int64_t)h * DV;
+  const int64_t o_row = (int64_t)p.H_v * DV;  // elements between tokens
+  int64_t o_t0 = 0;                           // first token of the chunk
+  int o_n = 0;                                // tokens in the chunk
+  auto store_o_tile = [&](int r0, int c0, const f32x4_t &acc) {
+    if constexpr (AB) {
+      const bool odd = (col & 1) != 0;
+      const uint32_t a = pack_bf16x2(p.scale * acc[0], p.scale * acc[1]);  // rows 0, 1
+      const uint32_t b = pack_bf16x2(p.scale * acc[2], p.scale * acc[3]);  // rows 2, 3
+      const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? a : b), 0xB1, 0xf, 0xf, false);
+      const uint32_t own = odd ? b : a;
+      const uint32_t left = odd ? other : own, right = odd ? own : other;  // columns c, c + 1
+      const int r = r0 + rq + (odd ? 2 : 0);
+      AT *dst = o_head + (o_t0 + r) * o_row + c0 + (col & ~1);
+      if (r < o_n) *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(right, left, 0x05040100u);
+      if (r + 1 < o_n)
+        *reinterpret_cast<uint32_t *>(dst + o_row) = __builtin_amdgcn_perm(right, left, 0x07060302u);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = r0 + rq + e;
+        if (r < o_n) o_head[(o_t0 + r) * o_row + c0 + col] = p.scale * acc[e];
+      }
     }
   };
 
@@ -177,7 +208,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     }
   }
   if (t_begin < t_end) {
-    fetch(t_begin, (int)std::min<int64_t>(C, t_end - t_begin));
+    fetch(t_begin);
     stage();
   }
   __syncthreads();
@@ -186,6 +217,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     const int n = (int)std::min<int64_t>(C, t_end - t0);
     const int64_t t1 = t0 + C;
     const bool more = t1 < t_end;
+    o_t0 = t0;
+    o_n = n;
 
     // ---- 2 and 5: S = K K^T, P = Q K^T for row block `wave` (a6), and Q M,
     // K M (a7) for the wave's d_v columns.  All of them read only this chunk's
@@ -286,7 +319,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     __syncthreads();
     // the next chunk's inputs, in flight through the rest of this chunk (issued
     // only now so the prefetch registers are free during the MFMA pass above)
-    if (more) fetch(t1, (int)std::min<int64_t>(C, t_end - t1));
+    if (more) fetch(t1);
 
     // ---- 5-8: the wave's d_v columns, in registers ----
     if (mwave) {
@@ -306,7 +339,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
         for (int r = 0; r < 16; ++r) Tw[(16 * bb + r) * L::LDT + c] = tc[r];
       }
-      // R = beta (V - gamma K M) for the delta rules, else R = V; um holds R
+      // R = beta (V - gamma K M) for the delta rules, else R = V (beta holds 1 on
+      // the chunk's tokens and 0 on its padded rows); um holds R
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         float vv[NA][4];
@@ -318,7 +352,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           const float br = bet[r], gr = gam[r];
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia)
-            um[tb][ia][e] = erase ? br * (vv[ia][e] - gr * um[tb][ia][e]) : vv[ia][e];
+            um[tb][ia][e] = br * (erase ? vv[ia][e] - gr * um[tb][ia][e] : vv[ia][e]);
         }
       }
       // 6: U = (I + A)^-1 R (delta rules), block forward substitution in
@@ -350,8 +384,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           }
         }
       }
-      // 7: O = gamma Q M + (L o P) U (a7), scaled, into the wave's columns of
-      // the V rows' LDS (this wave's V columns were consumed above)
+      // 7: O = gamma Q M + (L o P) U (a7), scaled, stored to HBM straight from
+      // the accumulator layout
       Frag<F32> fu[2][NA];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -379,11 +413,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], fs[n], fu[s2][ia]);
         }
 #pragma unroll
-        for (int ia = 0; ia < NA; ++ia) {
-          const int c = 16 * (wave * NA + ia) + col;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) put(Vh + (16 * tb + rq + e) * LDV + c, p.scale * qm[tb][ia][e]);
-        }
+        for (int ia = 0; ia < NA; ++ia) store_o_tile(16 * tb, 16 * (wave * NA + ia), qm[tb][ia]);
       }
       // 8: M <- gamma_last M + K^T diag(exp(G_last - G)) U: the decay weights
       // scale U's rows; K^T's fragments are read down the columns of the K rows
@@ -426,19 +456,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         }
       }
     }
-    __syncthreads();  // all reads of this chunk's LDS operands are done; O is in Vh
-#pragma unroll
-    for (int i = 0; i < V_PER; ++i) {
-      const int gi = tid + 256 * i;
-      const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
-      if (gi < V_GROUPS && r < n) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(Vh + r * LDV + c);
-        uint4 *dst = reinterpret_cast<uint4 *>(static_cast<AT *>(p.o) + ((t0 + r) * p.H_v + h) * DV + c);
-#pragma unroll
-        for (int e = 0; e < EW; ++e) dst[e] = src[e];
-      }
-    }
-    __syncthreads();  // O rows read out of Vh before the next chunk's V lands there
+    __syncthreads();  // all reads of this chunk's LDS operands are done
     if (more) stage();  // next chunk's K, Q, V and gates into LDS
     __syncthreads();
   }
