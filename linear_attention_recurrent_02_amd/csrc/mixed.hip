@@ -43,7 +43,7 @@ __global__ __launch_bounds__(256) void mixed_kernel(DecodeParams dp, PrefillPara
   __shared__ __align__(16) char smem[L::BYTES];
   if ((int)blockIdx.x < prefill_blocks) {
     const int chain = chain_of_block(blockIdx.x);
-    if (chain < n_chains) prefill_chain<SB, AB, DK, DV, F32>(pp, chain, smem);
+    if (chain < n_chains) prefill_chain<SB, AB, DK, DV, F32, 4>(pp, chain, smem);
     return;
   }
   // decode worker

@@ -69,7 +69,10 @@ struct PrefillParams {
 
 // LDS layout of the chain kernel (byte offsets).  OT is the operand storage
 // type: raw BF16 bits, or float on the FP32 path.  Rows are padded by 16
-// bytes so the 16 lanes of a fragment read hit different banks.
+// bytes so the 16 lanes of a fragment read hit different banks.  The chunk's
+// inputs (K, Q, V rows and the gates) live in one of two alternating sets:
+// while a chunk computes from one set, the next chunk's inputs are written
+// into the other.
 template <int DK, int DV, bool F32>
 struct PrefillLayout {
   using OT = std::conditional_t<F32, float, uint16_t>;
@@ -79,17 +82,19 @@ struct PrefillLayout {
   static constexpr int LDK = DKP + PADE;  // Kh, Qh (token rows)
   static constexpr int LDC = C + PADE;    // Sq (rows of 64 tokens)
   static constexpr int LDF = C + 4;       // Af, Tf (float)
-  static constexpr int LDV = DV + PADE;   // Vh / Oh rows (64 tokens x d_v)
+  static constexpr int LDV = DV + PADE;   // Vh rows (64 tokens x d_v)
+  // one input set
   static constexpr size_t KH = 0;
   static constexpr size_t QH = KH + (size_t)C * LDK * sizeof(OT);
-  static constexpr size_t SQ = QH + (size_t)C * LDK * sizeof(OT);
-  static constexpr size_t VH = SQ + (size_t)C * LDC * sizeof(OT);  // V, then O, row-major
-  static constexpr size_t AF = VH + (size_t)C * LDV * sizeof(OT);
+  static constexpr size_t VH = QH + (size_t)C * LDK * sizeof(OT);
+  static constexpr size_t GATES = VH + (size_t)C * LDV * sizeof(OT);  // G, gamma, beta, eGn
+  static constexpr size_t SET = GATES + 4 * C * 4;                    // bytes per set
+  // shared by both sets
+  static constexpr size_t SQ = 2 * SET;
+  static constexpr size_t AF = SQ + (size_t)C * LDC * sizeof(OT);
   static constexpr int LDT = 20;  // T_ii rows (float); 16-byte aligned rows
-  static constexpr size_t TW = AF + (size_t)C * LDF * 4;  // per wave: 4 blocks T_ii
-  static constexpr size_t TW_WAVE = (size_t)C * LDT;      // floats per wave
-  static constexpr size_t GATES = TW + 4 * TW_WAVE * 4;   // G, gamma, beta, eGn
-  static constexpr size_t BYTES = GATES + 4 * C * 4;
+  static constexpr size_t TF = AF + (size_t)C * LDF * 4;  // the four T_ii, stacked
+  static constexpr size_t BYTES = TF + (size_t)C * LDT * 4;
 };
 
 // ---- MFMA fragments -------------------------------------------------------

@@ -8,11 +8,19 @@
 
 namespace gdn {
 
+// Waves per chain: 8 (two per SIMD, each covering the other's latencies)
+// where the chain's registers fit in the 256 a wave then gets without
+// spilling -- a spill reload inside the chunk loop would wait on the
+// in-flight prefetch of the next chunk -- else 4.
+template <int DK, int DV, bool F32>
+constexpr int kPrefillWaves = (!F32 && (DK <= 64 || DV == 128)) ? 8 : 4;
+
 template <bool SB, bool AB, int DK, int DV, bool F32>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillParams p, int n_chains) {
+__global__ __launch_bounds__((64 * kPrefillWaves<DK, DV, F32>)) void prefill_kernel(PrefillParams p,
+                                                                                   int n_chains) {
   __shared__ __align__(16) char smem[PrefillLayout<DK, DV, F32>::BYTES];
   const int chain = chain_of_block(blockIdx.x);
-  if (chain < n_chains) prefill_chain<SB, AB, DK, DV, F32>(p, chain, smem);
+  if (chain < n_chains) prefill_chain<SB, AB, DK, DV, F32, kPrefillWaves<DK, DV, F32>>(p, chain, smem);
 }
 
 // ---- launcher --------------------------------------------------------------
@@ -37,8 +45,8 @@ static gdn_status launch_chains(const PrefillParams &p, hipStream_t s) {
   } else {
     const int n_chains = p.n_seq * p.H_v;
     const int blocks = (n_chains + 15) / 16 * 16;
-    hipLaunchKernelGGL((prefill_kernel<SB, AB, DK, DV, F32>), dim3(blocks), dim3(256), 0, s, p,
-                       n_chains);
+    hipLaunchKernelGGL((prefill_kernel<SB, AB, DK, DV, F32>), dim3(blocks),
+                       dim3(64 * kPrefillWaves<DK, DV, F32>), 0, s, p, n_chains);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
   }
 }

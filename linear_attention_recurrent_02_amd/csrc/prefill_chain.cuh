@@ -7,9 +7,12 @@
 // end of chunk c, so no chunk waits on a global-memory round trip.  The
 // workgroup barriers wait only on LDS (lgkmcnt), not on these loads.
 //
-// Work split: the chunk-local half (S, P, A, L o P, the scaled K^T, T) is
-// shared by the 4 waves through LDS; the M-dependent half runs per wave on
-// the wave's own d_v columns (NA column blocks of 16), entirely in registers.
+// Work split over NW waves (4 or 8): the chunk-local half (S, P, A, L o P,
+// T) is shared through LDS -- wave w forms the S and P tiles of row block
+// w % 4 in 16 / NW of the four column blocks; the M-dependent half runs per
+// wave on the wave's own d_v columns (NA column blocks of 16), entirely in
+// registers.  With 8 waves two share each SIMD, so one's LDS and MFMA
+// latencies are covered by the other's work.
 #pragma once
 
 #include <algorithm>
@@ -27,10 +30,12 @@ __device__ __forceinline__ int chain_of_block(int b) {
   return (b & ~15) + 2 * (w & 7) + (w >> 3);
 }
 
-// One (sequence, state head) chain; all 256 threads of the workgroup call it.
-// `smem` holds PrefillLayout<DK, DV, F32>::BYTES bytes, 16-byte aligned.
-template <bool SB, bool AB, int DK, int DV, bool F32>
+// One (sequence, state head) chain; all 64 NW threads of the workgroup call
+// it.  `smem` holds PrefillLayout<DK, DV, F32>::BYTES bytes, 16-byte aligned.
+template <bool SB, bool AB, int DK, int DV, bool F32, int NW>
 __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain, char *smem) {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves per chain");
+  constexpr int NT = 64 * NW;
   using L = PrefillLayout<DK, DV, F32>;
   using OT = typename L::OT;
   using AT = typename Elem<AB>::T;
@@ -40,23 +45,40 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   constexpr int NKB = L::DKP / 32;  // MFMA K-steps over d_k
   constexpr int DKB = DK / 16;      // 16-row blocks of d_k
   constexpr int DVB = DV / 16;      // 16-column blocks of d_v
-  constexpr int NA = DVB >= 4 ? DVB / 4 : 1;  // d_v blocks per wave
+  constexpr int NA = DVB >= NW ? DVB / NW : 1;  // d_v blocks per wave
+  constexpr int NCB = 16 / NW;                   // S / P column blocks per wave
+  // With 4 waves the wave's T rows ride along the Q M / K M MFMA steps; with 8
+  // the partner wave on the SIMD fills those gaps instead.
+  constexpr bool kInterleaveT = NW == 4;
+  // LDS operand fragments kept in flight ahead of the MFMA that uses them: one
+  // 16x16x32 MFMA is 16 cycles, an LDS round trip several times that
+  constexpr int RING = 3;
   constexpr int EW = 8 * (int)sizeof(AT) / 16;  // 16-byte vectors per 8 elements
-  constexpr int KQ_GROUPS = C * (DK / 8), KQ_PER = (KQ_GROUPS + 255) / 256;
-  constexpr int V_GROUPS = C * (DV / 8), V_PER = (V_GROUPS + 255) / 256;
+  constexpr int KQ_GROUPS = C * (DK / 8), KQ_PER = (KQ_GROUPS + NT - 1) / NT;
+  constexpr int V_GROUPS = C * (DV / 8), V_PER = (V_GROUPS + NT - 1) / NT;
   constexpr float LOG2E = 1.4426950408889634f;
-  OT *Kh = reinterpret_cast<OT *>(smem + L::KH);
-  OT *Qh = reinterpret_cast<OT *>(smem + L::QH);
+  // this chunk's input set (K, Q, V rows and gates); the sets alternate
+  OT *Kh, *Qh, *Vh;
+  float *Gs, *gam, *bet, *eGn;  // cumulative log2 decay, gamma, beta, exp(G_last - G)
+  auto use_set = [&](int b) {
+    char *base = smem + b * L::SET;
+    Kh = reinterpret_cast<OT *>(base + L::KH);
+    Qh = reinterpret_cast<OT *>(base + L::QH);
+    Vh = reinterpret_cast<OT *>(base + L::VH);
+    Gs = reinterpret_cast<float *>(base + L::GATES);
+    gam = Gs + C; bet = Gs + 2 * C; eGn = Gs + 3 * C;
+  };
   OT *Sq = reinterpret_cast<OT *>(smem + L::SQ);
-  OT *Vh = reinterpret_cast<OT *>(smem + L::VH);  // V rows, then the chunk's O rows
   float *Af = reinterpret_cast<float *>(smem + L::AF);
-  float *Tw = reinterpret_cast<float *>(smem + L::TW) + (threadIdx.x >> 6) * L::TW_WAVE;  // this wave's T_ii
-  float *Gs = reinterpret_cast<float *>(smem + L::GATES);  // cumulative log2 decay
-  float *gam = Gs + C, *bet = Gs + 2 * C, *eGn = Gs + 3 * C;
+  float *Tf = reinterpret_cast<float *>(smem + L::TF);  // T_ii = (I + A_ii)^-1, stacked
 
   const int seq = chain / p.H_v, h = chain % p.H_v, hq = h / p.group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int col = lane & 15, rq = 4 * (lane >> 4);  // accumulator layout: rows rq..rq+3, column col
+  const int RB = wave & 3, cb0 = (wave >> 2) * NCB;  // the wave's S / P row block and column blocks
+  // the wave forms T_RB,RB = (I + A_RB,RB)^-1: with 8 waves waves 0-3, with 4
+  // every wave (it holds diagonal block RB of A)
+  const bool diag = NW == 8 ? wave < 4 : (cb0 <= RB && RB < cb0 + NCB);
   const int64_t t_begin = p.cu[seq], t_end = p.cu[seq + 1];
   const int64_t rs = p.read_slot ? (int64_t)p.read_slot[seq] : seq;
   const int64_t ws = p.write_slot ? (int64_t)p.write_slot[seq] : seq;
@@ -83,7 +105,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     const int64_t last = t_end - 1;
 #pragma unroll
     for (int i = 0; i < KQ_PER; ++i) {
-      const int gi = tid + 256 * i;
+      const int gi = tid + NT * i;
       const int r = gi / (DK / 8), d = (gi % (DK / 8)) * 8;
       const int64_t off = (std::min(t0 + r, last) * p.H_qk + hq) * DK + d;
       const u32x4_t *sk = reinterpret_cast<const u32x4_t *>(static_cast<const AT *>(p.k) + off);
@@ -93,7 +115,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
-      const int gi = tid + 256 * i;
+      const int gi = tid + NT * i;
       const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
       const u32x4_t *sv = reinterpret_cast<const u32x4_t *>(
           static_cast<const AT *>(p.v) + (std::min(t0 + r, last) * p.H_v + h) * DV + c);
@@ -110,23 +132,27 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       p_valid = t0 + lane <= last;
     }
   };
-  auto stage = [&]() {
+  auto stage = [&](int b) {  // into input set b
+    char *base = smem + b * L::SET;
+    OT *const sK = reinterpret_cast<OT *>(base + L::KH), *const sQ = reinterpret_cast<OT *>(base + L::QH);
+    OT *const sV = reinterpret_cast<OT *>(base + L::VH);
+    float *const sG = reinterpret_cast<float *>(base + L::GATES);
 #pragma unroll
     for (int i = 0; i < KQ_PER; ++i) {
-      const int gi = tid + 256 * i;
-      if (KQ_GROUPS % 256 != 0 && gi >= KQ_GROUPS) continue;
+      const int gi = tid + NT * i;
+      if (KQ_GROUPS % NT != 0 && gi >= KQ_GROUPS) continue;
       const int r = gi / (DK / 8), d = (gi % (DK / 8)) * 8;
-      u32x4_t *dk = reinterpret_cast<u32x4_t *>(Kh + r * LDK + d);
-      u32x4_t *dq = reinterpret_cast<u32x4_t *>(Qh + r * LDK + d);
+      u32x4_t *dk = reinterpret_cast<u32x4_t *>(sK + r * LDK + d);
+      u32x4_t *dq = reinterpret_cast<u32x4_t *>(sQ + r * LDK + d);
 #pragma unroll
       for (int e = 0; e < EW; ++e) { dk[e] = pk[i][e]; dq[e] = pq[i][e]; }
     }
 #pragma unroll
     for (int i = 0; i < V_PER; ++i) {
-      const int gi = tid + 256 * i;
-      if (V_GROUPS % 256 != 0 && gi >= V_GROUPS) continue;
+      const int gi = tid + NT * i;
+      if (V_GROUPS % NT != 0 && gi >= V_GROUPS) continue;
       const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
-      u32x4_t *dv = reinterpret_cast<u32x4_t *>(Vh + r * LDV + c);
+      u32x4_t *dv = reinterpret_cast<u32x4_t *>(sV + r * LDV + c);
 #pragma unroll
       for (int e = 0; e < EW; ++e) dv[e] = pv[i][e];
     }
@@ -134,10 +160,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       // inclusive prefix sum of the log2 decays over the chunk's 64 tokens
       const float G = wave_inclusive_sum(p_valid && decay ? pg * LOG2E : 0.f);
       const float G_last = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(G), 63));
-      Gs[lane] = G;
-      gam[lane] = fast_exp2(G);
-      bet[lane] = p_valid ? (erase ? pb : 1.f) : 0.f;  // the plain rules take R = beta V
-      eGn[lane] = fast_exp2(G_last - G);
+      sG[lane] = G;
+      sG[C + lane] = fast_exp2(G);                                     // gamma
+      sG[2 * C + lane] = p_valid ? (erase ? pb : 1.f) : 0.f;           // beta (plain rules: R = beta V)
+      sG[3 * C + lane] = fast_exp2(G_last - G);                        // exp(G_last - G)
     }
   };
 
@@ -171,20 +197,20 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     }
   };
 
-  // padded K columns (d_k < 32 only) stay zero for the whole chain
+  // padded K columns (d_k < 32 only) stay zero for the whole chain, in both sets
   if constexpr (L::DKP > DK) {
     constexpr int PADC = L::DKP - DK;
-    for (int i = tid; i < 2 * C * PADC; i += 256) {
-      const int row = i / PADC, c = DK + i % PADC;
-      if (row < C) put(Kh + row * LDK + c, 0.f);
-      else put(Qh + (row - C) * LDK + c, 0.f);
+    for (int i = tid; i < 4 * C * PADC; i += NT) {
+      const int row = i / PADC, c = DK + i % PADC;  // rows of K0, Q0, K1, Q1
+      OT *rowp = reinterpret_cast<OT *>(smem + (row / (2 * C)) * L::SET + ((row / C) & 1 ? L::QH : L::KH));
+      put(rowp + (row % C) * LDK + c, 0.f);
     }
   }
 
   // ---- initial state (a8): read slot -> FP32 accumulators ----
   // macc[b][ia]: rows 16b.. of d_k, columns 16 (wave NA + ia).. of d_v, in the
   // accumulator layout (lane (g, n): rows 4g..4g+3 of column n)
-  const bool mwave = DVB >= 4 || wave < DVB;  // waves that own d_v columns
+  const bool mwave = DVB >= NW || wave < DVB;  // waves that own d_v columns
   f32x4_t macc[DKB][NA];
   const int64_t state_base = (rs * p.H_v + h) * (int64_t)DK * DV;
 #pragma unroll
@@ -209,27 +235,153 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   }
   if (t_begin < t_end) {
     fetch(t_begin);
-    stage();
+    stage(0);
   }
   __syncthreads();
 
-  for (int64_t t0 = t_begin; t0 < t_end; t0 += C) {
-    const int n = (int)std::min<int64_t>(C, t_end - t0);
-    const int64_t t1 = t0 + C;
-    const bool more = t1 < t_end;
-    o_t0 = t0;
-    o_n = n;
-
-    // ---- 2 and 5: S = K K^T, P = Q K^T for row block `wave` (a6), and Q M,
-    // K M (a7) for the wave's d_v columns.  All of them read only this chunk's
-    // K and Q rows and the state, so they share one pass over the d_k slabs
-    // and their MFMAs interleave. ----
-    f32x4_t sacc[4], pacc[4];
-#pragma unroll
-    for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sacc[cb][e] = pacc[cb][e] = 0.f;
+  if constexpr (NW == 8) {
+    // the two tiles above the diagonal that the O step's 32-wide slabs read,
+    // (0, 1) and (2, 3) of L o P, stay zero for the whole chain
+    for (int i = tid; i < 2 * 256; i += NT) {
+      const int t = i >> 8, r = 32 * t + ((i >> 4) & 15), c = 32 * t + 16 + (i & 15);
+      put(Sq + r * LDC + c, 0.f);
     }
+  }
+
+  int cur = 0;  // input set of the current chunk
+  for (int64_t t0 = t_begin; t0 < t_end; t0 += C, cur ^= 1) {
+    const int64_t t1 = t0 + C;
+    o_t0 = t0;
+    o_n = (int)std::min<int64_t>(C, t_end - t0);
+    use_set(cur);
+    // The next chunk's inputs, in flight while this chunk computes.  Fetched
+    // and staged on the last chunk too (clamped to the last token, into the
+    // set nobody reads next): with no branch around them, the register reuse
+    // at the loop head does not make the compiler wait for every outstanding
+    // memory operation, the O stores of the chunk before included.
+    fetch(t1);
+
+    // T_RB,RB = (I + A_RB,RB)^-1 from diagonal block RB of A, which this wave
+    // wrote: lane (g, c) forms column c by forward substitution (the four lane
+    // groups alike), one row per call.  Without erase A = 0 and T = I: formed
+    // all the same, branch-free.
+    float tc[16];
+    auto t_row = [&](int r) {
+      const float *arow = Af + (16 * RB + r) * LDF + 16 * RB;
+      float x = r == col ? 1.f : 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < r; ++s2) x = fmaf(-arow[s2], tc[s2], x);
+      tc[r] = x;
+    };
+
+    // 8 waves: the chunk-local products of the tiles that are used (the lower
+    // triangle; the upper tiles of S and P are never formed).  Waves 0-3: S of
+    // diagonal block b = wave, its A block and T_bb, a vector-ALU chain; waves
+    // 4-6: S and P of two tiles below the diagonal each; wave 7: P of the four
+    // diagonal tiles.  So every SIMD pairs a T wave with a product wave.
+    auto chunk_local_w8 = [&]() {
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      if (wave < 4) {
+        const int b = wave;
+        f32x4_t sd = z;  // S_bb = K_b K_b^T: both operands are the same fragment
+        Frag<F32> fk[NKB];
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) fk[kk] = load_frag<F32>(Kh, LDK, 16 * b, 32 * kk);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) sd = mma<F32>(sd, fk[kk], fk[kk]);
+        // A_bb stays in registers (no other wave reads the diagonal block):
+        // lane (g, n) holds rows 4g .. 4g+3 of column n
+        const float Gc = Gs[16 * b + col];
+        f32x4_t ab;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = rq + e;  // row inside the block
+          const float a = bet[16 * b + r] * fast_exp2(Gs[16 * b + r] - Gc) * sd[e];
+          ab[e] = erase && col < r ? a : 0.f;
+        }
+        // T_bb column `col` by forward substitution; each A entry is broadcast
+        // from the lane that holds it (v_readlane), so there is no LDS round trip
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float x = r == col ? 1.f : 0.f;
+#pragma unroll
+          for (int s2 = 0; s2 < r; ++s2) {
+            const int a = __builtin_amdgcn_readlane(__float_as_int(ab[r & 3]), 16 * (r >> 2) + s2);
+            x = fmaf(-__int_as_float(a), tc[s2], x);
+          }
+          tc[r] = x;
+        }
+      } else if (wave < 7) {
+        // tiles (i, j): wave 4 (1,0) (2,0); wave 5 (2,1) (3,0); wave 6 (3,1) (3,2)
+        const int w = wave - 4;
+        const int ti[2] = {w + 1, w == 0 ? 2 : 3}, tj[2] = {(w + 1) >> 1, w == 2 ? 2 : 0};
+        f32x4_t sa[2] = {z, z}, pa[2] = {z, z};
+        // steps f = (slab, tile), the fragments of step f + 1 loaded during step f
+        constexpr int NF = NKB * 2;
+        constexpr int RS = 2;  // steps in flight (three fragments each)
+        Frag<F32> fk[RS], fq[RS], fb[RS];
+        auto load_step = [&](int f) {
+          const int kk = f >> 1, t = f & 1;
+          fk[f % RS] = load_frag<F32>(Kh, LDK, 16 * ti[t], 32 * kk);
+          fq[f % RS] = load_frag<F32>(Qh, LDK, 16 * ti[t], 32 * kk);
+          fb[f % RS] = load_frag<F32>(Kh, LDK, 16 * tj[t], 32 * kk);
+        };
+#pragma unroll
+        for (int f = 0; f < RS - 1; ++f) load_step(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (f + RS - 1 < NF) load_step(f + RS - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          sa[f & 1] = mma<F32>(sa[f & 1], fk[f % RS], fb[f % RS]);
+          pa[f & 1] = mma<F32>(pa[f & 1], fq[f % RS], fb[f % RS]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // A and L o P; the tiles lie below the diagonal, so s < r throughout
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float Gc = Gs[16 * tj[t] + col];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ti[t] + rq + e, s = 16 * tj[t] + col;
+            const float dec = fast_exp2(Gs[r] - Gc);
+            Af[r * LDF + s] = erase ? bet[r] * dec * sa[t][e] : 0.f;
+            put(Sq + r * LDC + s, dec * pa[t][e]);
+          }
+        }
+      } else {
+        f32x4_t pd[4] = {z, z, z, z};  // P of the four diagonal tiles
+        // steps f = (slab, tile), the fragments of step f + 1 loaded during step f
+        constexpr int NF = NKB * 4;
+        constexpr int RS = 2;  // steps in flight (two fragments each)
+        Frag<F32> fq[RS], fb[RS];
+        auto load_step = [&](int f) {
+          fq[f % RS] = load_frag<F32>(Qh, LDK, 16 * (f & 3), 32 * (f >> 2));
+          fb[f % RS] = load_frag<F32>(Kh, LDK, 16 * (f & 3), 32 * (f >> 2));
+        };
+#pragma unroll
+        for (int f = 0; f < RS - 1; ++f) load_step(f);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (f + RS - 1 < NF) load_step(f + RS - 1);
+          __builtin_amdgcn_sched_barrier(0);
+          pd[f & 3] = mma<F32>(pd[f & 3], fq[f % RS], fb[f % RS]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float Gc = Gs[16 * b + col];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * b + rq + e;
+            const float dec = col <= rq + e ? fast_exp2(Gs[r] - Gc) : 0.f;
+            put(Sq + r * LDC + 16 * b + col, dec * pd[b][e]);
+          }
+        }
+      }
+    };
+
+
     f32x4_t qm[4][NA], um[4][NA];
 #pragma unroll
     for (int tb = 0; tb < 4; ++tb) {
@@ -239,46 +391,85 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         for (int e = 0; e < 4; ++e) qm[tb][ia][e] = um[tb][ia][e] = 0.f;
       }
     }
-    // S and P (S unused without erase: no branch, straight-line code), the
-    // fragments of step f + 1 loaded during step f's MFMAs
-    {
-      constexpr int NF = NKB * 4;  // (slab, column block)
-      Frag<F32> fk[2], fq[2], fb[2];
-      fk[0] = load_frag<F32>(Kh, LDK, 16 * wave, 0);
-      fq[0] = load_frag<F32>(Qh, LDK, 16 * wave, 0);
-      fb[0] = load_frag<F32>(Kh, LDK, 0, 0);
+    if constexpr (NW == 8) {
+      chunk_local_w8();
+    } else {
+      // ---- 2: S = K K^T, P = Q K^T (a6), the wave's tiles: row block RB,
+      // column blocks cb0 .. cb0 + NCB - 1 ----
+      f32x4_t sacc[NCB], pacc[NCB];
 #pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const int kk = f >> 2, cb = f & 3;
-        if (f + 1 < NF) {
-          const int kn = (f + 1) >> 2;
-          if (((f + 1) & 3) == 0) {
-            fk[kn & 1] = load_frag<F32>(Kh, LDK, 16 * wave, 32 * kn);
-            fq[kn & 1] = load_frag<F32>(Qh, LDK, 16 * wave, 32 * kn);
+      for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sacc[cb][e] = pacc[cb][e] = 0.f;
+      }
+      // S and P (S unused without erase: no branch, straight-line code), the
+      // fragments of step f + 1 loaded during step f's MFMAs
+      {
+        constexpr int NF = NKB * NCB;  // (slab, column block)
+        Frag<F32> fk[2], fq[2], fb[2];
+        fk[0] = load_frag<F32>(Kh, LDK, 16 * RB, 0);
+        fq[0] = load_frag<F32>(Qh, LDK, 16 * RB, 0);
+        fb[0] = load_frag<F32>(Kh, LDK, 16 * cb0, 0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          const int kk = f / NCB, cb = f % NCB;
+          if (f + 1 < NF) {
+            const int kn = (f + 1) / NCB;
+            if ((f + 1) % NCB == 0) {
+              fk[kn & 1] = load_frag<F32>(Kh, LDK, 16 * RB, 32 * kn);
+              fq[kn & 1] = load_frag<F32>(Qh, LDK, 16 * RB, 32 * kn);
+            }
+            fb[(f + 1) & 1] = load_frag<F32>(Kh, LDK, 16 * (cb0 + (f + 1) % NCB), 32 * kn);
           }
-          fb[(f + 1) & 1] = load_frag<F32>(Kh, LDK, 16 * ((f + 1) & 3), 32 * kn);
+          __builtin_amdgcn_sched_barrier(0);
+          sacc[cb] = mma<F32>(sacc[cb], fk[kk & 1], fb[f & 1]);
+          pacc[cb] = mma<F32>(pacc[cb], fq[kk & 1], fb[f & 1]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        sacc[cb] = mma<F32>(sacc[cb], fk[kk & 1], fb[f & 1]);
-        pacc[cb] = mma<F32>(pacc[cb], fq[kk & 1], fb[f & 1]);
-        __builtin_amdgcn_sched_barrier(0);
+      }
+      // ---- 3: A = strict_lower(beta_r e^{G_r-G_s} S), Sq = lower(e^{G_r-G_s} P),
+      // the wave's tiles ----
+      {
+        float Gr[4], br[4], Gc[NCB];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Gr[e] = Gs[16 * RB + rq + e];
+          br[e] = bet[16 * RB + rq + e];
+        }
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) Gc[cb] = Gs[16 * (cb0 + cb) + col];
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * RB + rq + e, s = 16 * (cb0 + cb) + col;
+            const float dec = s <= r ? fast_exp2(Gr[e] - Gc[cb]) : 0.f;
+            Af[r * LDF + s] = (erase && s < r) ? br[e] * dec * sacc[cb][e] : 0.f;
+            put(Sq + r * LDC + s, dec * pacc[cb][e]);
+          }
+        }
       }
     }
-    // Q M and K M with the A fragments double-buffered by hand: the load of
-    // fragment f+1 is issued before the MFMAs of fragment f (scheduling
-    // barriers keep the compiler from moving it back next to its use)
+    if constexpr (kInterleaveT) {
+      asm volatile("" ::: "memory");  // the A rows that t_row reads were written by this wave
+    }
+    // ---- 5: Q M and K M (a7) for the wave's d_v columns, the A fragments in a
+    // ring: the load of fragment f + RING - 1 is issued before the MFMAs of
+    // fragment f (scheduling barriers keep the compiler from moving it back
+    // next to its use) ----
     if (mwave) {
       constexpr int NF = NKB * 8;  // (slab, row block, q or k)
-      Frag<F32> fa[2];
+      Frag<F32> fa[RING];
       Frag<F32> fm[NA];
-      fa[0] = load_afrag<F32>(Qh, LDK, 0, 0);
+      auto load_a = [&](int f) {
+        return load_afrag<F32>((f & 1) ? Kh : Qh, LDK, 16 * ((f >> 1) & 3), 32 * (f >> 3));
+      };
+#pragma unroll
+      for (int f = 0; f < RING - 1; ++f) fa[f] = load_a(f);
 #pragma unroll
       for (int f = 0; f < NF; ++f) {
         const int kk = f >> 3, tb = (f >> 1) & 3, isk = f & 1;
-        if (f + 1 < NF) {
-          const int kn = (f + 1) >> 3, tn = ((f + 1) >> 1) & 3, kn_isk = (f + 1) & 1;
-          fa[(f + 1) & 1] = load_afrag<F32>(kn_isk ? Kh : Qh, LDK, 16 * tn, 32 * kn);
-        }
+        if (f + RING - 1 < NF) fa[(f + RING - 1) % RING] = load_a(f + RING - 1);
         if ((f & 7) == 0) {
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia) {
@@ -289,56 +480,27 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
-          if (isk) um[tb][ia] = mma<F32>(um[tb][ia], fa[f & 1], fm[ia]);
-          else qm[tb][ia] = mma<F32>(qm[tb][ia], fa[f & 1], fm[ia]);
+          if (isk) um[tb][ia] = mma<F32>(um[tb][ia], fa[f % RING], fm[ia]);
+          else qm[tb][ia] = mma<F32>(qm[tb][ia], fa[f % RING], fm[ia]);
+        }
+        if constexpr (kInterleaveT) {
+#pragma unroll
+          for (int r = 16 * f / NF; r < 16 * (f + 1) / NF; ++r) t_row(r);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+    } else if constexpr (kInterleaveT) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) t_row(r);
     }
-    // ---- 3: A = strict_lower(beta_r e^{G_r-G_s} S), Sq = lower(e^{G_r-G_s} P) ----
-    {
-      float Gr[4], br[4], Gc[4];
+    if (diag && lane < 16) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Gr[e] = Gs[16 * wave + rq + e];
-        br[e] = bet[16 * wave + rq + e];
-      }
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) Gc[cb] = Gs[16 * cb + col];
-#pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * wave + rq + e, s = 16 * cb + col;
-          const float dec = s <= r ? fast_exp2(Gr[e] - Gc[cb]) : 0.f;
-          Af[r * LDF + s] = (erase && s < r) ? br[e] * dec * sacc[cb][e] : 0.f;
-          put(Sq + r * LDC + s, dec * pacc[cb][e]);
-        }
-      }
+      for (int r = 0; r < 16; ++r) Tf[(16 * RB + r) * L::LDT + col] = tc[r];
     }
-    __syncthreads();
-    // the next chunk's inputs, in flight through the rest of this chunk (issued
-    // only now so the prefetch registers are free during the MFMA pass above)
-    if (more) fetch(t1);
+    __syncthreads();  // A, L o P and T are visible; every wave is done with the previous chunk
 
     // ---- 5-8: the wave's d_v columns, in registers ----
     if (mwave) {
-      // T_bb = (I + A_bb)^-1 for the four diagonal 16 x 16 blocks, by forward
-      // substitution: lane (bb, c) forms column c of T_bb; into this wave's Tw
-      if (erase) {
-        const int bb = lane >> 4, c = lane & 15;
-        float tc[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = r == c ? 1.f : 0.f;
-          const float *arow = Af + (16 * bb + r) * LDF + 16 * bb;
-#pragma unroll
-          for (int s2 = 0; s2 < r; ++s2) x = fmaf(-arow[s2], tc[s2], x);
-          tc[r] = x;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) Tw[(16 * bb + r) * L::LDT + c] = tc[r];
-      }
       // R = beta (V - gamma K M) for the delta rules, else R = V (beta holds 1 on
       // the chunk's tokens and 0 on its padded rows); um holds R
 #pragma unroll
@@ -367,7 +529,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           for (int j = 0; j < i; ++j, ++n) fa[n] = load_afrag16<F32>(Af, LDF, 16 * i, 16 * j, -1.f);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ft[i] = load_afrag16<F32>(Tw, L::LDT, 16 * i, 0, 1.f);
+        for (int i = 0; i < 4; ++i) ft[i] = load_afrag16<F32>(Tf, L::LDT, 16 * i, 0, 1.f);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0, n = 0; i < 4; ++i) {
@@ -415,6 +577,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) store_o_tile(16 * tb, 16 * (wave * NA + ia), qm[tb][ia]);
       }
+    }
+    // the next chunk's inputs into the other set (every wave finished reading
+    // it, in the previous chunk, before the barrier above)
+    stage(cur ^ 1);
+    if (mwave) {
       // 8: M <- gamma_last M + K^T diag(exp(G_last - G)) U: the decay weights
       // scale U's rows; K^T's fragments are read down the columns of the K rows
       Frag<F32> fe[2][NA];
@@ -440,25 +607,26 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           for (int e = 0; e < 4; ++e) macc[b][ia][e] *= gl;
         }
       }
-      // K^T fragments double-buffered: the next one loads during this one's MFMAs
+      // K^T fragments in a ring, RING - 1 loads ahead of their MFMAs
       {
         constexpr int NF = DKB * 2;  // (d_k block, token slab)
-        Frag<F32> fk[2];
-        fk[0] = load_afrag_t<F32>(Kh, LDK, 0, 0);
+        constexpr int RK = RING < NF ? RING : NF;
+        Frag<F32> fk[RK];
+        auto load_k = [&](int f) { return load_afrag_t<F32>(Kh, LDK, 16 * (f >> 1), 32 * (f & 1)); };
+#pragma unroll
+        for (int f = 0; f < RK - 1; ++f) fk[f] = load_k(f);
 #pragma unroll
         for (int f = 0; f < NF; ++f) {
-          if (f + 1 < NF) fk[(f + 1) & 1] = load_afrag_t<F32>(Kh, LDK, 16 * ((f + 1) >> 1), 32 * ((f + 1) & 1));
+          if (f + RK - 1 < NF) fk[(f + RK - 1) % RK] = load_k(f + RK - 1);
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia)
-            macc[f >> 1][ia] = mma<F32>(macc[f >> 1][ia], fk[f & 1], fe[f & 1][ia]);
+            macc[f >> 1][ia] = mma<F32>(macc[f >> 1][ia], fk[f % RK], fe[f & 1][ia]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
     }
-    __syncthreads();  // all reads of this chunk's LDS operands are done
-    if (more) stage();  // next chunk's K, Q, V and gates into LDS
-    __syncthreads();
+    __syncthreads();  // the next chunk's set is written; this chunk's reads are done
   }
 
   // ---- final state (a8): FP32 -> state dtype (RNE for BF16) -> write slot ----
