@@ -498,6 +498,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       for (int r = 0; r < 16; ++r) Tf[(16 * RB + r) * L::LDT + col] = tc[r];
     }
     __syncthreads();  // A, L o P and T are visible; every wave is done with the previous chunk
+    // the next chunk's inputs into the other set (every wave finished reading
+    // it, in the previous chunk, before the barrier above).  Staged before
+    // this chunk's O stores are issued, so waiting for the prefetch does not
+    // wait for them too.
+    stage(cur ^ 1);
 
     // ---- 5-8: the wave's d_v columns, in registers ----
     if (mwave) {
@@ -578,9 +583,6 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         for (int ia = 0; ia < NA; ++ia) store_o_tile(16 * tb, 16 * (wave * NA + ia), qm[tb][ia]);
       }
     }
-    // the next chunk's inputs into the other set (every wave finished reading
-    // it, in the previous chunk, before the barrier above)
-    stage(cur ^ 1);
     if (mwave) {
       // 8: M <- gamma_last M + K^T diag(exp(G_last - G)) U: the decay weights
       // scale U's rows; K^T's fragments are read down the columns of the K rows
