@@ -92,6 +92,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   }
   const bool decay = (p.rule & kRuleDecay) != 0;
   const bool erase = (p.rule & kRuleErase) != 0;
+  // 1 for the delta rules, else 0: a factor rather than a branch, so no LDS
+  // load ends up inside a branch of its own (that costs a round trip each)
+  const float ef = erase ? 1.f : 0.f;
 
   // ---- prefetch of one chunk's inputs into registers, and their staging ----
   // The loads are unconditional: a row past the sequence's end re-reads its
@@ -277,13 +280,83 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     // 8 waves: the chunk-local products of the tiles that are used (the lower
     // triangle; the upper tiles of S and P are never formed).  Waves 0-3: S of
     // diagonal block b = wave, its A block and T_bb, a vector-ALU chain; waves
-    // 4-6: S and P of two tiles below the diagonal each; wave 7: P of the four
-    // diagonal tiles.  So every SIMD pairs a T wave with a product wave.
+    // 4-7: S and P of the six tiles below the diagonal (two, two, one, one),
+    // waves 6 and 7 also P of two diagonal tiles each.  So every SIMD pairs a
+    // T wave with a product wave.
     auto chunk_local_w8 = [&]() {
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+      // S and P of off-diagonal tiles (i, j), i > j, into A and L o P (s < r
+      // throughout), the fragments of step f + 1 loaded during step f
+      auto offdiag = [&](const int *ti, const int *tj, auto ntiles) {
+        constexpr int NTL = decltype(ntiles)::value;
+        f32x4_t sa[NTL], pa[NTL];
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) sa[t] = pa[t] = z;
+        constexpr int NF = NKB * NTL;  // steps (slab, tile)
+        Frag<F32> fk[2], fq[2], fb[2];
+        auto load_step = [&](int f) {
+          const int kk = f / NTL, t = f % NTL;
+          fk[f & 1] = load_frag<F32>(Kh, LDK, 16 * ti[t], 32 * kk);
+          fq[f & 1] = load_frag<F32>(Qh, LDK, 16 * ti[t], 32 * kk);
+          fb[f & 1] = load_frag<F32>(Kh, LDK, 16 * tj[t], 32 * kk);
+        };
+        load_step(0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (f + 1 < NF) load_step(f + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          sa[f % NTL] = mma<F32>(sa[f % NTL], fk[f & 1], fb[f & 1]);
+          pa[f % NTL] = mma<F32>(pa[f % NTL], fq[f & 1], fb[f & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
+          const float Gc = Gs[16 * tj[t] + col];
+          const f32x4_t Gr = *reinterpret_cast<const f32x4_t *>(Gs + 16 * ti[t] + rq);
+          const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * ti[t] + rq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * ti[t] + rq + e, s = 16 * tj[t] + col;
+            const float dec = fast_exp2(Gr[e] - Gc);
+            Af[r * LDF + s] = (ef * br[e]) * dec * sa[t][e];
+            put(Sq + r * LDC + s, dec * pa[t][e]);
+          }
+        }
+      };
+      // P of diagonal tiles (b, b) into L o P, masked to s <= r
+      auto diag_p = [&](int b0) {
+        f32x4_t pd[2] = {z, z};
+        constexpr int NF = NKB * 2;  // steps (slab, tile)
+        Frag<F32> fq[2], fb[2];
+        auto load_step = [&](int f) {
+          fq[f & 1] = load_frag<F32>(Qh, LDK, 16 * (b0 + (f & 1)), 32 * (f >> 1));
+          fb[f & 1] = load_frag<F32>(Kh, LDK, 16 * (b0 + (f & 1)), 32 * (f >> 1));
+        };
+        load_step(0);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if (f + 1 < NF) load_step(f + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          pd[f & 1] = mma<F32>(pd[f & 1], fq[f & 1], fb[f & 1]);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int b = b0 + t;
+          const float Gc = Gs[16 * b + col];
+          const f32x4_t Gr = *reinterpret_cast<const f32x4_t *>(Gs + 16 * b + rq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * b + rq + e;
+            const float x = fast_exp2(Gr[e] - Gc) * pd[t][e];
+            put(Sq + r * LDC + 16 * b + col, col <= rq + e ? x : 0.f);
+          }
+        }
+      };
       if (wave < 4) {
+        // diagonal block b = wave: S_bb = K_b K_b^T, both operands the same fragment
         const int b = wave;
-        f32x4_t sd = z;  // S_bb = K_b K_b^T: both operands are the same fragment
+        f32x4_t sd = z;
         Frag<F32> fk[NKB];
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk) fk[kk] = load_frag<F32>(Kh, LDK, 16 * b, 32 * kk);
@@ -293,12 +366,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         // A_bb stays in registers (no other wave reads the diagonal block):
         // lane (g, n) holds rows 4g .. 4g+3 of column n
         const float Gc = Gs[16 * b + col];
+        const f32x4_t Gr = *reinterpret_cast<const f32x4_t *>(Gs + 16 * b + rq);
+        const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * b + rq);
         f32x4_t ab;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = rq + e;  // row inside the block
-          const float a = bet[16 * b + r] * fast_exp2(Gs[16 * b + r] - Gc) * sd[e];
-          ab[e] = erase && col < r ? a : 0.f;
+          const float a = (ef * br[e]) * fast_exp2(Gr[e] - Gc) * sd[e];
+          ab[e] = col < rq + e ? a : 0.f;  // row rq + e inside the block
         }
         // T_bb column `col` by forward substitution; each A entry is broadcast
         // from the lane that holds it (v_readlane), so there is no LDS round trip
@@ -312,72 +386,16 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           }
           tc[r] = x;
         }
-      } else if (wave < 7) {
-        // tiles (i, j): wave 4 (1,0) (2,0); wave 5 (2,1) (3,0); wave 6 (3,1) (3,2)
+      } else if (wave < 6) {
+        // wave 4: tiles (1,0) (2,0); wave 5: (2,1) (3,0)
         const int w = wave - 4;
-        const int ti[2] = {w + 1, w == 0 ? 2 : 3}, tj[2] = {(w + 1) >> 1, w == 2 ? 2 : 0};
-        f32x4_t sa[2] = {z, z}, pa[2] = {z, z};
-        // steps f = (slab, tile), the fragments of step f + 1 loaded during step f
-        constexpr int NF = NKB * 2;
-        constexpr int RS = 2;  // steps in flight (three fragments each)
-        Frag<F32> fk[RS], fq[RS], fb[RS];
-        auto load_step = [&](int f) {
-          const int kk = f >> 1, t = f & 1;
-          fk[f % RS] = load_frag<F32>(Kh, LDK, 16 * ti[t], 32 * kk);
-          fq[f % RS] = load_frag<F32>(Qh, LDK, 16 * ti[t], 32 * kk);
-          fb[f % RS] = load_frag<F32>(Kh, LDK, 16 * tj[t], 32 * kk);
-        };
-#pragma unroll
-        for (int f = 0; f < RS - 1; ++f) load_step(f);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          if (f + RS - 1 < NF) load_step(f + RS - 1);
-          __builtin_amdgcn_sched_barrier(0);
-          sa[f & 1] = mma<F32>(sa[f & 1], fk[f % RS], fb[f % RS]);
-          pa[f & 1] = mma<F32>(pa[f & 1], fq[f % RS], fb[f % RS]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // A and L o P; the tiles lie below the diagonal, so s < r throughout
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const float Gc = Gs[16 * tj[t] + col];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * ti[t] + rq + e, s = 16 * tj[t] + col;
-            const float dec = fast_exp2(Gs[r] - Gc);
-            Af[r * LDF + s] = erase ? bet[r] * dec * sa[t][e] : 0.f;
-            put(Sq + r * LDC + s, dec * pa[t][e]);
-          }
-        }
+        const int ti[2] = {w + 1, w + 2}, tj[2] = {w, 0};
+        offdiag(ti, tj, std::integral_constant<int, 2>());
       } else {
-        f32x4_t pd[4] = {z, z, z, z};  // P of the four diagonal tiles
-        // steps f = (slab, tile), the fragments of step f + 1 loaded during step f
-        constexpr int NF = NKB * 4;
-        constexpr int RS = 2;  // steps in flight (two fragments each)
-        Frag<F32> fq[RS], fb[RS];
-        auto load_step = [&](int f) {
-          fq[f % RS] = load_frag<F32>(Qh, LDK, 16 * (f & 3), 32 * (f >> 2));
-          fb[f % RS] = load_frag<F32>(Kh, LDK, 16 * (f & 3), 32 * (f >> 2));
-        };
-#pragma unroll
-        for (int f = 0; f < RS - 1; ++f) load_step(f);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          if (f + RS - 1 < NF) load_step(f + RS - 1);
-          __builtin_amdgcn_sched_barrier(0);
-          pd[f & 3] = mma<F32>(pd[f & 3], fq[f % RS], fb[f % RS]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const float Gc = Gs[16 * b + col];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * b + rq + e;
-            const float dec = col <= rq + e ? fast_exp2(Gs[r] - Gc) : 0.f;
-            put(Sq + r * LDC + 16 * b + col, dec * pd[b][e]);
-          }
-        }
+        // wave 6: tile (3,1) and P of diagonal tiles 0, 1; wave 7: (3,2) and 2, 3
+        const int ti[1] = {3}, tj[1] = {wave - 5};
+        offdiag(ti, tj, std::integral_constant<int, 1>());
+        diag_p(2 * (wave - 6));
       }
     };
 
@@ -430,12 +448,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       // ---- 3: A = strict_lower(beta_r e^{G_r-G_s} S), Sq = lower(e^{G_r-G_s} P),
       // the wave's tiles ----
       {
-        float Gr[4], br[4], Gc[NCB];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          Gr[e] = Gs[16 * RB + rq + e];
-          br[e] = bet[16 * RB + rq + e];
-        }
+        // gate rows as 16-byte loads and masks as selects, so no LDS load sits
+        // in a branch of its own
+        const f32x4_t Gr = *reinterpret_cast<const f32x4_t *>(Gs + 16 * RB + rq);
+        const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * RB + rq);
+        float Gc[NCB];
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) Gc[cb] = Gs[16 * (cb0 + cb) + col];
 #pragma unroll
@@ -443,8 +460,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * RB + rq + e, s = 16 * (cb0 + cb) + col;
-            const float dec = s <= r ? fast_exp2(Gr[e] - Gc[cb]) : 0.f;
-            Af[r * LDF + s] = (erase && s < r) ? br[e] * dec * sacc[cb][e] : 0.f;
+            const float e2 = fast_exp2(Gr[e] - Gc[cb]);
+            const float dec = s <= r ? e2 : 0.f;
+            const float a = (ef * br[e]) * dec * sacc[cb][e];
+            Af[r * LDF + s] = s < r ? a : 0.f;
             put(Sq + r * LDC + s, dec * pacc[cb][e]);
           }
         }
@@ -507,19 +526,21 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     // ---- 5-8: the wave's d_v columns, in registers ----
     if (mwave) {
       // R = beta (V - gamma K M) for the delta rules, else R = V (beta holds 1 on
-      // the chunk's tokens and 0 on its padded rows); um holds R
+      // the chunk's tokens and 0 on its padded rows); um holds R.  Branch-free:
+      // without erase ef = 0 and the K M term is an exact zero.  The lane's four
+      // rows of beta and gamma are one 16-byte load each.
 #pragma unroll
       for (int tb = 0; tb < 4; ++tb) {
         float vv[NA][4];
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) load_col4(Vh, LDV, 16 * tb, 16 * (wave * NA + ia), vv[ia]);
+        const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * tb + rq);
+        const f32x4_t gr = *reinterpret_cast<const f32x4_t *>(gam + 16 * tb + rq);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int r = 16 * tb + rq + e;
-          const float br = bet[r], gr = gam[r];
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia)
-            um[tb][ia][e] = br * (erase ? vv[ia][e] - gr * um[tb][ia][e] : vv[ia][e]);
+            um[tb][ia][e] = br[e] * (vv[ia][e] - (ef * gr[e]) * um[tb][ia][e]);
         }
       }
       // 6: U = (I + A)^-1 R (delta rules), block forward substitution in
@@ -569,10 +590,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tb = 0, n = 0; tb < 4; ++tb) {
+        const f32x4_t gr = *reinterpret_cast<const f32x4_t *>(gam + 16 * tb + rq);
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) qm[tb][ia][e] *= gam[16 * tb + rq + e];
+          for (int e = 0; e < 4; ++e) qm[tb][ia][e] *= gr[e];
         }
 #pragma unroll
         for (int s2 = 0; s2 <= tb / 2; ++s2, ++n) {
@@ -589,13 +611,15 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       Frag<F32> fe[2][NA];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
+        const f32x4_t elo = *reinterpret_cast<const f32x4_t *>(eGn + 32 * s2 + rq);
+        const f32x4_t ehi = *reinterpret_cast<const f32x4_t *>(eGn + 32 * s2 + 16 + rq);
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
           f32x4_t lo = um[2 * s2][ia], hi = um[2 * s2 + 1][ia];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            lo[e] *= eGn[32 * s2 + rq + e];
-            hi[e] *= eGn[32 * s2 + 16 + rq + e];
+            lo[e] *= elo[e];
+            hi[e] *= ehi[e];
           }
           fe[s2][ia] = bfrag<F32>(lo, hi);
         }
