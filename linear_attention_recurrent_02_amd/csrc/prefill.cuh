@@ -95,6 +95,10 @@ struct PrefillLayout {
   static constexpr int LDT = 20;  // T_ii rows (float); 16-byte aligned rows
   static constexpr size_t TF = AF + (size_t)C * LDF * 4;  // the four T_ii, stacked
   static constexpr size_t BYTES = TF + (size_t)C * LDT * 4;
+  // BF16 copies for the substitution's operands (-A below the diagonal, T_ii),
+  // where no FP32 reader needs them: in the AF and TF regions
+  static constexpr int LDAB = C + 8, LDTB = 16 + 8;
+  static_assert((size_t)C * LDAB * 2 <= (size_t)C * LDF * 4 && LDTB * 2 <= LDT * 4, "BF16 copies fit");
 };
 
 // ---- MFMA fragments -------------------------------------------------------
@@ -300,6 +304,14 @@ __device__ __forceinline__ Frag16<F32> load_afrag16(const float *base, int ld, i
   return f;
 }
 
+// the same 16 x 16 fragment of a row-major BF16 matrix (stored ready to use:
+// no conversion, no sign)
+__device__ __forceinline__ Frag16<false> load_afrag16(const uint16_t *base, int ld, int r0, int k0) {
+  const int l = threadIdx.x & 63;
+  Frag16<false> f;
+  f.v = *reinterpret_cast<const s16x4_t *>(base + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4));
+  return f;
+}
 template <bool F32>
 __device__ __forceinline__ f32x4_t mma16(f32x4_t c, const Frag16<F32> &a, const Frag16<F32> &b) {
   if constexpr (F32) {

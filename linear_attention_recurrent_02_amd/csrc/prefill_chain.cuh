@@ -52,7 +52,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   constexpr bool kInterleaveT = NW == 4;
   // LDS operand fragments kept in flight ahead of the MFMA that uses them: one
   // 16x16x32 MFMA is 16 cycles, an LDS round trip several times that
-  constexpr int RING = 3;
+  constexpr int RING = 4;
+  // 8 waves with BF16 operands: -A and T_ii are stored in BF16 ready for the
+  // substitution's MFMAs (no FP32 reader needs them)
+  constexpr bool kBfAT = NW == 8 && !F32;
   constexpr int EW = 8 * (int)sizeof(AT) / 16;  // 16-byte vectors per 8 elements
   constexpr int KQ_GROUPS = C * (DK / 8), KQ_PER = (KQ_GROUPS + NT - 1) / NT;
   constexpr int V_GROUPS = C * (DV / 8), V_PER = (V_GROUPS + NT - 1) / NT;
@@ -71,6 +74,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   OT *Sq = reinterpret_cast<OT *>(smem + L::SQ);
   float *Af = reinterpret_cast<float *>(smem + L::AF);
   float *Tf = reinterpret_cast<float *>(smem + L::TF);  // T_ii = (I + A_ii)^-1, stacked
+  uint16_t *Ab = reinterpret_cast<uint16_t *>(smem + L::AF);  // kBfAT: -A in BF16
+  uint16_t *Tb = reinterpret_cast<uint16_t *>(smem + L::TF);  // kBfAT: T_ii in BF16
 
   const int seq = chain / p.H_v, h = chain % p.H_v, hq = h / p.group;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -318,7 +323,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * ti[t] + rq + e, s = 16 * tj[t] + col;
             const float dec = fast_exp2(Gr[e] - Gc);
-            Af[r * LDF + s] = (ef * br[e]) * dec * sa[t][e];
+            const float a = (ef * br[e]) * dec * sa[t][e];
+            if constexpr (kBfAT) put(Ab + r * L::LDAB + s, -a);
+            else Af[r * LDF + s] = a;
             put(Sq + r * LDC + s, dec * pa[t][e]);
           }
         }
@@ -514,7 +521,10 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     }
     if (diag && lane < 16) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) Tf[(16 * RB + r) * L::LDT + col] = tc[r];
+      for (int r = 0; r < 16; ++r) {
+        if constexpr (kBfAT) put(Tb + (16 * RB + r) * L::LDTB + col, tc[r]);
+        else Tf[(16 * RB + r) * L::LDT + col] = tc[r];
+      }
     }
     __syncthreads();  // A, L o P and T are visible; every wave is done with the previous chunk
     // the next chunk's inputs into the other set (every wave finished reading
@@ -552,10 +562,16 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
         for (int i = 1, n = 0; i < 4; ++i) {
 #pragma unroll
-          for (int j = 0; j < i; ++j, ++n) fa[n] = load_afrag16<F32>(Af, LDF, 16 * i, 16 * j, -1.f);
+          for (int j = 0; j < i; ++j, ++n) {
+            if constexpr (kBfAT) fa[n] = load_afrag16(Ab, L::LDAB, 16 * i, 16 * j);
+            else fa[n] = load_afrag16<F32>(Af, LDF, 16 * i, 16 * j, -1.f);
+          }
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ft[i] = load_afrag16<F32>(Tf, L::LDT, 16 * i, 0, 1.f);
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (kBfAT) ft[i] = load_afrag16(Tb, L::LDTB, 16 * i, 0);
+          else ft[i] = load_afrag16<F32>(Tf, L::LDT, 16 * i, 0, 1.f);
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int i = 0, n = 0; i < 4; ++i) {
