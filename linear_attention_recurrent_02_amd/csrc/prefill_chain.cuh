@@ -53,9 +53,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   // LDS operand fragments kept in flight ahead of the MFMA that uses them: one
   // 16x16x32 MFMA is 16 cycles, an LDS round trip several times that
   constexpr int RING = 4;
-  // 8 waves with BF16 operands: -A and T_ii are stored in BF16 ready for the
+  // BF16 operands: -A and T_ii are stored in BF16 ready for the
   // substitution's MFMAs (no FP32 reader needs them)
-  constexpr bool kBfAT = NW == 8 && !F32;
+  constexpr bool kBfAT = !F32;
   constexpr int EW = 8 * (int)sizeof(AT) / 16;  // 16-byte vectors per 8 elements
   constexpr int KQ_GROUPS = C * (DK / 8), KQ_PER = (KQ_GROUPS + NT - 1) / NT;
   constexpr int V_GROUPS = C * (DV / 8), V_PER = (V_GROUPS + NT - 1) / NT;
@@ -270,15 +270,20 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     fetch(t1);
 
     // T_RB,RB = (I + A_RB,RB)^-1 from diagonal block RB of A, which this wave
-    // wrote: lane (g, c) forms column c by forward substitution (the four lane
-    // groups alike), one row per call.  Without erase A = 0 and T = I: formed
-    // all the same, branch-free.
+    // holds in registers (ab; lane (g, n): rows 4g .. 4g+3 of column n): lane
+    // (g, c) forms column c by forward substitution (the four lane groups
+    // alike), one row per call, each A entry broadcast from the lane that
+    // holds it (v_readlane), so there is no LDS round trip.  Without erase
+    // A = 0 and T = I: formed all the same, branch-free.
     float tc[16];
+    f32x4_t ab = {0.f, 0.f, 0.f, 0.f};
     auto t_row = [&](int r) {
-      const float *arow = Af + (16 * RB + r) * LDF + 16 * RB;
       float x = r == col ? 1.f : 0.f;
 #pragma unroll
-      for (int s2 = 0; s2 < r; ++s2) x = fmaf(-arow[s2], tc[s2], x);
+      for (int s2 = 0; s2 < r; ++s2) {
+        const int a = __builtin_amdgcn_readlane(__float_as_int(ab[r & 3]), 16 * (r >> 2) + s2);
+        x = fmaf(-__int_as_float(a), tc[s2], x);
+      }
       tc[r] = x;
     };
 
@@ -375,24 +380,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         const float Gc = Gs[16 * b + col];
         const f32x4_t Gr = *reinterpret_cast<const f32x4_t *>(Gs + 16 * b + rq);
         const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * b + rq);
-        f32x4_t ab;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float a = (ef * br[e]) * fast_exp2(Gr[e] - Gc) * sd[e];
           ab[e] = col < rq + e ? a : 0.f;  // row rq + e inside the block
         }
-        // T_bb column `col` by forward substitution; each A entry is broadcast
-        // from the lane that holds it (v_readlane), so there is no LDS round trip
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = r == col ? 1.f : 0.f;
-#pragma unroll
-          for (int s2 = 0; s2 < r; ++s2) {
-            const int a = __builtin_amdgcn_readlane(__float_as_int(ab[r & 3]), 16 * (r >> 2) + s2);
-            x = fmaf(-__int_as_float(a), tc[s2], x);
-          }
-          tc[r] = x;
-        }
+        for (int r = 0; r < 16; ++r) t_row(r);
       } else if (wave < 6) {
         // wave 4: tiles (1,0) (2,0); wave 5: (2,1) (3,0)
         const int w = wave - 4;
@@ -469,15 +463,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
             const int r = 16 * RB + rq + e, s = 16 * (cb0 + cb) + col;
             const float e2 = fast_exp2(Gr[e] - Gc[cb]);
             const float dec = s <= r ? e2 : 0.f;
-            const float a = (ef * br[e]) * dec * sacc[cb][e];
-            Af[r * LDF + s] = s < r ? a : 0.f;
+            const float a = s < r ? (ef * br[e]) * dec * sacc[cb][e] : 0.f;
+            if constexpr (kBfAT) put(Ab + r * L::LDAB + s, -a);
+            else Af[r * LDF + s] = a;
             put(Sq + r * LDC + s, dec * pacc[cb][e]);
+            if (cb0 + cb == RB) ab[e] = a;  // the wave's diagonal block, for its T
           }
         }
       }
-    }
-    if constexpr (kInterleaveT) {
-      asm volatile("" ::: "memory");  // the A rows that t_row reads were written by this wave
     }
     // ---- 5: Q M and K M (a7) for the wave's d_v columns, the A fragments in a
     // ring: the load of fragment f + RING - 1 is issued before the MFMAs of
