@@ -109,32 +109,65 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   u32x4_t pk[KQ_PER][EW], pq[KQ_PER][EW], pv[V_PER][EW];
   float pg = 0.f, pb = 0.f;  // wave 0: gate inputs of token `lane`
   bool p_valid = false;       // wave 0: token `lane` lies inside the sequence
+  // Addressing: a thread's load i of a chunk reads row r0 + i * RS (RS rows
+  // between the thread's loads), so its offset is a per-thread part fixed for
+  // the chain plus a uniform one; only a sequence's last chunk clamps rows.
+  constexpr int KQ_RS = NT / (DK / 8), V_RS = NT / (DV / 8);
+  const int64_t kq_row = (int64_t)p.H_qk * DK, v_row = (int64_t)p.H_v * DV;  // elements per token
+  const int kq_r0 = tid / (DK / 8), v_r0 = tid / (DV / 8);
+  const uint32_t kq_lane = (uint32_t)(kq_r0 * kq_row + (tid % (DK / 8)) * 8);
+  const uint32_t v_lane = (uint32_t)(v_r0 * v_row + (tid % (DV / 8)) * 8);
+  const uint32_t g_lane = (uint32_t)(lane * p.H_v);
   auto fetch = [&](int64_t t0) {
     const int64_t last = t_end - 1;
+    const AT *const kb = static_cast<const AT *>(p.k) + t0 * kq_row + hq * DK;
+    const AT *const qb = static_cast<const AT *>(p.q) + t0 * kq_row + hq * DK;
+    const AT *const vb = static_cast<const AT *>(p.v) + t0 * v_row + h * DV;
+    if (t0 + C - 1 <= last) {  // a whole chunk: no clamping
 #pragma unroll
-    for (int i = 0; i < KQ_PER; ++i) {
-      const int gi = tid + NT * i;
-      const int r = gi / (DK / 8), d = (gi % (DK / 8)) * 8;
-      const int64_t off = (std::min(t0 + r, last) * p.H_qk + hq) * DK + d;
-      const u32x4_t *sk = reinterpret_cast<const u32x4_t *>(static_cast<const AT *>(p.k) + off);
-      const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(static_cast<const AT *>(p.q) + off);
+      for (int i = 0; i < KQ_PER; ++i) {
+        // threads past the chunk's groups (small d_k only) load nothing: their
+        // rows would lie past the chunk, and stage() skips them
+        if (KQ_GROUPS % NT != 0 && tid + NT * i >= KQ_GROUPS) continue;
+        const int64_t off = kq_lane + (int64_t)i * KQ_RS * kq_row;
+        const u32x4_t *sk = reinterpret_cast<const u32x4_t *>(kb + off);
+        const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(qb + off);
 #pragma unroll
-      for (int e = 0; e < EW; ++e) { pk[i][e] = sk[e]; pq[i][e] = sq[e]; }
-    }
+        for (int e = 0; e < EW; ++e) { pk[i][e] = sk[e]; pq[i][e] = sq[e]; }
+      }
 #pragma unroll
-    for (int i = 0; i < V_PER; ++i) {
-      const int gi = tid + NT * i;
-      const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
-      const u32x4_t *sv = reinterpret_cast<const u32x4_t *>(
-          static_cast<const AT *>(p.v) + (std::min(t0 + r, last) * p.H_v + h) * DV + c);
+      for (int i = 0; i < V_PER; ++i) {
+        if (V_GROUPS % NT != 0 && tid + NT * i >= V_GROUPS) continue;
+        const u32x4_t *sv = reinterpret_cast<const u32x4_t *>(vb + v_lane + (int64_t)i * V_RS * v_row);
 #pragma unroll
-      for (int e = 0; e < EW; ++e) pv[i][e] = sv[e];
+        for (int e = 0; e < EW; ++e) pv[i][e] = sv[e];
+      }
+    } else {
+      const int rmax = (int)(last - t0);
+#pragma unroll
+      for (int i = 0; i < KQ_PER; ++i) {
+        const int gi = tid + NT * i;
+        const int r = std::min(gi / (DK / 8), rmax), d = (gi % (DK / 8)) * 8;
+        const int64_t off = r * kq_row + d;
+        const u32x4_t *sk = reinterpret_cast<const u32x4_t *>(kb + off);
+        const u32x4_t *sq = reinterpret_cast<const u32x4_t *>(qb + off);
+#pragma unroll
+        for (int e = 0; e < EW; ++e) { pk[i][e] = sk[e]; pq[i][e] = sq[e]; }
+      }
+#pragma unroll
+      for (int i = 0; i < V_PER; ++i) {
+        const int gi = tid + NT * i;
+        const int r = std::min(gi / (DV / 8), rmax), c = (gi % (DV / 8)) * 8;
+        const u32x4_t *sv = reinterpret_cast<const u32x4_t *>(vb + r * v_row + c);
+#pragma unroll
+        for (int e = 0; e < EW; ++e) pv[i][e] = sv[e];
+      }
     }
     if (wave == 0) {
       // raw values only: any arithmetic on them here would wait for the whole
       // fetch (loads retire in order); stage() masks them.  g and beta may be
       // NULL under the rules that do not use them.
-      const int64_t gt = std::min(t0 + lane, last) * p.H_v + h;
+      const int64_t gt = t0 * p.H_v + h + (t0 + lane <= last ? (int64_t)g_lane : (last - t0) * p.H_v);
       if (decay) pg = p.g[gt];
       if (erase) pb = p.beta[gt];
       p_valid = t0 + lane <= last;
@@ -179,28 +212,32 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   // the accumulator layout, scaled and stored (only rows inside the chunk).
   // BF16: each lane swaps halves with its neighbour column (lane ^ 1), so a
   // lane stores two rows of a column pair as 4-byte words.
+  // Addresses: a uniform base per chunk, a per-lane offset fixed for the
+  // chain (32-bit: it spans at most 16 token rows) and a uniform per-tile part.
   AT *const o_head = static_cast<AT *>(p.o) + (int64_t)h * DV;
   const int64_t o_row = (int64_t)p.H_v * DV;  // elements between tokens
-  int64_t o_t0 = 0;                           // first token of the chunk
-  int o_n = 0;                                // tokens in the chunk
-  auto store_o_tile = [&](int r0, int c0, const f32x4_t &acc) {
+  const bool o_odd = (col & 1) != 0;
+  const uint32_t o_lane = AB ? (uint32_t)((rq + (o_odd ? 2 : 0)) * o_row + (col & ~1))
+                             : (uint32_t)(rq * o_row + col);  // elements
+  AT *o_base = o_head;  // row 0 of the chunk
+  int o_n = 0;          // tokens in the chunk
+  auto store_o_tile = [&](int r0, int c0, const f32x4_t &acc, bool whole) {
+    AT *const dst = o_base + r0 * o_row + c0 + o_lane;
     if constexpr (AB) {
-      const bool odd = (col & 1) != 0;
       const uint32_t a = pack_bf16x2(p.scale * acc[0], p.scale * acc[1]);  // rows 0, 1
       const uint32_t b = pack_bf16x2(p.scale * acc[2], p.scale * acc[3]);  // rows 2, 3
-      const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)(odd ? a : b), 0xB1, 0xf, 0xf, false);
-      const uint32_t own = odd ? b : a;
-      const uint32_t left = odd ? other : own, right = odd ? own : other;  // columns c, c + 1
-      const int r = r0 + rq + (odd ? 2 : 0);
-      AT *dst = o_head + (o_t0 + r) * o_row + c0 + (col & ~1);
-      if (r < o_n) *reinterpret_cast<uint32_t *>(dst) = __builtin_amdgcn_perm(right, left, 0x05040100u);
-      if (r + 1 < o_n)
-        *reinterpret_cast<uint32_t *>(dst + o_row) = __builtin_amdgcn_perm(right, left, 0x07060302u);
+      const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)(o_odd ? a : b), 0xB1, 0xf, 0xf, false);
+      const uint32_t own = o_odd ? b : a;
+      const uint32_t left = o_odd ? other : own, right = o_odd ? own : other;  // columns c, c + 1
+      const uint32_t w0 = __builtin_amdgcn_perm(right, left, 0x05040100u);
+      const uint32_t w1 = __builtin_amdgcn_perm(right, left, 0x07060302u);
+      const int r = r0 + rq + (o_odd ? 2 : 0);
+      if (whole || r < o_n) *reinterpret_cast<uint32_t *>(dst) = w0;
+      if (whole || r + 1 < o_n) *reinterpret_cast<uint32_t *>(dst + o_row) = w1;
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = r0 + rq + e;
-        if (r < o_n) o_head[(o_t0 + r) * o_row + c0 + col] = p.scale * acc[e];
+        if (whole || r0 + rq + e < o_n) dst[e * o_row] = p.scale * acc[e];
       }
     }
   };
@@ -259,7 +296,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   int cur = 0;  // input set of the current chunk
   for (int64_t t0 = t_begin; t0 < t_end; t0 += C, cur ^= 1) {
     const int64_t t1 = t0 + C;
-    o_t0 = t0;
+    o_base = o_head + t0 * o_row;
     o_n = (int)std::min<int64_t>(C, t_end - t0);
     use_set(cur);
     // The next chunk's inputs, in flight while this chunk computes.  Fetched
@@ -610,8 +647,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
           for (int ia = 0; ia < NA; ++ia) qm[tb][ia] = mma<F32>(qm[tb][ia], fs[n], fu[s2][ia]);
         }
+        // whole chunks store without row checks (a uniform branch)
+        if (o_n == C) {
 #pragma unroll
-        for (int ia = 0; ia < NA; ++ia) store_o_tile(16 * tb, 16 * (wave * NA + ia), qm[tb][ia]);
+          for (int ia = 0; ia < NA; ++ia) store_o_tile(16 * tb, 16 * (wave * NA + ia), qm[tb][ia], true);
+        } else {
+#pragma unroll
+          for (int ia = 0; ia < NA; ++ia) store_o_tile(16 * tb, 16 * (wave * NA + ia), qm[tb][ia], false);
+        }
       }
     }
     if (mwave) {
