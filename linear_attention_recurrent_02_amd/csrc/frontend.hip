@@ -35,6 +35,7 @@ constexpr int kFeDepth = 8;   // tokens loaded ahead per thread
 constexpr int kFeBlocksPerCU = 3;  // resident workgroups per CU the grid aims at
 static_assert(kFeRun <= 64, "sequence starts in a run are a 64-bit mask");
 static_assert(kFeRun % kFeDepth == 0, "a whole run is a whole number of ring turns");
+static_assert(kFeDepth % 4 == 0, "the conv window ring has four token slots");
 
 // One of the three tensors of the front-end, split into chunks of `lpr`
 // 16-byte pieces (a power of two; a chunk holds whole heads).
@@ -84,6 +85,25 @@ __device__ __forceinline__ int64_t ordered_after(float (&x)[CH], int64_t v) {
 // SiLU with the hardware exp and reciprocal: x * 1 / (1 + e^-x)
 __device__ __forceinline__ float silu_fast(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+// one DPP permutation of a float, every lane reading the lane CTRL selects
+template <int CTRL>
+__device__ __forceinline__ float dpp_perm(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
+}
+
+// Sum over the N lanes of a head (N a power of two, at most 32), left in all
+// of them: the pairs of an xor butterfly, formed by DPP inside each 16-lane
+// row (quad permutes, then the half-row and row mirrors), a shuffle across rows.
+template <int N>
+__device__ __forceinline__ float head_sum(float x) {
+  if constexpr (N >= 2) x += dpp_perm<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (N >= 4) x += dpp_perm<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (N >= 8) x += dpp_perm<0x141>(x);  // row_half_mirror: the other quad
+  if constexpr (N >= 16) x += dpp_perm<0x140>(x); // row_mirror: the other half row
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
 }
 
 template <bool AB, int D, bool NORM, bool GATES>
@@ -140,16 +160,22 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
     return m;
   };
 
-  // x1, x2, x3 = the previous three tokens of this piece (0 before the sequence)
-  float x1[CH], x2[CH], x3[CH];
+  // The conv window is a ring of four token slots: token ts + j lives in slot
+  // j % 4 (runs and the unrolled steps are multiples of 4 tokens, so every
+  // slot index is a constant and the window slides without register copies).
+  // Slots 3, 2, 1 start as tokens ts - 1, ts - 2, ts - 3 (0 before the sequence).
+  float xw[4][CH];
   if (ts - 1 < s_start) h1 = make_uint4(0, 0, 0, 0);
   if (ts - 2 < s_start) h2 = make_uint4(0, 0, 0, 0);
   if (ts - 3 < s_start) h3 = make_uint4(0, 0, 0, 0);
-  E::unpack(h1, x1); E::unpack(h2, x2); E::unpack(h3, x3);
+  E::unpack(h1, xw[3]); E::unpack(h2, xw[2]); E::unpack(h3, xw[1]);
 
-  // one token: conv + SiLU (+ L2 norm) of x0 given the window, then slide it;
+  // one token, slot u % 4: conv + SiLU (+ L2 norm) of x0 given the window;
   // `check` = the run holds a sequence start (bit i of resets clears the window)
-  auto step = [&](const float (&x0)[CH], bool check, uint64_t resets, int i, float (&y)[CH]) {
+  auto step = [&](const float (&x0)[CH], bool check, uint64_t resets, int i, int u, float (&y)[CH]) {
+    float(&x1)[CH] = xw[(u + 3) & 3];
+    float(&x2)[CH] = xw[(u + 2) & 3];
+    float(&x3)[CH] = xw[(u + 1) & 3];
     if (check && ((resets >> i) & 1ull)) {
 #pragma unroll
       for (int c = 0; c < CH; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
@@ -158,15 +184,13 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
     for (int c = 0; c < CH; ++c) {
       const float acc = fmaf(w[c].x, x3[c], fmaf(w[c].y, x2[c], fmaf(w[c].z, x1[c], w[c].w * x0[c])));
       y[c] = silu_fast(acc);
-      x3[c] = x2[c]; x2[c] = x1[c]; x1[c] = x0[c];
+      xw[u & 3][c] = x0[c];
     }
     if constexpr (NORM) {
       float ss = 0.f;
 #pragma unroll
       for (int c = 0; c < CH; ++c) ss = fmaf(y[c], y[c], ss);
-#pragma unroll
-      for (int off = 1; off < PPH; off <<= 1) ss += __shfl_xor(ss, off);
-      const float inv = 1.0f / sqrtf(ss + p.eps);
+      const float inv = __builtin_amdgcn_rsqf(head_sum<PPH>(ss) + p.eps);  // hardware 1/sqrt
 #pragma unroll
       for (int c = 0; c < CH; ++c) y[c] *= inv;
     }
@@ -188,7 +212,7 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
         // refill the slot only after it has been unpacked, so the load can
         // land in the slot's own registers (no copies, no early waits)
         ring[u] = ld(ordered_after(x0, min(t + kFeDepth, tl)));
-        step(x0, check, resets, b0 + u, y);
+        step(x0, check, resets, b0 + u, u, y);
         nt_store16(dst + t * row_bytes, E::pack(y));
       }
     }
@@ -210,7 +234,7 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
         float x0[CH], y[CH];
         E::unpack(ring[u], x0);
         ring[u] = ld(min(t + kFeDepth, tl));
-        step(x0, true, resets, b0 + u, y);
+        step(x0, true, resets, b0 + u, u, y);
         if (t < te) nt_store16(dst + t * row_bytes, E::pack(y));
       }
     }
