@@ -336,9 +336,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       // throughout), the fragments of step f + 1 loaded during step f
       auto offdiag = [&](const int *ti, const int *tj, auto ntiles) {
         constexpr int NTL = decltype(ntiles)::value;
-        f32x4_t sa[NTL], pa[NTL];
-#pragma unroll
-        for (int t = 0; t < NTL; ++t) sa[t] = pa[t] = z;
+        f32x4_t sa[NTL], pa[NTL];  // set by their first MFMA
         constexpr int NF = NKB * NTL;  // steps (slab, tile)
         Frag<F32> fk[2], fq[2], fb[2];
         auto load_step = [&](int f) {
@@ -352,8 +350,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         for (int f = 0; f < NF; ++f) {
           if (f + 1 < NF) load_step(f + 1);
           __builtin_amdgcn_sched_barrier(0);
-          sa[f % NTL] = mma<F32>(sa[f % NTL], fk[f & 1], fb[f & 1]);
-          pa[f % NTL] = mma<F32>(pa[f % NTL], fq[f & 1], fb[f & 1]);
+          sa[f % NTL] = mma<F32>(f < NTL ? z : sa[f % NTL], fk[f & 1], fb[f & 1]);
+          pa[f % NTL] = mma<F32>(f < NTL ? z : pa[f % NTL], fq[f & 1], fb[f & 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -374,7 +372,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       };
       // P of diagonal tiles (b, b) into L o P, masked to s <= r
       auto diag_p = [&](int b0) {
-        f32x4_t pd[2] = {z, z};
+        f32x4_t pd[2];  // set by their first MFMA
         constexpr int NF = NKB * 2;  // steps (slab, tile)
         Frag<F32> fq[2], fb[2];
         auto load_step = [&](int f) {
@@ -386,7 +384,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         for (int f = 0; f < NF; ++f) {
           if (f + 1 < NF) load_step(f + 1);
           __builtin_amdgcn_sched_barrier(0);
-          pd[f & 1] = mma<F32>(pd[f & 1], fq[f & 1], fb[f & 1]);
+          pd[f & 1] = mma<F32>(f < 2 ? z : pd[f & 1], fq[f & 1], fb[f & 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -405,13 +403,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       if (wave < 4) {
         // diagonal block b = wave: S_bb = K_b K_b^T, both operands the same fragment
         const int b = wave;
-        f32x4_t sd = z;
+        f32x4_t sd;
         Frag<F32> fk[NKB];
 #pragma unroll
         for (int kk = 0; kk < NKB; ++kk) fk[kk] = load_frag<F32>(Kh, LDK, 16 * b, 32 * kk);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kk = 0; kk < NKB; ++kk) sd = mma<F32>(sd, fk[kk], fk[kk]);
+        for (int kk = 0; kk < NKB; ++kk) sd = mma<F32>(kk == 0 ? z : sd, fk[kk], fk[kk]);
         // A_bb stays in registers (no other wave reads the diagonal block):
         // lane (g, n) holds rows 4g .. 4g+3 of column n
         const float Gc = Gs[16 * b + col];
@@ -438,26 +436,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     };
 
 
-    f32x4_t qm[4][NA], um[4][NA];
-#pragma unroll
-    for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-      for (int ia = 0; ia < NA; ++ia) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) qm[tb][ia][e] = um[tb][ia][e] = 0.f;
-      }
-    }
+    f32x4_t qm[4][NA], um[4][NA];  // set by their first MFMA (K-step 0 starts from zero)
     if constexpr (NW == 8) {
       chunk_local_w8();
     } else {
       // ---- 2: S = K K^T, P = Q K^T (a6), the wave's tiles: row block RB,
       // column blocks cb0 .. cb0 + NCB - 1 ----
-      f32x4_t sacc[NCB], pacc[NCB];
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sacc[cb][e] = pacc[cb][e] = 0.f;
-      }
+      f32x4_t sacc[NCB], pacc[NCB];  // set by their first MFMA
+      const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
       // S and P (S unused without erase: no branch, straight-line code), the
       // fragments of step f + 1 loaded during step f's MFMAs
       {
@@ -478,8 +464,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
             fb[(f + 1) & 1] = load_frag<F32>(Kh, LDK, 16 * (cb0 + (f + 1) % NCB), 32 * kn);
           }
           __builtin_amdgcn_sched_barrier(0);
-          sacc[cb] = mma<F32>(sacc[cb], fk[kk & 1], fb[f & 1]);
-          pacc[cb] = mma<F32>(pacc[cb], fq[kk & 1], fb[f & 1]);
+          sacc[cb] = mma<F32>(kk == 0 ? z : sacc[cb], fk[kk & 1], fb[f & 1]);
+          pacc[cb] = mma<F32>(kk == 0 ? z : pacc[cb], fq[kk & 1], fb[f & 1]);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -536,8 +522,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
-          if (isk) um[tb][ia] = mma<F32>(um[tb][ia], fa[f % RING], fm[ia]);
-          else qm[tb][ia] = mma<F32>(qm[tb][ia], fa[f % RING], fm[ia]);
+          const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+          if (isk) um[tb][ia] = mma<F32>(kk == 0 ? z : um[tb][ia], fa[f % RING], fm[ia]);
+          else qm[tb][ia] = mma<F32>(kk == 0 ? z : qm[tb][ia], fa[f % RING], fm[ia]);
         }
         if constexpr (kInterleaveT) {
 #pragma unroll
