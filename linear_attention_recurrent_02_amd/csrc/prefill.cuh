@@ -87,8 +87,10 @@ struct PrefillLayout {
   static constexpr size_t KH = 0;
   static constexpr size_t QH = KH + (size_t)C * LDK * sizeof(OT);
   static constexpr size_t VH = QH + (size_t)C * LDK * sizeof(OT);
-  static constexpr size_t GATES = VH + (size_t)C * LDV * sizeof(OT);  // G, gamma, beta, eGn
-  static constexpr size_t SET = GATES + 4 * C * 4;                    // bytes per set
+  // G, gamma, beta, exp(G_last - G), scale * gamma, e * gamma (e = 1 for the
+  // delta rules, else 0)
+  static constexpr size_t GATES = VH + (size_t)C * LDV * sizeof(OT);
+  static constexpr size_t SET = GATES + 6 * C * 4;  // bytes per set
   // shared by both sets
   static constexpr size_t SQ = 2 * SET;
   static constexpr size_t AF = SQ + (size_t)C * LDC * sizeof(OT);

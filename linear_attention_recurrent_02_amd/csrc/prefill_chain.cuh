@@ -63,13 +63,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   // this chunk's input set (K, Q, V rows and gates); the sets alternate
   OT *Kh, *Qh, *Vh;
   float *Gs, *gam, *bet, *eGn;  // cumulative log2 decay, gamma, beta, exp(G_last - G)
+  float *gsc, *gme;             // scale * gamma (the read-out), e * gamma (R's K M term)
   auto use_set = [&](int b) {
     char *base = smem + b * L::SET;
     Kh = reinterpret_cast<OT *>(base + L::KH);
     Qh = reinterpret_cast<OT *>(base + L::QH);
     Vh = reinterpret_cast<OT *>(base + L::VH);
     Gs = reinterpret_cast<float *>(base + L::GATES);
-    gam = Gs + C; bet = Gs + 2 * C; eGn = Gs + 3 * C;
+    gam = Gs + C; bet = Gs + 2 * C; eGn = Gs + 3 * C; gsc = Gs + 4 * C; gme = Gs + 5 * C;
   };
   OT *Sq = reinterpret_cast<OT *>(smem + L::SQ);
   float *Af = reinterpret_cast<float *>(smem + L::AF);
@@ -205,11 +206,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       sG[C + lane] = fast_exp2(G);                                     // gamma
       sG[2 * C + lane] = p_valid ? (erase ? pb : 1.f) : 0.f;           // beta (plain rules: R = beta V)
       sG[3 * C + lane] = fast_exp2(G_last - G);                        // exp(G_last - G)
+      sG[4 * C + lane] = p.scale * fast_exp2(G);                       // scale * gamma
+      sG[5 * C + lane] = ef * fast_exp2(G);                            // e * gamma
     }
   };
 
   // O rows r0 + rq .. r0 + rq + 3 of column c0 + col, held by this lane in
-  // the accumulator layout, scaled and stored (only rows inside the chunk).
+  // the accumulator layout (already scaled: the read-out scale rides on
+  // scale * gamma and on L o P), stored (only rows inside the chunk).
   // BF16: each lane swaps halves with its neighbour column (lane ^ 1), so a
   // lane stores two rows of a column pair as 4-byte words.
   // Addresses: a uniform base per chunk, a per-lane offset fixed for the
@@ -224,8 +228,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   auto store_o_tile = [&](int r0, int c0, const f32x4_t &acc, bool whole) {
     AT *const dst = o_base + r0 * o_row + c0 + o_lane;
     if constexpr (AB) {
-      const uint32_t a = pack_bf16x2(p.scale * acc[0], p.scale * acc[1]);  // rows 0, 1
-      const uint32_t b = pack_bf16x2(p.scale * acc[2], p.scale * acc[3]);  // rows 2, 3
+      const uint32_t a = pack_bf16x2(acc[0], acc[1]);  // rows 0, 1
+      const uint32_t b = pack_bf16x2(acc[2], acc[3]);  // rows 2, 3
       const uint32_t other = (uint32_t)__builtin_amdgcn_mov_dpp((int)(o_odd ? a : b), 0xB1, 0xf, 0xf, false);
       const uint32_t own = o_odd ? b : a;
       const uint32_t left = o_odd ? other : own, right = o_odd ? own : other;  // columns c, c + 1
@@ -237,7 +241,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        if (whole || r0 + rq + e < o_n) dst[e * o_row] = p.scale * acc[e];
+        if (whole || r0 + rq + e < o_n) dst[e * o_row] = acc[e];
       }
     }
   };
@@ -366,7 +370,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
             const float a = (ef * br[e]) * dec * sa[t][e];
             if constexpr (kBfAT) put(Ab + r * L::LDAB + s, -a);
             else Af[r * LDF + s] = a;
-            put(Sq + r * LDC + s, dec * pa[t][e]);
+            put(Sq + r * LDC + s, p.scale * (dec * pa[t][e]));
           }
         }
       };
@@ -395,7 +399,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 16 * b + rq + e;
-            const float x = fast_exp2(Gr[e] - Gc) * pd[t][e];
+            const float x = p.scale * (fast_exp2(Gr[e] - Gc) * pd[t][e]);
             put(Sq + r * LDC + 16 * b + col, col <= rq + e ? x : 0.f);
           }
         }
@@ -489,7 +493,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
             const float a = s < r ? (ef * br[e]) * dec * sacc[cb][e] : 0.f;
             if constexpr (kBfAT) put(Ab + r * L::LDAB + s, -a);
             else Af[r * LDF + s] = a;
-            put(Sq + r * LDC + s, dec * pacc[cb][e]);
+            put(Sq + r * LDC + s, p.scale * (dec * pacc[cb][e]));
             if (cb0 + cb == RB) ab[e] = a;  // the wave's diagonal block, for its T
           }
         }
@@ -562,12 +566,11 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) load_col4(Vh, LDV, 16 * tb, 16 * (wave * NA + ia), vv[ia]);
         const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * tb + rq);
-        const f32x4_t gr = *reinterpret_cast<const f32x4_t *>(gam + 16 * tb + rq);
+        const f32x4_t gr = *reinterpret_cast<const f32x4_t *>(gme + 16 * tb + rq);  // e * gamma
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
 #pragma unroll
-          for (int ia = 0; ia < NA; ++ia)
-            um[tb][ia][e] = br[e] * (vv[ia][e] - (ef * gr[e]) * um[tb][ia][e]);
+          for (int ia = 0; ia < NA; ++ia) um[tb][ia][e] = br[e] * (vv[ia][e] - gr[e] * um[tb][ia][e]);
         }
       }
       // 6: U = (I + A)^-1 R (delta rules), block forward substitution in
@@ -605,8 +608,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
           }
         }
       }
-      // 7: O = gamma Q M + (L o P) U (a7), scaled, stored to HBM straight from
-      // the accumulator layout
+      // 7: O = scale (gamma Q M + (L o P) U) (a7), as (scale gamma) Q M +
+      // (scale L o P) U, stored to HBM straight from the accumulator layout
       Frag<F32> fu[2][NA];
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
@@ -623,7 +626,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int tb = 0, n = 0; tb < 4; ++tb) {
-        const f32x4_t gr = *reinterpret_cast<const f32x4_t *>(gam + 16 * tb + rq);
+        const f32x4_t gr = *reinterpret_cast<const f32x4_t *>(gsc + 16 * tb + rq);  // scale * gamma
 #pragma unroll
         for (int ia = 0; ia < NA; ++ia) {
 #pragma unroll
