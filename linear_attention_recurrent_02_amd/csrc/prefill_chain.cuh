@@ -303,12 +303,6 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     o_base = o_head + t0 * o_row;
     o_n = (int)std::min<int64_t>(C, t_end - t0);
     use_set(cur);
-    // The next chunk's inputs, in flight while this chunk computes.  Fetched
-    // and staged on the last chunk too (clamped to the last token, into the
-    // set nobody reads next): with no branch around them, the register reuse
-    // at the loop head does not make the compiler wait for every outstanding
-    // memory operation, the O stores of the chunk before included.
-    fetch(t1);
 
     // T_RB,RB = (I + A_RB,RB)^-1 from diagonal block RB of A, which this wave
     // holds in registers (ab; lane (g, n): rows 4g .. 4g+3 of column n): lane
@@ -499,6 +493,13 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         }
       }
     }
+    // The next chunk's inputs, in flight while this chunk computes (issued
+    // after the chunk-local products, when the previous chunk's O stores have
+    // drained).  Fetched and staged on the last chunk too (clamped to the last
+    // token, into the set nobody reads next): with no branch around them, the
+    // register reuse at the loop head does not make the compiler wait for
+    // every outstanding memory operation.
+    fetch(t1);
     // ---- 5: Q M and K M (a7) for the wave's d_v columns, the A fragments in a
     // ring: the load of fragment f + RING - 1 is issued before the MFMAs of
     // fragment f (scheduling barriers keep the compiler from moving it back
