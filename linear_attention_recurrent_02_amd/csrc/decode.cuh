@@ -115,15 +115,16 @@ struct DecodeTileRegs {
 // Phase 1 of a tile: resolve the slots (a1) and issue every load -- this
 // token's q, k, v first, then the state tile -- without waiting for any of
 // them, so the caller can overlap them with the previous tile's phase 2.  All
-// NT threads of the workgroup call it with the same (r, h).
+// NT threads of a group call it with the same (r, h), each passing its index
+// in the group as `tid`: the workgroup, or one of its aligned NT-thread parts
+// (each with its own `red`).
 template <bool SB, bool AB, int DK, int DV, int NT>
 __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t r, int h,
-                                                 DecodeTileRegs<SB, AB, DK, DV, NT> &t) {
+                                                 DecodeTileRegs<SB, AB, DK, DV, NT> &t, int tid) {
   using S = DecodeShape<SB, DK, DV, NT>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT;
   constexpr bool ALL_LIVE = S::ALL_LIVE;
   using SE = Elem<SB>;
-  const int tid = threadIdx.x;
   const int cv = tid % LPR;  // column vector: columns [cv*VEC, cv*VEC + VEC)
   const int row0 = (tid / LPR) * RPT;  // rows [row0, row0 + RPT)
 
@@ -191,13 +192,12 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
 template <bool SB, bool AB, int DK, int DV, int NT>
 __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
                                                    DecodeTileRegs<SB, AB, DK, DV, NT> &t,
-                                                   float *red) {
+                                                   float *red, int tid) {
   using S = DecodeShape<SB, DK, DV, NT>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT, NW = S::NW;
   constexpr bool ALL_LIVE = S::ALL_LIVE;
   using SE = Elem<SB>;
   if (!t.valid) return;
-  const int tid = threadIdx.x;
   const int cv = tid % LPR;
   const int row0 = (tid / LPR) * RPT;
   const bool rows_live = ALL_LIVE || row0 < DK;
@@ -316,8 +316,8 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
 template <bool SB, bool AB, int DK, int DV, int NT>
 __device__ __forceinline__ void decode_tile(const DecodeParams &p, int64_t r, int h, float *red) {
   DecodeTileRegs<SB, AB, DK, DV, NT> t;
-  decode_tile_load<SB, AB, DK, DV, NT>(p, r, h, t);
-  decode_tile_finish<SB, AB, DK, DV, NT>(p, t, red);
+  decode_tile_load<SB, AB, DK, DV, NT>(p, r, h, t, (int)threadIdx.x);
+  decode_tile_finish<SB, AB, DK, DV, NT>(p, t, red, (int)threadIdx.x);
 }
 
 // Threads per workgroup for a (state dtype, d_k, d_v) instance: enough lanes

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(GDN_DECODE_MAX_THREADS) void decode_kernel(DecodePa
   auto load = [&](int64_t tile, Regs &dst) {
     const int pos = (int)(tile / p.H_v);
     decode_tile_load<SB, AB, DK, DV, NT>(p, ordered ? order_lds[pos] : pos,
-                                         (int)(tile % p.H_v), dst);
+                                         (int)(tile % p.H_v), dst, (int)threadIdx.x);
   };
 #if GDN_DECODE_PIPELINE
   Regs cur, nxt;
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(GDN_DECODE_MAX_THREADS) void decode_kernel(DecodePa
     const int64_t tn = t + gridDim.x;
     const bool more = tn < n_tiles;
     if (more) load(tn, nxt);
-    decode_tile_finish<SB, AB, DK, DV, NT>(p, cur, red);
+    decode_tile_finish<SB, AB, DK, DV, NT>(p, cur, red, (int)threadIdx.x);
     if (!more) break;
     cur = nxt;
     t = tn;
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(GDN_DECODE_MAX_THREADS) void decode_kernel(DecodePa
   for (; t < n_tiles; t += gridDim.x) {
     Regs cur;
     load(t, cur);
-    decode_tile_finish<SB, AB, DK, DV, NT>(p, cur, red);
+    decode_tile_finish<SB, AB, DK, DV, NT>(p, cur, red, (int)threadIdx.x);
   }
 #endif
 }

@@ -7,9 +7,15 @@
 // persistent decode workers that stream the decode tiles in write-slot
 // order on the CUs the chains leave free.  Each block runs exactly the device
 // code of gdn_prefill or gdn_decode, so the results equal the two calls made
-// separately.  A block holds the prefill chain's LDS, so one block fits per
-// CU; a decode worker therefore keeps two tiles in flight (the next tile's
-// loads are issued before the current tile is reduced and stored).
+// separately.  Blocks have the chain's width (64 threads per chain wave); a
+// decode block splits into 256-thread workers, the width of gdn_decode's
+// tiles, each with its own reduction LDS.  A block holds the prefill chain's
+// LDS, so one block fits per CU; each decode worker therefore keeps two tiles
+// in flight (the next tile's loads are issued before the current tile is
+// reduced and stored).  The workers of a block share its barriers: a tile's
+// barriers are uniform within its worker, the workers exchange no data, and
+// a barrier waits only for waves that have not ended, so they may meet at any
+// of one another's barriers.
 //
 // Both halves must describe the same layer shape (heads, d_k, d_v, state and
 // activation dtypes).  With raw prefill inputs the front-end kernel runs
@@ -26,38 +32,48 @@ DecodeParams make_decode_params(const gdn_decode_args &a);
 
 template <bool SB, bool AB, int DK, int DV, bool F32>
 struct MixedLayout {
-  static constexpr int NT = 256;
+  // the chain's waves, except with FP32 state: a worker's two FP32 tiles in
+  // flight need more registers than a wave of a 512-thread block gets
+  static constexpr int NW = SB ? kPrefillWaves<DK, DV, F32> : 4;
+  static constexpr int NT = 64 * NW;                          // threads per block
+  static constexpr int DT = 256;                              // threads per decode worker
+  static constexpr int NH = NT / DT;                          // decode workers per block
+  static_assert(NT % DT == 0, "whole decode workers per block");
   static constexpr size_t PREFILL = PrefillLayout<DK, DV, F32>::BYTES;
-  static constexpr size_t RED = sizeof(float) * DecodeShape<SB, DK, DV, NT>::LDS_FLOATS;
+  // one worker's reduction area, rounded to 16 bytes so every worker's is aligned alike
+  static constexpr size_t RED = (sizeof(float) * DecodeShape<SB, DK, DV, DT>::LDS_FLOATS + 15) / 16 * 16;
   static constexpr size_t ORDER = slot_order_lds_bytes(kOrderMaxB, kOrderMaxSlots, NT);
-  static constexpr size_t DECODE = RED + ORDER;
+  static constexpr size_t DECODE = NH * RED + ORDER;
   static constexpr size_t BYTES = PREFILL > DECODE ? PREFILL : DECODE;
 };
 
 template <bool SB, bool AB, int DK, int DV, bool F32>
-__global__ __launch_bounds__(256) void mixed_kernel(DecodeParams dp, PrefillParams pp,
-                                                    int n_chains, int prefill_blocks,
-                                                    int ordered) {
+__global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32>::NT)) void mixed_kernel(
+    DecodeParams dp, PrefillParams pp, int n_chains, int prefill_blocks, int ordered) {
   using L = MixedLayout<SB, AB, DK, DV, F32>;
-  constexpr int NT = L::NT;
+  constexpr int NT = L::NT, DT = L::DT;
   __shared__ __align__(16) char smem[L::BYTES];
   if ((int)blockIdx.x < prefill_blocks) {
     const int chain = chain_of_block(blockIdx.x);
-    if (chain < n_chains) prefill_chain<SB, AB, DK, DV, F32, 4>(pp, chain, smem);
+    if (chain < n_chains)
+      prefill_chain<SB, AB, DK, DV, F32, L::NW>(pp, chain, smem);
     return;
   }
-  // decode worker
-  float *red = reinterpret_cast<float *>(smem);
-  int *order = reinterpret_cast<int *>(smem + L::RED);
+  // decode workers: DT-thread parts of the block
+  const int part = (int)threadIdx.x / DT;  // uniform in a wave
+  const int tid = (int)threadIdx.x % DT;   // the thread within its worker
+  float *red = reinterpret_cast<float *>(smem + part * L::RED);
+  int *order = reinterpret_cast<int *>(smem + L::NH * L::RED);
   if (ordered) build_slot_order<NT>(dp.write_slot, dp.B, dp.n_slots, order);
   const int64_t n_tiles = (int64_t)dp.B * dp.H_v;
-  const int64_t workers = (int64_t)gridDim.x - prefill_blocks;
-  int64_t t = (int64_t)blockIdx.x - prefill_blocks;
+  const int64_t workers = ((int64_t)gridDim.x - prefill_blocks) * L::NH;
+  int64_t t = ((int64_t)blockIdx.x - prefill_blocks) * L::NH + part;
   if (t >= n_tiles) return;
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT>;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, DT>;
   auto load = [&](int64_t tile, Regs &dst) {
     const int pos = (int)(tile / dp.H_v);
-    decode_tile_load<SB, AB, DK, DV, NT>(dp, ordered ? order[pos] : pos, (int)(tile % dp.H_v), dst);
+    decode_tile_load<SB, AB, DK, DV, DT>(dp, ordered ? order[pos] : pos, (int)(tile % dp.H_v), dst,
+                                         tid);
   };
   Regs cur, nxt;
   load(t, cur);
@@ -65,7 +81,7 @@ __global__ __launch_bounds__(256) void mixed_kernel(DecodeParams dp, PrefillPara
     const int64_t tn = t + workers;
     const bool more = tn < n_tiles;
     if (more) load(tn, nxt);
-    decode_tile_finish<SB, AB, DK, DV, NT>(dp, cur, red);
+    decode_tile_finish<SB, AB, DK, DV, DT>(dp, cur, red, tid);
     if (!more) break;
     cur = nxt;
     t = tn;
@@ -88,7 +104,7 @@ static gdn_status launch_mixed_t(const DecodeParams &dp, const PrefillParams &pp
       return GDN_ERR_LAUNCH;
     // decode workers on the CUs the chains leave free (at least a quarter of the chip)
     const int64_t free_cus = std::max<int64_t>(cus - n_chains, std::max(1, cus / 4));
-    const int64_t workers = tiles > 0 ? std::min<int64_t>(tiles, free_cus) : 0;
+    const int64_t workers = tiles > 0 ? std::min<int64_t>((tiles + L::NH - 1) / L::NH, free_cus) : 0;
     const int ordered =
         dp.write_slot != nullptr && dp.B <= kOrderMaxB && dp.n_slots <= kOrderMaxSlots ? 1 : 0;
     const int64_t grid = (n_chains > 0 ? prefill_blocks : 0) + workers;

@@ -8,13 +8,6 @@
 
 namespace gdn {
 
-// Waves per chain: 8 (two per SIMD, each covering the other's latencies)
-// where the chain's registers fit in the 256 a wave then gets without
-// spilling -- a spill reload inside the chunk loop would wait on the
-// in-flight prefetch of the next chunk -- else 4.
-template <int DK, int DV, bool F32>
-constexpr int kPrefillWaves = (!F32 && (DK <= 64 || DV == 128)) ? 8 : 4;
-
 template <bool SB, bool AB, int DK, int DV, bool F32>
 __global__ __launch_bounds__((64 * kPrefillWaves<DK, DV, F32>)) void prefill_kernel(PrefillParams p,
                                                                                    int n_chains) {

@@ -30,6 +30,13 @@ __device__ __forceinline__ int chain_of_block(int b) {
   return (b & ~15) + 2 * (w & 7) + (w >> 3);
 }
 
+// Waves per chain: 8 (two per SIMD, each covering the other's latencies)
+// where the chain's registers fit in the 256 a wave then gets without
+// spilling -- a spill reload inside the chunk loop would wait on the
+// in-flight prefetch of the next chunk -- else 4.
+template <int DK, int DV, bool F32>
+constexpr int kPrefillWaves = (!F32 && (DK <= 64 || DV == 128)) ? 8 : 4;
+
 // One (sequence, state head) chain; all 64 NW threads of the workgroup call
 // it.  `smem` holds PrefillLayout<DK, DV, F32>::BYTES bytes, 16-byte aligned.
 template <bool SB, bool AB, int DK, int DV, bool F32, int NW>

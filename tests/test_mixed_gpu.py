@@ -112,6 +112,22 @@ def test_mixed_one_half_empty():
     assert torch.equal(do, so) and torch.equal(pool, spool)
 
 
+def test_mixed_uneven_workers():
+    """Decode workers of one block with different tile counts: 200 short
+    prefills (one state head each) leave the decode half its minimum of a
+    quarter of the CUs, and 131 decode tiles over those workers give the first
+    few two tiles and the rest one, so one worker of a block ends while its
+    partner still reduces.  Mixed = separate bit for bit."""
+    say("mixed uneven decode workers")
+    lengths = np.random.default_rng(11).integers(1, 81, size=200)
+    c = build(403, 131, lengths, 1, 1, 128, 512, frontend=False, std=0.05)
+    for rule in ("gated_delta", "linear"):
+        do, po, pool = run_mixed(c, rule)
+        so, spo, spool = run_separate(c, rule)
+        assert torch.equal(do, so) and torch.equal(po, spo), rule
+        assert torch.equal(pool.view(torch.int16), spool.view(torch.int16)), rule
+
+
 def test_mixed_full_size_sampled():
     """448 decode requests (each update rule on a quarter of them would need four
     calls; here all four rules run back to back on the same pool state) plus 4
