@@ -37,6 +37,29 @@ __device__ __forceinline__ int chain_of_block(int b) {
 template <int DK, int DV, bool F32>
 constexpr int kPrefillWaves = (!F32 && (DK <= 64 || DV == 128)) ? 8 : 4;
 
+// Chunk-local tiles of the 8-wave chain's product waves 4-7.  A fragment id
+// is 2 b for block b (16 rows) of K and 2 b + 1 for block b of Q, one 32-wide
+// slab at a time; a wave loads each fragment it needs once per slab, into the
+// slot of its position in `frag`.
+struct LocalTiles {
+  int nf;        // fragments per slab
+  int frag[6];   // fragment id of each slot
+  int nod;       // tiles below the diagonal: S and P of (i, j)
+  int od[2][5];  // i, j, and the slots of K_i, Q_i, K_j
+  int ndp;       // diagonal tiles: P of (b, b)
+  int dp[2][3];  // b, and the slots of Q_b, K_b
+};
+constexpr LocalTiles kLocalTiles[4] = {
+    // wave 4: (1,0) (2,0) from K0 K1 Q1 K2 Q2
+    {5, {0, 2, 3, 4, 5, 0}, 2, {{1, 0, 1, 2, 0}, {2, 0, 3, 4, 0}}, 0, {{0, 0, 0}, {0, 0, 0}}},
+    // wave 5: (2,1) (3,0) from K1 K2 Q2 K0 K3 Q3
+    {6, {2, 4, 5, 0, 6, 7}, 2, {{2, 1, 1, 2, 0}, {3, 0, 4, 5, 3}}, 0, {{0, 0, 0}, {0, 0, 0}}},
+    // wave 6: (3,1), P of (1,1) and (0,0) from K3 Q3 K1 Q1 K0 Q0
+    {6, {6, 7, 2, 3, 0, 1}, 1, {{3, 1, 0, 1, 2}, {0, 0, 0, 0, 0}}, 2, {{1, 3, 2}, {0, 5, 4}}},
+    // wave 7: (3,2), P of (2,2) and (3,3) from K3 Q3 K2 Q2
+    {4, {6, 7, 4, 5, 0, 0}, 1, {{3, 2, 0, 1, 2}, {0, 0, 0, 0, 0}}, 2, {{2, 3, 2}, {3, 1, 0}}},
+};
+
 // One (sequence, state head) chain; all 64 NW threads of the workgroup call
 // it.  `smem` holds PrefillLayout<DK, DV, F32>::BYTES bytes, 16-byte aligned.
 template <bool SB, bool AB, int DK, int DV, bool F32, int NW>
@@ -333,40 +356,49 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     // triangle; the upper tiles of S and P are never formed).  Waves 0-3: S of
     // diagonal block b = wave, its A block and T_bb, a vector-ALU chain; waves
     // 4-7: S and P of the six tiles below the diagonal (two, two, one, one),
-    // waves 6 and 7 also P of two diagonal tiles each.  So every SIMD pairs a
-    // T wave with a product wave.
+    // waves 6 and 7 also P of two diagonal tiles each (kLocalTiles).  So every
+    // SIMD pairs a T wave with a product wave.
     auto chunk_local_w8 = [&]() {
       const f32x4_t z = {0.f, 0.f, 0.f, 0.f};
-      // S and P of off-diagonal tiles (i, j), i > j, into A and L o P (s < r
-      // throughout), the fragments of step f + 1 loaded during step f
-      auto offdiag = [&](const int *ti, const int *tj, auto ntiles) {
-        constexpr int NTL = decltype(ntiles)::value;
-        f32x4_t sa[NTL], pa[NTL];  // set by their first MFMA
-        constexpr int NF = NKB * NTL;  // steps (slab, tile)
-        Frag<F32> fk[2], fq[2], fb[2];
-        auto load_step = [&](int f) {
-          const int kk = f / NTL, t = f % NTL;
-          fk[f & 1] = load_frag<F32>(Kh, LDK, 16 * ti[t], 32 * kk);
-          fq[f & 1] = load_frag<F32>(Qh, LDK, 16 * ti[t], 32 * kk);
-          fb[f & 1] = load_frag<F32>(Kh, LDK, 16 * tj[t], 32 * kk);
-        };
-        load_step(0);
+      // Product wave W: its tiles' S and P over the 32-wide slabs, every
+      // fragment of slab kk + 1 loaded during slab kk's MFMAs; then A and L o P
+      // of the tiles below the diagonal (s < r throughout) and L o P of the
+      // diagonal tiles (masked to s <= r) into LDS.
+      auto products = [&](auto wi) {
+        constexpr LocalTiles c = kLocalTiles[decltype(wi)::value];
+        Frag<F32> fr[2][6];
+        f32x4_t sa[2], pa[2], pd[2];  // set by their first MFMA
+        auto load_slab = [&](int kk, Frag<F32>(&dst)[6]) {
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          if (f + 1 < NF) load_step(f + 1);
+          for (int f = 0; f < c.nf; ++f) {
+            const int id = c.frag[f];
+            dst[f] = load_frag<F32>((id & 1) ? Qh : Kh, LDK, 16 * (id >> 1), 32 * kk);
+          }
+        };
+        load_slab(0, fr[0]);
+#pragma unroll
+        for (int kk = 0; kk < NKB; ++kk) {
+          if (kk + 1 < NKB) load_slab(kk + 1, fr[(kk + 1) & 1]);
           __builtin_amdgcn_sched_barrier(0);
-          sa[f % NTL] = mma<F32>(f < NTL ? z : sa[f % NTL], fk[f & 1], fb[f & 1]);
-          pa[f % NTL] = mma<F32>(f < NTL ? z : pa[f % NTL], fq[f & 1], fb[f & 1]);
+#pragma unroll
+          for (int t = 0; t < c.nod; ++t) {
+            sa[t] = mma<F32>(kk == 0 ? z : sa[t], fr[kk & 1][c.od[t][2]], fr[kk & 1][c.od[t][4]]);
+            pa[t] = mma<F32>(kk == 0 ? z : pa[t], fr[kk & 1][c.od[t][3]], fr[kk & 1][c.od[t][4]]);
+          }
+#pragma unroll
+          for (int t = 0; t < c.ndp; ++t)
+            pd[t] = mma<F32>(kk == 0 ? z : pd[t], fr[kk & 1][c.dp[t][1]], fr[kk & 1][c.dp[t][2]]);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-          const float Gc = Gs[16 * tj[t] + col];
-          const f32x4_t Gr = *reinterpret_cast<const f32x4_t *>(Gs + 16 * ti[t] + rq);
-          const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * ti[t] + rq);
+        for (int t = 0; t < c.nod; ++t) {
+          const int ti = c.od[t][0], tj = c.od[t][1];
+          const float Gc = Gs[16 * tj + col];
+          const f32x4_t Gr = *reinterpret_cast<const f32x4_t *>(Gs + 16 * ti + rq);
+          const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * ti + rq);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const int r = 16 * ti[t] + rq + e, s = 16 * tj[t] + col;
+            const int r = 16 * ti + rq + e, s = 16 * tj + col;
             const float dec = fast_exp2(Gr[e] - Gc);
             const float a = (ef * br[e]) * dec * sa[t][e];
             if constexpr (kBfAT) put(Ab + r * L::LDAB + s, -a);
@@ -374,27 +406,9 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
             put(Sq + r * LDC + s, p.scale * (dec * pa[t][e]));
           }
         }
-      };
-      // P of diagonal tiles (b, b) into L o P, masked to s <= r
-      auto diag_p = [&](int b0) {
-        f32x4_t pd[2];  // set by their first MFMA
-        constexpr int NF = NKB * 2;  // steps (slab, tile)
-        Frag<F32> fq[2], fb[2];
-        auto load_step = [&](int f) {
-          fq[f & 1] = load_frag<F32>(Qh, LDK, 16 * (b0 + (f & 1)), 32 * (f >> 1));
-          fb[f & 1] = load_frag<F32>(Kh, LDK, 16 * (b0 + (f & 1)), 32 * (f >> 1));
-        };
-        load_step(0);
 #pragma unroll
-        for (int f = 0; f < NF; ++f) {
-          if (f + 1 < NF) load_step(f + 1);
-          __builtin_amdgcn_sched_barrier(0);
-          pd[f & 1] = mma<F32>(f < 2 ? z : pd[f & 1], fq[f & 1], fb[f & 1]);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int b = b0 + t;
+        for (int t = 0; t < c.ndp; ++t) {
+          const int b = c.dp[t][0];
           const float Gc = Gs[16 * b + col];
           const f32x4_t Gr = *reinterpret_cast<const f32x4_t *>(Gs + 16 * b + rq);
 #pragma unroll
@@ -427,16 +441,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) t_row(r);
-      } else if (wave < 6) {
-        // wave 4: tiles (1,0) (2,0); wave 5: (2,1) (3,0)
-        const int w = wave - 4;
-        const int ti[2] = {w + 1, w + 2}, tj[2] = {w, 0};
-        offdiag(ti, tj, std::integral_constant<int, 2>());
+      } else if (wave == 4) {
+        products(std::integral_constant<int, 0>());
+      } else if (wave == 5) {
+        products(std::integral_constant<int, 1>());
+      } else if (wave == 6) {
+        products(std::integral_constant<int, 2>());
       } else {
-        // wave 6: tile (3,1) and P of diagonal tiles 0, 1; wave 7: (3,2) and 2, 3
-        const int ti[1] = {3}, tj[1] = {wave - 5};
-        offdiag(ti, tj, std::integral_constant<int, 1>());
-        diag_p(2 * (wave - 6));
+        products(std::integral_constant<int, 3>());
       }
     };
 
