@@ -24,7 +24,7 @@
 
 #include "decode.cuh"
 #include "order.cuh"
-#include "prefill_chain.cuh"
+#include "prefill_pipe.cuh"
 
 namespace gdn {
 
@@ -39,7 +39,9 @@ struct MixedLayout {
   static constexpr int DT = 256;                              // threads per decode worker
   static constexpr int NH = NT / DT;                          // decode workers per block
   static_assert(NT % DT == 0, "whole decode workers per block");
-  static constexpr size_t PREFILL = PrefillLayout<DK, DV, F32>::BYTES;
+  // with the chain's own wave count the block runs gdn_prefill's chain
+  static constexpr bool OWN_CHAIN = NW == kPrefillWaves<DK, DV, F32>;
+  static constexpr size_t PREFILL = OWN_CHAIN ? kChainLds<DK, DV, F32> : PrefillLayout<DK, DV, F32>::BYTES;
   // one worker's reduction area, rounded to 16 bytes so every worker's is aligned alike
   static constexpr size_t RED = (sizeof(float) * DecodeShape<SB, DK, DV, DT>::LDS_FLOATS + 15) / 16 * 16;
   static constexpr size_t ORDER = slot_order_lds_bytes(kOrderMaxB, kOrderMaxSlots, NT);
@@ -55,8 +57,10 @@ __global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32>::NT)) void mixed_
   __shared__ __align__(16) char smem[L::BYTES];
   if ((int)blockIdx.x < prefill_blocks) {
     const int chain = chain_of_block(blockIdx.x);
-    if (chain < n_chains)
-      prefill_chain<SB, AB, DK, DV, F32, L::NW>(pp, chain, smem);
+    if (chain < n_chains) {
+      if constexpr (L::OWN_CHAIN) run_chain<SB, AB, DK, DV, F32>(pp, chain, smem);
+      else prefill_chain<SB, AB, DK, DV, F32, L::NW>(pp, chain, smem);
+    }
     return;
   }
   // decode workers: DT-thread parts of the block

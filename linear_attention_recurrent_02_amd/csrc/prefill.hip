@@ -1,19 +1,20 @@
 // prefill.hip -- the chunked-prefill kernel (one workgroup per (sequence,
-// state head) chain, the chain itself in prefill_chain.cuh) and the
+// state head) chain, the chain itself in prefill_pipe.cuh or
+// prefill_chain.cuh) and the
 // gdn_prefill launcher: the front-end kernel into the workspace when the
 // inputs are raw, then the chains.
 #include <algorithm>
 
-#include "prefill_chain.cuh"
+#include "prefill_pipe.cuh"
 
 namespace gdn {
 
 template <bool SB, bool AB, int DK, int DV, bool F32>
 __global__ __launch_bounds__((64 * kPrefillWaves<DK, DV, F32>)) void prefill_kernel(PrefillParams p,
                                                                                    int n_chains) {
-  __shared__ __align__(16) char smem[PrefillLayout<DK, DV, F32>::BYTES];
+  __shared__ __align__(16) char smem[kChainLds<DK, DV, F32>];
   const int chain = chain_of_block(blockIdx.x);
-  if (chain < n_chains) prefill_chain<SB, AB, DK, DV, F32, kPrefillWaves<DK, DV, F32>>(p, chain, smem);
+  if (chain < n_chains) run_chain<SB, AB, DK, DV, F32>(p, chain, smem);
 }
 
 // ---- launcher --------------------------------------------------------------
@@ -32,8 +33,7 @@ PrefillParams make_prefill_params(const gdn_prefill_args &a, const void *q, cons
 template <bool SB, bool AB, int DK, int DV>
 static gdn_status launch_chains(const PrefillParams &p, hipStream_t s) {
   constexpr bool F32 = !AB;  // FP32 activations take the FP32 MFMA path
-  using L = PrefillLayout<DK, DV, F32>;
-  if constexpr (L::BYTES > 160 * 1024) {
+  if constexpr (kChainLds<DK, DV, F32> > 160 * 1024) {
     return GDN_ERR_UNSUPPORTED;  // FP32 operands at d = 128 do not fit in LDS
   } else {
     const int n_chains = p.n_seq * p.H_v;
