@@ -30,12 +30,22 @@ __device__ __forceinline__ int chain_of_block(int b) {
   return (b & ~15) + 2 * (w & 7) + (w >> 3);
 }
 
-// Waves per chain: 8 (two per SIMD, each covering the other's latencies)
-// where the chain's registers fit in the 256 a wave then gets without
-// spilling -- a spill reload inside the chunk loop would wait on the
+// Waves per plain chain: 8 (two per SIMD, each covering the other's
+// latencies) where the chain's registers fit in the 256 a wave then gets
+// without spilling -- a spill reload inside the chunk loop would wait on the
 // in-flight prefetch of the next chunk -- else 4.
 template <int DK, int DV, bool F32>
-constexpr int kPrefillWaves = (!F32 && (DK <= 64 || DV == 128)) ? 8 : 4;
+constexpr int kPlainWaves = (!F32 && (DK <= 64 || DV == 128)) ? 8 : 4;
+
+// Shapes that run the pipelined chain (prefill_pipe.cuh, always 8 waves):
+// BF16 activations, whole 32-wide K slabs, and d_v a multiple of 64 so each
+// of its four consumer waves owns whole 16-column blocks.
+template <int DK, int DV, bool F32>
+constexpr bool kPrefillPipe = !F32 && DK >= 32 && DV % 64 == 0;
+
+// Waves per chain, whichever design runs it.
+template <int DK, int DV, bool F32>
+constexpr int kPrefillWaves = kPrefillPipe<DK, DV, F32> ? 8 : kPlainWaves<DK, DV, F32>;
 
 // Chunk-local tiles of the 8-wave chain's product waves 4-7.  A fragment id
 // is 2 b for block b (16 rows) of K and 2 b + 1 for block b of Q, one 32-wide

@@ -66,11 +66,6 @@ constexpr PipeTiles kPipeTiles[4] = {
     {6, {6, 7, 4, 5, 2, 0}, 2, {{2, 1, 2, 3, 4}, {3, 0, 0, 1, 5}}},  // (3,3) (2,1) (3,0)
 };
 
-// Shapes that run the pipelined chain (BF16 activations; the others run
-// prefill_chain with the wave count kPrefillWaves).
-template <int DK, int DV, bool F32>
-constexpr bool kPrefillPipe = !F32 && DK == 128 && DV == 128;
-
 template <bool SB, bool AB, int DK, int DV>
 __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int chain, char *smem) {
   static_assert(AB, "BF16 activations");
@@ -598,7 +593,7 @@ __device__ __forceinline__ void run_chain(const PrefillParams &p, int chain, cha
     static_assert(kPrefillWaves<DK, DV, F32> == 8, "the pipelined chain runs 8 waves");
     prefill_chain_pipe<SB, AB, DK, DV>(p, chain, smem);
   } else {
-    prefill_chain<SB, AB, DK, DV, F32, kPrefillWaves<DK, DV, F32>>(p, chain, smem);
+    prefill_chain<SB, AB, DK, DV, F32, kPlainWaves<DK, DV, F32>>(p, chain, smem);
   }
 }
 
