@@ -348,6 +348,10 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
   // Both meet the same barriers: two in the prologue, two per chunk.
   const int n_chunks = (int)((t_end - t_begin + C - 1) / C);
   if (consumer) {
+    // the consumers are the chain's critical path (the producers finish their
+    // chunk with time to spare): when both waves of a SIMD can issue, they go
+    // first (measured: 0.6%)
+    __builtin_amdgcn_s_setprio(1);
     // ---- consumers: initial state (a8), read slot -> FP32 accumulators ------
     // macc[b][ia]: rows 16b.. of d_k, columns 16 (cw NA + ia).. of d_v
     f32x4_t macc[DKB][NA];
