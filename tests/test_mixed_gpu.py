@@ -20,9 +20,9 @@ def dev(t):
     return None if t is None else t.to(DEV)
 
 
-def build(wl, n_dec, lengths, Hqk, Hv, d, n_slots, frontend, std=0.02):
+def build(wl, n_dec, lengths, Hqk, Hv, d, n_slots, frontend, std=0.02, sdt=torch.bfloat16):
     q, k, v, g, beta = (dev(t) for t in syn.token_inputs(wl, 1, n_dec, Hqk, Hv, d, d))
-    pool = syn.state_pool(wl, 0, n_slots, Hv, d, d, torch.bfloat16, std=std)
+    pool = syn.state_pool(wl, 0, n_slots, Hv, d, d, sdt, std=std)
     drs, dws, prs, pws = syn.mixed_slots(wl, n_dec, len(lengths), n_slots)
     cu = syn.cu_from_lengths(lengths)
     N = int(cu[-1])
@@ -83,6 +83,19 @@ def test_mixed_equals_separate_and_oracle(rule):
     untouched = np.setdiff1d(np.arange(48), w)
     assert torch.equal(pool.cpu()[untouched].view(torch.int16),
                        c["pool"][untouched].view(torch.int16))
+
+
+def test_mixed_fp32_state_equals_separate():
+    """FP32 state pool with BF16 activations at d = 128: the mixed launch runs
+    4-wave blocks (plain chains) while gdn_prefill runs the pipelined chain;
+    the two chains compute the same products in the same order, so the
+    results still equal the separate calls bit for bit."""
+    say("mixed fp32 state")
+    c = build(404, 7, [70, 130, 1], 2, 4, 128, 48, frontend=False, std=0.05, sdt=torch.float32)
+    do, po, pool = run_mixed(c, "gated_delta")
+    so, spo, spool = run_separate(c, "gated_delta")
+    assert torch.equal(do, so) and torch.equal(po, spo)
+    assert torch.equal(pool, spool)
 
 
 def test_mixed_one_half_empty():

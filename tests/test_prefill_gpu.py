@@ -83,6 +83,18 @@ def test_prefill_bf16_ragged(rule):
     assert torch.equal(dpool.cpu()[others].view(torch.int16), case[6][others].view(torch.int16))
 
 
+def test_prefill_bf16_fp32_state():
+    """BF16 q/k/v/o with an FP32 state pool at d = 128 (the pipelined chain
+    reading and writing FP32 slots): ragged sequences, one fresh request."""
+    say("prefill bf16 act, fp32 state")
+    case = prefill_case(211, [5, 64, 130], 2, 4, 128, 128, 8, torch.float32, torch.bfloat16,
+                        std=0.05, fresh=(0,))
+    o, dpool, ro, rpool = run_prefill_both(case, "gated_delta")
+    ws = case[8].numpy()
+    assert seq_err(f64(o), ro, case[0]) < 2e-2
+    assert scaled_err(f64(dpool)[ws], rpool[ws], 2) < 2e-2
+
+
 @pytest.mark.parametrize("rule", RULES)
 def test_prefill_fp32_rules(rule):
     say("prefill fp32", rule)
