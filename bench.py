@@ -184,7 +184,7 @@ def run_prefill(args, torch, gdn, syn):
                          a_raw=x["a_raw"], b_raw=x["b_raw"])
 
     def timed(fn, reps):
-        for _ in range(2):
+        for _ in range(args.prefill_warmup):  # untimed: the first calls run slower
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -241,7 +241,7 @@ def run_mixed(args, torch, gdn, syn):
                 raise gdn.GdnError("separate", code)
 
     def timed(fn, reps):
-        for _ in range(2):
+        for _ in range(args.prefill_warmup):  # untimed: the first calls run slower
             fn()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -296,7 +296,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
-    ap.add_argument("--prefill-reps", type=int, default=10)
+    ap.add_argument("--prefill-reps", type=int, default=20)
+    ap.add_argument("--prefill-warmup", type=int, default=10,
+                    help="untimed calls before the prefill and mixed timings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a device copy of known size (for counter calibration)")
     args = ap.parse_args()
