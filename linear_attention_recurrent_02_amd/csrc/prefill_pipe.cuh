@@ -29,7 +29,8 @@
 namespace gdn {
 
 // LDS layout of the pipelined chain (byte offsets): two input sets as in
-// PrefillLayout, then two chunk-local sets of BF16 L o P (scaled), -A and T_ii.
+// PrefillLayout, two chunk-local sets of BF16 L o P (scaled), -A and T_ii,
+// and one FP32 diagonal block of A per producer wave.
 template <int DK, int DV>
 struct PipeLayout {
   using B = PrefillLayout<DK, DV, false>;
