@@ -129,9 +129,6 @@ def run_decode(args, torch, gdn, syn):
     return res, layers
 
 
-PREFILL_FLOPS_PER_TOKEN_HEAD = None  # computed from the chunk algebra below
-
-
 def prefill_useful_flops(lengths, H_v, d_k, d_v, C=64):
     """Useful flops of the chunked recurrence (per chunk of n tokens and head):
     K K^T and Q K^T (lower triangle incl. diagonal), the triangular solve,
