@@ -194,6 +194,26 @@ def run_prefill(args, torch, gdn, syn):
 
     ms = timed(step, args.prefill_reps)
     ms_fe = timed(fe_only, args.prefill_reps)
+
+    # the same call storing an intermediate checkpoint every 1024 tokens (block-aligned prefix
+    # cache slots): the pool's slots that are not write slots, 7 per sequence
+    ck_every = 1024
+    per_seq = int((max(lengths) // ck_every))
+    free = np.setdiff1d(np.arange(wl["n_slots"]), ws.cpu().numpy())[:len(lengths) * per_seq]
+    ck = torch.from_numpy(free.astype(np.int32).reshape(len(lengths), per_seq)).cuda()
+    a_ck, o_ck, keep_ck = gdn.make_prefill_args(cu, x["q_raw"], x["k_raw"], x["v_raw"], pool, rs, ws,
+                                                H_qk=Hqk, H_v=Hv, a_raw=x["a_raw"], b_raw=x["b_raw"],
+                                                conv_wq=x["conv_wq"], conv_wk=x["conv_wk"],
+                                                conv_wv=x["conv_wv"], ckpt_interval=ck_every,
+                                                ckpt_slot=ck)
+
+    def step_ck():
+        code = lib.gdn_prefill(ctypes.byref(a_ck), s())
+        if code:
+            raise gdn.GdnError("gdn_prefill", code)
+
+    ms_ck = timed(step_ck, args.prefill_reps)
+    n_ck = int(sum(int(L) // ck_every for L in lengths))
     flops = prefill_useful_flops(lengths, Hv, d, d)
     algo_bytes = N * ((2 * Hqk * d + Hv * d) * 2 + Hv * d * 2 + 2 * Hv * 4) + len(lengths) * Hv * d * d * 2
     return dict(workload="prefill_varlen", tokens=N, lengths=[int(v) for v in lengths],
@@ -203,7 +223,8 @@ def run_prefill(args, torch, gdn, syn):
                 mfma_frac=round(flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
                 algorithmic_GBps=round(algo_bytes / (ms / 1e3) / 1e9, 1),
                 hbm_frac=round(algo_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
-                longest_chain_chunks=int((max(lengths) + 63) // 64))
+                longest_chain_chunks=int((max(lengths) + 63) // 64),
+                ckpt_every_1024_ms=round(ms_ck, 3), ckpt_count=n_ck)
 
 
 def run_mixed(args, torch, gdn, syn):

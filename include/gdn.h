@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -139,7 +139,8 @@ typedef struct gdn_prefill_args {
   int32_t use_frontend; /* 0 or 1 */
   int32_t conv_k;      /* conv width; 4 (ignored when use_frontend = 0) */
   int32_t chunk;       /* 64 */
-  int32_t reserved0;   /* must be 0 */
+  int32_t ckpt_interval; /* 0, or tokens between intermediate checkpoints: a positive multiple
+                            of chunk (see ckpt_slot) */
   int64_t n_tokens;    /* total tokens = cu_seqlens[n_seq] */
   int64_t n_slots;
   float scale;         /* read-out scale */
@@ -164,6 +165,19 @@ typedef struct gdn_prefill_args {
   void *workspace;     /* device scratch of gdn_prefill_workspace_size() bytes (may be NULL if 0) */
   size_t workspace_bytes;
   uint32_t *status;    /* optional device word */
+  /* Intermediate checkpoints at block boundaries ("Gated DeltaNet" glossary
+   * entry, Why it matters: hybrid prefix caching keeps GDN checkpoints in
+   * their own slots, aligned to KV block boundaries).  With ckpt_interval > 0,
+   * ckpt_slot[s * ckpt_per_seq + j] receives sequence s's state after its
+   * first (j + 1) * ckpt_interval tokens, if it has that many (j <
+   * ckpt_per_seq): FP32 across chunks, rounded once when stored as BF16, the
+   * value a prefill of just those tokens would store in its write slot.  -1
+   * stores nothing; an index outside [-1, n_slots) stores nothing and sets
+   * GDN_DEVICE_BAD_SLOT.  Checkpoint slots follow the write-slot contract
+   * (unique, no other request's read slot).  Ignored when ckpt_interval = 0. */
+  const int32_t *ckpt_slot; /* [n_seq, ckpt_per_seq] device */
+  int32_t ckpt_per_seq;
+  int32_t reserved1;   /* must be 0 */
 } gdn_prefill_args;
 
 /* Bytes of one slot (all H_v heads of one request, one layer).  The ONNX

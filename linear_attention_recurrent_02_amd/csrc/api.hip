@@ -47,7 +47,7 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
   if (a->n_seq < 0 || a->n_tokens < 0 || a->n_slots < 0) return GDN_ERR_SHAPE;
   if (!valid_rule(a->rule)) return GDN_ERR_RULE;
   if (!valid_dtype(a->state_dtype) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
-  if (a->reserved0 != 0) return GDN_ERR_UNSUPPORTED;
+  if (a->reserved1 != 0) return GDN_ERR_UNSUPPORTED;
   if (a->use_frontend != 0 && a->use_frontend != 1) return GDN_ERR_UNSUPPORTED;
   gdn_status st = check_heads(a->H_qk, a->H_v, a->d_k, a->d_v);
   if (st != GDN_OK) return st;
@@ -79,6 +79,12 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
   // FP32 activations keep FP32 MFMA operands in LDS, which fits d_k, d_v <= 64
   if (a->act_dtype == GDN_F32 && (a->d_k > 64 || a->d_v > 64)) return GDN_ERR_UNSUPPORTED;
   if ((!a->read_slot || !a->write_slot) && a->n_slots < a->n_seq) return GDN_ERR_SHAPE;
+  // intermediate checkpoints: a whole number of chunks apart, and somewhere to put them
+  if (a->ckpt_interval < 0 || a->ckpt_interval % a->chunk != 0) return GDN_ERR_SHAPE;
+  if (a->ckpt_interval > 0) {
+    if (a->ckpt_per_seq <= 0) return GDN_ERR_SHAPE;
+    if (!a->ckpt_slot) return GDN_ERR_NULL;
+  }
   const size_t need = gdn::prefill_workspace_bytes(*a);
   if (need > 0 && (!a->workspace || a->workspace_bytes < need)) return GDN_ERR_WORKSPACE;
   return GDN_OK;

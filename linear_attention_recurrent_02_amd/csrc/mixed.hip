@@ -49,7 +49,7 @@ struct MixedLayout {
   static constexpr size_t BYTES = PREFILL > DECODE ? PREFILL : DECODE;
 };
 
-template <bool SB, bool AB, int DK, int DV, bool F32>
+template <bool SB, bool AB, int DK, int DV, bool F32, bool CK>
 __global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32>::NT)) void mixed_kernel(
     DecodeParams dp, PrefillParams pp, int n_chains, int prefill_blocks, int ordered) {
   using L = MixedLayout<SB, AB, DK, DV, F32>;
@@ -58,8 +58,8 @@ __global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32>::NT)) void mixed_
   if ((int)blockIdx.x < prefill_blocks) {
     const int chain = chain_of_block(blockIdx.x);
     if (chain < n_chains) {
-      if constexpr (L::OWN_CHAIN) run_chain<SB, AB, DK, DV, F32>(pp, chain, smem);
-      else prefill_chain<SB, AB, DK, DV, F32, L::NW>(pp, chain, smem);
+      if constexpr (L::OWN_CHAIN) run_chain<SB, AB, DK, DV, F32, CK>(pp, chain, smem);
+      else prefill_chain<SB, AB, DK, DV, F32, L::NW, CK>(pp, chain, smem);
     }
     return;
   }
@@ -113,8 +113,15 @@ static gdn_status launch_mixed_t(const DecodeParams &dp, const PrefillParams &pp
         dp.write_slot != nullptr && dp.B <= kOrderMaxB && dp.n_slots <= kOrderMaxSlots ? 1 : 0;
     const int64_t grid = (n_chains > 0 ? prefill_blocks : 0) + workers;
     if (grid == 0) return GDN_OK;
-    hipLaunchKernelGGL((mixed_kernel<SB, AB, DK, DV, F32>), dim3((unsigned)grid), dim3(L::NT), 0, s,
-                       dp, pp, n_chains, n_chains > 0 ? prefill_blocks : 0, ordered);
+    // the instance with intermediate checkpoints only when they are asked for
+    if (pp.ckpt_chunks > 0)
+      hipLaunchKernelGGL((mixed_kernel<SB, AB, DK, DV, F32, true>), dim3((unsigned)grid),
+                         dim3(L::NT), 0, s, dp, pp, n_chains,
+                         n_chains > 0 ? prefill_blocks : 0, ordered);
+    else
+      hipLaunchKernelGGL((mixed_kernel<SB, AB, DK, DV, F32, false>), dim3((unsigned)grid),
+                         dim3(L::NT), 0, s, dp, pp, n_chains,
+                         n_chains > 0 ? prefill_blocks : 0, ordered);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
   }
 }

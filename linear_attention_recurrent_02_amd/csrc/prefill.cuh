@@ -65,6 +65,10 @@ struct PrefillParams {
   const int32_t *read_slot, *write_slot;
   void *o;
   uint32_t *status;
+  // intermediate checkpoints: after every ckpt_chunks chunks (0 = none), the
+  // state goes to ckpt_slot[seq * ckpt_per_seq + j]
+  int32_t ckpt_chunks, ckpt_per_seq;
+  const int32_t *ckpt_slot;
 };
 
 // LDS layout of the chain kernel (byte offsets).  OT is the operand storage

@@ -9,12 +9,12 @@
 
 namespace gdn {
 
-template <bool SB, bool AB, int DK, int DV, bool F32>
+template <bool SB, bool AB, int DK, int DV, bool F32, bool CK>
 __global__ __launch_bounds__((64 * kPrefillWaves<DK, DV, F32>)) void prefill_kernel(PrefillParams p,
                                                                                    int n_chains) {
   __shared__ __align__(16) char smem[kChainLds<DK, DV, F32>];
   const int chain = chain_of_block(blockIdx.x);
-  if (chain < n_chains) run_chain<SB, AB, DK, DV, F32>(p, chain, smem);
+  if (chain < n_chains) run_chain<SB, AB, DK, DV, F32, CK>(p, chain, smem);
 }
 
 // ---- launcher --------------------------------------------------------------
@@ -27,6 +27,9 @@ PrefillParams make_prefill_params(const gdn_prefill_args &a, const void *q, cons
   p.q = q; p.k = k; p.v = v; p.g = g; p.beta = beta;
   p.pool = a.state_pool; p.read_slot = a.read_slot; p.write_slot = a.write_slot;
   p.o = a.o; p.status = a.status;
+  p.ckpt_chunks = a.ckpt_interval > 0 ? a.ckpt_interval / a.chunk : 0;
+  p.ckpt_per_seq = a.ckpt_per_seq;
+  p.ckpt_slot = a.ckpt_slot;
   return p;
 }
 
@@ -38,8 +41,13 @@ static gdn_status launch_chains(const PrefillParams &p, hipStream_t s) {
   } else {
     const int n_chains = p.n_seq * p.H_v;
     const int blocks = (n_chains + 15) / 16 * 16;
-    hipLaunchKernelGGL((prefill_kernel<SB, AB, DK, DV, F32>), dim3(blocks),
-                       dim3(64 * kPrefillWaves<DK, DV, F32>), 0, s, p, n_chains);
+    // the instance with intermediate checkpoints only when they are asked for
+    if (p.ckpt_chunks > 0)
+      hipLaunchKernelGGL((prefill_kernel<SB, AB, DK, DV, F32, true>), dim3(blocks),
+                         dim3(64 * kPrefillWaves<DK, DV, F32>), 0, s, p, n_chains);
+    else
+      hipLaunchKernelGGL((prefill_kernel<SB, AB, DK, DV, F32, false>), dim3(blocks),
+                         dim3(64 * kPrefillWaves<DK, DV, F32>), 0, s, p, n_chains);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
   }
 }

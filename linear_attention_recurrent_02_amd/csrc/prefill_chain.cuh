@@ -72,7 +72,9 @@ constexpr LocalTiles kLocalTiles[4] = {
 
 // One (sequence, state head) chain; all 64 NW threads of the workgroup call
 // it.  `smem` holds PrefillLayout<DK, DV, F32>::BYTES bytes, 16-byte aligned.
-template <bool SB, bool AB, int DK, int DV, bool F32, int NW>
+// CK: the instance that stores intermediate checkpoints (the launcher picks
+// it only when they are asked for, so the others carry none of its code).
+template <bool SB, bool AB, int DK, int DV, bool F32, int NW, bool CK = false>
 __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain, char *smem) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per chain");
   constexpr int NT = 64 * NW;
@@ -322,6 +324,21 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
       }
     }
   }
+  // FP32 state -> state dtype (RNE for BF16) -> a slot (waves that own d_v
+  // columns): the final state, and the intermediate checkpoints
+  auto store_state = [&](int64_t slot) {
+    const int64_t out_base = (slot * p.H_v + h) * (int64_t)DK * DV;
+#pragma unroll
+    for (int b = 0; b < DKB; ++b) {
+#pragma unroll
+      for (int ia = 0; ia < NA; ++ia) {
+        const int d = 16 * b + rq, c = 16 * (wave * NA + ia) + col;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          Elem<SB>::store1(p.pool, out_base + (int64_t)(d + e) * DV + c, macc[b][ia][e]);
+      }
+    }
+  };
   if (t_begin < t_end) {
     fetch(t_begin);
     stage(0);
@@ -724,23 +741,23 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
         }
       }
     }
+    // an intermediate checkpoint after this chunk (a uniform branch)
+    if (CK && p.ckpt_chunks > 0 && t1 <= t_end && ((t1 - t_begin) / C) % p.ckpt_chunks == 0) {
+      const int j = (int)((t1 - t_begin) / C / p.ckpt_chunks) - 1;
+      if (j < p.ckpt_per_seq) {
+        const int64_t cs = p.ckpt_slot[(int64_t)seq * p.ckpt_per_seq + j];
+        if (cs >= 0 && cs < p.n_slots) {
+          if (mwave) store_state(cs);
+        } else if (cs != -1 && tid == 0 && p.status) {
+          atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+        }
+      }
+    }
     __syncthreads();  // the next chunk's set is written; this chunk's reads are done
   }
 
   // ---- final state (a8): FP32 -> state dtype (RNE for BF16) -> write slot ----
-  if (ws >= 0 && mwave) {
-    const int64_t out_base = (ws * p.H_v + h) * (int64_t)DK * DV;
-#pragma unroll
-    for (int b = 0; b < DKB; ++b) {
-#pragma unroll
-      for (int ia = 0; ia < NA; ++ia) {
-        const int d = 16 * b + rq, c = 16 * (wave * NA + ia) + col;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          Elem<SB>::store1(p.pool, out_base + (int64_t)(d + e) * DV + c, macc[b][ia][e]);
-      }
-    }
-  }
+  if (ws >= 0 && mwave) store_state(ws);
 }
 
 }  // namespace gdn

@@ -67,7 +67,8 @@ constexpr PipeTiles kPipeTiles[4] = {
     {6, {6, 7, 4, 5, 2, 0}, 2, {{2, 1, 2, 3, 4}, {3, 0, 0, 1, 5}}},  // (3,3) (2,1) (3,0)
 };
 
-template <bool SB, bool AB, int DK, int DV>
+// CK: the instance that stores intermediate checkpoints.
+template <bool SB, bool AB, int DK, int DV, bool CK = false>
 __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int chain, char *smem) {
   static_assert(AB, "BF16 activations");
   constexpr bool F32 = false;
@@ -378,6 +379,21 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
       }
     }
 
+    // FP32 state -> state dtype (RNE for BF16) -> a slot: the final state, and
+    // the intermediate checkpoints
+    auto store_state = [&](int64_t slot) {
+      const int64_t out_base = (slot * p.H_v + h) * (int64_t)DK * DV;
+#pragma unroll
+      for (int b = 0; b < DKB; ++b) {
+#pragma unroll
+        for (int ia = 0; ia < NA; ++ia) {
+          const int d = 16 * b + rq, c = 16 * (cw * NA + ia) + col;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Elem<SB>::store1(p.pool, out_base + (int64_t)(d + e) * DV + c, macc[b][ia][e]);
+        }
+      }
+    };
     __syncthreads();  // prologue: chunk 0 staged
     __syncthreads();  // prologue: chunk 0's chunk-local set formed
     f32x4_t qm[4][NA], um[4][NA];  // set by their first MFMA (K-step 0 starts from zero)
@@ -541,22 +557,19 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      // an intermediate checkpoint after this chunk (a uniform branch)
+      if (CK && p.ckpt_chunks > 0 && (c + 1) % p.ckpt_chunks == 0) {
+        const int j = (c + 1) / p.ckpt_chunks - 1;
+        if (j < p.ckpt_per_seq && (int64_t)(c + 1) * C <= t_end - t_begin) {
+          const int64_t cs = p.ckpt_slot[(int64_t)seq * p.ckpt_per_seq + j];
+          if (cs >= 0 && cs < p.n_slots) store_state(cs);
+          else if (cs != -1 && tid == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+        }
+      }
       __syncthreads();  // X: chunk c's sets are free; chunk c + 1's local set is written
     }
     // ---- final state (a8): FP32 -> state dtype (RNE for BF16) -> write slot ----
-    if (ws >= 0) {
-      const int64_t out_base = (ws * p.H_v + h) * (int64_t)DK * DV;
-#pragma unroll
-      for (int b = 0; b < DKB; ++b) {
-#pragma unroll
-        for (int ia = 0; ia < NA; ++ia) {
-          const int d = 16 * b + rq, c = 16 * (cw * NA + ia) + col;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            Elem<SB>::store1(p.pool, out_base + (int64_t)(d + e) * DV + c, macc[b][ia][e]);
-        }
-      }
-    }
+    if (ws >= 0) store_state(ws);
   } else {
     // prologue: chunk 0 staged and its chunk-local set formed, chunk 1 in flight
     if (n_chunks > 0) {
@@ -592,13 +605,13 @@ template <int DK, int DV, bool F32>
 constexpr size_t kChainLds =
     kPrefillPipe<DK, DV, F32> ? PipeLayout<DK, DV>::BYTES : PrefillLayout<DK, DV, F32>::BYTES;
 
-template <bool SB, bool AB, int DK, int DV, bool F32>
+template <bool SB, bool AB, int DK, int DV, bool F32, bool CK = false>
 __device__ __forceinline__ void run_chain(const PrefillParams &p, int chain, char *smem) {
   if constexpr (kPrefillPipe<DK, DV, F32>) {
     static_assert(kPrefillWaves<DK, DV, F32> == 8, "the pipelined chain runs 8 waves");
-    prefill_chain_pipe<SB, AB, DK, DV>(p, chain, smem);
+    prefill_chain_pipe<SB, AB, DK, DV, CK>(p, chain, smem);
   } else {
-    prefill_chain<SB, AB, DK, DV, F32, kPlainWaves<DK, DV, F32>>(p, chain, smem);
+    prefill_chain<SB, AB, DK, DV, F32, kPlainWaves<DK, DV, F32>, CK>(p, chain, smem);
   }
 }
 

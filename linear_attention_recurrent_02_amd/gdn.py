@@ -39,13 +39,15 @@ class DecodeArgs(ctypes.Structure):
 class PrefillArgs(ctypes.Structure):
     _fields_ = [("n_seq", _I32), ("H_qk", _I32), ("H_v", _I32), ("d_k", _I32), ("d_v", _I32),
                 ("rule", _I32), ("state_dtype", _I32), ("act_dtype", _I32),
-                ("use_frontend", _I32), ("conv_k", _I32), ("chunk", _I32), ("reserved0", _I32),
+                ("use_frontend", _I32), ("conv_k", _I32), ("chunk", _I32),
+                ("ckpt_interval", _I32),
                 ("n_tokens", _I64), ("n_slots", _I64), ("scale", ctypes.c_float),
                 ("eps", ctypes.c_float), ("cu_seqlens", _P), ("q", _P), ("k", _P), ("v", _P),
                 ("g", _P), ("beta", _P), ("a_raw", _P), ("b_raw", _P), ("conv_wq", _P),
                 ("conv_wk", _P), ("conv_wv", _P), ("state_pool", _P), ("read_slot", _P),
                 ("write_slot", _P), ("o", _P), ("workspace", _P),
-                ("workspace_bytes", ctypes.c_size_t), ("status", _P)]
+                ("workspace_bytes", ctypes.c_size_t), ("status", _P), ("ckpt_slot", _P),
+                ("ckpt_per_seq", _I32), ("reserved1", _I32)]
 
 
 class GdnError(RuntimeError):
@@ -220,16 +222,19 @@ def gdn_decode(q, k, v, g, beta, state_pool, read_slot=None, write_slot=None, o=
 def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slot=None, o=None, *,
                       H_qk, H_v, g=None, beta=None, a_raw=None, b_raw=None, conv_wq=None,
                       conv_wk=None, conv_wv=None, rule="gated_delta", scale=1.0, eps=1e-6,
-                      chunk=64, workspace=None, status=None):
+                      chunk=64, workspace=None, status=None, ckpt_interval=0, ckpt_slot=None):
     """Build a PrefillArgs struct.  q, k: [N, H_qk*d_k] (or [N, H_qk, d_k]);
     v: [N, H_v*d_v]; with conv weights given the front-end runs (a_raw,
-    b_raw are the gate logits), otherwise g, beta are used as given.
+    b_raw are the gate logits), otherwise g, beta are used as given.  With
+    ckpt_interval > 0 (a multiple of chunk), ckpt_slot [n_seq, per_seq] int32
+    names the slots of the intermediate checkpoints.
     Returns (args, o, keepalive); allocates the workspace when needed."""
     for name, t in (("cu_seqlens", cu_seqlens), ("q", q), ("k", k), ("v", v),
                     ("state_pool", state_pool), ("read_slot", read_slot),
                     ("write_slot", write_slot), ("o", o), ("g", g), ("beta", beta),
                     ("a_raw", a_raw), ("b_raw", b_raw), ("conv_wq", conv_wq),
-                    ("conv_wk", conv_wk), ("conv_wv", conv_wv), ("status", status)):
+                    ("conv_wk", conv_wk), ("conv_wv", conv_wv), ("status", status),
+                    ("ckpt_slot", ckpt_slot)):
         _dev(t, name)
     N = q.shape[0]
     d_k = q.numel() // max(1, N * H_qk) if N else state_pool.shape[2]
@@ -246,7 +251,7 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
     a.use_frontend = 1 if use_fe else 0
     a.conv_k = conv_wq.shape[1] if use_fe else 4
     a.chunk = chunk
-    a.reserved0 = 0
+    a.ckpt_interval = int(ckpt_interval)
     a.n_tokens = N
     a.n_slots = state_pool.shape[0]
     a.scale, a.eps = float(scale), float(eps)
@@ -255,13 +260,16 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
     a.conv_wq, a.conv_wk, a.conv_wv = _ptr(conv_wq), _ptr(conv_wk), _ptr(conv_wv)
     a.state_pool, a.read_slot, a.write_slot = _ptr(state_pool), _ptr(read_slot), _ptr(write_slot)
     a.o, a.status = _ptr(o), _ptr(status)
+    a.ckpt_slot = _ptr(ckpt_slot)
+    a.ckpt_per_seq = 0 if ckpt_slot is None else int(ckpt_slot.shape[-1])
+    a.reserved1 = 0
     need = int(load_library().gdn_prefill_workspace_size(ctypes.byref(a)))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     keep = (cu_seqlens, q, k, v, state_pool, read_slot, write_slot, o, g, beta, a_raw, b_raw,
-            conv_wq, conv_wk, conv_wv, workspace, status)
+            conv_wq, conv_wk, conv_wv, workspace, status, ckpt_slot)
     return a, o, keep
 
 
@@ -291,7 +299,7 @@ def gdn_frontend(cu_seqlens, q_raw, k_raw, v_raw, *, H_qk, H_v, conv_wq, conv_wk
     a.rule = RULES["gated_delta"]
     a.state_dtype = F32
     a.act_dtype = _dtype_code(q_raw)
-    a.use_frontend, a.conv_k, a.chunk, a.reserved0 = 1, conv_wq.shape[1], 64, 0
+    a.use_frontend, a.conv_k, a.chunk, a.ckpt_interval = 1, conv_wq.shape[1], 64, 0
     a.n_tokens, a.n_slots = N, 0
     a.scale, a.eps = 1.0, float(eps)
     a.cu_seqlens, a.q, a.k, a.v = _ptr(cu_seqlens), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw)

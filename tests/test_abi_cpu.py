@@ -27,7 +27,7 @@ def test_struct_layout_matches():
     lib = gdn.load_library()
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
-    assert gdn.gdn_abi_version() == 1
+    assert gdn.gdn_abi_version() == 2
 
 
 def test_state_bytes_against_the_pages():
@@ -102,7 +102,7 @@ def _prefill_args(**over):
     a = B.PrefillArgs()
     a.n_seq, a.H_qk, a.H_v, a.d_k, a.d_v = 2, 2, 4, 128, 128
     a.rule, a.state_dtype, a.act_dtype = 3, 1, 1
-    a.use_frontend, a.conv_k, a.chunk, a.reserved0 = 1, 4, 64, 0
+    a.use_frontend, a.conv_k, a.chunk, a.ckpt_interval = 1, 4, 64, 0
     a.n_tokens, a.n_slots, a.scale, a.eps = 100, 8, 1.0, 1e-6
     for f in ("cu_seqlens", "q", "k", "v", "a_raw", "b_raw", "conv_wq", "conv_wk", "conv_wv",
               "state_pool", "o", "g", "beta"):
@@ -122,6 +122,11 @@ def _prefill_args(**over):
     (dict(q=FAKE + 2), ALIGN), (dict(v=FAKE + 8), ALIGN), (dict(conv_wv=FAKE + 4), ALIGN),
     (dict(o=FAKE + 2), ALIGN), (dict(state_pool=FAKE + 8), ALIGN),
     (dict(workspace=FAKE + 8, workspace_bytes=1 << 40), ALIGN),
+    # intermediate checkpoints: a positive multiple of the chunk, a slot matrix, reserved1 = 0
+    (dict(ckpt_interval=32), SHAPE), (dict(ckpt_interval=-64), SHAPE),
+    (dict(ckpt_interval=64), SHAPE), (dict(ckpt_interval=64, ckpt_per_seq=2), NULL),
+    (dict(reserved1=1), UNSUP),
+    (dict(ckpt_interval=128, ckpt_per_seq=2, ckpt_slot=FAKE), WORKSPACE),  # the checks pass
 ])
 def test_prefill_validation(over, code):
     lib = gdn.load_library()

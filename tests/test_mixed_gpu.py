@@ -98,6 +98,24 @@ def test_mixed_fp32_state_equals_separate():
     assert torch.equal(pool, spool)
 
 
+def test_mixed_checkpoints_equal_separate():
+    """Intermediate prefill checkpoints (every 64 tokens) through the mixed
+    launch land exactly where gdn_prefill puts them."""
+    say("mixed checkpoints")
+    c = build(405, 9, [70, 130, 1], 2, 4, 128, 64, frontend=False, std=0.05)
+    used = set(c["drs"].tolist()) | set(c["dws"].tolist()) | set(c["prs"].tolist()) | set(c["pws"].tolist())
+    free = [x for x in range(64) if x not in used]
+    ck = torch.tensor(free[:6], dtype=torch.int32).reshape(3, 2)
+    c["pin"]["kw"] = dict(c["pin"]["kw"], ckpt_interval=64, ckpt_slot=dev(ck))
+    do, po, pool = run_mixed(c, "gated_delta")
+    so, spo, spool = run_separate(c, "gated_delta")
+    assert torch.equal(do, so) and torch.equal(po, spo)
+    assert torch.equal(pool.view(torch.int16), spool.view(torch.int16))
+    # sequence 1 (130 tokens) reached checkpoints at 64 and 128, sequence 0 at 64
+    for slot in (int(ck[0, 0]), int(ck[1, 0]), int(ck[1, 1])):
+        assert not torch.equal(pool[slot].cpu(), c["pool"][slot])
+
+
 def test_mixed_one_half_empty():
     say("mixed empty halves")
     c = build(402, 6, [90], 1, 2, 64, 16, frontend=False, std=0.05)

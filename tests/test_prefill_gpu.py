@@ -83,6 +83,91 @@ def test_prefill_bf16_ragged(rule):
     assert torch.equal(dpool.cpu()[others].view(torch.int16), case[6][others].view(torch.int16))
 
 
+def checkpoint_case(wl, lengths, d, sdt, adt, per_seq, skip=()):
+    """A prefill case plus a checkpoint slot matrix [n_seq, per_seq] drawn from
+    the slots that are neither read nor written (entries in `skip` are -1)."""
+    n_seq = len(lengths)
+    n_slots = 2 * n_seq + n_seq * per_seq + 4
+    case = prefill_case(wl, lengths, 1, 2, d, d, n_slots, sdt, adt, std=0.1, fresh=(0,))
+    used = set(case[7].tolist()) | set(case[8].tolist())
+    free = [s for s in np.random.default_rng(wl).permutation(n_slots) if s not in used]
+    ck = np.array(free[:n_seq * per_seq], np.int32).reshape(n_seq, per_seq)
+    for s_, j in skip:
+        ck[s_, j] = -1
+    return case, ck
+
+
+@pytest.mark.parametrize("d,dt,tol,interval", [(128, torch.bfloat16, 2e-2, 64),
+                                               (128, torch.bfloat16, 2e-2, 128),
+                                               (32, torch.float32, 1e-4, 64)])
+def test_prefill_checkpoints(d, dt, tol, interval):
+    """Intermediate checkpoints at block boundaries: slot [s, j] holds sequence
+    s's state after its first (j + 1) * interval tokens, i.e. the state that a
+    prefill of just those tokens stores (checked against the oracle run on each
+    prefix); slots past a sequence's end and -1 entries are left alone, and the
+    outputs and final states are those of a prefill without checkpoints.  d = 128
+    runs the pipelined chain, d = 32 in FP32 the plain one."""
+    say("prefill checkpoints", d, interval)
+    lengths = [300, 128, 64, 65, 0, 1, 256]
+    case, ck = checkpoint_case(212, lengths, d, dt, dt, per_seq=4, skip=((0, 1),))
+    cu, q, k, v, g, beta, pool, rs, ws = case
+    dpool = dev(pool)
+    o = gdn_prefill(dev(cu), dev(q), dev(k), dev(v), dpool, dev(rs), dev(ws), H_qk=1, H_v=2,
+                    g=dev(g), beta=dev(beta), ckpt_interval=interval,
+                    ckpt_slot=dev(torch.from_numpy(ck)))
+    torch.cuda.synchronize()
+    rnd = dt == torch.bfloat16
+    ro, rpool, code = oracle.sequences(cu.numpy(), f64(q), f64(k), f64(v), f64(g), f64(beta),
+                                       f64(pool), rs.numpy(), ws.numpy(), round_state=rnd)
+    assert code == 0
+    assert seq_err(f64(o), ro, cu) < tol
+    assert scaled_err(f64(dpool)[ws.numpy()], rpool[ws.numpy()], 2) < tol
+    got = f64(dpool.cpu())
+    written = set()
+    for s_, L in enumerate(lengths):
+        for j in range(ck.shape[1]):
+            n = (j + 1) * interval
+            slot = int(ck[s_, j])
+            if slot < 0 or n > L:
+                continue
+            a, b = int(cu[s_]), int(cu[s_]) + n
+            _, ppool, c2 = oracle.sequences(np.array([0, n], np.int32), f64(q[a:b]), f64(k[a:b]),
+                                            f64(v[a:b]), f64(g[a:b]), f64(beta[a:b]), f64(pool),
+                                            rs.numpy()[s_:s_ + 1], np.array([slot], np.int32),
+                                            round_state=rnd)
+            assert c2 == 0
+            assert scaled_err(got[slot], ppool[slot], 2) < tol, (s_, j)
+            written.add(slot)
+    expect = sum(1 for s_, L in enumerate(lengths) for j in range(ck.shape[1])
+                 if (j + 1) * interval <= L and ck[s_, j] >= 0)
+    assert len(written) == expect > 0
+    untouched = np.setdiff1d(np.arange(pool.shape[0]),
+                             np.concatenate([ws.numpy(), np.array(sorted(written), np.int64)]))
+    assert torch.equal(dpool.cpu()[untouched], pool[untouched])
+
+
+def test_prefill_checkpoint_bad_slot():
+    """An out-of-range checkpoint slot stores nothing and sets the status bit;
+    everything else is computed as usual."""
+    say("prefill checkpoint bad slot")
+    case, ck = checkpoint_case(213, [130, 64], 128, torch.bfloat16, torch.bfloat16, per_seq=2)
+    cu, q, k, v, g, beta, pool, rs, ws = case
+    ck[0, 1] = pool.shape[0] + 3
+    status = torch.zeros(1, dtype=torch.int32, device=DEV)
+    dpool = dev(pool)
+    gdn_prefill(dev(cu), dev(q), dev(k), dev(v), dpool, dev(rs), dev(ws), H_qk=1, H_v=2,
+                g=dev(g), beta=dev(beta), ckpt_interval=64, ckpt_slot=dev(torch.from_numpy(ck)),
+                status=status)
+    torch.cuda.synchronize()
+    assert int(status.item()) & 1
+    ro, rpool, code = oracle.sequences(cu.numpy(), f64(q), f64(k), f64(v), f64(g), f64(beta),
+                                       f64(pool), rs.numpy(), ws.numpy(), round_state=True)
+    assert scaled_err(f64(dpool)[ws.numpy()], rpool[ws.numpy()], 2) < 2e-2
+    # the valid checkpoints (sequence 0 at 64, sequence 1 at 64) were stored
+    for s_, j in ((0, 0), (1, 0)):
+        assert not torch.equal(dpool.cpu()[int(ck[s_, j])], pool[int(ck[s_, j])])
+
+
 def test_prefill_bf16_fp32_state():
     """BF16 q/k/v/o with an FP32 state pool at d = 128 (the pipelined chain
     reading and writing FP32 slots): ragged sequences, one fresh request."""
