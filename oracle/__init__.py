@@ -59,6 +59,9 @@ def _load():
         lib.oracle_frontend.restype = i32
         lib.oracle_frontend.argtypes = [i32, P, i32, i32, i32, i32, i32, f64,
                                         P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_conv_decode.restype = i32
+        lib.oracle_conv_decode.argtypes = [i32, i32, i32, i32, i32, i32, f64, i64,
+                                           P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_version.restype = i32
         _lib = lib
     return _lib
@@ -163,3 +166,56 @@ def frontend(cu_seqlens, q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw, *, Hqk, 
     if code != 0:
         raise ValueError("oracle_frontend rejected its arguments")
     return qo.reshape(N, Hqk, dk), ko.reshape(N, Hqk, dk), vo.reshape(N, Hv, dv), g, beta
+
+
+def conv_decode(q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw, conv_pool, read_slot=None,
+                write_slot=None, *, Hqk, Hv, eps=1e-6):
+    """One decode token of the front-end for B requests, conv window from slots.
+
+    q_raw, k_raw: [B, Hqk*dk]; v_raw: [B, Hv*dv]; w*: [channels, K]; a_raw,
+    b_raw: [B, Hv]; conv_pool: [n_slots, K-1, 2*Hqk*dk + Hv*dv] (a float64
+    copy is updated and returned).  Returns ``(q, k, v, g, beta, pool_after,
+    code)`` with q, k as [B, Hqk, dk] and v as [B, Hv, dv]; code 1 means a
+    request was skipped for an out-of-range slot (its outputs stay 0).
+    """
+    q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw = map(
+        _f64, (q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw))
+    pool = _f64(conv_pool).copy()
+    B = q_raw.shape[0]
+    dk = q_raw.shape[1] // Hqk
+    dv = v_raw.shape[1] // Hv
+    K = wq.shape[1]
+    if pool.ndim != 3 or pool.shape[1] != K - 1 or pool.shape[2] != 2 * Hqk * dk + Hv * dv:
+        raise ValueError("conv_pool must be [n_slots, K-1, 2*Hqk*dk + Hv*dv]")
+    rs, ws = _i32(read_slot), _i32(write_slot)
+    qo, ko, vo = np.zeros_like(q_raw), np.zeros_like(k_raw), np.zeros_like(v_raw)
+    g = np.zeros((B, Hv), np.float64)
+    beta = np.zeros((B, Hv), np.float64)
+    code = _load().oracle_conv_decode(B, Hqk, Hv, dk, dv, K, float(eps), pool.shape[0],
+                                      _p(q_raw), _p(k_raw), _p(v_raw), _p(wq), _p(wk), _p(wv),
+                                      _p(a_raw), _p(b_raw), _p(pool), _p(rs), _p(ws), _p(qo),
+                                      _p(ko), _p(vo), _p(g), _p(beta))
+    if code < 0:
+        raise ValueError("oracle_conv_decode rejected its arguments")
+    return (qo.reshape(B, Hqk, dk), ko.reshape(B, Hqk, dk), vo.reshape(B, Hv, dv), g, beta,
+            pool, code)
+
+
+def conv_tail(cu_seqlens, q_raw, k_raw, v_raw, K=4):
+    """The conv window each sequence leaves behind: its last K-1 raw inputs.
+
+    Returns [n_seq, K-1, 2*Hqk*dk + Hv*dv] (q|k|v channels, oldest token
+    first), zero where a sequence has fewer than K-1 tokens: the history a
+    decode step of that sequence continues from.
+    """
+    q_raw, k_raw, v_raw = map(_f64, (q_raw, k_raw, v_raw))
+    cu = _i32(cu_seqlens)
+    rows = np.concatenate([q_raw, k_raw, v_raw], axis=1)
+    out = np.zeros((cu.shape[0] - 1, K - 1, rows.shape[1]), np.float64)
+    for s in range(cu.shape[0] - 1):
+        t0, t1 = int(cu[s]), int(cu[s + 1])
+        for j in range(K - 1):
+            t = t1 - (K - 1) + j
+            if t >= t0:
+                out[s, j] = rows[t]
+    return out

@@ -51,6 +51,12 @@
  *    a sequence boundary), then SiLU; q and k are then L2-normalised per
  *    (token, head) as y / sqrt(sum y^2 + eps); g = -softplus(a_raw) and
  *    beta = sigmoid(b_raw).
+ *  - Decode-side conv: the window a decode token sees is the conv_k-1 raw
+ *    inputs before it, kept per request in a conv-state slot ([conv_k-1,
+ *    channels], oldest first, channels in q|k|v order); read index -1 = no
+ *    history (zeros, a fresh request), write index -1 = not stored, the same
+ *    slot contract as the recurrent state.  The stored window holds raw
+ *    inputs, so it is exact in the input precision.
  */
 #include <math.h>
 #include <pthread.h>
@@ -58,7 +64,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_VERSION 1
+#define ORACLE_VERSION 2
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -351,4 +357,77 @@ int oracle_frontend(int n_seq, const int32_t *cu, int Hqk, int Hv, int dk, int d
     }
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* decode-side front-end: one token per request, conv window from a slot     */
+
+/* One decode token of the front-end for B requests.  The conv is part of the
+ * layer (Gated DeltaNet glossary, Engineering details), so a decode token's
+ * window continues the raw inputs of the tokens before it; those conv_k-1
+ * inputs live in a conv-state slot, read and written like the recurrent
+ * state's slots (Recurrent state glossary, Why it matters).
+ * q_raw, k_raw: [B, Hqk*dk]; v_raw: [B, Hv*dv]; w*: [channels, K];
+ * a_raw, b_raw: [B, Hv]; pool: [n_slots, K-1, C], C = 2*Hqk*dk + Hv*dv in
+ * q|k|v channel order, entry 0 the oldest token, updated in place.  Outputs
+ * as oracle_frontend's for one token per request.  A request with a slot
+ * index outside [-1, n_slots) is skipped (nothing written) and the result
+ * is 1; otherwise 0; -1 on bad arguments. */
+int oracle_conv_decode(int B, int Hqk, int Hv, int dk, int dv, int K, double eps,
+                       int64_t n_slots, const double *q_raw, const double *k_raw,
+                       const double *v_raw, const double *wq, const double *wk,
+                       const double *wv, const double *a_raw, const double *b_raw,
+                       double *pool, const int32_t *read_slot, const int32_t *write_slot,
+                       double *q_out, double *k_out, double *v_out, double *g_out,
+                       double *beta_out) {
+  if (B < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || K < 1 || n_slots < 0) return -1;
+  const int64_t cq = (int64_t)Hqk * dk, cv = (int64_t)Hv * dv, C = 2 * cq + cv;
+  const int64_t slot_len = (int64_t)(K - 1) * C;
+  double *win = (double *)malloc(sizeof(double) * (size_t)(K * C > 0 ? K * C : 1));
+  if (!win) return -1;
+  int bad = 0;
+  for (int64_t r = 0; r < B; ++r) {
+    int64_t rs, ws;
+    if (!resolve_slots(read_slot, write_slot, r, n_slots, &rs, &ws)) { bad = 1; continue; }
+    /* the window: K-1 tokens of history (zeros without a read slot), then this token */
+    for (int j = 0; j < K - 1; ++j)
+      for (int64_t c = 0; c < C; ++c)
+        win[j * C + c] = rs >= 0 ? pool[rs * slot_len + j * C + c] : 0.0;
+    for (int64_t c = 0; c < C; ++c) {
+      double x;
+      if (c < cq) x = q_raw[r * cq + c];
+      else if (c < 2 * cq) x = k_raw[r * cq + (c - cq)];
+      else x = v_raw[r * cv + (c - 2 * cq)];
+      win[(int64_t)(K - 1) * C + c] = x;
+    }
+    /* conv over the window + SiLU, channel by channel */
+    for (int64_t c = 0; c < C; ++c) {
+      const double *w;
+      double *y;
+      if (c < cq) { w = wq + c * K; y = q_out + r * cq + c; }
+      else if (c < 2 * cq) { w = wk + (c - cq) * K; y = k_out + r * cq + (c - cq); }
+      else { w = wv + (c - 2 * cq) * K; y = v_out + r * cv + (c - 2 * cq); }
+      double s = 0.0;
+      for (int j = 0; j < K; ++j) s += w[j] * win[(int64_t)j * C + c];
+      *y = s * sigmoid(s);
+    }
+    /* q and k to unit L2 norm per head; the gates */
+    for (int h = 0; h < Hqk; ++h) {
+      double *yq = q_out + r * cq + (int64_t)h * dk, *yk = k_out + r * cq + (int64_t)h * dk;
+      double sq = 0.0, sk = 0.0;
+      for (int i = 0; i < dk; ++i) { sq += yq[i] * yq[i]; sk += yk[i] * yk[i]; }
+      double nq = sqrt(sq + eps), nk = sqrt(sk + eps);
+      for (int i = 0; i < dk; ++i) { yq[i] /= nq; yk[i] /= nk; }
+    }
+    for (int h = 0; h < Hv; ++h) {
+      g_out[r * Hv + h] = -softplus(a_raw[r * Hv + h]);
+      beta_out[r * Hv + h] = sigmoid(b_raw[r * Hv + h]);
+    }
+    /* the window slides by one token into the write slot */
+    if (ws >= 0)
+      for (int j = 0; j < K - 1; ++j)
+        for (int64_t c = 0; c < C; ++c) pool[ws * slot_len + j * C + c] = win[(int64_t)(j + 1) * C + c];
+  }
+  free(win);
+  return bad;
 }
