@@ -9,7 +9,8 @@ synthetic tensors already resident in HBM.
 
 Prints ONE JSON line: tokens/s, state GB/s and the fraction of HBM peak for
 the decode kernel, the CPU oracle timed on a bounded sample of the same
-workload, and (when built) chunked-prefill tokens/s.
+workload, the decode-side conv front-end (alone and ahead of each layer's
+decode), chunked-prefill tokens/s and the mixed launch.
 """
 from __future__ import annotations
 
@@ -127,6 +128,86 @@ def run_decode(args, torch, gdn, syn):
                total_GBps=L * per_launch / (ms_step / 1e3) / 1e9,
                avg_launch_us=launch_s * 1e6, bytes_per_launch=per_launch)
     return res, layers
+
+
+def conv_bytes_per_launch(B, H_qk, H_v, d_k, d_v, act_bytes=2):
+    """Algorithmic bytes of one conv-decode launch: per request the raw row in,
+    the q|k|v row out, the 3-token window read and written; a/b in, g/beta
+    out; the conv taps (FP32, 4 per channel) once."""
+    C = 2 * H_qk * d_k + H_v * d_v
+    return B * C * act_bytes * (1 + 1 + 3 + 3) + B * H_v * 4 * 4 + C * 4 * 4
+
+
+def run_conv(args, torch, gdn, syn, layers):
+    """The decode-side front-end for the same 48-layer B=512 batch: one
+    gdn_conv_decode launch per layer (a 512-slot BF16 conv pool per layer, the
+    layer's state slots), writing the q, k, v, g, beta that the layer's
+    gdn_decode reads.  Times the conv launches alone and the full decode step
+    (conv then decode, per layer), each captured in one HIP graph."""
+    wl = syn.WORKLOADS["decode_b512_x48"]
+    B, Hqk, Hv, dk, dv, n = wl["B"], wl["H_qk"], wl["H_v"], wl["d_k"], wl["d_v"], wl["n_slots"]
+    C = 2 * Hqk * dk + Hv * dv
+    convs = []
+    for l, (da, keep) in enumerate(layers):
+        q, k, v, g, beta, pool, rs, ws = keep[:8]
+        x = {kk: vv.cuda() for kk, vv in syn.frontend_inputs(wl["index"], 100 + l, B, Hqk, Hv,
+                                                             dk, dv, 4).items()}
+        cpool = syn.conv_pool(wl["index"], l, n, C, 4, torch.bfloat16, on_device=True)
+        ca, ckeep = gdn.make_conv_args(x["q_raw"], x["k_raw"], x["v_raw"], cpool, H_qk=Hqk,
+                                       H_v=Hv, read_slot=rs, write_slot=ws, a_raw=x["a_raw"],
+                                       b_raw=x["b_raw"], conv_wq=x["conv_wq"],
+                                       conv_wk=x["conv_wk"], conv_wv=x["conv_wv"],
+                                       outputs=(q, k, v, g, beta))
+        convs.append((ca, ckeep, da))
+    torch.cuda.synchronize()
+    lib = gdn.load_library()
+
+    def conv_only():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for ca, _, _ in convs:
+            code = lib.gdn_conv_decode(ctypes.byref(ca), s)
+            if code:
+                raise gdn.GdnError("gdn_conv_decode", code)
+
+    def conv_then_decode():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for ca, _, da in convs:
+            code = lib.gdn_conv_decode(ctypes.byref(ca), s) or lib.gdn_decode(ctypes.byref(da), s)
+            if code:
+                raise gdn.GdnError("conv + decode", code)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        run = fn
+        if not args.no_graph:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            torch.cuda.synchronize()
+            run = graph.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_conv = timed(conv_only)
+    ms_step = timed(conv_then_decode)
+    L = len(convs)
+    per_launch = conv_bytes_per_launch(B, Hqk, Hv, dk, dv)
+    us = ms_conv * 1e3 / L
+    gbps = per_launch / (us / 1e6) / 1e9
+    return dict(workload="decode_b512_x48 front-end", kernel="conv_decode_kernel<bf16, 128>",
+                avg_launch_us=round(us, 2), per_launch_bytes=per_launch,
+                algorithmic_GBps=round(gbps, 1), hbm_frac=round(gbps / HBM_PEAK_GBPS, 4),
+                decode_with_conv_ms_per_step=round(ms_step, 4),
+                decode_with_conv_tokens_per_s=round(B / (ms_step / 1e3), 1))
 
 
 def prefill_useful_flops(lengths, H_v, d_k, d_v, C=64):
@@ -314,6 +395,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of a HIP graph")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
+    ap.add_argument("--no-conv", action="store_true",
+                    help="skip the decode-side conv (front-end) measurement")
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=10,
                     help="untimed calls before the prefill and mixed timings")
@@ -358,6 +441,10 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = run_cpu_baseline(args, torch, layers, syn)
+    conv = None
+    if not args.no_conv:
+        conv = run_conv(args, torch, gdn, syn, layers)
+        log(f"conv: {conv}")
     prefill = None
     if not args.no_prefill:
         del layers[:]
@@ -391,6 +478,7 @@ def main():
         "hbm_frac": round(dec["total_GBps"] / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "conv_decode": conv,
         "prefill": prefill,
         "mixed": mixed,
     }

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 2
+#define GDN_ABI_VERSION 3
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -180,6 +180,49 @@ typedef struct gdn_prefill_args {
   int32_t reserved1;   /* must be 0 */
 } gdn_prefill_args;
 
+/* The front-end's conv window across calls.  The short conv is part of the
+ * layer ("Gated DeltaNet" glossary entry, Engineering details), so a decode
+ * token's conv window holds the raw inputs of the conv_k - 1 tokens before
+ * it.  They live per request in a conv-state slot of conv_pool, laid out
+ * [n_slots, conv_k - 1, C] in act_dtype with C = 2 * H_qk * d_k + H_v * d_v
+ * channels in q|k|v order, the oldest token first; slots follow the
+ * recurrent state's read/write rules ("Recurrent state" glossary entry, Why
+ * it matters).  gdn_conv_decode runs the front-end for one token per request
+ * and slides the window; gdn_conv_store fills slots from prefilled
+ * sequences.  A prefill itself starts from an empty window. */
+typedef struct gdn_conv_args {
+  int32_t B;           /* requests (gdn_conv_decode) or sequences (gdn_conv_store), >= 0 */
+  int32_t H_qk, H_v, d_k, d_v;
+  int32_t act_dtype;   /* gdn_dtype of the raw inputs, q_out/k_out/v_out and conv_pool */
+  int32_t conv_k;      /* conv width; 4 */
+  int32_t reserved0;   /* must be 0 */
+  int64_t n_slots;     /* conv_pool capacity in slots */
+  int64_t n_tokens;    /* gdn_conv_store: rows of q/k/v (= cu_seqlens[B]); ignored by decode */
+  float eps;           /* L2-norm epsilon (decode), e.g. 1e-6 */
+  int32_t reserved1;   /* must be 0 */
+  const void *q;       /* raw [B or n_tokens, H_qk * d_k] act_dtype */
+  const void *k;       /* raw [B or n_tokens, H_qk * d_k] act_dtype */
+  const void *v;       /* raw [B or n_tokens, H_v * d_v] act_dtype */
+  const float *a_raw;  /* decode: [B, H_v], g = -softplus(a_raw) */
+  const float *b_raw;  /* decode: [B, H_v], beta = sigmoid(b_raw) */
+  const float *conv_wq;  /* decode: [H_qk * d_k, conv_k] taps (tap j multiplies x[t-conv_k+1+j]) */
+  const float *conv_wk;  /* decode: [H_qk * d_k, conv_k] */
+  const float *conv_wv;  /* decode: [H_v * d_v, conv_k] */
+  void *conv_pool;     /* [n_slots, conv_k - 1, C] act_dtype, read and written in place */
+  const int32_t *read_slot;  /* decode: [B] or NULL (-1 = empty window, a fresh request) */
+  const int32_t *write_slot; /* [B] or NULL (-1 = not stored) */
+  const int32_t *cu_seqlens; /* store: [B + 1] device offsets into q/k/v; a sequence with
+                                cu[s] < 0, cu[s+1] < cu[s] or cu[s+1] > n_tokens is skipped
+                                and sets GDN_DEVICE_BAD_SEQ */
+  void *q_out;         /* decode: [B, H_qk, d_k] act_dtype, unit L2 norm per head */
+  void *k_out;         /* decode: [B, H_qk, d_k] act_dtype */
+  void *v_out;         /* decode: [B, H_v, d_v] act_dtype */
+  float *g_out;        /* decode: [B, H_v] */
+  float *beta_out;     /* decode: [B, H_v] */
+  uint32_t *status;    /* optional device word; slot indices outside [-1, n_slots) skip the
+                          request and set GDN_DEVICE_BAD_SLOT */
+} gdn_conv_args;
+
 /* Bytes of one slot (all H_v heads of one request, one layer).  The ONNX
  * LinearAttention section of "Seven Architectures ..." sizes 64 heads of
  * 128 x 128 at 16 bits as 2 MB per request. */
@@ -204,6 +247,22 @@ gdn_status gdn_decode(const gdn_decode_args *args, void *stream);
  * act_dtype; g_out, beta_out [n_tokens, H_v] FP32.  No recurrence is run. */
 gdn_status gdn_frontend(const gdn_prefill_args *args, void *q_out, void *k_out, void *v_out,
                         float *g_out, float *beta_out, void *stream);
+
+/* The front-end for one decode token per request (the same conv + SiLU,
+ * L2 norm and gates as gdn_frontend, bitwise equal for the same window):
+ * the window is the read slot's conv_k - 1 raw tokens and this token; the
+ * window slid by one token (the last conv_k - 1 raw inputs) is stored into
+ * the write slot.  The outputs feed gdn_decode. */
+gdn_status gdn_conv_decode(const gdn_conv_args *args, void *stream);
+
+/* After a prefill of B sequences packed by cu_seqlens: store each sequence's
+ * last conv_k - 1 raw inputs (zeros before its first token) into
+ * conv_pool[write_slot[s]], so that decode continues its conv window. */
+gdn_status gdn_conv_store(const gdn_conv_args *args, void *stream);
+
+/* Bytes of one conv-state slot. */
+size_t gdn_conv_slot_bytes(int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v, int32_t conv_k,
+                           int32_t act_dtype);
 
 /* Chunked prefill: initial state from read_slot[s], outputs for every token,
  * final state (FP32 across chunks, rounded once when stored as BF16) into
@@ -231,6 +290,7 @@ int32_t gdn_abi_version(void);
  * binding can check its own layout */
 size_t gdn_sizeof_decode_args(void);
 size_t gdn_sizeof_prefill_args(void);
+size_t gdn_sizeof_conv_args(void);
 
 #ifdef __cplusplus
 }

@@ -5,7 +5,8 @@ The compute lives in the HIP library ``libgdn.so`` (C ABI: include/gdn.h);
 Importing the package loads nothing; the first binding call loads the
 library and raises if it has not been built.
 """
-from .gdn import (DecodeArgs, GdnError, PrefillArgs, gdn_abi_version, gdn_decode,  # noqa: F401
+from .gdn import (ConvArgs, DecodeArgs, GdnError, PrefillArgs, gdn_abi_version,  # noqa: F401
+                  gdn_conv_decode, gdn_conv_slot_bytes, gdn_conv_store, gdn_decode,
                   gdn_frontend, gdn_mixed, gdn_parse_rule, gdn_prefill, gdn_state_bytes,
-                  gdn_status_string, gdn_validate_slots, load_library, make_decode_args,
-                  make_prefill_args)
+                  gdn_status_string, gdn_validate_slots, load_library, make_conv_args,
+                  make_decode_args, make_prefill_args)

@@ -90,6 +90,38 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
   return GDN_OK;
 }
 
+// decode: the conv step for B requests; otherwise the store after a prefill
+gdn_status check_conv(const gdn_conv_args *a, bool decode) {
+  if (!a) return GDN_ERR_NULL;
+  if (a->B < 0 || a->n_slots < 0 || a->n_tokens < 0) return GDN_ERR_SHAPE;
+  if (!valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
+  if (a->reserved0 != 0 || a->reserved1 != 0) return GDN_ERR_UNSUPPORTED;
+  if (a->H_qk <= 0 || a->H_v <= 0 || a->d_k <= 0 || a->d_v <= 0) return GDN_ERR_SHAPE;
+  if (!supported_d(a->d_k) || !supported_d(a->d_v)) return GDN_ERR_UNSUPPORTED;
+  if (a->conv_k != 4) return GDN_ERR_UNSUPPORTED;
+  if (decode && !(a->eps >= 0.0f)) return GDN_ERR_SHAPE;
+  if (gdn::conv_grid_rows(*a) > 65535) return GDN_ERR_UNSUPPORTED;  // grid size
+  if (!decode && a->n_tokens > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;
+  if (a->B == 0) return !decode && a->n_tokens != 0 ? GDN_ERR_SHAPE : GDN_OK;
+  if (!a->write_slot && a->n_slots < a->B) return GDN_ERR_SHAPE;
+  if (decode && !a->read_slot && a->n_slots < a->B) return GDN_ERR_SHAPE;
+  if (!a->conv_pool) return GDN_ERR_NULL;
+  if (!al16(a->conv_pool)) return GDN_ERR_ALIGN;
+  if (decode) {
+    if (!a->q || !a->k || !a->v || !a->a_raw || !a->b_raw) return GDN_ERR_NULL;
+    if (!a->conv_wq || !a->conv_wk || !a->conv_wv) return GDN_ERR_NULL;
+    if (!a->q_out || !a->k_out || !a->v_out || !a->g_out || !a->beta_out) return GDN_ERR_NULL;
+    if (!al16(a->conv_wq) || !al16(a->conv_wk) || !al16(a->conv_wv) || !al16(a->q_out) ||
+        !al16(a->k_out) || !al16(a->v_out))
+      return GDN_ERR_ALIGN;
+  } else {
+    if (!a->cu_seqlens) return GDN_ERR_NULL;
+    if (a->n_tokens > 0 && (!a->q || !a->k || !a->v)) return GDN_ERR_NULL;
+  }
+  if (!al16(a->q) || !al16(a->k) || !al16(a->v)) return GDN_ERR_ALIGN;
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +161,26 @@ gdn_status gdn_frontend(const gdn_prefill_args *args, void *q_out, void *k_out, 
   if (!args->a_raw || !args->b_raw) return GDN_ERR_NULL;
   return gdn::launch_frontend(*args, q_out, k_out, v_out, g_out, beta_out,
                               static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_conv_decode(const gdn_conv_args *args, void *stream) {
+  gdn_status st = check_conv(args, true);
+  if (st != GDN_OK || args->B == 0) return st;
+  return gdn::launch_conv_decode(*args, static_cast<hipStream_t>(stream));
+}
+
+gdn_status gdn_conv_store(const gdn_conv_args *args, void *stream) {
+  gdn_status st = check_conv(args, false);
+  if (st != GDN_OK || args->B == 0) return st;
+  return gdn::launch_conv_store(*args, static_cast<hipStream_t>(stream));
+}
+
+size_t gdn_conv_slot_bytes(int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v, int32_t conv_k,
+                           int32_t act_dtype) {
+  if (H_qk <= 0 || H_v <= 0 || d_k <= 0 || d_v <= 0 || conv_k < 1 || !valid_dtype(act_dtype))
+    return 0;
+  const size_t C = 2 * (size_t)H_qk * (size_t)d_k + (size_t)H_v * (size_t)d_v;
+  return (size_t)(conv_k - 1) * C * (act_dtype == GDN_BF16 ? 2u : 4u);
 }
 
 gdn_status gdn_prefill(const gdn_prefill_args *args, void *stream) {
@@ -191,5 +243,6 @@ const char *gdn_status_string(int32_t status) {
 int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
 size_t gdn_sizeof_decode_args(void) { return sizeof(gdn_decode_args); }
 size_t gdn_sizeof_prefill_args(void) { return sizeof(gdn_prefill_args); }
+size_t gdn_sizeof_conv_args(void) { return sizeof(gdn_conv_args); }
 
 }  // extern "C"

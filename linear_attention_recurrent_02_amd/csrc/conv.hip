@@ -1,0 +1,208 @@
+// conv.hip -- the front-end's conv window across calls.
+//
+// The short conv is part of a GDN layer ("Gated DeltaNet" glossary,
+// Engineering details), so a decode token's window holds the raw inputs of
+// the three tokens before it.  Those live per request in a conv-state slot
+// ([3, C] raw values, oldest first, C = 2*H_qk*d_k + H_v*d_v channels in
+// q|k|v order) with the recurrent state's read/write slot rules ("Recurrent
+// state" glossary, Why it matters: a checkpoint read slot may differ from the
+// live write slot).
+//
+//  - conv_decode_kernel: one token per request -- window = slot history +
+//    this token, conv + SiLU (+ L2 norm for q, k), gates, and the window slid
+//    by one token into the write slot.  The arithmetic is frontend.cuh's, so
+//    the outputs are bitwise those of the prefill front-end for the same
+//    token and window.
+//  - conv_store_kernel: the window a prefilled sequence leaves behind (its
+//    last three raw inputs, zeros before its first token) into a slot.
+//
+// HBM-bound and tiny next to the recurrent state (48 KiB of window per
+// request against 1 MiB of state at 32 heads of 128 x 128 BF16): one thread
+// per 16-byte piece of a row (8 BF16 or 4 FP32 channels), blockIdx.x = the
+// request, blockIdx.y = a 256-piece span of its row, so every load and store
+// is contiguous across lanes.  A head's pieces are neighbouring lanes, so its
+// L2 norm is frontend.cuh's DPP butterfly.
+#include <algorithm>
+
+#include "device.h"
+#include "frontend.cuh"
+#include "internal.h"
+
+namespace gdn {
+
+constexpr int kConvThreads = 256;
+constexpr int kConvHist = 3;  // raw tokens a window keeps (conv width 4)
+
+struct ConvParams {
+  int32_t n;          // requests (decode) or sequences (store)
+  int32_t H_v;
+  int32_t pq, pv;     // 16-byte pieces per row of q (= of k) and of v
+  int64_t n_slots;
+  int64_t n_tokens;   // store: rows of the raw inputs
+  float eps;
+  const char *q, *k, *v;
+  const float *wq, *wk, *wv;  // [channels, 4]
+  const float *a_raw, *b_raw;
+  char *pool;         // [n_slots, 3, C] in the input dtype
+  const int32_t *read_slot, *write_slot, *cu;
+  char *q_out, *k_out, *v_out;
+  float *g_out, *beta_out;
+  uint32_t *status;
+};
+
+// which of q, k, v a piece of the concatenated row belongs to, and where
+struct PieceOf {
+  int region;      // 0 q, 1 k, 2 v
+  int local;       // piece index inside that tensor's row
+  int64_t row_b;   // bytes per row of that tensor
+};
+
+__device__ __forceinline__ PieceOf piece_of(const ConvParams &p, int piece) {
+  PieceOf r;
+  if (piece < p.pq) { r.region = 0; r.local = piece; r.row_b = (int64_t)p.pq * 16; }
+  else if (piece < 2 * p.pq) { r.region = 1; r.local = piece - p.pq; r.row_b = (int64_t)p.pq * 16; }
+  else { r.region = 2; r.local = piece - 2 * p.pq; r.row_b = (int64_t)p.pv * 16; }
+  return r;
+}
+
+template <bool AB, int DK>
+__global__ __launch_bounds__(kConvThreads) void conv_decode_kernel(ConvParams p) {
+  using E = Elem<AB>;
+  constexpr int CH = E::kPer16B;
+  constexpr int PPH = DK / CH;  // pieces per q/k head: a power of two, at most 32
+  const int r = blockIdx.x;
+  const int P = 2 * p.pq + p.pv;
+  const int64_t rs = p.read_slot ? p.read_slot[r] : r;
+  const int64_t ws = p.write_slot ? p.write_slot[r] : r;
+  if (rs < -1 || rs >= p.n_slots || ws < -1 || ws >= p.n_slots) {
+    if (blockIdx.y == 0 && threadIdx.x == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+    return;
+  }
+  if (blockIdx.y == 0)
+    for (int h = threadIdx.x; h < p.H_v; h += kConvThreads) {
+      const int64_t gi = (int64_t)r * p.H_v + h;
+      p.g_out[gi] = gate_g(p.a_raw[gi]);
+      p.beta_out[gi] = gate_beta(p.b_raw[gi]);
+    }
+  const int piece = blockIdx.y * kConvThreads + threadIdx.x;
+  // pieces past the row end are whole heads of v or nothing (q and k end on a head boundary)
+  if (piece >= P) return;
+  const PieceOf at = piece_of(p, piece);
+  const char *raw = at.region == 0 ? p.q : at.region == 1 ? p.k : p.v;
+  const float *wt = at.region == 0 ? p.wq : at.region == 1 ? p.wk : p.wv;
+  char *out = at.region == 0 ? p.q_out : at.region == 1 ? p.k_out : p.v_out;
+
+  const int64_t slot_b = (int64_t)kConvHist * P * 16;
+  const uint4 x0 = nt_load16(raw + r * at.row_b + (int64_t)at.local * 16);
+  uint4 h[kConvHist];  // h[0] = token t-3 ... h[2] = token t-1
+#pragma unroll
+  for (int j = 0; j < kConvHist; ++j)
+    h[j] = rs >= 0 ? nt_load16(p.pool + rs * slot_b + ((int64_t)j * P + piece) * 16)
+                   : make_uint4(0, 0, 0, 0);
+  float4 w[CH];
+  const float4 *wsrc = reinterpret_cast<const float4 *>(wt) + (int64_t)at.local * CH;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) w[c] = wsrc[c];
+
+  float f0[CH], f1[CH], f2[CH], f3[CH], y[CH];
+  E::unpack(x0, f0); E::unpack(h[2], f1); E::unpack(h[1], f2); E::unpack(h[0], f3);
+#pragma unroll
+  for (int c = 0; c < CH; ++c) y[c] = conv4_silu(w[c], f3[c], f2[c], f1[c], f0[c]);
+  // a head's lanes are all q, all k or all v (regions start on head boundaries)
+  if (at.region < 2) l2_scale<PPH>(y, p.eps);
+  nt_store16(out + r * at.row_b + (int64_t)at.local * 16, E::pack(y));
+
+  // slide the window into the write slot (raw values, copied bit for bit); a
+  // slot read and written by the same request is safe: each lane reads its
+  // own pieces before it stores them
+  if (ws >= 0) {
+    char *dst = p.pool + ws * slot_b + (int64_t)piece * 16;
+    nt_store16(dst, h[1]);
+    nt_store16(dst + (int64_t)P * 16, h[2]);
+    nt_store16(dst + (int64_t)2 * P * 16, x0);
+  }
+}
+
+__global__ __launch_bounds__(kConvThreads) void conv_store_kernel(ConvParams p) {
+  const int s = blockIdx.x;
+  const int P = 2 * p.pq + p.pv;
+  const int64_t t0 = p.cu[s], t1 = p.cu[s + 1];
+  if (t0 < 0 || t1 < t0 || t1 > p.n_tokens) {
+    if (blockIdx.y == 0 && threadIdx.x == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SEQ);
+    return;
+  }
+  const int64_t ws = p.write_slot ? p.write_slot[s] : s;
+  if (ws < -1 || ws >= p.n_slots) {
+    if (blockIdx.y == 0 && threadIdx.x == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+    return;
+  }
+  const int piece = blockIdx.y * kConvThreads + threadIdx.x;
+  if (ws < 0 || piece >= P) return;
+  const PieceOf at = piece_of(p, piece);
+  const char *raw = (at.region == 0 ? p.q : at.region == 1 ? p.k : p.v) + (int64_t)at.local * 16;
+  char *dst = p.pool + ws * (int64_t)kConvHist * P * 16 + (int64_t)piece * 16;
+#pragma unroll
+  for (int j = 0; j < kConvHist; ++j) {
+    const int64_t t = t1 - kConvHist + j;
+    const uint4 x = t >= t0 ? nt_load16(raw + t * at.row_b) : make_uint4(0, 0, 0, 0);
+    nt_store16(dst + (int64_t)j * P * 16, x);
+  }
+}
+
+static ConvParams make_conv_params(const gdn_conv_args &a) {
+  const int per = a.act_dtype == GDN_BF16 ? 8 : 4;
+  ConvParams p;
+  p.n = a.B; p.H_v = a.H_v;
+  p.pq = a.H_qk * a.d_k / per; p.pv = a.H_v * a.d_v / per;
+  p.n_slots = a.n_slots; p.n_tokens = a.n_tokens; p.eps = a.eps;
+  p.q = static_cast<const char *>(a.q); p.k = static_cast<const char *>(a.k);
+  p.v = static_cast<const char *>(a.v);
+  p.wq = a.conv_wq; p.wk = a.conv_wk; p.wv = a.conv_wv;
+  p.a_raw = a.a_raw; p.b_raw = a.b_raw;
+  p.pool = static_cast<char *>(a.conv_pool);
+  p.read_slot = a.read_slot; p.write_slot = a.write_slot; p.cu = a.cu_seqlens;
+  p.q_out = static_cast<char *>(a.q_out); p.k_out = static_cast<char *>(a.k_out);
+  p.v_out = static_cast<char *>(a.v_out);
+  p.g_out = a.g_out; p.beta_out = a.beta_out; p.status = a.status;
+  return p;
+}
+
+// the grid: one column per request / sequence, ceil(pieces / 256) rows
+static dim3 conv_grid(const ConvParams &p) {
+  const int P = 2 * p.pq + p.pv;
+  return dim3((unsigned)p.n, (unsigned)((P + kConvThreads - 1) / kConvThreads));
+}
+
+int64_t conv_grid_rows(const gdn_conv_args &a) {
+  const int per = a.act_dtype == GDN_BF16 ? 8 : 4;
+  const int64_t P = (2 * (int64_t)a.H_qk * a.d_k + (int64_t)a.H_v * a.d_v) / per;
+  return (P + kConvThreads - 1) / kConvThreads;
+}
+
+gdn_status launch_conv_decode(const gdn_conv_args &a, hipStream_t s) {
+  const ConvParams p = make_conv_params(a);
+  const dim3 grid = conv_grid(p);
+  const bool ab = a.act_dtype == GDN_BF16;
+#define GDN_CONV_CASE(AB_, DK_) \
+  hipLaunchKernelGGL((conv_decode_kernel<AB_, DK_>), grid, dim3(kConvThreads), 0, s, p)
+#define GDN_CONV_DK(AB_)                          \
+  switch (a.d_k) {                                \
+    case 16: GDN_CONV_CASE(AB_, 16); break;       \
+    case 32: GDN_CONV_CASE(AB_, 32); break;       \
+    case 64: GDN_CONV_CASE(AB_, 64); break;       \
+    case 128: GDN_CONV_CASE(AB_, 128); break;     \
+    default: return GDN_ERR_UNSUPPORTED;          \
+  }
+  if (ab) { GDN_CONV_DK(true) } else { GDN_CONV_DK(false) }
+#undef GDN_CONV_DK
+#undef GDN_CONV_CASE
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+gdn_status launch_conv_store(const gdn_conv_args &a, hipStream_t s) {
+  const ConvParams p = make_conv_params(a);
+  hipLaunchKernelGGL(conv_store_kernel, conv_grid(p), dim3(kConvThreads), 0, s, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+}  // namespace gdn

@@ -24,6 +24,7 @@
 #include <type_traits>
 
 #include "device.h"
+#include "frontend.cuh"
 #include "internal.h"
 
 namespace gdn {
@@ -83,30 +84,6 @@ __device__ __forceinline__ int64_t ordered_after(float (&x)[CH], int64_t v) {
 #pragma unroll
   for (int c = 0; c < CH; ++c) asm volatile("" : "+v"(x[c]), "+v"(v));
   return v;
-}
-
-// SiLU with the hardware exp and reciprocal: x * 1 / (1 + e^-x)
-__device__ __forceinline__ float silu_fast(float x) {
-  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
-}
-
-// one DPP permutation of a float, every lane reading the lane CTRL selects
-template <int CTRL>
-__device__ __forceinline__ float dpp_perm(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xf, 0xf, false));
-}
-
-// Sum over the N lanes of a head (N a power of two, at most 32), left in all
-// of them: the pairs of an xor butterfly, formed by DPP inside each 16-lane
-// row (quad permutes, then the half-row and row mirrors), a shuffle across rows.
-template <int N>
-__device__ __forceinline__ float head_sum(float x) {
-  if constexpr (N >= 2) x += dpp_perm<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-  if constexpr (N >= 4) x += dpp_perm<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-  if constexpr (N >= 8) x += dpp_perm<0x141>(x);  // row_half_mirror: the other quad
-  if constexpr (N >= 16) x += dpp_perm<0x140>(x); // row_mirror: the other half row
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
-  return x;
 }
 
 template <bool AB, int D, bool NORM, bool GATES>
@@ -185,18 +162,10 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
-      const float acc = fmaf(w[c].x, x3[c], fmaf(w[c].y, x2[c], fmaf(w[c].z, x1[c], w[c].w * x0[c])));
-      y[c] = silu_fast(acc);
+      y[c] = conv4_silu(w[c], x3[c], x2[c], x1[c], x0[c]);
       xw[u & 3][c] = x0[c];
     }
-    if constexpr (NORM) {
-      float ss = 0.f;
-#pragma unroll
-      for (int c = 0; c < CH; ++c) ss = fmaf(y[c], y[c], ss);
-      const float inv = __builtin_amdgcn_rsqf(head_sum<PPH>(ss) + p.eps);  // hardware 1/sqrt
-#pragma unroll
-      for (int c = 0; c < CH; ++c) y[c] *= inv;
-    }
+    if constexpr (NORM) l2_scale<PPH>(y, p.eps);
   };
 
   // whole runs: token t comes from ring slot (t - ts) % kFeDepth, which is
@@ -251,14 +220,8 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
     const int64_t n = (te - ts) * nh;
     for (int64_t i = lane; i < n; i += lpr) {
       const int64_t gi = (ts + i / nh) * p.H_v + h0 + (int)(i % nh);
-      // g = -softplus(a) computed as -(max(a,0) + log1p(exp(-|a|))); beta = sigmoid(b)
-      if (p.a_raw) {
-        const float a = p.a_raw[gi];
-        p.g_out[gi] = -(fmaxf(a, 0.f) + log1pf(expf(-fabsf(a))));
-      } else {
-        p.g_out[gi] = 0.f;
-      }
-      p.beta_out[gi] = p.b_raw ? 1.0f / (1.0f + expf(-p.b_raw[gi])) : 1.0f;
+      p.g_out[gi] = p.a_raw ? gate_g(p.a_raw[gi]) : 0.f;
+      p.beta_out[gi] = p.b_raw ? gate_beta(p.b_raw[gi]) : 1.0f;
     }
   }
 }

@@ -19,6 +19,9 @@ gdn_status launch_frontend(const gdn_prefill_args &a, void *q_out, void *k_out, 
 gdn_status launch_prefill(const gdn_prefill_args &a, hipStream_t stream);
 gdn_status launch_mixed(const gdn_decode_args &d, const gdn_prefill_args &p, hipStream_t stream);
 size_t prefill_workspace_bytes(const gdn_prefill_args &a);
+gdn_status launch_conv_decode(const gdn_conv_args &a, hipStream_t stream);
+gdn_status launch_conv_store(const gdn_conv_args &a, hipStream_t stream);
+int64_t conv_grid_rows(const gdn_conv_args &a);  // blockIdx.y extent of the conv kernels
 
 struct PrefillParams;
 // Kernel parameters of a prefill call; runs the front-end kernel into the

@@ -50,6 +50,17 @@ class PrefillArgs(ctypes.Structure):
                 ("ckpt_per_seq", _I32), ("reserved1", _I32)]
 
 
+class ConvArgs(ctypes.Structure):
+    _fields_ = [("B", _I32), ("H_qk", _I32), ("H_v", _I32), ("d_k", _I32), ("d_v", _I32),
+                ("act_dtype", _I32), ("conv_k", _I32), ("reserved0", _I32),
+                ("n_slots", _I64), ("n_tokens", _I64), ("eps", ctypes.c_float),
+                ("reserved1", _I32), ("q", _P), ("k", _P), ("v", _P), ("a_raw", _P),
+                ("b_raw", _P), ("conv_wq", _P), ("conv_wk", _P), ("conv_wv", _P),
+                ("conv_pool", _P), ("read_slot", _P), ("write_slot", _P), ("cu_seqlens", _P),
+                ("q_out", _P), ("k_out", _P), ("v_out", _P), ("g_out", _P), ("beta_out", _P),
+                ("status", _P)]
+
+
 class GdnError(RuntimeError):
     def __init__(self, fn: str, code: int):
         self.code = code
@@ -82,6 +93,12 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _P]
     lib.gdn_mixed.restype = _I32
     lib.gdn_mixed.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(PrefillArgs), _P]
+    lib.gdn_conv_decode.restype = _I32
+    lib.gdn_conv_decode.argtypes = [ctypes.POINTER(ConvArgs), _P]
+    lib.gdn_conv_store.restype = _I32
+    lib.gdn_conv_store.argtypes = [ctypes.POINTER(ConvArgs), _P]
+    lib.gdn_conv_slot_bytes.restype = ctypes.c_size_t
+    lib.gdn_conv_slot_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32]
     lib.gdn_validate_slots.restype = _I32
     lib.gdn_validate_slots.argtypes = [_P, _P, _I32, _I64]
     lib.gdn_status_string.restype = ctypes.c_char_p
@@ -90,8 +107,10 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_abi_version.argtypes = []
     lib.gdn_sizeof_decode_args.restype = ctypes.c_size_t
     lib.gdn_sizeof_prefill_args.restype = ctypes.c_size_t
+    lib.gdn_sizeof_conv_args.restype = ctypes.c_size_t
     if lib.gdn_sizeof_decode_args() != ctypes.sizeof(DecodeArgs) or \
-            lib.gdn_sizeof_prefill_args() != ctypes.sizeof(PrefillArgs):
+            lib.gdn_sizeof_prefill_args() != ctypes.sizeof(PrefillArgs) or \
+            lib.gdn_sizeof_conv_args() != ctypes.sizeof(ConvArgs):
         raise RuntimeError("libgdn.so argument-struct layout differs from this binding")
     _lib = lib
     return lib
@@ -324,3 +343,82 @@ def gdn_mixed(decode_args: DecodeArgs, prefill_args: PrefillArgs, stream=None):
                                     _stream(stream))
     if code:
         raise GdnError("gdn_mixed", code)
+
+
+def gdn_conv_slot_bytes(H_qk: int, H_v: int, d_k: int, d_v: int, conv_k: int = 4,
+                        act_dtype: int = BF16) -> int:
+    return int(load_library().gdn_conv_slot_bytes(H_qk, H_v, d_k, d_v, conv_k, act_dtype))
+
+
+def make_conv_args(q_raw, k_raw, v_raw, conv_pool, *, H_qk, H_v, read_slot=None, write_slot=None,
+                   cu_seqlens=None, a_raw=None, b_raw=None, conv_wq=None, conv_wk=None,
+                   conv_wv=None, outputs=None, eps=1e-6, status=None):
+    """Build a ConvArgs struct.  Decode (cu_seqlens None): q_raw, k_raw [B,
+    H_qk*d_k], v_raw [B, H_v*d_v]; store: the same over n_tokens rows with
+    cu_seqlens [B+1].  conv_pool: [n_slots, conv_k-1, 2*H_qk*d_k + H_v*d_v].
+    outputs: (q, k, v, g, beta) tensors or None.  Returns (args, keepalive)."""
+    for name, t in (("q_raw", q_raw), ("k_raw", k_raw), ("v_raw", v_raw),
+                    ("conv_pool", conv_pool), ("read_slot", read_slot),
+                    ("write_slot", write_slot), ("cu_seqlens", cu_seqlens), ("a_raw", a_raw),
+                    ("b_raw", b_raw), ("conv_wq", conv_wq), ("conv_wk", conv_wk),
+                    ("conv_wv", conv_wv), ("status", status)):
+        _dev(t, name)
+    rows = q_raw.shape[0]
+    B = rows if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    d_k = q_raw.shape[-1] // H_qk if q_raw.dim() == 2 else q_raw.shape[-1]
+    d_v = v_raw.shape[-1] // H_v if v_raw.dim() == 2 else v_raw.shape[-1]
+    a = ConvArgs()
+    a.B, a.H_qk, a.H_v, a.d_k, a.d_v = B, H_qk, H_v, d_k, d_v
+    a.act_dtype = _dtype_code(q_raw)
+    a.conv_k = conv_pool.shape[1] + 1
+    a.reserved0 = a.reserved1 = 0
+    a.n_slots = conv_pool.shape[0]
+    a.n_tokens = 0 if cu_seqlens is None else rows
+    a.eps = float(eps)
+    a.q, a.k, a.v = _ptr(q_raw), _ptr(k_raw), _ptr(v_raw)
+    a.a_raw, a.b_raw = _ptr(a_raw), _ptr(b_raw)
+    a.conv_wq, a.conv_wk, a.conv_wv = _ptr(conv_wq), _ptr(conv_wk), _ptr(conv_wv)
+    a.conv_pool, a.read_slot, a.write_slot = _ptr(conv_pool), _ptr(read_slot), _ptr(write_slot)
+    a.cu_seqlens, a.status = _ptr(cu_seqlens), _ptr(status)
+    if outputs is not None:
+        for name, t in zip(("q_out", "k_out", "v_out", "g_out", "beta_out"), outputs):
+            setattr(a, name, _ptr(_dev(t, name)))
+    keep = (q_raw, k_raw, v_raw, conv_pool, read_slot, write_slot, cu_seqlens, a_raw, b_raw,
+            conv_wq, conv_wk, conv_wv, outputs, status)
+    return a, keep
+
+
+def gdn_conv_decode(q_raw, k_raw, v_raw, conv_pool, read_slot=None, write_slot=None, *, H_qk,
+                    H_v, conv_wq, conv_wk, conv_wv, a_raw, b_raw, eps=1e-6, status=None,
+                    stream=None):
+    """The front-end for one decode token per request, conv window from
+    conv_pool (updated in place).  Returns (q [B,H_qk,d_k], k, v [B,H_v,d_v],
+    g, beta)."""
+    B = q_raw.shape[0]
+    d_k = q_raw.shape[-1] // H_qk if q_raw.dim() == 2 else q_raw.shape[-1]
+    d_v = v_raw.shape[-1] // H_v if v_raw.dim() == 2 else v_raw.shape[-1]
+    dev = q_raw.device
+    q = torch.empty((B, H_qk, d_k), dtype=q_raw.dtype, device=dev)
+    k = torch.empty_like(q)
+    v = torch.empty((B, H_v, d_v), dtype=v_raw.dtype, device=dev)
+    g = torch.empty((B, H_v), dtype=torch.float32, device=dev)
+    beta = torch.empty_like(g)
+    a, keep = make_conv_args(q_raw, k_raw, v_raw, conv_pool, H_qk=H_qk, H_v=H_v,
+                             read_slot=read_slot, write_slot=write_slot, a_raw=a_raw,
+                             b_raw=b_raw, conv_wq=conv_wq, conv_wk=conv_wk, conv_wv=conv_wv,
+                             outputs=(q, k, v, g, beta), eps=eps, status=status)
+    code = load_library().gdn_conv_decode(ctypes.byref(a), _stream(stream))
+    if code:
+        raise GdnError("gdn_conv_decode", code)
+    return q, k, v, g, beta
+
+
+def gdn_conv_store(cu_seqlens, q_raw, k_raw, v_raw, conv_pool, write_slot=None, *, H_qk, H_v,
+                   status=None, stream=None):
+    """Store each prefilled sequence's last conv_k-1 raw inputs into
+    conv_pool[write_slot[s]]."""
+    a, keep = make_conv_args(q_raw, k_raw, v_raw, conv_pool, H_qk=H_qk, H_v=H_v,
+                             write_slot=write_slot, cu_seqlens=cu_seqlens, status=status)
+    code = load_library().gdn_conv_store(ctypes.byref(a), _stream(stream))
+    if code:
+        raise GdnError("gdn_conv_store", code)

@@ -24,7 +24,7 @@ import numpy as np
 import torch
 
 # stream ids keep independent draws independent
-_S_Q, _S_K, _S_V, _S_G, _S_B, _S_STATE, _S_SLOTS, _S_LEN, _S_W, _S_RAW = range(10)
+_S_Q, _S_K, _S_V, _S_G, _S_B, _S_STATE, _S_SLOTS, _S_LEN, _S_W, _S_RAW, _S_CONV = range(11)
 
 WORKLOADS = {
     # tiny FP32 recurrence: B=1, H=2, d=16, T=32, zero initial state
@@ -151,6 +151,21 @@ def frontend_inputs(wl: int, layer: int, n_tok: int, H_qk: int, H_v: int, d_k: i
     return dict(q_raw=_cast(q, act_dtype), k_raw=_cast(k, act_dtype), v_raw=_cast(v, act_dtype),
                 conv_wq=_cast(wq, f32), conv_wk=_cast(wk, f32), conv_wv=_cast(wv, f32),
                 a_raw=_cast(a_raw, f32), b_raw=_cast(b_raw, f32))
+
+
+def conv_pool(wl: int, layer: int, n_slots: int, channels: int, conv_k: int = 4,
+              act_dtype: torch.dtype = torch.bfloat16, on_device: bool = False) -> torch.Tensor:
+    """A conv-state pool [n_slots, conv_k-1, channels] of raw inputs ~ N(0, 1)
+    in act_dtype: earlier tokens' raw q|k|v rows, as a decode step finds them.
+    ``on_device`` draws on the current CUDA device with a seeded torch
+    generator (for benchmark-sized pools); otherwise a float64 NumPy draw."""
+    shape = (n_slots, conv_k - 1, channels)
+    if on_device:
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(2_000_029 * (int(wl) + 1) + 7907 * int(layer) + 29)
+        return torch.randn(shape, generator=gen, device="cuda", dtype=torch.float32).to(act_dtype)
+    a = rng(wl, layer, _S_CONV).standard_normal(shape)
+    return _cast(a, act_dtype)
 
 
 def mixed_slots(wl: int, n_decode: int, n_prefill: int, n_slots: int, frac: float = 0.25):

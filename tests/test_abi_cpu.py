@@ -27,7 +27,8 @@ def test_struct_layout_matches():
     lib = gdn.load_library()
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
-    assert gdn.gdn_abi_version() == 2
+    assert lib.gdn_sizeof_conv_args() == ctypes.sizeof(B.ConvArgs)
+    assert gdn.gdn_abi_version() == 3
 
 
 def test_state_bytes_against_the_pages():
@@ -176,3 +177,60 @@ def test_validate_slots():
     assert v([0, -2], [1, 2], 2, 8) == SLOTS
     assert v(None, None, 4, 4) == OK
     assert v(None, None, 5, 4) == SLOTS
+
+
+def test_conv_slot_bytes():
+    # three raw tokens of 2*16*128 + 32*128 = 8192 BF16 channels: 48 KiB per request
+    assert gdn.gdn_conv_slot_bytes(16, 32, 128, 128, 4, B.BF16) == 3 * 8192 * 2 == 48 * 1024
+    assert gdn.gdn_conv_slot_bytes(16, 32, 128, 128, 4, B.F32) == 96 * 1024
+    assert gdn.gdn_conv_slot_bytes(0, 32, 128, 128, 4, B.BF16) == 0
+    assert gdn.gdn_conv_slot_bytes(1, 1, 16, 16, 4, 7) == 0
+
+
+def _conv_args(**over):
+    a = B.ConvArgs()
+    a.B, a.H_qk, a.H_v, a.d_k, a.d_v = 4, 2, 4, 64, 64
+    a.act_dtype, a.conv_k, a.n_slots, a.n_tokens, a.eps = B.BF16, 4, 8, 0, 1e-6
+    for f in ("q", "k", "v", "a_raw", "b_raw", "conv_wq", "conv_wk", "conv_wv", "conv_pool",
+              "q_out", "k_out", "v_out", "g_out", "beta_out"):
+        setattr(a, f, FAKE)
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+CONV_BAD = [
+    (dict(B=-1), SHAPE), (dict(n_slots=-1), SHAPE), (dict(act_dtype=5), DTYPE),
+    (dict(reserved0=1), UNSUP), (dict(reserved1=1), UNSUP), (dict(H_qk=0), SHAPE),
+    (dict(d_k=48), UNSUP), (dict(d_v=256), UNSUP), (dict(conv_k=3), UNSUP),
+    (dict(eps=-1.0), SHAPE), (dict(n_slots=3), SHAPE), (dict(conv_pool=None), NULL),
+    (dict(q=None), NULL), (dict(a_raw=None), NULL), (dict(conv_wv=None), NULL),
+    (dict(beta_out=None), NULL), (dict(conv_pool=FAKE + 8), ALIGN), (dict(q_out=FAKE + 4), ALIGN),
+    (dict(conv_wk=FAKE + 4), ALIGN), (dict(H_v=2000000, d_v=128), UNSUP),
+]
+
+
+@pytest.mark.parametrize("over,code", CONV_BAD)
+def test_conv_decode_validation(over, code):
+    a = _conv_args(**over)
+    assert gdn.load_library().gdn_conv_decode(ctypes.byref(a), None) == code
+
+
+def test_conv_store_validation_and_empty():
+    lib = gdn.load_library()
+    a = _conv_args(n_tokens=10, cu_seqlens=None)
+    assert lib.gdn_conv_store(ctypes.byref(a), None) == NULL
+    a = _conv_args(n_tokens=10, cu_seqlens=FAKE, v=None)
+    assert lib.gdn_conv_store(ctypes.byref(a), None) == NULL
+    a = _conv_args(n_tokens=-1, cu_seqlens=FAKE)
+    assert lib.gdn_conv_store(ctypes.byref(a), None) == SHAPE
+    a = _conv_args(n_tokens=1 << 31, cu_seqlens=FAKE)
+    assert lib.gdn_conv_store(ctypes.byref(a), None) == UNSUP
+    # the store needs no decode inputs or outputs
+    a = _conv_args(n_tokens=10, cu_seqlens=FAKE, a_raw=None, conv_wq=None, q_out=None,
+                   n_slots=2, write_slot=None)
+    assert lib.gdn_conv_store(ctypes.byref(a), None) == SHAPE   # NULL write_slot needs B slots
+    # empty batches launch nothing
+    assert lib.gdn_conv_decode(ctypes.byref(_conv_args(B=0, q=None, conv_pool=None)), None) == OK
+    assert lib.gdn_conv_store(ctypes.byref(_conv_args(B=0, cu_seqlens=None)), None) == OK
+    assert lib.gdn_conv_store(ctypes.byref(_conv_args(B=0, n_tokens=5)), None) == SHAPE
