@@ -19,8 +19,8 @@
 // HBM-bound and tiny next to the recurrent state (48 KiB of window per
 // request against 1 MiB of state at 32 heads of 128 x 128 BF16): one thread
 // per 16-byte piece of a row (8 BF16 or 4 FP32 channels), blockIdx.x = the
-// request, blockIdx.y = a 256-piece span of its row, so every load and store
-// is contiguous across lanes.  A head's pieces are neighbouring lanes, so its
+// group of requests, blockIdx.y = a 256-piece span of the row, so every load
+// and store is contiguous across lanes.  A head's pieces are neighbouring lanes, so its
 // L2 norm is frontend.cuh's DPP butterfly.
 #include <algorithm>
 
@@ -65,25 +65,48 @@ __device__ __forceinline__ PieceOf piece_of(const ConvParams &p, int piece) {
   return r;
 }
 
-template <bool AB, int DK>
+// requests per workgroup of the decode step: each lane loads its conv taps
+// once and keeps the loads of all RB requests in flight together (at B = 512,
+// H_qk = 16, H_v = 32, d = 128: 21.1 us per launch with one request, 16.7 with
+// two or four, 21.1 with eight, which leaves too few workgroups)
+#ifndef GDN_CONV_REQS
+#define GDN_CONV_REQS 2
+#endif
+constexpr int kConvReqs = GDN_CONV_REQS;
+
+template <bool AB, int DK, int RB>
 __global__ __launch_bounds__(kConvThreads) void conv_decode_kernel(ConvParams p) {
   using E = Elem<AB>;
   constexpr int CH = E::kPer16B;
   constexpr int PPH = DK / CH;  // pieces per q/k head: a power of two, at most 32
-  const int r = blockIdx.x;
   const int P = 2 * p.pq + p.pv;
-  const int64_t rs = p.read_slot ? p.read_slot[r] : r;
-  const int64_t ws = p.write_slot ? p.write_slot[r] : r;
-  if (rs < -1 || rs >= p.n_slots || ws < -1 || ws >= p.n_slots) {
-    if (blockIdx.y == 0 && threadIdx.x == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
-    return;
+  const int r0 = blockIdx.x * RB;
+  // per request: its slots, or skipped (past the batch end, or a slot out of range)
+  int64_t rs[RB], ws[RB];
+  bool live[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i) {
+    const int r = r0 + i;
+    live[i] = r < p.n;
+    rs[i] = ws[i] = -1;
+    if (live[i]) {
+      rs[i] = p.read_slot ? p.read_slot[r] : r;
+      ws[i] = p.write_slot ? p.write_slot[r] : r;
+      if (rs[i] < -1 || rs[i] >= p.n_slots || ws[i] < -1 || ws[i] >= p.n_slots) {
+        live[i] = false;
+        if (blockIdx.y == 0 && threadIdx.x == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+      }
+    }
   }
   if (blockIdx.y == 0)
-    for (int h = threadIdx.x; h < p.H_v; h += kConvThreads) {
-      const int64_t gi = (int64_t)r * p.H_v + h;
-      p.g_out[gi] = gate_g(p.a_raw[gi]);
-      p.beta_out[gi] = gate_beta(p.b_raw[gi]);
-    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+      if (live[i])
+        for (int h = threadIdx.x; h < p.H_v; h += kConvThreads) {
+          const int64_t gi = (int64_t)(r0 + i) * p.H_v + h;
+          p.g_out[gi] = gate_g(p.a_raw[gi]);
+          p.beta_out[gi] = gate_beta(p.b_raw[gi]);
+        }
   const int piece = blockIdx.y * kConvThreads + threadIdx.x;
   // pieces past the row end are whole heads of v or nothing (q and k end on a head boundary)
   if (piece >= P) return;
@@ -91,35 +114,47 @@ __global__ __launch_bounds__(kConvThreads) void conv_decode_kernel(ConvParams p)
   const char *raw = at.region == 0 ? p.q : at.region == 1 ? p.k : p.v;
   const float *wt = at.region == 0 ? p.wq : at.region == 1 ? p.wk : p.wv;
   char *out = at.region == 0 ? p.q_out : at.region == 1 ? p.k_out : p.v_out;
-
   const int64_t slot_b = (int64_t)kConvHist * P * 16;
-  const uint4 x0 = nt_load16(raw + r * at.row_b + (int64_t)at.local * 16);
-  uint4 h[kConvHist];  // h[0] = token t-3 ... h[2] = token t-1
+
+  // every load of the RB requests first: the raw piece and the window (h[.][0] = token t-3)
+  uint4 x0[RB], h[RB][kConvHist];
 #pragma unroll
-  for (int j = 0; j < kConvHist; ++j)
-    h[j] = rs >= 0 ? nt_load16(p.pool + rs * slot_b + ((int64_t)j * P + piece) * 16)
-                   : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < RB; ++i) {
+    x0[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < kConvHist; ++j) h[i][j] = make_uint4(0, 0, 0, 0);
+    if (live[i]) {
+      x0[i] = nt_load16(raw + (int64_t)(r0 + i) * at.row_b + (int64_t)at.local * 16);
+      if (rs[i] >= 0)
+#pragma unroll
+        for (int j = 0; j < kConvHist; ++j)
+          h[i][j] = nt_load16(p.pool + rs[i] * slot_b + ((int64_t)j * P + piece) * 16);
+    }
+  }
   float4 w[CH];
   const float4 *wsrc = reinterpret_cast<const float4 *>(wt) + (int64_t)at.local * CH;
 #pragma unroll
   for (int c = 0; c < CH; ++c) w[c] = wsrc[c];
 
-  float f0[CH], f1[CH], f2[CH], f3[CH], y[CH];
-  E::unpack(x0, f0); E::unpack(h[2], f1); E::unpack(h[1], f2); E::unpack(h[0], f3);
 #pragma unroll
-  for (int c = 0; c < CH; ++c) y[c] = conv4_silu(w[c], f3[c], f2[c], f1[c], f0[c]);
-  // a head's lanes are all q, all k or all v (regions start on head boundaries)
-  if (at.region < 2) l2_scale<PPH>(y, p.eps);
-  nt_store16(out + r * at.row_b + (int64_t)at.local * 16, E::pack(y));
-
-  // slide the window into the write slot (raw values, copied bit for bit); a
-  // slot read and written by the same request is safe: each lane reads its
-  // own pieces before it stores them
-  if (ws >= 0) {
-    char *dst = p.pool + ws * slot_b + (int64_t)piece * 16;
-    nt_store16(dst, h[1]);
-    nt_store16(dst + (int64_t)P * 16, h[2]);
-    nt_store16(dst + (int64_t)2 * P * 16, x0);
+  for (int i = 0; i < RB; ++i) {
+    if (!live[i]) continue;
+    float f0[CH], f1[CH], f2[CH], f3[CH], y[CH];
+    E::unpack(x0[i], f0); E::unpack(h[i][2], f1); E::unpack(h[i][1], f2); E::unpack(h[i][0], f3);
+#pragma unroll
+    for (int c = 0; c < CH; ++c) y[c] = conv4_silu(w[c], f3[c], f2[c], f1[c], f0[c]);
+    // a head's lanes are all q, all k or all v (regions start on head boundaries)
+    if (at.region < 2) l2_scale<PPH>(y, p.eps);
+    nt_store16(out + (int64_t)(r0 + i) * at.row_b + (int64_t)at.local * 16, E::pack(y));
+    // slide the window into the write slot (raw values, copied bit for bit); a
+    // slot read and written by the same request is safe: each lane reads its
+    // own pieces before it stores them
+    if (ws[i] >= 0) {
+      char *dst = p.pool + ws[i] * slot_b + (int64_t)piece * 16;
+      nt_store16(dst, h[i][1]);
+      nt_store16(dst + (int64_t)P * 16, h[i][2]);
+      nt_store16(dst + (int64_t)2 * P * 16, x0[i]);
+    }
   }
 }
 
@@ -167,10 +202,11 @@ static ConvParams make_conv_params(const gdn_conv_args &a) {
   return p;
 }
 
-// the grid: one column per request / sequence, ceil(pieces / 256) rows
-static dim3 conv_grid(const ConvParams &p) {
+// the grid: one column per `per_col` requests / sequences, ceil(pieces / 256) rows
+static dim3 conv_grid(const ConvParams &p, int per_col) {
   const int P = 2 * p.pq + p.pv;
-  return dim3((unsigned)p.n, (unsigned)((P + kConvThreads - 1) / kConvThreads));
+  return dim3((unsigned)((p.n + per_col - 1) / per_col),
+              (unsigned)((P + kConvThreads - 1) / kConvThreads));
 }
 
 int64_t conv_grid_rows(const gdn_conv_args &a) {
@@ -181,10 +217,10 @@ int64_t conv_grid_rows(const gdn_conv_args &a) {
 
 gdn_status launch_conv_decode(const gdn_conv_args &a, hipStream_t s) {
   const ConvParams p = make_conv_params(a);
-  const dim3 grid = conv_grid(p);
+  const dim3 grid = conv_grid(p, kConvReqs);
   const bool ab = a.act_dtype == GDN_BF16;
 #define GDN_CONV_CASE(AB_, DK_) \
-  hipLaunchKernelGGL((conv_decode_kernel<AB_, DK_>), grid, dim3(kConvThreads), 0, s, p)
+  hipLaunchKernelGGL((conv_decode_kernel<AB_, DK_, kConvReqs>), grid, dim3(kConvThreads), 0, s, p)
 #define GDN_CONV_DK(AB_)                          \
   switch (a.d_k) {                                \
     case 16: GDN_CONV_CASE(AB_, 16); break;       \
@@ -201,7 +237,7 @@ gdn_status launch_conv_decode(const gdn_conv_args &a, hipStream_t s) {
 
 gdn_status launch_conv_store(const gdn_conv_args &a, hipStream_t s) {
   const ConvParams p = make_conv_params(a);
-  hipLaunchKernelGGL(conv_store_kernel, conv_grid(p), dim3(kConvThreads), 0, s, p);
+  hipLaunchKernelGGL(conv_store_kernel, conv_grid(p, 1), dim3(kConvThreads), 0, s, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }
 
