@@ -59,6 +59,9 @@ def _load():
         lib.oracle_frontend.restype = i32
         lib.oracle_frontend.argtypes = [i32, P, i32, i32, i32, i32, i32, f64,
                                         P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_decode_cw.restype = i32
+        lib.oracle_decode_cw.argtypes = [i32, i32, i32, i32, i32, i64, i32, f64, i32,
+                                         P, P, P, P, P, P, P, P, P, i32]
         lib.oracle_conv_decode.restype = i32
         lib.oracle_conv_decode.argtypes = [i32, i32, i32, i32, i32, i32, f64, i64,
                                            P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
@@ -116,6 +119,31 @@ def decode(q, k, v, g, beta, pool, read_slot=None, write_slot=None, *, rule="gat
                                  n_threads or default_threads())
     if code < 0:
         raise ValueError("oracle_decode rejected its arguments")
+    return o, pool, code
+
+
+def decode_cw(q, k, v, g, beta, pool, read_slot=None, write_slot=None, *, rule="gated_delta",
+              scale=1.0, round_state=False, n_threads=None):
+    """One decode token for B requests with a per-key-channel decay.
+
+    As ``decode`` except g is [B, Hv, dk] (the log-decay of each key channel;
+    the Kimi Linear section's channel-wise gate).  Returns ``(o, pool_after,
+    code)``.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    pool = _f64(pool).copy()
+    B, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if g.shape != (B, Hv, dk):
+        raise ValueError("g must be [B, Hv, dk]")
+    rs, ws = _i32(read_slot), _i32(write_slot)
+    o = np.zeros((B, Hv, dv), np.float64)
+    code = _load().oracle_decode_cw(B, Hqk, Hv, dk, dv, pool.shape[0], _rule(rule), float(scale),
+                                    int(bool(round_state)), _p(q), _p(k), _p(v), _p(g), _p(beta),
+                                    _p(pool), _p(rs), _p(ws), _p(o),
+                                    n_threads or default_threads())
+    if code < 0:
+        raise ValueError("oracle_decode_cw rejected its arguments")
     return o, pool, code
 
 

@@ -51,6 +51,13 @@
  *    a sequence boundary), then SiLU; q and k are then L2-normalised per
  *    (token, head) as y / sqrt(sum y^2 + eps); g = -softplus(a_raw) and
  *    beta = sigmoid(b_raw).
+ *  - Channel-wise decay (Kimi Delta Attention, "Seven Architectures ...",
+ *    Kimi Linear section): one log-decay per key channel, alpha_i = exp(g_i);
+ *    the state is decayed row by row first, and the delta correction then
+ *    reads the decayed state: S~ = Diag(alpha) S, S' = S~ + beta k (v - S~^T
+ *    k)^T (without erase: S~ + k v^T).  The same page's GDN-2 section puts
+ *    the decay after the erase and says that recovers KDA, which holds only
+ *    for a scalar decay; the Kimi Linear section's own formula is followed.
  *  - Decode-side conv: the window a decode token sees is the conv_k-1 raw
  *    inputs before it, kept per request in a conv-state slot ([conv_k-1,
  *    channels], oldest first, channels in q|k|v order); read index -1 = no
@@ -64,7 +71,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_VERSION 2
+#define ORACLE_VERSION 3
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -430,4 +437,82 @@ int oracle_conv_decode(int B, int Hqk, int Hv, int dk, int dv, int K, double eps
   }
   free(win);
   return bad;
+}
+
+/* ------------------------------------------------------------------------ */
+/* decode with channel-wise decay: one log-decay per key channel             */
+
+typedef struct {
+  int B, Hqk, Hv, dk, dv, rule, round_state;
+  int64_t n_slots;
+  double scale;
+  const double *q, *k, *v, *g, *beta;
+  double *pool;
+  const int32_t *read_slot, *write_slot;
+  double *o;
+  volatile int *bad;
+} decode_cw_ctx;
+
+static void decode_cw_unit(void *p, int64_t unit, double *work) {
+  decode_cw_ctx *c = (decode_cw_ctx *)p;
+  int64_t r = unit / c->Hv;
+  int h = (int)(unit % c->Hv);
+  int hq = (int)((int64_t)h * c->Hqk / c->Hv);
+  int64_t rs, ws;
+  if (!resolve_slots(c->read_slot, c->write_slot, r, c->n_slots, &rs, &ws)) {
+    *c->bad = 1;
+    return;
+  }
+  const int dk = c->dk, dv = c->dv;
+  int64_t tile = (int64_t)dk * dv;
+  double *S = work, *rd = work + tile;
+  if (rs >= 0) memcpy(S, c->pool + (rs * c->Hv + h) * tile, tile * sizeof(double));
+  else memset(S, 0, tile * sizeof(double));
+  const double *q = c->q + (r * c->Hqk + hq) * dk, *k = c->k + (r * c->Hqk + hq) * dk;
+  const double *v = c->v + (r * c->Hv + h) * dv, *g = c->g + (r * c->Hv + h) * dk;
+  const double beta = c->beta ? c->beta[r * c->Hv + h] : 1.0;
+  const int decay = c->rule == 1 || c->rule == 3, erase = c->rule >= 2;
+  /* decay row i (key channel i) by its own alpha_i */
+  if (decay)
+    for (int i = 0; i < dk; ++i) {
+      const double a = exp(g[i]);
+      for (int j = 0; j < dv; ++j) S[(int64_t)i * dv + j] *= a;
+    }
+  /* the write: beta k (v - S~^T k)^T with erase, k v^T without */
+  for (int j = 0; j < dv; ++j) {
+    double read = 0.0;
+    if (erase)
+      for (int i = 0; i < dk; ++i) read += S[(int64_t)i * dv + j] * k[i];
+    rd[j] = erase ? beta * (v[j] - read) : v[j];
+  }
+  for (int i = 0; i < dk; ++i)
+    for (int j = 0; j < dv; ++j) S[(int64_t)i * dv + j] += k[i] * rd[j];
+  /* read-out from the new state */
+  double *o = c->o + (r * c->Hv + h) * dv;
+  for (int j = 0; j < dv; ++j) {
+    double acc = 0.0;
+    for (int i = 0; i < dk; ++i) acc += S[(int64_t)i * dv + j] * q[i];
+    o[j] = c->scale * acc;
+  }
+  if (ws >= 0) {
+    double *dst = c->pool + (ws * c->Hv + h) * tile;
+    for (int64_t e = 0; e < tile; ++e) dst[e] = c->round_state ? oracle_round_bf16(S[e]) : S[e];
+  }
+}
+
+/* One decode token for B requests with a per-key-channel decay (Kimi Delta
+ * Attention, Kimi Linear section).  As oracle_decode, except g is
+ * [B, Hv, dk]: the log-decay of each key channel of each state head. */
+int oracle_decode_cw(int B, int Hqk, int Hv, int dk, int dv, int64_t n_slots, int rule,
+                     double scale, int round_state, const double *q, const double *k,
+                     const double *v, const double *g, const double *beta, double *pool,
+                     const int32_t *read_slot, const int32_t *write_slot, double *o,
+                     int n_threads) {
+  if (B < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || rule < 0 || rule > 3) return -1;
+  if (Hv % Hqk != 0) return -1;
+  volatile int bad = 0;
+  decode_cw_ctx c = {B, Hqk, Hv, dk, dv, rule, round_state, n_slots, scale, q, k, v, g, beta,
+                     pool, read_slot, write_slot, o, &bad};
+  if (run_units(decode_cw_unit, &c, (int64_t)B * Hv, (size_t)dk * dv + dv, n_threads)) return -1;
+  return bad ? 1 : 0;
 }
