@@ -10,7 +10,8 @@ synthetic tensors already resident in HBM.
 Prints ONE JSON line: tokens/s, state GB/s and the fraction of HBM peak for
 the decode kernel, the CPU oracle timed on a bounded sample of the same
 workload, the decode-side conv front-end (alone and ahead of each layer's
-decode), chunked-prefill tokens/s and the mixed launch.
+decode), the decode with a per-key-channel decay, chunked-prefill tokens/s
+and the mixed launch.
 """
 from __future__ import annotations
 
@@ -210,6 +211,61 @@ def run_conv(args, torch, gdn, syn, layers):
                 decode_with_conv_tokens_per_s=round(B / (ms_step / 1e3), 1))
 
 
+def run_decode_cw(args, torch, gdn, syn, layers):
+    """The same 48-layer B=512 decode with a per-key-channel decay (g of shape
+    [B, H_v, d_k], Kimi Delta Attention's channel-wise gate): the decode
+    kernel's channel-wise instance, one HIP graph of 48 launches."""
+    wl = syn.WORKLOADS["decode_b512_x48"]
+    B, Hqk, Hv, dk, dv = wl["B"], wl["H_qk"], wl["H_v"], wl["d_k"], wl["d_v"]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4242)
+    cws = []
+    for a, keep in layers:
+        q, k, v, g, beta, pool, rs, ws = keep[:8]
+        gcw = -torch.nn.functional.softplus(
+            torch.randn((B, Hv, dk), generator=gen, device="cuda", dtype=torch.float32))
+        ca, _, ckeep = gdn.make_decode_args(q, k, v, gcw, beta, pool, rs, ws)
+        cws.append((ca, ckeep))
+    torch.cuda.synchronize()
+    lib = gdn.load_library()
+
+    def step():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for ca, _ in cws:
+            code = lib.gdn_decode(ctypes.byref(ca), s)
+            if code:
+                raise gdn.GdnError("gdn_decode", code)
+
+    step()
+    torch.cuda.synchronize()
+    run = step
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    state_b, other_b = decode_bytes_per_launch(B, Hqk, Hv, dk, dv)
+    per_launch = state_b + other_b + B * Hv * (dk - 1) * 4   # g grows from [B, H_v] to [B, H_v, d_k]
+    us = ms * 1e3 / len(cws)
+    gbps = per_launch / (us / 1e6) / 1e9
+    return dict(workload="decode_b512_x48, per-key-channel decay",
+                kernel="decode_kernel<bf16 state, bf16 act, 128, 128, channel decay>",
+                ms_per_step=round(ms, 4), tokens_per_s=round(B / (ms / 1e3), 1),
+                avg_launch_us=round(us, 2), per_launch_bytes=per_launch,
+                algorithmic_GBps=round(gbps, 1), hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
+
+
 def prefill_useful_flops(lengths, H_v, d_k, d_v, C=64):
     """Useful flops of the chunked recurrence (per chunk of n tokens and head):
     K K^T and Q K^T (lower triangle incl. diagonal), the triangular solve,
@@ -396,7 +452,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-conv", action="store_true",
-                    help="skip the decode-side conv (front-end) measurement")
+                    help="skip the decode-side conv and the channel-wise decay measurements")
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=10,
                     help="untimed calls before the prefill and mixed timings")
@@ -445,6 +501,10 @@ def main():
     if not args.no_conv:
         conv = run_conv(args, torch, gdn, syn, layers)
         log(f"conv: {conv}")
+    decode_cw = None
+    if not args.no_conv:
+        decode_cw = run_decode_cw(args, torch, gdn, syn, layers)
+        log(f"decode, channel-wise decay: {decode_cw}")
     prefill = None
     if not args.no_prefill:
         del layers[:]
@@ -479,6 +539,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "conv_decode": conv,
+        "decode_channel_decay": decode_cw,
         "prefill": prefill,
         "mixed": mixed,
     }

@@ -67,7 +67,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 3
+#define GDN_ABI_VERSION 4
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -77,6 +77,14 @@ typedef enum gdn_rule {
 } gdn_rule;
 
 typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+/* How the decay of the gated rules is given.  HEAD: one per (token, state
+ * head), Gated DeltaNet's scalar forget gate.  CHANNEL: one per key channel
+ * of each state head, the channel-wise gate of Kimi Delta Attention ("Seven
+ * Architectures ...", Kimi Linear section): row i of the state decays by
+ * exp(g_i) before the delta correction reads the state, i.e.
+ * M' = D M + beta k (v - (D M)^T k)^T with D = Diag(exp(g)). */
+typedef enum gdn_decay_mode { GDN_DECAY_HEAD = 0, GDN_DECAY_CHANNEL = 1 } gdn_decay_mode;
 
 typedef enum gdn_status {
   GDN_OK = 0,
@@ -111,11 +119,13 @@ typedef struct gdn_decode_args {
   int32_t act_dtype;   /* gdn_dtype of q, k, v and o */
   int64_t n_slots;     /* pool capacity in slots */
   float scale;         /* read-out scale (1.0 for none) */
-  int32_t reserved0;   /* must be 0 */
+  int32_t decay_mode;  /* gdn_decay_mode: the shape of g (gdn_decode only; gdn_mixed takes
+                          GDN_DECAY_HEAD) */
   const void *q;       /* [B, H_qk, d_k] act_dtype; normalised by the caller */
   const void *k;       /* [B, H_qk, d_k] act_dtype */
   const void *v;       /* [B, H_v, d_v] act_dtype */
-  const float *g;      /* [B, H_v] log-decay (unused by linear and delta; may be NULL then) */
+  const float *g;      /* log-decay, [B, H_v] (GDN_DECAY_HEAD) or [B, H_v, d_k]
+                          (GDN_DECAY_CHANNEL); unused by linear and delta (may be NULL then) */
   const float *beta;   /* [B, H_v] write strength (unused by linear and gated; may be NULL then) */
   void *state_pool;    /* [n_slots, H_v, d_k, d_v] state_dtype, read and written in place */
   const int32_t *read_slot;  /* [B] or NULL */

@@ -26,7 +26,8 @@ gdn_status check_decode(const gdn_decode_args *a) {
   if (a->B < 0 || a->n_slots < 0) return GDN_ERR_SHAPE;
   if (!valid_rule(a->rule)) return GDN_ERR_RULE;
   if (!valid_dtype(a->state_dtype) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
-  if (a->reserved0 != 0) return GDN_ERR_UNSUPPORTED;
+  if (a->decay_mode != GDN_DECAY_HEAD && a->decay_mode != GDN_DECAY_CHANNEL)
+    return GDN_ERR_UNSUPPORTED;
   gdn_status st = check_heads(a->H_qk, a->H_v, a->d_k, a->d_v);
   if (st != GDN_OK) return st;
   if ((int64_t)a->B * a->H_v > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;  // grid size
@@ -193,6 +194,7 @@ gdn_status gdn_mixed(const gdn_decode_args *decode, const gdn_prefill_args *pref
                      void *stream) {
   gdn_status st = check_decode(decode);
   if (st != GDN_OK) return st;
+  if (decode->decay_mode != GDN_DECAY_HEAD) return GDN_ERR_UNSUPPORTED;  // one decode instance
   st = check_prefill(prefill, true);
   if (st != GDN_OK) return st;
   if (decode->B == 0 && prefill->n_seq == 0) return GDN_OK;

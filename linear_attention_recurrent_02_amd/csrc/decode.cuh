@@ -16,6 +16,11 @@
 // for the current token, a per-head scalar (k . q) times a small vector.  The
 // read-out therefore never waits for the new state.
 //
+// With a per-key-channel decay (CW: Kimi Delta Attention, the same Kimi
+// Linear section) the decay multiplies row i by a_i = exp(g_i) before the
+// delta correction reads the state, so the reductions take a_i k_i and
+// a_i q_i, a = 1 in delta and o, and the update is M'_i = a_i M_i + k_i delta.
+//
 // Work split (gfx950, wave64): every column j of the update is independent
 // given k, q and v, so a lane owns VEC consecutive columns (one 16-byte
 // vector per row) and RPT consecutive rows; LPR lanes cover one row, so each
@@ -95,7 +100,7 @@ struct DecodeShape {
 // the thread's runs of k, q (RPT rows) and v (VEC columns) are whole 16-byte
 // vectors they are kept packed as loaded (half the registers for BF16) and
 // unpacked in phase 2.
-template <bool SB, bool AB, int DK, int DV, int NT>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false>
 struct DecodeTileRegs {
   using S = DecodeShape<SB, DK, DV, NT>;
   static constexpr int AV = Elem<AB>::kPer16B;  // activation elements per 16 bytes
@@ -107,6 +112,7 @@ struct DecodeTileRegs {
   uint4 kp[KN], qp[KN], vp[VN];     // packed k, q, v (PACKED)
   float kr[PACKED ? 1 : S::RPT], qr[PACKED ? 1 : S::RPT], vv[PACKED ? 1 : S::VEC];
   float a, bw;                      // decay and write strength
+  float ar[CW ? S::RPT : 1];        // CW: the decay of each of this thread's rows
   int64_t r, ws;                    // request, write slot
   int h;
   bool valid;                       // false: a bad slot (the tile is skipped)
@@ -118,9 +124,10 @@ struct DecodeTileRegs {
 // NT threads of a group call it with the same (r, h), each passing its index
 // in the group as `tid`: the workgroup, or one of its aligned NT-thread parts
 // (each with its own `red`).
-template <bool SB, bool AB, int DK, int DV, int NT>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false>
 __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t r, int h,
-                                                 DecodeTileRegs<SB, AB, DK, DV, NT> &t, int tid) {
+                                                 DecodeTileRegs<SB, AB, DK, DV, NT, CW> &t,
+                                                 int tid) {
   using S = DecodeShape<SB, DK, DV, NT>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT;
   constexpr bool ALL_LIVE = S::ALL_LIVE;
@@ -143,7 +150,7 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
   // this token's q, k (rows of this thread), v (its columns); issued before
   // the state tile: loads return in order, so waiting for these leaves the
   // state loads in flight
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT>;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW>;
   using AT = typename Elem<AB>::T;
   if constexpr (Regs::PACKED) {
     const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.k) +
@@ -181,7 +188,16 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
   }
   const bool decay = (p.rule & kRuleDecay) != 0;
   const bool erase = (p.rule & kRuleErase) != 0;
-  t.a = decay ? expf(p.g[r * p.H_v + h]) : 1.0f;
+  if constexpr (CW) {
+    // g is [B, H_v, d_k]: this thread's rows' log-decays
+    t.a = 1.0f;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      t.ar[i] = decay && (ALL_LIVE || row0 + i < DK)
+                    ? expf(p.g[(r * p.H_v + h) * DK + row0 + i]) : 1.0f;
+  } else {
+    t.a = decay ? expf(p.g[r * p.H_v + h]) : 1.0f;
+  }
   t.bw = erase ? p.beta[r * p.H_v + h] : 1.0f;
 }
 
@@ -189,9 +205,9 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
 // and the store to the write slot (a5).  `red` is LDS of
 // DecodeShape::LDS_FLOATS floats.  For NW > 1 it has three barriers (the last
 // lets the caller reuse `red`); a skipped tile has none, uniformly.
-template <bool SB, bool AB, int DK, int DV, int NT>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false>
 __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
-                                                   DecodeTileRegs<SB, AB, DK, DV, NT> &t,
+                                                   DecodeTileRegs<SB, AB, DK, DV, NT, CW> &t,
                                                    float *red, int tid) {
   using S = DecodeShape<SB, DK, DV, NT>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT, NW = S::NW;
@@ -206,7 +222,7 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
   const int64_t r = t.r;
   const int h = t.h;
   constexpr int64_t TILE = (int64_t)DK * DV;
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT>;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW>;
   float kr[RPT], qr[RPT], vv[VEC];
   if constexpr (Regs::PACKED) {
 #pragma unroll
@@ -232,10 +248,12 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
   for (int i = 0; i < RPT; ++i) {
     float f[VEC];
     SE::unpack(t.m[i], f);
+    // CW: the decayed row a_i M_i is what k and q read
+    const float kd = CW ? t.ar[i] * kr[i] : kr[i], qd = CW ? t.ar[i] * qr[i] : qr[i];
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      u[e] = fmaf(f[e], kr[i], u[e]);
-      w[e] = fmaf(f[e], qr[i], w[e]);
+      u[e] = fmaf(f[e], kd, u[e]);
+      w[e] = fmaf(f[e], qd, w[e]);
     }
     kq = fmaf(kr[i], qr[i], kq);
   }
@@ -304,8 +322,9 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
       if (!ALL_LIVE && row0 + i >= DK) continue;
       float f[VEC];
       SE::unpack(t.m[i], f);
+      const float ai = CW ? t.ar[i] : a;
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) f[e] = fmaf(kr[i], d[e], a * f[e]);
+      for (int e = 0; e < VEC; ++e) f[e] = fmaf(kr[i], d[e], ai * f[e]);
       stream_store(dst + (int64_t)(row0 + i) * LPR + cv, SE::pack(f));
     }
   }

@@ -19,6 +19,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 
 RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3}
 F32, BF16 = 0, 1
+DECAY_HEAD, DECAY_CHANNEL = 0, 1
 DEVICE_BAD_SLOT = 1
 DEVICE_BAD_SEQ = 2
 
@@ -30,7 +31,7 @@ _I64 = ctypes.c_int64
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("B", _I32), ("H_qk", _I32), ("H_v", _I32), ("d_k", _I32), ("d_v", _I32),
                 ("rule", _I32), ("state_dtype", _I32), ("act_dtype", _I32),
-                ("n_slots", _I64), ("scale", ctypes.c_float), ("reserved0", _I32),
+                ("n_slots", _I64), ("scale", ctypes.c_float), ("decay_mode", _I32),
                 ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
                 ("state_pool", _P), ("read_slot", _P), ("write_slot", _P), ("o", _P),
                 ("status", _P)]
@@ -202,7 +203,8 @@ def gdn_validate_slots(read_slot, write_slot, n: int, n_slots: int) -> int:
 def make_decode_args(q, k, v, g, beta, state_pool, read_slot=None, write_slot=None, o=None, *,
                      rule="gated_delta", scale=1.0, status=None):
     """Build a DecodeArgs struct.  q, k: [B, H_qk, d_k]; v: [B, H_v, d_v];
-    g, beta: [B, H_v] float32; state_pool: [n_slots, H_v, d_k, d_v];
+    g: [B, H_v] float32, or [B, H_v, d_k] for a per-key-channel decay; beta:
+    [B, H_v] float32; state_pool: [n_slots, H_v, d_k, d_v];
     read_slot / write_slot: [B] int32 or None.  Returns (args, o, keepalive)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
                     ("state_pool", state_pool), ("read_slot", read_slot),
@@ -219,7 +221,8 @@ def make_decode_args(q, k, v, g, beta, state_pool, read_slot=None, write_slot=No
     a.act_dtype = _dtype_code(q)
     a.n_slots = state_pool.shape[0]
     a.scale = float(scale)
-    a.reserved0 = 0
+    # g [B, H_v]: one decay per state head; [B, H_v, d_k]: one per key channel
+    a.decay_mode = DECAY_CHANNEL if g is not None and g.dim() == 3 else DECAY_HEAD
     a.q, a.k, a.v, a.g, a.beta = _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta)
     a.state_pool, a.read_slot, a.write_slot = _ptr(state_pool), _ptr(read_slot), _ptr(write_slot)
     a.o, a.status = _ptr(o), _ptr(status)

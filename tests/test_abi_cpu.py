@@ -28,7 +28,7 @@ def test_struct_layout_matches():
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
     assert lib.gdn_sizeof_conv_args() == ctypes.sizeof(B.ConvArgs)
-    assert gdn.gdn_abi_version() == 3
+    assert gdn.gdn_abi_version() == 4
 
 
 def test_state_bytes_against_the_pages():
@@ -62,7 +62,7 @@ def _decode_args(**over):
     a = B.DecodeArgs()
     a.B, a.H_qk, a.H_v, a.d_k, a.d_v = 4, 2, 4, 128, 128
     a.rule, a.state_dtype, a.act_dtype = 3, 1, 1
-    a.n_slots, a.scale, a.reserved0 = 8, 1.0, 0
+    a.n_slots, a.scale, a.decay_mode = 8, 1.0, 0
     for f in ("q", "k", "v", "g", "beta", "state_pool", "o"):
         setattr(a, f, FAKE)
     for k, v in over.items():
@@ -78,7 +78,7 @@ def _call_decode(a):
     (dict(rule=4), RULE), (dict(rule=-1), RULE),
     (dict(state_dtype=2), DTYPE), (dict(act_dtype=-1), DTYPE),
     (dict(B=-1), SHAPE), (dict(n_slots=-1), SHAPE), (dict(H_qk=0), SHAPE), (dict(d_k=0), SHAPE),
-    (dict(H_qk=3), UNSUP), (dict(d_k=48), UNSUP), (dict(d_v=256), UNSUP), (dict(reserved0=1), UNSUP),
+    (dict(H_qk=3), UNSUP), (dict(d_k=48), UNSUP), (dict(d_v=256), UNSUP), (dict(decay_mode=2), UNSUP), (dict(decay_mode=-1), UNSUP),
     (dict(q=None), NULL), (dict(state_pool=None), NULL), (dict(o=None), NULL),
     (dict(g=None), NULL), (dict(beta=None), NULL),
     (dict(n_slots=3), SHAPE),  # identity slots need n_slots >= B
