@@ -189,12 +189,14 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
   const bool decay = (p.rule & kRuleDecay) != 0;
   const bool erase = (p.rule & kRuleErase) != 0;
   if constexpr (CW) {
-    // g is [B, H_v, d_k]: this thread's rows' log-decays
+    // g is [B, H_v, d_k]: this thread's rows' log-decays, through the
+    // hardware exponential (RPT of them per thread; expf measured 0.8%
+    // slower per B=512 launch)
     t.a = 1.0f;
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
       t.ar[i] = decay && (ALL_LIVE || row0 + i < DK)
-                    ? expf(p.g[(r * p.H_v + h) * DK + row0 + i]) : 1.0f;
+                    ? __expf(p.g[(r * p.H_v + h) * DK + row0 + i]) : 1.0f;
   } else {
     t.a = decay ? expf(p.g[r * p.H_v + h]) : 1.0f;
   }
