@@ -192,3 +192,61 @@ def test_conv_decode_full_size():
     ref = run_oracle(x, f64(pool0), rs, ws, Hqk, Hv)
     check(out, ref, adt)
     np.testing.assert_array_equal(f64(pool), ref[5])
+
+
+def test_prefill_store_then_conv_decode_steps_match_the_oracle():
+    """A whole layer across calls: gdn_prefill (fused front-end) over L tokens of
+    each sequence, gdn_conv_store, then two decode steps of conv then
+    gdn_decode (in-place slots) == the oracle's front-end and token recurrence
+    over all L + 2 tokens."""
+    say("prefill + conv store + 2 x (conv decode + decode) vs oracle")
+    from linear_attention_recurrent_02_amd import gdn_decode, gdn_prefill
+    Hqk, Hv, d = 2, 4, 64
+    adt = torch.bfloat16
+    L = [1, 3, 70, 129]
+    full = [l + 2 for l in L]
+    N = int(sum(full))
+    x = syn.frontend_inputs(407, 0, N, Hqk, Hv, d, d, K, adt)
+    cu_full = syn.cu_from_lengths(full)
+    starts = cu_full[:-1].long()
+    pre = torch.cat([torch.arange(int(s), int(s) + l) for s, l in zip(starts, L)]).long()
+    pick = lambda key, rows: x[key][rows].contiguous()
+    n = len(L)
+    slots = torch.arange(n, dtype=torch.int32, device=DEV)
+    pool = torch.zeros((n, Hv, d, d), dtype=torch.float32, device=DEV)
+    cpool = torch.zeros((n, K - 1, channels(Hqk, Hv, d, d)), dtype=adt, device=DEV)
+    cu_pre = dev(syn.cu_from_lengths(L))
+    o_pre = gdn_prefill(cu_pre, dev(pick("q_raw", pre)), dev(pick("k_raw", pre)),
+                        dev(pick("v_raw", pre)), pool, torch.full((n,), -1, dtype=torch.int32,
+                                                                  device=DEV), slots,
+                        H_qk=Hqk, H_v=Hv, a_raw=dev(pick("a_raw", pre)),
+                        b_raw=dev(pick("b_raw", pre)), conv_wq=dev(x["conv_wq"]),
+                        conv_wk=dev(x["conv_wk"]), conv_wv=dev(x["conv_wv"]))
+    gdn_conv_store(cu_pre, dev(pick("q_raw", pre)), dev(pick("k_raw", pre)),
+                   dev(pick("v_raw", pre)), cpool, slots, H_qk=Hqk, H_v=Hv)
+    outs = []
+    for step in range(2):
+        rows = starts + torch.tensor(L) + step
+        xd = {kk: pick(kk, rows) for kk in ("q_raw", "k_raw", "v_raw", "a_raw", "b_raw")}
+        xd.update({kk: x[kk] for kk in ("conv_wq", "conv_wk", "conv_wv")})
+        q, k, v, g, b = run_decode(xd, cpool, slots, slots, Hqk, Hv)
+        outs.append(gdn_decode(q, k, v, g, b, pool, slots, slots))
+    torch.cuda.synchronize()
+    # oracle: front-end over whole sequences (its q, k, v rounded to the activation dtype
+    # where the GPU path stores them), then the token recurrence from a zero state
+    rq, rk, rv, rg, rb = oracle.frontend(cu_full.numpy(), f64(x["q_raw"]), f64(x["k_raw"]),
+                                         f64(x["v_raw"]), f64(x["conv_wq"]), f64(x["conv_wk"]),
+                                         f64(x["conv_wv"]), f64(x["a_raw"]), f64(x["b_raw"]),
+                                         Hqk=Hqk, Hv=Hv)
+    rq, rk, rv = (oracle.round_bf16(t) for t in (rq, rk, rv))
+    ro, rpool, code = oracle.sequences(cu_full.numpy(), rq, rk, rv, rg, rb,
+                                       np.zeros((n, Hv, d, d)), [-1] * n, list(range(n)))
+    assert code == 0
+    t = tol(adt)
+    last = [int(s) + l for s, l in zip(starts, L)]
+    for step in range(2):
+        want = ro[[r + step for r in last]]
+        assert scaled_err(f64(outs[step]), want, 2) < t
+    assert scaled_err(f64(pool), rpool, 2) < t
+    got_pre = f64(o_pre)
+    assert scaled_err(got_pre, ro[pre.numpy()], 2) < t
