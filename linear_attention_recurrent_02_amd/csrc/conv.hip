@@ -69,10 +69,7 @@ __device__ __forceinline__ PieceOf piece_of(const ConvParams &p, int piece) {
 // once and keeps the loads of all RB requests in flight together (at B = 512,
 // H_qk = 16, H_v = 32, d = 128: 21.1 us per launch with one request, 16.7 with
 // two or four, 21.1 with eight, which leaves too few workgroups)
-#ifndef GDN_CONV_REQS
-#define GDN_CONV_REQS 2
-#endif
-constexpr int kConvReqs = GDN_CONV_REQS;
+constexpr int kConvReqs = 2;
 
 template <bool AB, int DK, int RB>
 __global__ __launch_bounds__(kConvThreads) void conv_decode_kernel(ConvParams p) {

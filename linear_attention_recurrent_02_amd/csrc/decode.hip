@@ -9,44 +9,25 @@
 
 namespace gdn {
 
-
 template <bool SB, bool AB, int DK, int DV, bool CW>
-__global__ __launch_bounds__(GDN_DECODE_MAX_THREADS) void decode_kernel(DecodeParams p,
-                                                                         int ordered) {
+__global__ __launch_bounds__(kDecodeMaxThreads) void decode_kernel(DecodeParams p, int ordered) {
   constexpr int NT = decode_threads<SB, DK, DV>();
   __shared__ float red[DecodeShape<SB, DK, DV, NT>::LDS_FLOATS];
   extern __shared__ int order_lds[];
   if (ordered) build_slot_order<NT>(p.write_slot, p.B, p.n_slots, order_lds);
   const int64_t n_tiles = (int64_t)p.B * p.H_v;
-  // software pipeline: the next tile's loads are issued before this tile's
-  // reduction and store, so each workgroup keeps loads in flight throughout
+  // one tile at a time: a software-pipelined loop (the next tile's loads in
+  // flight during this tile's reduction and store) measured slower on MI355X
+  // (196 against 191 us per B = 512 launch), its extra registers costing more
+  // occupancy than the overlap gains
   using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW>;
-  int64_t t = blockIdx.x;
-  if (t >= n_tiles) return;
-  auto load = [&](int64_t tile, Regs &dst) {
-    const int pos = (int)(tile / p.H_v);
-    decode_tile_load<SB, AB, DK, DV, NT, CW>(p, ordered ? order_lds[pos] : pos,
-                                             (int)(tile % p.H_v), dst, (int)threadIdx.x);
-  };
-#if GDN_DECODE_PIPELINE
-  Regs cur, nxt;
-  load(t, cur);
-  for (;;) {
-    const int64_t tn = t + gridDim.x;
-    const bool more = tn < n_tiles;
-    if (more) load(tn, nxt);
-    decode_tile_finish<SB, AB, DK, DV, NT, CW>(p, cur, red, (int)threadIdx.x);
-    if (!more) break;
-    cur = nxt;
-    t = tn;
-  }
-#else
-  for (; t < n_tiles; t += gridDim.x) {
+  for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int pos = (int)(t / p.H_v);
     Regs cur;
-    load(t, cur);
+    decode_tile_load<SB, AB, DK, DV, NT, CW>(p, ordered ? order_lds[pos] : pos, (int)(t % p.H_v),
+                                             cur, (int)threadIdx.x);
     decode_tile_finish<SB, AB, DK, DV, NT, CW>(p, cur, red, (int)threadIdx.x);
   }
-#endif
 }
 
 DecodeParams make_decode_params(const gdn_decode_args &a) {

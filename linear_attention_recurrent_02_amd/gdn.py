@@ -149,6 +149,42 @@ def _dev(t, name):
     return t
 
 
+_ACT = (torch.bfloat16, torch.float32)
+
+
+def _need(t, name, *, dtype=None, dtypes=None, shape=None):
+    """Check a tensor's dtype and exact shape (None passes: absence is the
+    library's to judge).  Runs before any device check, so a wrong dtype or
+    shape is reported as such on any device."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise ValueError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(int(x) for x in shape)}, "
+                         f"got {tuple(t.shape)}")
+    return t
+
+
+def _row_dim(t, name, rows, heads):
+    """Per-head size of a [rows, heads * d] or [rows, heads, d] tensor."""
+    if t.dim() == 3:
+        if t.shape[0] != rows or t.shape[1] != heads:
+            raise ValueError(f"{name} must be [{rows}, {heads}, d], got {tuple(t.shape)}")
+        return int(t.shape[2])
+    if t.dim() != 2 or t.shape[0] != rows or t.shape[1] % heads != 0 or t.shape[1] == 0:
+        raise ValueError(f"{name} must be [{rows}, {heads} * d], got {tuple(t.shape)}")
+    return int(t.shape[1]) // heads
+
+
+def _status(t):
+    return _need(t, "status", dtypes=(torch.int32,), shape=(1,)) if t is not None else None
+
+
 def _rule(rule) -> int:
     if isinstance(rule, str):
         out = _I32()
@@ -206,12 +242,32 @@ def make_decode_args(q, k, v, g, beta, state_pool, read_slot=None, write_slot=No
     g: [B, H_v] float32, or [B, H_v, d_k] for a per-key-channel decay; beta:
     [B, H_v] float32; state_pool: [n_slots, H_v, d_k, d_v];
     read_slot / write_slot: [B] int32 or None.  Returns (args, o, keepalive)."""
+    _need(q, "q", dtypes=_ACT)
+    if q.dim() != 3:
+        raise ValueError(f"q must be [B, H_qk, d_k], got {tuple(q.shape)}")
+    B, H_qk, d_k = q.shape
+    _need(k, "k", dtype=q.dtype, shape=q.shape)
+    _need(v, "v", dtype=q.dtype)
+    if v.dim() != 3 or v.shape[0] != B:
+        raise ValueError(f"v must be [B={B}, H_v, d_v], got {tuple(v.shape)}")
+    H_v, d_v = v.shape[1], v.shape[2]
+    if g is not None and g.dim() == 3:
+        _need(g, "g", dtype=torch.float32, shape=(B, H_v, d_k))
+    else:
+        _need(g, "g", dtype=torch.float32, shape=(B, H_v))
+    _need(beta, "beta", dtype=torch.float32, shape=(B, H_v))
+    _need(state_pool, "state_pool", dtypes=_ACT)
+    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H_v, d_k, d_v):
+        raise ValueError(f"state_pool must be [n_slots, {H_v}, {d_k}, {d_v}], "
+                         f"got {tuple(state_pool.shape)}")
+    _need(read_slot, "read_slot", dtype=torch.int32, shape=(B,))
+    _need(write_slot, "write_slot", dtype=torch.int32, shape=(B,))
+    _need(o, "o", dtype=q.dtype, shape=(B, H_v, d_v))
+    _status(status)
     for name, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
                     ("state_pool", state_pool), ("read_slot", read_slot),
                     ("write_slot", write_slot), ("o", o), ("status", status)):
         _dev(t, name)
-    B, H_qk, d_k = q.shape
-    H_v, d_v = v.shape[1], v.shape[2]
     if o is None:
         o = torch.empty((B, H_v, d_v), dtype=q.dtype, device=q.device)
     a = DecodeArgs()
@@ -251,27 +307,55 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
     ckpt_interval > 0 (a multiple of chunk), ckpt_slot [n_seq, per_seq] int32
     names the slots of the intermediate checkpoints.
     Returns (args, o, keepalive); allocates the workspace when needed."""
+    _need(cu_seqlens, "cu_seqlens", dtype=torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must be [n_seq + 1]")
+    n_seq = cu_seqlens.shape[0] - 1
+    _need(q, "q", dtypes=_ACT)
+    _need(state_pool, "state_pool", dtypes=_ACT)
+    if state_pool.dim() != 4:
+        raise ValueError(f"state_pool must be [n_slots, H_v, d_k, d_v], got {tuple(state_pool.shape)}")
+    N = q.shape[0]
+    d_k = _row_dim(q, "q", N, H_qk) if N else state_pool.shape[2]
+    _need(k, "k", dtype=q.dtype, shape=q.shape)
+    _need(v, "v", dtype=q.dtype)
+    d_v = _row_dim(v, "v", N, H_v) if N else state_pool.shape[3]
+    if tuple(state_pool.shape[1:]) != (H_v, d_k, d_v):
+        raise ValueError(f"state_pool must be [n_slots, {H_v}, {d_k}, {d_v}], "
+                         f"got {tuple(state_pool.shape)}")
+    _need(read_slot, "read_slot", dtype=torch.int32, shape=(n_seq,))
+    _need(write_slot, "write_slot", dtype=torch.int32, shape=(n_seq,))
+    _need(o, "o", dtype=q.dtype, shape=(N, H_v, d_v))
+    for name, t in (("g", g), ("beta", beta), ("a_raw", a_raw), ("b_raw", b_raw)):
+        _need(t, name, dtype=torch.float32, shape=(N, H_v))
+    use_fe = conv_wq is not None
+    K = conv_wq.shape[-1] if use_fe and conv_wq.dim() == 2 else 4
+    _need(conv_wq, "conv_wq", dtype=torch.float32, shape=(H_qk * d_k, K))
+    _need(conv_wk, "conv_wk", dtype=torch.float32, shape=(H_qk * d_k, K))
+    _need(conv_wv, "conv_wv", dtype=torch.float32, shape=(H_v * d_v, K))
+    if ckpt_slot is not None:
+        _need(ckpt_slot, "ckpt_slot", dtype=torch.int32)
+        if ckpt_slot.dim() != 2 or ckpt_slot.shape[0] != n_seq:
+            raise ValueError(f"ckpt_slot must be [{n_seq}, per_seq], got {tuple(ckpt_slot.shape)}")
+    _need(workspace, "workspace", dtype=torch.uint8)
+    _status(status)
     for name, t in (("cu_seqlens", cu_seqlens), ("q", q), ("k", k), ("v", v),
                     ("state_pool", state_pool), ("read_slot", read_slot),
                     ("write_slot", write_slot), ("o", o), ("g", g), ("beta", beta),
                     ("a_raw", a_raw), ("b_raw", b_raw), ("conv_wq", conv_wq),
                     ("conv_wk", conv_wk), ("conv_wv", conv_wv), ("status", status),
-                    ("ckpt_slot", ckpt_slot)):
+                    ("ckpt_slot", ckpt_slot), ("workspace", workspace)):
         _dev(t, name)
-    N = q.shape[0]
-    d_k = q.numel() // max(1, N * H_qk) if N else state_pool.shape[2]
-    d_v = v.numel() // max(1, N * H_v) if N else state_pool.shape[3]
-    use_fe = conv_wq is not None
     if o is None:
         o = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
     a = PrefillArgs()
-    a.n_seq = cu_seqlens.shape[0] - 1
+    a.n_seq = n_seq
     a.H_qk, a.H_v, a.d_k, a.d_v = H_qk, H_v, d_k, d_v
     a.rule = _rule(rule)
     a.state_dtype = _dtype_code(state_pool)
     a.act_dtype = _dtype_code(q)
     a.use_frontend = 1 if use_fe else 0
-    a.conv_k = conv_wq.shape[1] if use_fe else 4
+    a.conv_k = K
     a.chunk = chunk
     a.ckpt_interval = int(ckpt_interval)
     a.n_tokens = N
@@ -308,20 +392,34 @@ def gdn_prefill(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slot=None
 def gdn_frontend(cu_seqlens, q_raw, k_raw, v_raw, *, H_qk, H_v, conv_wq, conv_wk, conv_wv,
                  a_raw, b_raw, eps=1e-6, stream=None):
     """The front-end alone: returns (q [N,H_qk,d_k], k, v [N,H_v,d_v], g, beta)."""
+    _need(cu_seqlens, "cu_seqlens", dtype=torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+        raise ValueError("cu_seqlens must be [n_seq + 1]")
+    _need(q_raw, "q_raw", dtypes=_ACT)
+    N = q_raw.shape[0]
+    if N == 0:
+        raise ValueError("gdn_frontend needs at least one token")
+    d_k = _row_dim(q_raw, "q_raw", N, H_qk)
+    d_v = _row_dim(v_raw, "v_raw", N, H_v)
+    _need(k_raw, "k_raw", dtype=q_raw.dtype, shape=q_raw.shape)
+    _need(v_raw, "v_raw", dtype=q_raw.dtype)
+    K = conv_wq.shape[-1] if conv_wq.dim() == 2 else 4
+    _need(conv_wq, "conv_wq", dtype=torch.float32, shape=(H_qk * d_k, K))
+    _need(conv_wk, "conv_wk", dtype=torch.float32, shape=(H_qk * d_k, K))
+    _need(conv_wv, "conv_wv", dtype=torch.float32, shape=(H_v * d_v, K))
+    _need(a_raw, "a_raw", dtype=torch.float32, shape=(N, H_v))
+    _need(b_raw, "b_raw", dtype=torch.float32, shape=(N, H_v))
     for name, t in (("cu_seqlens", cu_seqlens), ("q_raw", q_raw), ("k_raw", k_raw),
                     ("v_raw", v_raw), ("conv_wq", conv_wq), ("conv_wk", conv_wk),
                     ("conv_wv", conv_wv), ("a_raw", a_raw), ("b_raw", b_raw)):
         _dev(t, name)
-    N = q_raw.shape[0]
-    d_k = q_raw.numel() // max(1, N * H_qk)
-    d_v = v_raw.numel() // max(1, N * H_v)
     a = PrefillArgs()
     a.n_seq = cu_seqlens.shape[0] - 1
     a.H_qk, a.H_v, a.d_k, a.d_v = H_qk, H_v, d_k, d_v
     a.rule = RULES["gated_delta"]
     a.state_dtype = F32
     a.act_dtype = _dtype_code(q_raw)
-    a.use_frontend, a.conv_k, a.chunk, a.ckpt_interval = 1, conv_wq.shape[1], 64, 0
+    a.use_frontend, a.conv_k, a.chunk, a.ckpt_interval = 1, K, 64, 0
     a.n_tokens, a.n_slots = N, 0
     a.scale, a.eps = 1.0, float(eps)
     a.cu_seqlens, a.q, a.k, a.v = _ptr(cu_seqlens), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw)
@@ -360,20 +458,54 @@ def make_conv_args(q_raw, k_raw, v_raw, conv_pool, *, H_qk, H_v, read_slot=None,
     H_qk*d_k], v_raw [B, H_v*d_v]; store: the same over n_tokens rows with
     cu_seqlens [B+1].  conv_pool: [n_slots, conv_k-1, 2*H_qk*d_k + H_v*d_v].
     outputs: (q, k, v, g, beta) tensors or None.  Returns (args, keepalive)."""
+    _need(q_raw, "q_raw", dtypes=_ACT)
+    rows = q_raw.shape[0]
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", dtype=torch.int32)
+        if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
+            raise ValueError("cu_seqlens must be [n_seq + 1]")
+    B = rows if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    _need(conv_pool, "conv_pool", dtype=q_raw.dtype)
+    if conv_pool.dim() != 3:
+        raise ValueError(f"conv_pool must be [n_slots, conv_k - 1, C], got {tuple(conv_pool.shape)}")
+    if rows:
+        d_k = _row_dim(q_raw, "q_raw", rows, H_qk)
+        d_v = _row_dim(v_raw, "v_raw", rows, H_v)
+    else:  # an empty store: the head sizes come from the pool's channel count
+        d_k = q_raw.shape[-1] // H_qk if q_raw.dim() == 2 else q_raw.shape[-1]
+        d_v = v_raw.shape[-1] // H_v if v_raw.dim() == 2 else v_raw.shape[-1]
+    _need(k_raw, "k_raw", dtype=q_raw.dtype, shape=q_raw.shape)
+    _need(v_raw, "v_raw", dtype=q_raw.dtype)
+    C = 2 * H_qk * d_k + H_v * d_v
+    if conv_pool.shape[2] != C:
+        raise ValueError(f"conv_pool must have {C} channels (2*H_qk*d_k + H_v*d_v), "
+                         f"got {tuple(conv_pool.shape)}")
+    K = conv_pool.shape[1] + 1
+    _need(read_slot, "read_slot", dtype=torch.int32, shape=(B,))
+    _need(write_slot, "write_slot", dtype=torch.int32, shape=(B,))
+    _need(a_raw, "a_raw", dtype=torch.float32, shape=(B, H_v))
+    _need(b_raw, "b_raw", dtype=torch.float32, shape=(B, H_v))
+    _need(conv_wq, "conv_wq", dtype=torch.float32, shape=(H_qk * d_k, K))
+    _need(conv_wk, "conv_wk", dtype=torch.float32, shape=(H_qk * d_k, K))
+    _need(conv_wv, "conv_wv", dtype=torch.float32, shape=(H_v * d_v, K))
+    if outputs is not None:
+        qo, ko, vo, go, bo = outputs
+        _need(qo, "q_out", dtype=q_raw.dtype, shape=(B, H_qk, d_k))
+        _need(ko, "k_out", dtype=q_raw.dtype, shape=(B, H_qk, d_k))
+        _need(vo, "v_out", dtype=q_raw.dtype, shape=(B, H_v, d_v))
+        _need(go, "g_out", dtype=torch.float32, shape=(B, H_v))
+        _need(bo, "beta_out", dtype=torch.float32, shape=(B, H_v))
+    _status(status)
     for name, t in (("q_raw", q_raw), ("k_raw", k_raw), ("v_raw", v_raw),
                     ("conv_pool", conv_pool), ("read_slot", read_slot),
                     ("write_slot", write_slot), ("cu_seqlens", cu_seqlens), ("a_raw", a_raw),
                     ("b_raw", b_raw), ("conv_wq", conv_wq), ("conv_wk", conv_wk),
                     ("conv_wv", conv_wv), ("status", status)):
         _dev(t, name)
-    rows = q_raw.shape[0]
-    B = rows if cu_seqlens is None else cu_seqlens.shape[0] - 1
-    d_k = q_raw.shape[-1] // H_qk if q_raw.dim() == 2 else q_raw.shape[-1]
-    d_v = v_raw.shape[-1] // H_v if v_raw.dim() == 2 else v_raw.shape[-1]
     a = ConvArgs()
     a.B, a.H_qk, a.H_v, a.d_k, a.d_v = B, H_qk, H_v, d_k, d_v
     a.act_dtype = _dtype_code(q_raw)
-    a.conv_k = conv_pool.shape[1] + 1
+    a.conv_k = K
     a.reserved0 = a.reserved1 = 0
     a.n_slots = conv_pool.shape[0]
     a.n_tokens = 0 if cu_seqlens is None else rows
