@@ -41,7 +41,8 @@ struct MixedLayout {
   static_assert(NT % DT == 0, "whole decode workers per block");
   // with the chain's own wave count the block runs gdn_prefill's chain
   static constexpr bool OWN_CHAIN = NW == kPrefillWaves<DK, DV, F32>;
-  static constexpr size_t PREFILL = OWN_CHAIN ? kChainLds<DK, DV, F32> : PrefillLayout<DK, DV, F32>::BYTES;
+  static constexpr size_t PREFILL =
+      OWN_CHAIN ? kChainLds<DK, DV, F32, AB> : PrefillLayout<DK, DV, F32, AB>::BYTES;
   // one worker's reduction area, rounded to 16 bytes so every worker's is aligned alike
   static constexpr size_t RED = (sizeof(float) * DecodeShape<SB, DK, DV, DT>::LDS_FLOATS + 15) / 16 * 16;
   static constexpr size_t ORDER = slot_order_lds_bytes(kOrderMaxB, kOrderMaxSlots, NT);
@@ -94,7 +95,7 @@ __global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32>::NT)) void mixed_
 
 template <bool SB, bool AB, int DK, int DV>
 static gdn_status launch_mixed_t(const DecodeParams &dp, const PrefillParams &pp, hipStream_t s) {
-  constexpr bool F32 = !AB;
+  constexpr bool F32 = !AB || !SB;  // the prefill chain's arithmetic, as in gdn_prefill
   using L = MixedLayout<SB, AB, DK, DV, F32>;
   if constexpr (L::BYTES > 160 * 1024) {
     return GDN_ERR_UNSUPPORTED;

@@ -71,29 +71,33 @@ struct PrefillParams {
   const int32_t *ckpt_slot;
 };
 
-// LDS layout of the chain kernel (byte offsets).  OT is the operand storage
-// type: raw BF16 bits, or float on the FP32 path.  Rows are padded by 16
+// LDS layout of the chain kernel (byte offsets).  IT is the storage type of
+// the staged inputs (K, Q, V rows: the activation dtype, BF16 bits or float);
+// OT that of the chunk-local operand L o P: BF16 bits, or float on the FP32
+// path (F32), which also keeps A and T_ii in float.  Rows are padded by 16
 // bytes so the 16 lanes of a fragment read hit different banks.  The chunk's
 // inputs (K, Q, V rows and the gates) live in one of two alternating sets:
 // while a chunk computes from one set, the next chunk's inputs are written
 // into the other.
-template <int DK, int DV, bool F32>
+template <int DK, int DV, bool F32, bool AB = !F32>
 struct PrefillLayout {
+  using IT = std::conditional_t<AB, uint16_t, float>;
   using OT = std::conditional_t<F32, float, uint16_t>;
+  static_assert(F32 || AB, "FP32 activations take FP32 operands");
   static constexpr int C = 64;
   static constexpr int DKP = DK < 32 ? 32 : DK;  // MFMA K-steps are 32 wide
-  static constexpr int PADE = 16 / (int)sizeof(OT);
-  static constexpr int LDK = DKP + PADE;  // Kh, Qh (token rows)
-  static constexpr int LDC = C + PADE;    // Sq (rows of 64 tokens)
+  static constexpr int PADI = 16 / (int)sizeof(IT), PADO = 16 / (int)sizeof(OT);
+  static constexpr int LDK = DKP + PADI;  // Kh, Qh (token rows)
+  static constexpr int LDC = C + PADO;    // Sq (rows of 64 tokens)
   static constexpr int LDF = C + 4;       // Af, Tf (float)
-  static constexpr int LDV = DV + PADE;   // Vh rows (64 tokens x d_v)
+  static constexpr int LDV = DV + PADI;   // Vh rows (64 tokens x d_v)
   // one input set
   static constexpr size_t KH = 0;
-  static constexpr size_t QH = KH + (size_t)C * LDK * sizeof(OT);
-  static constexpr size_t VH = QH + (size_t)C * LDK * sizeof(OT);
+  static constexpr size_t QH = KH + (size_t)C * LDK * sizeof(IT);
+  static constexpr size_t VH = QH + (size_t)C * LDK * sizeof(IT);
   // G, gamma, beta, exp(G_last - G), scale * gamma, e * gamma (e = 1 for the
   // delta rules, else 0)
-  static constexpr size_t GATES = VH + (size_t)C * LDV * sizeof(OT);
+  static constexpr size_t GATES = VH + (size_t)C * LDV * sizeof(IT);
   static constexpr size_t SET = GATES + 6 * C * 4;  // bytes per set
   // shared by both sets
   static constexpr size_t SQ = 2 * SET;
@@ -105,6 +109,7 @@ struct PrefillLayout {
   // where no FP32 reader needs them: in the AF and TF regions
   static constexpr int LDAB = C + 8, LDTB = 16 + 8;
   static_assert((size_t)C * LDAB * 2 <= (size_t)C * LDF * 4 && LDTB * 2 <= LDT * 4, "BF16 copies fit");
+  static_assert(SET % 16 == 0, "16-byte aligned sets");
 };
 
 // ---- MFMA fragments -------------------------------------------------------
@@ -127,12 +132,27 @@ __device__ __forceinline__ const void *frag_addr(const void *base, int esize, in
   return static_cast<const char *>(base) + ((r0 + (l & 15)) * ld + k0 + 8 * (l >> 4)) * esize;
 }
 
+// Eight BF16 values (16 raw bytes) as an operand fragment: as loaded for BF16
+// operands, widened exactly for FP32 ones.
+template <bool F32>
+__device__ __forceinline__ Frag<F32> frag_of_bf16(const uint4 &u) {
+  Frag<F32> f;
+  if constexpr (F32) {
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      f.v[2 * j] = bf16_lo(w[j]);
+      f.v[2 * j + 1] = bf16_hi(w[j]);
+    }
+  } else {
+    f.v = __builtin_bit_cast(bf16x8_t, u);
+  }
+  return f;
+}
+
 template <bool F32>
 __device__ __forceinline__ Frag<F32> load_frag(const uint16_t *base, int ld, int r0, int k0) {
-  static_assert(!F32, "FP32 fragments come from float buffers");
-  Frag<false> f;
-  f.v = __builtin_bit_cast(bf16x8_t, *static_cast<const uint4 *>(frag_addr(base, 2, ld, r0, k0)));
-  return f;
+  return frag_of_bf16<F32>(*static_cast<const uint4 *>(frag_addr(base, 2, ld, r0, k0)));
 }
 template <bool F32>
 __device__ __forceinline__ Frag<F32> load_frag(const float *base, int ld, int r0, int k0) {
@@ -190,16 +210,13 @@ __device__ __forceinline__ Frag<F32> bfrag(const f32x4_t &lo, const f32x4_t &hi)
 // at columns k0 + 4g + {0..3} and k0 + 16 + 4g + {0..3}.
 template <bool F32>
 __device__ __forceinline__ Frag<F32> load_afrag(const uint16_t *base, int ld, int r0, int k0) {
-  static_assert(!F32, "FP32 fragments come from float buffers");
   const int l = threadIdx.x & 63;
   const uint16_t *row = base + (r0 + (l & 15)) * ld + k0 + 4 * (l >> 4);
   uint4 u;
   const uint2 a = *reinterpret_cast<const uint2 *>(row);
   const uint2 b = *reinterpret_cast<const uint2 *>(row + 16);
   u.x = a.x; u.y = a.y; u.z = b.x; u.w = b.y;
-  Frag<false> f;
-  f.v = __builtin_bit_cast(bf16x8_t, u);
-  return f;
+  return frag_of_bf16<F32>(u);
 }
 template <bool F32>
 __device__ __forceinline__ Frag<F32> load_afrag(const float *base, int ld, int r0, int k0) {
@@ -226,16 +243,13 @@ __device__ __forceinline__ Frag<F32> load_afrag(const float *base, int ld, int r
 // row k0 + 4g + s / 4, columns r0 + 4 (s % 4) .. +3 -- 8 contiguous bytes.
 template <bool F32>
 __device__ __forceinline__ Frag<F32> load_afrag_t(const uint16_t *base, int ld, int r0, int k0) {
-  static_assert(!F32, "FP32 fragments come from float buffers");
   typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
   const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
   const uint16_t *a = base + (k0 + 4 * g + (s >> 2)) * ld + r0 + 4 * (s & 3);
   const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a));
   const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(a + 16 * ld));
   const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
-  Frag<false> f;
-  f.v = __builtin_bit_cast(bf16x8_t, make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
-  return f;
+  return frag_of_bf16<F32>(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
 }
 // Four consecutive rows of one column, in the accumulator layout: lane (g, n)
 // gets base[(r0 + 4g + e) * ld + c0 + n], e = 0..3 -- one transposing load

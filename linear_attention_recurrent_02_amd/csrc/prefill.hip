@@ -12,7 +12,7 @@ namespace gdn {
 template <bool SB, bool AB, int DK, int DV, bool F32, bool CK>
 __global__ __launch_bounds__((64 * kPrefillWaves<DK, DV, F32>)) void prefill_kernel(PrefillParams p,
                                                                                    int n_chains) {
-  __shared__ __align__(16) char smem[kChainLds<DK, DV, F32>];
+  __shared__ __align__(16) char smem[kChainLds<DK, DV, F32, AB>];
   const int chain = chain_of_block(blockIdx.x);
   if (chain < n_chains) run_chain<SB, AB, DK, DV, F32, CK>(p, chain, smem);
 }
@@ -35,9 +35,11 @@ PrefillParams make_prefill_params(const gdn_prefill_args &a, const void *q, cons
 
 template <bool SB, bool AB, int DK, int DV>
 static gdn_status launch_chains(const PrefillParams &p, hipStream_t s) {
-  constexpr bool F32 = !AB;  // FP32 activations take the FP32 MFMA path
-  if constexpr (kChainLds<DK, DV, F32> > 160 * 1024) {
-    return GDN_ERR_UNSUPPORTED;  // FP32 operands at d = 128 do not fit in LDS
+  // FP32 arithmetic (FP32 MFMA operands) for an FP32 state or FP32
+  // activations; BF16 MFMA operands only when both are BF16
+  constexpr bool F32 = !AB || !SB;
+  if constexpr (kChainLds<DK, DV, F32, AB> > 160 * 1024) {
+    return GDN_ERR_UNSUPPORTED;  // FP32 activation tiles at d = 128 do not fit in LDS
   } else {
     const int n_chains = p.n_seq * p.H_v;
     const int blocks = (n_chains + 15) / 16 * 16;

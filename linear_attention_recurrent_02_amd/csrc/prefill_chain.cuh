@@ -78,10 +78,11 @@ template <bool SB, bool AB, int DK, int DV, bool F32, int NW, bool CK = false>
 __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain, char *smem) {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves per chain");
   constexpr int NT = 64 * NW;
-  using L = PrefillLayout<DK, DV, F32>;
-  using OT = typename L::OT;
+  using L = PrefillLayout<DK, DV, F32, AB>;
+  using OT = typename L::OT;  // L o P
+  using IT = typename L::IT;  // staged K, Q, V rows
   using AT = typename Elem<AB>::T;
-  static_assert(sizeof(AT) == sizeof(OT), "operands are staged in the activation dtype");
+  static_assert(sizeof(AT) == sizeof(IT), "inputs are staged in the activation dtype");
   constexpr int C = L::C;
   constexpr int LDK = L::LDK, LDC = L::LDC, LDF = L::LDF, LDV = L::LDV;
   constexpr int NKB = L::DKP / 32;  // MFMA K-steps over d_k
@@ -103,14 +104,14 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   constexpr int V_GROUPS = C * (DV / 8), V_PER = (V_GROUPS + NT - 1) / NT;
   constexpr float LOG2E = 1.4426950408889634f;
   // this chunk's input set (K, Q, V rows and gates); the sets alternate
-  OT *Kh, *Qh, *Vh;
+  IT *Kh, *Qh, *Vh;
   float *Gs, *gam, *bet, *eGn;  // cumulative log2 decay, gamma, beta, exp(G_last - G)
   float *gsc, *gme;             // scale * gamma (the read-out), e * gamma (R's K M term)
   auto use_set = [&](int b) {
     char *base = smem + b * L::SET;
-    Kh = reinterpret_cast<OT *>(base + L::KH);
-    Qh = reinterpret_cast<OT *>(base + L::QH);
-    Vh = reinterpret_cast<OT *>(base + L::VH);
+    Kh = reinterpret_cast<IT *>(base + L::KH);
+    Qh = reinterpret_cast<IT *>(base + L::QH);
+    Vh = reinterpret_cast<IT *>(base + L::VH);
     Gs = reinterpret_cast<float *>(base + L::GATES);
     gam = Gs + C; bet = Gs + 2 * C; eGn = Gs + 3 * C; gsc = Gs + 4 * C; gme = Gs + 5 * C;
   };
@@ -218,8 +219,8 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
   };
   auto stage = [&](int b) {  // into input set b
     char *base = smem + b * L::SET;
-    OT *const sK = reinterpret_cast<OT *>(base + L::KH), *const sQ = reinterpret_cast<OT *>(base + L::QH);
-    OT *const sV = reinterpret_cast<OT *>(base + L::VH);
+    IT *const sK = reinterpret_cast<IT *>(base + L::KH), *const sQ = reinterpret_cast<IT *>(base + L::QH);
+    IT *const sV = reinterpret_cast<IT *>(base + L::VH);
     float *const sG = reinterpret_cast<float *>(base + L::GATES);
 #pragma unroll
     for (int i = 0; i < KQ_PER; ++i) {
@@ -293,7 +294,7 @@ __device__ __forceinline__ void prefill_chain(const PrefillParams &p, int chain,
     constexpr int PADC = L::DKP - DK;
     for (int i = tid; i < 4 * C * PADC; i += NT) {
       const int row = i / PADC, c = DK + i % PADC;  // rows of K0, Q0, K1, Q1
-      OT *rowp = reinterpret_cast<OT *>(smem + (row / (2 * C)) * L::SET + ((row / C) & 1 ? L::QH : L::KH));
+      IT *rowp = reinterpret_cast<IT *>(smem + (row / (2 * C)) * L::SET + ((row / C) & 1 ? L::QH : L::KH));
       put(rowp + (row % C) * LDK + c, 0.f);
     }
   }

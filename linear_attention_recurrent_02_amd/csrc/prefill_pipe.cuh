@@ -601,9 +601,9 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
 }
 
 // The chain a shape runs, and its LDS bytes.
-template <int DK, int DV, bool F32>
+template <int DK, int DV, bool F32, bool AB>
 constexpr size_t kChainLds =
-    kPrefillPipe<DK, DV, F32> ? PipeLayout<DK, DV>::BYTES : PrefillLayout<DK, DV, F32>::BYTES;
+    kPrefillPipe<DK, DV, F32> ? PipeLayout<DK, DV>::BYTES : PrefillLayout<DK, DV, F32, AB>::BYTES;
 
 template <bool SB, bool AB, int DK, int DV, bool F32, bool CK = false>
 __device__ __forceinline__ void run_chain(const PrefillParams &p, int chain, char *smem) {

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 from linear_attention_recurrent_02_amd import gdn_decode, synthetic as syn
-from gpu_util import f64, say, scaled_err, tol
+from gpu_util import f64, say, scaled_err, state_tol, tol
 
 pytestmark = pytest.mark.gpu
 RULES = ["linear", "gated", "delta", "gated_delta"]
@@ -85,7 +85,7 @@ def test_decode_shapes_and_dtypes(dk, dv, sdt, adt):
     o, dpool, ro, rpool, code = run_both(case, "gated_delta", scale=0.5)
     ws = case[7].numpy()
     assert scaled_err(f64(o), ro, 2) < tol(adt)
-    assert scaled_err(f64(dpool)[ws], rpool[ws], 2) < tol(sdt)
+    assert scaled_err(f64(dpool)[ws], rpool[ws], 2) < state_tol(sdt)
 
 
 @pytest.mark.parametrize("group", [1, 4])
@@ -206,26 +206,25 @@ def test_empty_batch_is_a_no_op():
     assert o.shape == (0, 4, 64) and torch.equal(pool, before)
 
 
-def test_decode_b512_full_size_sampled():
+def test_decode_b512_full_size():
     """Batch 512 at the benchmark's shapes (one layer: a 512-slot, 512 MiB BF16 pool,
-    in place), checked on 24 sampled requests computed one by one by the oracle."""
-    say("decode_b512 one layer, sampled")
+    in place, slots a seeded permutation), every (request, head) tile's o and
+    written state against the oracle."""
+    say("decode_b512 one layer, every request")
     B, Hqk, Hv, d, n = 512, 16, 32, 128, 512
     q, k, v, g, beta = syn.token_inputs(2, 0, B, Hqk, Hv, d, d, torch.bfloat16)
     pool = syn.state_pool(2, 0, n, Hv, d, d, torch.bfloat16, on_device=True)
     rs, ws = syn.distinct_slots(2, 0, n, B, in_place=True)
-    sample = np.random.default_rng(5).choice(B, 24, replace=False)
-    before = pool[rs[sample].long().to(DEV)].cpu()
+    before = pool.cpu()
     dq, dk_, dv_, dg, db = (t.to(DEV) for t in (q, k, v, g, beta))
     o = gdn_decode(dq, dk_, dv_, dg, db, pool, rs.to(DEV), ws.to(DEV))
     torch.cuda.synchronize()
-    sel = torch.from_numpy(sample)
-    ro, rpool, _ = oracle.decode(f64(q[sel]), f64(k[sel]), f64(v[sel]), f64(g[sel]),
-                                 f64(beta[sel]), f64(before), np.arange(24, dtype=np.int32),
-                                 np.arange(24, dtype=np.int32), round_state=True)
-    assert scaled_err(f64(o.cpu()[sel]), ro, 2) < 2e-2
-    after = pool[ws[sample].long().to(DEV)].cpu()
-    assert scaled_err(f64(after), rpool, 2) < 2e-2
+    ro, rpool, code = oracle.decode(f64(q), f64(k), f64(v), f64(g), f64(beta), f64(before),
+                                    rs.numpy(), ws.numpy(), round_state=True)
+    assert code == 0
+    assert scaled_err(f64(o.cpu()), ro, 2) < 2e-2
+    w = ws.numpy()
+    assert scaled_err(f64(pool.cpu())[w], rpool[w], 2) < 2e-2
 
 
 @pytest.mark.parametrize("B,n_slots", [(4200, 8400), (64, 40000)])

@@ -9,7 +9,7 @@ import oracle
 from linear_attention_recurrent_02_amd import (gdn_decode, gdn_mixed, gdn_prefill,
                                                make_decode_args, make_prefill_args,
                                                synthetic as syn)
-from gpu_util import f64, say, scaled_err, seq_err
+from gpu_util import f64, say, scaled_err, seq_err, state_tol, tol
 
 pytestmark = pytest.mark.gpu
 RULES = ["linear", "gated", "delta", "gated_delta"]
@@ -85,17 +85,27 @@ def test_mixed_equals_separate_and_oracle(rule):
                        c["pool"][untouched].view(torch.int16))
 
 
-def test_mixed_fp32_state_equals_separate():
-    """FP32 state pool with BF16 activations at d = 128: the mixed launch runs
-    4-wave blocks (plain chains) while gdn_prefill runs the pipelined chain;
-    the two chains compute the same products in the same order, so the
-    results still equal the separate calls bit for bit."""
+def test_mixed_fp32_state_equals_separate_and_oracle():
+    """FP32 state pool with BF16 activations at d = 128: the mixed launch's
+    chains and gdn_prefill both run the FP32 chain (4 waves), so the results
+    equal the separate calls bit for bit, and the FP32 states (decode and
+    prefill halves) meet the FP32 bar against the oracle."""
     say("mixed fp32 state")
     c = build(404, 7, [70, 130, 1], 2, 4, 128, 48, frontend=False, std=0.05, sdt=torch.float32)
     do, po, pool = run_mixed(c, "gated_delta")
     so, spo, spool = run_separate(c, "gated_delta")
     assert torch.equal(do, so) and torch.equal(po, spo)
     assert torch.equal(pool, spool)
+    q, k, v, g, beta = c["dec"]
+    ro, rpool, _ = oracle.decode(f64(q), f64(k), f64(v), f64(g), f64(beta), f64(c["pool"]),
+                                 c["drs"].numpy(), c["dws"].numpy(), round_state=False)
+    pq, pk, pv, pg, pb = c["pin"]["final"]
+    rpo, rpool, _ = oracle.sequences(c["cu"].numpy(), f64(pq), f64(pk), f64(pv), f64(pg), f64(pb),
+                                     rpool, c["prs"].numpy(), c["pws"].numpy(), round_state=False)
+    assert scaled_err(f64(do), ro, 2) < tol(torch.bfloat16)
+    assert seq_err(f64(po), rpo, c["cu"]) < tol(torch.bfloat16)
+    w = np.concatenate([c["dws"].numpy(), c["pws"].numpy()])
+    assert scaled_err(f64(pool)[w], rpool[w], 2) < state_tol(torch.float32)
 
 
 def test_mixed_checkpoints_equal_separate():
@@ -159,36 +169,42 @@ def test_mixed_uneven_workers():
         assert torch.equal(pool.view(torch.int16), spool.view(torch.int16)), rule
 
 
-def test_mixed_full_size_sampled():
-    """448 decode requests (each update rule on a quarter of them would need four
-    calls; here all four rules run back to back on the same pool state) plus 4
-    prefills of 8192 tokens through the fused front-end, one 1024-slot BF16 pool,
-    25% of the requests reading a checkpoint slot.  Mixed = separate bit for bit;
-    the oracle checks 16 sampled decode requests and two heads of every prefill."""
+def test_mixed_full_size():
+    """448 decode requests (each update rule in turn, every rule from the same
+    pool state) plus 4 prefills of 8192 tokens through the fused front-end, one
+    1024-slot BF16 pool, 25% of the requests reading a checkpoint slot.  Mixed =
+    separate bit for bit; every decode request's o and written state against
+    the oracle, and eight state heads of every prefill."""
     wl = syn.WORKLOADS["mixed"]
     Hqk, Hv, d = wl["H_qk"], wl["H_v"], wl["d_k"]
+    nd = wl["n_decode"]
     lengths = [wl["prefill_len"]] * wl["n_prefill"]
-    c = build(wl["index"], wl["n_decode"], lengths, Hqk, Hv, d, wl["n_slots"], frontend=True)
+    c = build(wl["index"], nd, lengths, Hqk, Hv, d, wl["n_slots"], frontend=True)
+    # the decode half's initial states, one per request (zero for a fresh one)
+    rs_all = c["drs"].numpy()
+    start = np.zeros((nd, Hv, d, d))
+    live = rs_all >= 0
+    start[live] = f64(c["pool"][torch.from_numpy(rs_all[live]).long()])
+    own = np.arange(nd, dtype=np.int32)
+    q, k, v, g, beta = (t.cpu() for t in c["dec"])
+    w_dec = c["dws"].numpy()
     for rule in RULES:
         say("mixed full size", rule)
         do, po, pool = run_mixed(c, rule)
         so, spo, spool = run_separate(c, rule)
         assert torch.equal(do, so) and torch.equal(po, spo), rule
         assert torch.equal(pool.view(torch.int16), spool.view(torch.int16)), rule
-        sample = np.random.default_rng(7).choice(wl["n_decode"], 16, replace=False)
-        q, k, v, g, beta = (t[sample].cpu() for t in c["dec"])
-        rs = c["drs"].numpy()[sample]
-        ro, _, _ = oracle.decode(f64(q), f64(k), f64(v), f64(g), f64(beta),
-                                 f64(c["pool"][torch.from_numpy(np.maximum(rs, 0)).long()]),
-                                 np.where(rs >= 0, np.arange(16), -1).astype(np.int32),
-                                 np.full(16, -1, np.int32), rule=rule, round_state=True)
-        assert scaled_err(f64(do.cpu()[sample]), ro, 2) < 2e-2, rule
-    # prefill half (gated_delta) on two heads, initial states from the pool
+        ro, rpool, _ = oracle.decode(f64(q), f64(k), f64(v), f64(g), f64(beta), start,
+                                     np.where(live, own, -1).astype(np.int32), own, rule=rule,
+                                     round_state=True)
+        assert scaled_err(f64(do.cpu()), ro, 2) < 2e-2, rule
+        assert scaled_err(f64(pool[torch.from_numpy(w_dec).long().to(DEV)].cpu()), rpool, 2) < 2e-2, rule
+    # prefill half (gated_delta) on eight state heads, initial states from the pool
     x = c["pin"]["raw"]
     cu = c["cu"]
     pc = po.cpu()
     pool_after = pool.cpu()
-    for j in (0, 9):
+    for j in (0, 5, 9, 15):
         hs = [2 * j, 2 * j + 1]
         qs, vs = slice(j * d, (j + 1) * d), slice(2 * j * d, (2 * j + 2) * d)
         rq, rk, rv, rg, rb = oracle.frontend(cu.numpy(), f64(x["q_raw"][:, qs]),
