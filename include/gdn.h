@@ -28,7 +28,8 @@
  *    state pool, the front-end's raw inputs, conv weights and outputs, and
  *    the workspace are read and written as 16-byte vectors and must be
  *    16-byte aligned (GDN_ERR_ALIGN otherwise); the library never allocates, frees or
- *    synchronises, keeps no global mutable state, and reads argument structs
+ *    synchronises, keeps no global mutable state other than one cached device
+ *    address per GPU for gdn_prefill_noalloc, and reads argument structs
  *    only during the call.  All work is enqueued on `stream` (a hipStream_t;
  *    NULL = the null stream).
  *  - State tensors hold M = S with rows indexed by the key dimension:
@@ -67,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 4
+#define GDN_ABI_VERSION 5
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -96,7 +97,9 @@ typedef enum gdn_status {
   GDN_ERR_WORKSPACE = 6,   /* workspace missing or smaller than gdn_prefill_workspace_size */
   GDN_ERR_LAUNCH = 7,      /* the HIP runtime refused a launch */
   GDN_ERR_SLOTS = 8,       /* gdn_validate_slots found a range error or a hazard */
-  GDN_ERR_ALIGN = 9        /* a tensor pointer that is read as 16-byte vectors is not 16-byte aligned */
+  GDN_ERR_ALIGN = 9,       /* a tensor pointer that is read as 16-byte vectors is not 16-byte aligned */
+  GDN_ERR_SCRATCH = 10     /* gdn_prefill_noalloc: the call needs more workspace than the
+                              library's fixed device workspace holds */
 } gdn_status;
 
 /* bits set in the optional device status word: a request (decode) or
@@ -278,6 +281,27 @@ size_t gdn_conv_slot_bytes(int32_t H_qk, int32_t H_v, int32_t d_k, int32_t d_v, 
  * final state (FP32 across chunks, rounded once when stored as BF16) into
  * write_slot[s]. */
 gdn_status gdn_prefill(const gdn_prefill_args *args, void *stream);
+
+/* gdn_prefill for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * The same kernels and results as gdn_prefill, but the front-end's workspace
+ * is a fixed device array inside the library (gdn_noalloc_workspace_bytes()
+ * bytes, 128 MiB: 8,065 tokens with the fused front-end at H_qk = 16,
+ * H_v = 32, d = 128 in BF16, any number without it; gdn_prefill_workspace_size()
+ * tells what a call needs), so args->workspace
+ * and args->workspace_bytes are ignored.  The caller still owns and passes
+ * every input and output.  Nothing is allocated or freed: each GPU the
+ * library runs on holds its own copy of the array from the first use until
+ * the process ends, and the first call on a device looks up its address
+ * (hipGetSymbolAddress).  A call that would need more workspace returns
+ * GDN_ERR_SCRATCH and launches nothing; other errors as for gdn_prefill.
+ * Calls on one GPU share its array, whatever their stream: calls that
+ * overlap in time on one GPU race (serialise them, e.g. on one stream).  No
+ * part of the array needs clearing: each call writes every byte it reads. */
+gdn_status gdn_prefill_noalloc(const gdn_prefill_args *args, void *stream);
+
+/* Bytes of gdn_prefill_noalloc's fixed workspace (host-only). */
+size_t gdn_noalloc_workspace_bytes(void);
 
 /* A decode batch and a prefill batch in ONE kernel launch (each half has its
  * own rule and slot arrays; they may share a pool).  The halves' results are

@@ -2,9 +2,17 @@
 // argument validation (host only, before any HIP call) and dispatch.
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "internal.h"
+
+// The workspace of gdn_prefill_noalloc: a fixed device array of this file, one
+// copy on every GPU the library runs on, held until the process ends.  In host
+// code `scratch` names a host-side stand-in, never device memory: host code
+// uses only the per-device address that hipGetSymbolAddress returns.
+static constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -123,6 +131,25 @@ gdn_status check_conv(const gdn_conv_args *a, bool decode) {
   return GDN_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+gdn_status scratch_address(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return GDN_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return GDN_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GDN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -190,6 +217,27 @@ gdn_status gdn_prefill(const gdn_prefill_args *args, void *stream) {
   return gdn::launch_prefill(*args, static_cast<hipStream_t>(stream));
 }
 
+gdn_status gdn_prefill_noalloc(const gdn_prefill_args *args, void *stream) {
+  if (!args) return GDN_ERR_NULL;
+  gdn_prefill_args a = *args;
+  a.workspace = nullptr;
+  a.workspace_bytes = 0;
+  // every other check first; the only one left to fail is the workspace's
+  gdn_status st = check_prefill(&a, true);
+  if (st != GDN_OK && st != GDN_ERR_WORKSPACE) return st;
+  if (a.n_seq == 0) return GDN_OK;
+  const size_t need = gdn::prefill_workspace_bytes(a);
+  if (need > kScratchBytes) return GDN_ERR_SCRATCH;
+  if (need > 0) {
+    st = scratch_address(&a.workspace);
+    if (st != GDN_OK) return st;
+    a.workspace_bytes = kScratchBytes;
+  }
+  return gdn::launch_prefill(a, static_cast<hipStream_t>(stream));
+}
+
+size_t gdn_noalloc_workspace_bytes(void) { return kScratchBytes; }
+
 gdn_status gdn_mixed(const gdn_decode_args *decode, const gdn_prefill_args *prefill,
                      void *stream) {
   gdn_status st = check_decode(decode);
@@ -238,6 +286,7 @@ const char *gdn_status_string(int32_t status) {
     case GDN_ERR_LAUNCH: return "kernel launch failed";
     case GDN_ERR_SLOTS: return "slot index out of range or slot hazard";
     case GDN_ERR_ALIGN: return "a vector-accessed tensor is not 16-byte aligned";
+    case GDN_ERR_SCRATCH: return "the call needs more than the fixed no-allocation workspace";
   }
   return "unknown status";
 }

@@ -92,6 +92,10 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_frontend.argtypes = [ctypes.POINTER(PrefillArgs), _P, _P, _P, _P, _P, _P]
     lib.gdn_prefill.restype = _I32
     lib.gdn_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _P]
+    lib.gdn_prefill_noalloc.restype = _I32
+    lib.gdn_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _P]
+    lib.gdn_noalloc_workspace_bytes.restype = ctypes.c_size_t
+    lib.gdn_noalloc_workspace_bytes.argtypes = []
     lib.gdn_mixed.restype = _I32
     lib.gdn_mixed.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(PrefillArgs), _P]
     lib.gdn_conv_decode.restype = _I32
@@ -300,13 +304,15 @@ def gdn_decode(q, k, v, g, beta, state_pool, read_slot=None, write_slot=None, o=
 def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slot=None, o=None, *,
                       H_qk, H_v, g=None, beta=None, a_raw=None, b_raw=None, conv_wq=None,
                       conv_wk=None, conv_wv=None, rule="gated_delta", scale=1.0, eps=1e-6,
-                      chunk=64, workspace=None, status=None, ckpt_interval=0, ckpt_slot=None):
+                      chunk=64, workspace=None, status=None, ckpt_interval=0, ckpt_slot=None,
+                      alloc_workspace=True):
     """Build a PrefillArgs struct.  q, k: [N, H_qk*d_k] (or [N, H_qk, d_k]);
     v: [N, H_v*d_v]; with conv weights given the front-end runs (a_raw,
     b_raw are the gate logits), otherwise g, beta are used as given.  With
     ckpt_interval > 0 (a multiple of chunk), ckpt_slot [n_seq, per_seq] int32
     names the slots of the intermediate checkpoints.
-    Returns (args, o, keepalive); allocates the workspace when needed."""
+    Returns (args, o, keepalive); allocates the workspace when needed unless
+    alloc_workspace is False."""
     _need(cu_seqlens, "cu_seqlens", dtype=torch.int32)
     if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
         raise ValueError("cu_seqlens must be [n_seq + 1]")
@@ -370,7 +376,7 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
     a.ckpt_per_seq = 0 if ckpt_slot is None else int(ckpt_slot.shape[-1])
     a.reserved1 = 0
     need = int(load_library().gdn_prefill_workspace_size(ctypes.byref(a)))
-    if need and workspace is None:
+    if need and workspace is None and alloc_workspace:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -387,6 +393,27 @@ def gdn_prefill(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slot=None
     if code:
         raise GdnError("gdn_prefill", code)
     return o
+
+
+def gdn_prefill_noalloc(cu_seqlens, q, k, v, state_pool, read_slot, write_slot, o, *,
+                        stream=None, **kw):
+    """gdn_prefill without any allocation: the library's fixed device
+    workspace replaces the caller's, and the caller passes o [N, H_v, d_v]
+    (nothing is allocated here either).  Returns o."""
+    if o is None:
+        raise ValueError("gdn_prefill_noalloc needs the output tensor o")
+    if kw.get("workspace") is not None:
+        raise ValueError("gdn_prefill_noalloc uses the library's workspace, not the caller's")
+    a, o, keep = make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot, write_slot, o,
+                                   alloc_workspace=False, **kw)
+    code = load_library().gdn_prefill_noalloc(ctypes.byref(a), _stream(stream))
+    if code:
+        raise GdnError("gdn_prefill_noalloc", code)
+    return o
+
+
+def gdn_noalloc_workspace_bytes() -> int:
+    return int(load_library().gdn_noalloc_workspace_bytes())
 
 
 def gdn_frontend(cu_seqlens, q_raw, k_raw, v_raw, *, H_qk, H_v, conv_wq, conv_wk, conv_wv,

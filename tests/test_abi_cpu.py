@@ -11,7 +11,7 @@ import linear_attention_recurrent_02_amd as gdn
 from linear_attention_recurrent_02_amd import gdn as B
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-OK, NULL, SHAPE, DTYPE, RULE, UNSUP, WORKSPACE, LAUNCH, SLOTS, ALIGN = range(10)
+OK, NULL, SHAPE, DTYPE, RULE, UNSUP, WORKSPACE, LAUNCH, SLOTS, ALIGN, SCRATCH = range(11)
 FAKE = 0x10000  # never dereferenced: these calls fail validation before any device work
 
 
@@ -28,7 +28,7 @@ def test_struct_layout_matches():
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
     assert lib.gdn_sizeof_conv_args() == ctypes.sizeof(B.ConvArgs)
-    assert gdn.gdn_abi_version() == 4
+    assert gdn.gdn_abi_version() == 5
 
 
 def test_state_bytes_against_the_pages():
@@ -53,7 +53,7 @@ def test_parse_rule():
 
 
 def test_status_strings():
-    for c in range(10):
+    for c in range(11):
         assert gdn.gdn_status_string(c) != "unknown status"
     assert gdn.gdn_status_string(99) == "unknown status"
 
@@ -133,6 +133,40 @@ def test_prefill_validation(over, code):
     lib = gdn.load_library()
     a = _prefill_args(**over)
     assert lib.gdn_prefill(ctypes.byref(a), None) == code
+
+
+NOALLOC_SAME = [
+    (dict(chunk=32), UNSUP), (dict(rule=9), RULE), (dict(act_dtype=3), DTYPE),
+    (dict(n_seq=-1), SHAPE), (dict(cu_seqlens=None), NULL), (dict(conv_wk=None), NULL),
+    (dict(H_v=5), UNSUP), (dict(n_slots=1), SHAPE), (dict(q=FAKE + 2), ALIGN),
+    (dict(ckpt_interval=32), SHAPE), (dict(reserved1=1), UNSUP),
+]
+
+
+@pytest.mark.parametrize("over,code", NOALLOC_SAME)
+def test_prefill_noalloc_validation(over, code):
+    """The no-allocation prefill refuses what gdn_prefill refuses, before any
+    device work (its workspace fields are ignored, so they cannot fail)."""
+    lib = gdn.load_library()
+    a = _prefill_args(**over)
+    assert lib.gdn_prefill_noalloc(ctypes.byref(a), None) == code
+    assert lib.gdn_prefill(ctypes.byref(a), None) == code
+
+
+def test_prefill_noalloc_too_large_and_empty():
+    lib = gdn.load_library()
+    cap = lib.gdn_noalloc_workspace_bytes()
+    assert cap == 128 << 20
+    # the workload's heads: 16,640 workspace bytes per token (q, k, v in BF16,
+    # g and beta in FP32), so 8,065 tokens fit and 8,066 do not
+    a = _prefill_args(H_qk=16, H_v=32, n_tokens=8065)
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(a)) <= cap
+    a = _prefill_args(H_qk=16, H_v=32, n_tokens=8066)
+    assert lib.gdn_prefill_workspace_size(ctypes.byref(a)) > cap
+    assert lib.gdn_prefill_noalloc(ctypes.byref(a), None) == SCRATCH
+    # an empty batch is a no-op, as for gdn_prefill
+    assert lib.gdn_prefill_noalloc(ctypes.byref(_prefill_args(n_seq=0, n_tokens=0)), None) == OK
+    assert lib.gdn_prefill_noalloc(None, None) == NULL
 
 
 def test_prefill_workspace_size():
