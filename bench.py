@@ -131,6 +131,83 @@ def run_decode(args, torch, gdn, syn):
     return res, layers
 
 
+def run_copy(args, torch):
+    """A plain device-to-device copy of 1 GiB (torch's copy kernel), timed
+    like the decode: the practical streaming ceiling on this machine."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 10
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return dict(bytes_moved=2 * n, ms=round(ms, 4), GBps=round(2 * n / (ms / 1e3) / 1e9, 1))
+
+
+def run_decode_b64(args, torch, gdn, syn):
+    """The B = 64 decode step (H_qk = 16, H_v = 32, d = 128, 64 live slots of a
+    256-slot BF16 pool, distinct read and write slots) for each update rule.
+    Its 134 MB of state would sit in the 256 MB last-level cache if one pool
+    were reused, so each timed step runs the call once on each of 8
+    independent pools (2 GiB in all) in turn; one HIP graph per rule."""
+    wl = syn.WORKLOADS["decode_b64"]
+    B, Hqk, Hv, dk, dv, n = wl["B"], wl["H_qk"], wl["H_v"], wl["d_k"], wl["d_v"], wl["n_slots"]
+    P = 8
+    pools = []
+    for p in range(P):
+        q, k, v, g, beta = (t.cuda() for t in syn.token_inputs(wl["index"], p, B, Hqk, Hv, dk, dv))
+        pool = syn.state_pool(wl["index"], p, n, Hv, dk, dv, torch.bfloat16, on_device=True)
+        rs, ws = (t.cuda() for t in syn.distinct_slots(wl["index"], p, n, B, in_place=False))
+        pools.append((q, k, v, g, beta, pool, rs, ws))
+    torch.cuda.synchronize()
+    lib = gdn.load_library()
+    state_b, other_b = decode_bytes_per_launch(B, Hqk, Hv, dk, dv)
+    per_launch = state_b + other_b
+    out = {}
+    for rule in ("linear", "gated", "delta", "gated_delta"):
+        calls = [gdn.make_decode_args(*t[:8], rule=rule) for t in pools]
+
+        def step():
+            s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+            for a, _, _ in calls:
+                code = lib.gdn_decode(ctypes.byref(a), s)
+                if code:
+                    raise gdn.GdnError("gdn_decode", code)
+
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 4 * args.steps
+        e0.record()
+        for _ in range(reps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * P)
+        gbps = per_launch / (us / 1e6) / 1e9
+        out[rule] = dict(avg_launch_us=round(us, 2), algorithmic_GBps=round(gbps, 1),
+                         hbm_frac=round(gbps / HBM_PEAK_GBPS, 4),
+                         tokens_per_s=round(B / (us / 1e6), 1))
+    return dict(workload="decode_b64 (64 of 256 slots, distinct read/write, 8 rotating pools)",
+                kernel="decode_kernel<bf16 state, bf16 act, 128, 128>", per_launch_bytes=per_launch,
+                pools=P, rules=out)
+
+
 def conv_bytes_per_launch(B, H_qk, H_v, d_k, d_v, act_bytes=2):
     """Algorithmic bytes of one conv-decode launch: per request the raw row in,
     the q|k|v row out, the 3-token window read and written; a/b in, g/beta
@@ -376,13 +453,16 @@ def run_mixed(args, torch, gdn, syn):
     drs, dws, prs, pws = (t.cuda() for t in syn.mixed_slots(wl["index"], nd, npf, wl["n_slots"]))
     cu = syn.cu_from_lengths([L] * npf).cuda()
     x = {kk: vv.cuda() for kk, vv in syn.frontend_inputs(wl["index"], 2, L * npf, Hqk, Hv, d, d, 4).items()}
-    da, do, dkeep = gdn.make_decode_args(q, k, v, g, beta, pool, drs, dws)
+    decs = {rule: gdn.make_decode_args(q, k, v, g, beta, pool, drs, dws, rule=rule)
+            for rule in ("linear", "gated", "delta", "gated_delta")}
     pa, po, pkeep = gdn.make_prefill_args(cu, x["q_raw"], x["k_raw"], x["v_raw"], pool, prs, pws,
                                           H_qk=Hqk, H_v=Hv, a_raw=x["a_raw"], b_raw=x["b_raw"],
                                           conv_wq=x["conv_wq"], conv_wk=x["conv_wk"],
                                           conv_wv=x["conv_wv"])
     lib = gdn.load_library()
     s = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    da = None  # the decode half's arguments, one update rule at a time
 
     def mixed():
         code = lib.gdn_mixed(ctypes.byref(da), ctypes.byref(pa), s())
@@ -407,12 +487,19 @@ def run_mixed(args, torch, gdn, syn):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps
 
-    ms_mixed = timed(mixed, args.prefill_reps)
-    ms_sep = timed(separate, args.prefill_reps)
     tokens = nd + npf * L
+    rules = {}
+    for rule, (a, _, _) in decs.items():
+        da = a
+        ms_mixed = timed(mixed, args.prefill_reps)
+        ms_sep = timed(separate, args.prefill_reps)
+        rules[rule] = dict(ms=round(ms_mixed, 3), tokens_per_s=round(tokens / (ms_mixed / 1e3), 1),
+                           separate_ms=round(ms_sep, 3),
+                           speedup_vs_separate=round(ms_sep / ms_mixed, 3))
+    gd = rules["gated_delta"]
     return dict(workload="mixed", decode_requests=nd, prefill_tokens=npf * L,
-                ms=round(ms_mixed, 3), tokens_per_s=round(tokens / (ms_mixed / 1e3), 1),
-                separate_ms=round(ms_sep, 3), speedup_vs_separate=round(ms_sep / ms_mixed, 3))
+                ms=gd["ms"], tokens_per_s=gd["tokens_per_s"], separate_ms=gd["separate_ms"],
+                speedup_vs_separate=gd["speedup_vs_separate"], decode_rules=rules)
 
 
 def run_cpu_baseline(args, torch, layers, syn):
@@ -437,9 +524,33 @@ def run_cpu_baseline(args, torch, layers, syn):
         del hpool
     B = layers[0][1][0].shape[0]
     per_layer = sum(times) / len(times)
+    # one thread, on the first 64 requests of layer 0 (scaled to the batch)
+    _, keep = layers[0]
+    q, k, v, g, beta, pool, rs, ws = keep[:8]
+    n1 = 64
+    f = lambda t: t[:n1].detach().to("cpu", torch.float64).numpy()
+    hrs = rs[:n1].cpu().numpy()
+    hpool = pool[torch.from_numpy(hrs).long().to(pool.device)].detach().to("cpu", torch.float64).numpy()
+    own = np.arange(n1, dtype=np.int32)
+    t0 = time.perf_counter()
+    oracle.decode(f(q), f(k), f(v), f(g), f(beta), hpool, own, own, round_state=True, n_threads=1)
+    t1 = (time.perf_counter() - t0) * B / n1
+    del hpool
+    model = "?"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return dict(value=B / (per_layer * len(layers)), unit="tokens/s", cores=threads, kind="oracle",
                 sample=f"FP64 oracle on layers {picks} of {len(layers)} at B={B} (all request-heads), "
-                       f"{per_layer:.2f}s per layer; tokens/s extrapolated to {len(layers)} layers")
+                       f"{per_layer:.2f}s per layer; tokens/s extrapolated to {len(layers)} layers",
+                one_thread_value=B / (t1 * len(layers)),
+                one_thread_sample=f"1 thread, {n1} requests of layer 0 ({t1 * n1 / B:.2f}s), "
+                                  f"scaled to B={B} and {len(layers)} layers",
+                cpu_model=model, nproc=os.cpu_count())
 
 
 def main():
@@ -453,6 +564,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill measurement")
     ap.add_argument("--no-conv", action="store_true",
                     help="skip the decode-side conv and the channel-wise decay measurements")
+    ap.add_argument("--no-b64", action="store_true", help="skip the B=64 decode leg")
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=10,
                     help="untimed calls before the prefill and mixed timings")
@@ -487,10 +599,13 @@ def main():
         log(f"copy calibration: 3 copies of {n} bytes")
         del src, dst
 
+    copy = run_copy(args, torch)
+    log(f"copy: {copy}")
     dec, layers = run_decode(args, torch, gdn, syn)
     achieved = dec["bytes_per_launch"] / (dec["avg_launch_us"] / 1e6) / 1e9
     roofline = dict(bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBPS, unit="GB/s",
                     frac=round(achieved / HBM_PEAK_GBPS, 4), traffic=recorded_traffic(),
+                    copy_GBps=copy["GBps"], frac_of_copy=round(achieved / copy["GBps"], 4),
                     kernel="decode_kernel<bf16 state, bf16 act, 128, 128>",
                     per_launch_bytes=dec["bytes_per_launch"],
                     avg_launch_us=round(dec["avg_launch_us"], 2))
@@ -508,6 +623,13 @@ def main():
     prefill = None
     if not args.no_prefill:
         del layers[:]
+        torch.cuda.empty_cache()
+    decode_b64 = None
+    if not args.no_b64:
+        decode_b64 = run_decode_b64(args, torch, gdn, syn)
+        log(f"decode B=64: {decode_b64}")
+        torch.cuda.empty_cache()
+    if not args.no_prefill:
         torch.cuda.empty_cache()
         prefill = run_prefill(args, torch, gdn, syn)
         log(f"prefill: {prefill}")
@@ -537,7 +659,9 @@ def main():
         "total_GBps": round(dec["total_GBps"], 1),
         "hbm_frac": round(dec["total_GBps"] / HBM_PEAK_GBPS, 4),
         "roofline": roofline,
+        "copy": copy,
         "cpu_baseline": cpu,
+        "decode_b64": decode_b64,
         "conv_decode": conv,
         "decode_channel_decay": decode_cw,
         "prefill": prefill,
