@@ -65,6 +65,14 @@ def _load():
         lib.oracle_conv_decode.restype = i32
         lib.oracle_conv_decode.argtypes = [i32, i32, i32, i32, i32, i32, f64, i64,
                                            P, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_q8_encode.restype = i32
+        lib.oracle_q8_encode.argtypes = [i64, i32, i32, i32, P, P, P, P]
+        lib.oracle_decode_q8.restype = i32
+        lib.oracle_decode_q8.argtypes = [i32, i32, i32, i32, i32, i64, i32, f64, i32,
+                                         P, P, P, P, P, P, P, P, P, i32]
+        lib.oracle_decode_cw_q8.restype = i32
+        lib.oracle_decode_cw_q8.argtypes = [i32, i32, i32, i32, i32, i64, i32, f64, i32,
+                                            P, P, P, P, P, P, P, P, P, i32]
         lib.oracle_version.restype = i32
         _lib = lib
     return _lib
@@ -247,3 +255,111 @@ def conv_tail(cu_seqlens, q_raw, k_raw, v_raw, K=4):
             if t >= t0:
                 out[s, j] = rows[t]
     return out
+
+
+# ----------------------------------------------------------------------------
+# 8-bit state storage: the first n_hi key channels (rows) of every tile in
+# BF16, the other rows INT8 with one binary32 scale each (oracle.c states the
+# quantisation).  A stored tile is laid out as
+#   [n_hi, dv] BF16 bits | [dk - n_hi, dv] int8 codes | [dk - n_hi] binary32 scales
+# (little endian), one tile per (slot, head).
+
+def q8_tile_bytes(dk: int, dv: int, n_hi: int) -> int:
+    return n_hi * dv * 2 + (dk - n_hi) * dv + 4 * (dk - n_hi)
+
+
+def q8_encode(values, n_hi: int):
+    """Encode tiles [..., dk, dv] (float64 values).  Returns (bf16 rows as
+    float64 [..., n_hi, dv], codes int8 [..., dk-n_hi, dv], scales float32
+    [..., dk-n_hi])."""
+    v = _f64(values)
+    lead, (dk, dv) = v.shape[:-2], v.shape[-2:]
+    n = int(np.prod(lead)) if lead else 1
+    hi = np.zeros((n, n_hi, dv), np.float64)
+    codes = np.zeros((n, dk - n_hi, dv), np.int8)
+    scales = np.zeros((n, dk - n_hi), np.float32)
+    code = _load().oracle_q8_encode(n, dk, dv, n_hi, _p(v), _p(hi), _p(codes), _p(scales))
+    if code != 0:
+        raise ValueError("oracle_q8_encode rejected its arguments")
+    return (hi.reshape(*lead, n_hi, dv), codes.reshape(*lead, dk - n_hi, dv),
+            scales.reshape(*lead, dk - n_hi))
+
+
+def q8_pack(values, n_hi: int) -> np.ndarray:
+    """Tiles [..., dk, dv] of float64 values -> their stored bytes [...,
+    q8_tile_bytes] (uint8)."""
+    v = _f64(values)
+    dk, dv = v.shape[-2:]
+    hi, codes, scales = q8_encode(v, n_hi)
+    lead = v.shape[:-2]
+    n = int(np.prod(lead)) if lead else 1
+    bits = (hi.reshape(n, -1).astype(np.float32).view(np.uint32) >> 16).astype("<u2")
+    out = np.concatenate([bits.view(np.uint8).reshape(n, -1),
+                          codes.reshape(n, -1).view(np.uint8),
+                          scales.reshape(n, -1).astype("<f4").view(np.uint8).reshape(n, -1)],
+                         axis=1)
+    assert out.shape[1] == q8_tile_bytes(dk, dv, n_hi)
+    return out.reshape(*lead, out.shape[1])
+
+
+def q8_unpack(raw, dk: int, dv: int, n_hi: int) -> np.ndarray:
+    """Stored bytes [..., q8_tile_bytes] -> the float64 values they represent
+    [..., dk, dv]: a BF16 row widened, an INT8 row as code * scale in
+    binary32."""
+    raw = np.ascontiguousarray(np.asarray(raw, np.uint8))
+    tb = q8_tile_bytes(dk, dv, n_hi)
+    lead = raw.shape[:-1]
+    assert raw.shape[-1] == tb, (raw.shape, tb)
+    n = int(np.prod(lead)) if lead else 1
+    r = raw.reshape(n, tb)
+    a, b = n_hi * dv * 2, n_hi * dv * 2 + (dk - n_hi) * dv
+    hi = (r[:, :a].copy().view("<u2").astype(np.uint32) << 16).view(np.float32)
+    codes = r[:, a:b].copy().view(np.int8).astype(np.float32).reshape(n, dk - n_hi, dv)
+    scales = r[:, b:].copy().view("<f4").reshape(n, dk - n_hi, 1)
+    lo = (codes * scales).astype(np.float32)
+    out = np.concatenate([hi.reshape(n, n_hi, dv), lo], axis=1).astype(np.float64)
+    return out.reshape(*lead, dk, dv)
+
+
+def decode_q8(q, k, v, g, beta, pool, read_slot=None, write_slot=None, *, n_hi,
+              rule="gated_delta", scale=1.0, n_threads=None):
+    """One decode token for B requests on a pool kept in the 8-bit format.
+
+    pool: [n_slots, Hv, dk, dv] of the values the stored tiles represent (e.g.
+    q8_unpack of the stored bytes); a copy is updated with the new states as
+    stored (quantised) and returned.  Returns ``(o, pool_after, code)``.
+    """
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    pool = _f64(pool).copy()
+    B, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    rs, ws = _i32(read_slot), _i32(write_slot)
+    o = np.zeros((B, Hv, dv), np.float64)
+    code = _load().oracle_decode_q8(B, Hqk, Hv, dk, dv, pool.shape[0], _rule(rule),
+                                    float(scale), int(n_hi), _p(q), _p(k), _p(v), _p(g),
+                                    _p(beta), _p(pool), _p(rs), _p(ws), _p(o),
+                                    n_threads or default_threads())
+    if code < 0:
+        raise ValueError("oracle_decode_q8 rejected its arguments")
+    return o, pool, code
+
+
+def decode_cw_q8(q, k, v, g, beta, pool, read_slot=None, write_slot=None, *, n_hi,
+                 rule="gated_delta", scale=1.0, n_threads=None):
+    """``decode_cw`` (g of shape [B, Hv, dk]) with the state stored in the
+    8-bit format; pool as for ``decode_q8``.  Returns ``(o, pool_after, code)``."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    pool = _f64(pool).copy()
+    B, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if g.shape != (B, Hv, dk):
+        raise ValueError("g must be [B, Hv, dk]")
+    rs, ws = _i32(read_slot), _i32(write_slot)
+    o = np.zeros((B, Hv, dv), np.float64)
+    code = _load().oracle_decode_cw_q8(B, Hqk, Hv, dk, dv, pool.shape[0], _rule(rule),
+                                       float(scale), int(n_hi), _p(q), _p(k), _p(v), _p(g),
+                                       _p(beta), _p(pool), _p(rs), _p(ws), _p(o),
+                                       n_threads or default_threads())
+    if code < 0:
+        raise ValueError("oracle_decode_cw_q8 rejected its arguments")
+    return o, pool, code

@@ -64,6 +64,20 @@
  *    history (zeros, a fresh request), write index -1 = not stored, the same
  *    slot contract as the recurrent state.  The stored window holds raw
  *    inputs, so it is exact in the input precision.
+ *  - 8-bit state storage ("Seven Architectures ...", ONNX LinearAttention /
+ *    FlashInfer section and Limitations: DAMP keeps the high-risk key
+ *    channels in higher precision and the rest in INT8, about 9.9 bits per
+ *    value).  A key channel is a row of the d_k x d_v tile.  The first n_hi
+ *    rows are stored in BF16; every other row in INT8 with its own scale:
+ *    s = rowmax / 127, code = round-to-nearest-even(x * (127 / rowmax))
+ *    clamped to [-127, 127], stored value code * s (a zero row: codes 0,
+ *    s = 0).  The pages fix neither the scale granularity nor the rounding;
+ *    this per-row absmax form is the plainest.  The code is an integer that
+ *    floating point decides, so the decision is taken in binary32, the
+ *    precision of the stored scale: x, rowmax, 127 / rowmax, the product and
+ *    code * s are binary32 values.  Which channels are high-risk is a
+ *    calibration result the pages leave to DAMP; here they are the first
+ *    n_hi (a model orders its key channels so).
  */
 #include <math.h>
 #include <pthread.h>
@@ -71,7 +85,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_VERSION 3
+#define ORACLE_VERSION 4
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -451,7 +465,10 @@ typedef struct {
   const int32_t *read_slot, *write_slot;
   double *o;
   volatile int *bad;
+  int n_hi; /* >= 0: the state is stored in the 8-bit format with n_hi BF16 rows */
 } decode_cw_ctx;
+
+static void q8_store(double *M, int dk, int dv, int n_hi, int8_t *codes, float *scales);
 
 static void decode_cw_unit(void *p, int64_t unit, double *work) {
   decode_cw_ctx *c = (decode_cw_ctx *)p;
@@ -496,7 +513,12 @@ static void decode_cw_unit(void *p, int64_t unit, double *work) {
   }
   if (ws >= 0) {
     double *dst = c->pool + (ws * c->Hv + h) * tile;
-    for (int64_t e = 0; e < tile; ++e) dst[e] = c->round_state ? oracle_round_bf16(S[e]) : S[e];
+    if (c->n_hi >= 0) {
+      q8_store(S, dk, dv, c->n_hi, NULL, NULL);
+      memcpy(dst, S, tile * sizeof(double));
+    } else {
+      for (int64_t e = 0; e < tile; ++e) dst[e] = c->round_state ? oracle_round_bf16(S[e]) : S[e];
+    }
   }
 }
 
@@ -512,7 +534,127 @@ int oracle_decode_cw(int B, int Hqk, int Hv, int dk, int dv, int64_t n_slots, in
   if (Hv % Hqk != 0) return -1;
   volatile int bad = 0;
   decode_cw_ctx c = {B, Hqk, Hv, dk, dv, rule, round_state, n_slots, scale, q, k, v, g, beta,
-                     pool, read_slot, write_slot, o, &bad};
+                     pool, read_slot, write_slot, o, &bad, -1};
   if (run_units(decode_cw_unit, &c, (int64_t)B * Hv, (size_t)dk * dv + dv, n_threads)) return -1;
+  return bad ? 1 : 0;
+}
+
+/* The same with the state stored in the 8-bit format (n_hi BF16 rows, the
+ * rest INT8 per row; pool holds the values the stored tiles represent). */
+int oracle_decode_cw_q8(int B, int Hqk, int Hv, int dk, int dv, int64_t n_slots, int rule,
+                        double scale, int n_hi, const double *q, const double *k,
+                        const double *v, const double *g, const double *beta, double *pool,
+                        const int32_t *read_slot, const int32_t *write_slot, double *o,
+                        int n_threads) {
+  if (B < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || rule < 0 || rule > 3) return -1;
+  if (Hv % Hqk != 0 || n_hi < 0 || n_hi > dk) return -1;
+  volatile int bad = 0;
+  decode_cw_ctx c = {B, Hqk, Hv, dk, dv, rule, 0, n_slots, scale, q, k, v, g, beta,
+                     pool, read_slot, write_slot, o, &bad, n_hi};
+  if (run_units(decode_cw_unit, &c, (int64_t)B * Hv, (size_t)dk * dv + dv, n_threads)) return -1;
+  return bad ? 1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 8-bit state storage with a BF16 head of key channels                      */
+
+/* Store one d_k x d_v tile in the 8-bit format and replace its values by the
+ * ones the stored tile represents.  codes [(dk - n_hi) * dv] and scales
+ * [dk - n_hi] receive the stored INT8 rows when non-NULL. */
+static void q8_store(double *M, int dk, int dv, int n_hi, int8_t *codes, float *scales) {
+  for (int i = 0; i < dk; ++i) {
+    double *row = M + (int64_t)i * dv;
+    if (i < n_hi) {
+      for (int j = 0; j < dv; ++j) row[j] = oracle_round_bf16(row[j]);
+      continue;
+    }
+    float m = 0.0f;
+    for (int j = 0; j < dv; ++j) {
+      float ax = fabsf((float)row[j]);
+      if (ax > m) m = ax;
+    }
+    const float inv = m > 0.0f ? 127.0f / m : 0.0f;
+    const float sc = m / 127.0f;
+    for (int j = 0; j < dv; ++j) {
+      float y = (float)row[j] * inv;
+      if (y > 127.0f) y = 127.0f;
+      if (y < -127.0f) y = -127.0f;
+      const float c = nearbyintf(y);
+      row[j] = (double)(c * sc);
+      if (codes) codes[(int64_t)(i - n_hi) * dv + j] = (int8_t)c;
+    }
+    if (scales) scales[i - n_hi] = sc;
+  }
+}
+
+/* Encode n_tiles tiles of values [n_tiles, dk, dv] in the 8-bit format: the
+ * BF16 rows are returned as their (exact) values in bf16_rows [n_tiles, n_hi,
+ * dv]; codes [n_tiles, dk - n_hi, dv]; scales [n_tiles, dk - n_hi].  values
+ * is left unchanged.  Returns 0, or -1 on bad arguments. */
+int oracle_q8_encode(int64_t n_tiles, int dk, int dv, int n_hi, const double *values,
+                     double *bf16_rows, int8_t *codes, float *scales) {
+  if (n_tiles < 0 || dk <= 0 || dv <= 0 || n_hi < 0 || n_hi > dk) return -1;
+  const int64_t tile = (int64_t)dk * dv;
+  double *M = (double *)malloc(sizeof(double) * (size_t)tile);
+  if (!M) return -1;
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    memcpy(M, values + t * tile, sizeof(double) * (size_t)tile);
+    q8_store(M, dk, dv, n_hi, codes + t * (int64_t)(dk - n_hi) * dv, scales + t * (dk - n_hi));
+    memcpy(bf16_rows + t * (int64_t)n_hi * dv, M, sizeof(double) * (size_t)n_hi * dv);
+  }
+  free(M);
+  return 0;
+}
+
+typedef struct {
+  int B, Hqk, Hv, dk, dv, rule, n_hi;
+  int64_t n_slots;
+  double scale;
+  const double *q, *k, *v, *g, *beta;
+  double *pool;
+  const int32_t *read_slot, *write_slot;
+  double *o;
+  volatile int *bad;
+} decode_q8_ctx;
+
+static void decode_q8_unit(void *p, int64_t unit, double *work) {
+  decode_q8_ctx *c = (decode_q8_ctx *)p;
+  int64_t r = unit / c->Hv;
+  int h = (int)(unit % c->Hv);
+  int hq = (int)((int64_t)h * c->Hqk / c->Hv);
+  int64_t rs, ws;
+  if (!resolve_slots(c->read_slot, c->write_slot, r, c->n_slots, &rs, &ws)) {
+    *c->bad = 1;
+    return;
+  }
+  int64_t tile = (int64_t)c->dk * c->dv;
+  double *M = work, *tmp = work + tile;
+  if (rs >= 0) memcpy(M, c->pool + (rs * c->Hv + h) * tile, tile * sizeof(double));
+  else memset(M, 0, tile * sizeof(double));
+  token_step(M, c->dk, c->dv, c->rule, c->scale,
+             c->q + (r * c->Hqk + hq) * c->dk, c->k + (r * c->Hqk + hq) * c->dk,
+             c->v + (r * c->Hv + h) * c->dv, c->g[r * c->Hv + h], c->beta[r * c->Hv + h],
+             tmp, c->o + (r * c->Hv + h) * c->dv);
+  if (ws >= 0) {
+    q8_store(M, c->dk, c->dv, c->n_hi, NULL, NULL);
+    memcpy(c->pool + (ws * c->Hv + h) * tile, M, tile * sizeof(double));
+  }
+}
+
+/* One decode token for B requests on a state pool kept in the 8-bit format.
+ * As oracle_decode, except that pool holds the values the stored tiles
+ * represent and the new state is stored in the 8-bit format (n_hi BF16
+ * rows, the rest INT8 per row) at the write slot. */
+int oracle_decode_q8(int B, int Hqk, int Hv, int dk, int dv, int64_t n_slots, int rule,
+                     double scale, int n_hi, const double *q, const double *k, const double *v,
+                     const double *g, const double *beta, double *pool,
+                     const int32_t *read_slot, const int32_t *write_slot, double *o,
+                     int n_threads) {
+  if (B < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || rule < 0 || rule > 3) return -1;
+  if (Hv % Hqk != 0 || n_hi < 0 || n_hi > dk) return -1;
+  volatile int bad = 0;
+  decode_q8_ctx c = {B, Hqk, Hv, dk, dv, rule, n_hi, n_slots, scale, q, k, v, g, beta,
+                     pool, read_slot, write_slot, o, &bad};
+  if (run_units(decode_q8_unit, &c, (int64_t)B * Hv, (size_t)dk * dv + dv, n_threads)) return -1;
   return bad ? 1 : 0;
 }
