@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 5
+#define GDN_ABI_VERSION 6
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -77,7 +77,23 @@ typedef enum gdn_rule {
   GDN_RULE_GATED_DELTA = 3
 } gdn_rule;
 
-typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+/* Element types.  GDN_Q8 is a state storage format only (gdn_decode's
+ * state_dtype): DAMP's mixed precision ("Seven Architectures ...", ONNX
+ * LinearAttention / FlashInfer section and Limitations: high-risk key
+ * channels kept in higher precision, the rest in INT8, ~9.9 bits per value).
+ * Each (slot, head) tile stores its first state_bf16_rows key channels (rows)
+ * in BF16 and every other row in INT8 with one binary32 scale per row:
+ *   [state_bf16_rows, d_v] BF16 | [d_k - state_bf16_rows, d_v] int8 codes |
+ *   [d_k - state_bf16_rows] binary32 scales
+ * (gdn_state_q8_bytes per head).  An INT8 row represents code * scale; when
+ * stored it is requantised against its own largest magnitude rowmax:
+ * code = round-to-nearest-even(x * (127 / rowmax)) within [-127, 127] and
+ * scale = rowmax / 127, in binary32 (an all-zero row: codes and scale 0).
+ * INT8 rows hold finite values only.  The BF16 rows are the model's
+ * high-risk key channels: a calibration that picks other channels orders the
+ * key dimension of its q/k projections so they come first (the conv, norm
+ * and recurrence treat key channels alike). */
+typedef enum gdn_dtype { GDN_F32 = 0, GDN_BF16 = 1, GDN_Q8 = 2 } gdn_dtype;
 
 /* How the decay of the gated rules is given.  HEAD: one per (token, state
  * head), Gated DeltaNet's scalar forget gate.  CHANNEL: one per key channel
@@ -118,7 +134,9 @@ typedef struct gdn_decode_args {
   int32_t H_v;         /* state heads (the H_kv of the state shape), multiple of H_qk */
   int32_t d_k, d_v;    /* state tile is d_k x d_v */
   int32_t rule;        /* gdn_rule */
-  int32_t state_dtype; /* gdn_dtype of state_pool: BF16 storage with FP32 compute, or FP32 */
+  int32_t state_dtype; /* gdn_dtype of state_pool: BF16 storage with FP32 compute, FP32, or
+                          GDN_Q8 (then state_pool is [n_slots, H_v, gdn_state_q8_bytes(1, ...)]
+                          bytes; gdn_decode only) */
   int32_t act_dtype;   /* gdn_dtype of q, k, v and o */
   int64_t n_slots;     /* pool capacity in slots */
   float scale;         /* read-out scale (1.0 for none) */
@@ -135,6 +153,9 @@ typedef struct gdn_decode_args {
   const int32_t *write_slot; /* [B] or NULL */
   void *o;             /* [B, H_v, d_v] act_dtype */
   uint32_t *status;    /* optional device word; bits are OR-ed in, never cleared */
+  int32_t state_bf16_rows; /* state_dtype GDN_Q8: key channels per tile kept in BF16, a
+                              multiple of 8 in [0, d_k]; must be 0 otherwise */
+  int32_t reserved0;   /* must be 0 */
 } gdn_decode_args;
 
 /* Prefill: the same recurrence over n_seq variable-length sequences packed
@@ -240,6 +261,12 @@ typedef struct gdn_conv_args {
  * LinearAttention section of "Seven Architectures ..." sizes 64 heads of
  * 128 x 128 at 16 bits as 2 MB per request. */
 size_t gdn_state_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t state_dtype);
+
+/* Bytes of one slot in the 8-bit format (GDN_Q8): per head
+ * bf16_rows * d_v * 2 + (d_k - bf16_rows) * (d_v + 4); 0 for invalid sizes
+ * (bf16_rows must be a multiple of 8 in [0, d_k]).  At d_k = d_v = 128 with
+ * 24 BF16 rows that is 19,872 bytes per head, 9.70 bits per value. */
+size_t gdn_state_q8_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t bf16_rows);
 
 /* Workspace that gdn_prefill / gdn_mixed need for these arguments (host-only
  * arithmetic on the sizes; no pointer is read). */

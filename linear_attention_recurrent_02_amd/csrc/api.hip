@@ -33,7 +33,12 @@ gdn_status check_decode(const gdn_decode_args *a) {
   if (!a) return GDN_ERR_NULL;
   if (a->B < 0 || a->n_slots < 0) return GDN_ERR_SHAPE;
   if (!valid_rule(a->rule)) return GDN_ERR_RULE;
-  if (!valid_dtype(a->state_dtype) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
+  const bool q8 = a->state_dtype == GDN_Q8;
+  if ((!valid_dtype(a->state_dtype) && !q8) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
+  if (a->reserved0 != 0) return GDN_ERR_UNSUPPORTED;
+  if (q8 ? (a->state_bf16_rows < 0 || a->state_bf16_rows > a->d_k || a->state_bf16_rows % 8 != 0)
+         : a->state_bf16_rows != 0)
+    return GDN_ERR_SHAPE;
   if (a->decay_mode != GDN_DECAY_HEAD && a->decay_mode != GDN_DECAY_CHANNEL)
     return GDN_ERR_UNSUPPORTED;
   gdn_status st = check_heads(a->H_qk, a->H_v, a->d_k, a->d_v);
@@ -55,6 +60,7 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
   if (!a) return GDN_ERR_NULL;
   if (a->n_seq < 0 || a->n_tokens < 0 || a->n_slots < 0) return GDN_ERR_SHAPE;
   if (!valid_rule(a->rule)) return GDN_ERR_RULE;
+  if (a->state_dtype == GDN_Q8) return GDN_ERR_UNSUPPORTED;  // the 8-bit format is decode-only
   if (!valid_dtype(a->state_dtype) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
   if (a->reserved1 != 0) return GDN_ERR_UNSUPPORTED;
   if (a->use_frontend != 0 && a->use_frontend != 1) return GDN_ERR_UNSUPPORTED;
@@ -159,6 +165,13 @@ size_t gdn_state_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t state_dtyp
   return (size_t)H_v * (size_t)d_k * (size_t)d_v * (state_dtype == GDN_BF16 ? 2u : 4u);
 }
 
+size_t gdn_state_q8_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t bf16_rows) {
+  if (H_v <= 0 || d_k <= 0 || d_v <= 0 || bf16_rows < 0 || bf16_rows > d_k || bf16_rows % 8)
+    return 0;
+  const size_t lo = (size_t)(d_k - bf16_rows);
+  return (size_t)H_v * ((size_t)bf16_rows * d_v * 2 + lo * d_v + lo * 4);
+}
+
 size_t gdn_prefill_workspace_size(const gdn_prefill_args *args) {
   return args ? gdn::prefill_workspace_bytes(*args) : 0;
 }
@@ -242,7 +255,9 @@ gdn_status gdn_mixed(const gdn_decode_args *decode, const gdn_prefill_args *pref
                      void *stream) {
   gdn_status st = check_decode(decode);
   if (st != GDN_OK) return st;
-  if (decode->decay_mode != GDN_DECAY_HEAD) return GDN_ERR_UNSUPPORTED;  // one decode instance
+  // one decode instance: the per-head decay on a BF16 or FP32 state
+  if (decode->decay_mode != GDN_DECAY_HEAD || decode->state_dtype == GDN_Q8)
+    return GDN_ERR_UNSUPPORTED;
   st = check_prefill(prefill, true);
   if (st != GDN_OK) return st;
   if (decode->B == 0 && prefill->n_seq == 0) return GDN_OK;

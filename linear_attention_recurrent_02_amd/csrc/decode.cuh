@@ -21,6 +21,16 @@
 // delta correction reads the state, so the reductions take a_i k_i and
 // a_i q_i, a = 1 in delta and o, and the update is M'_i = a_i M_i + k_i delta.
 //
+// With 8-bit storage (Q8: DAMP's mixed precision, "Seven Architectures ...",
+// ONNX LinearAttention / FlashInfer section) the first hi_rows key channels
+// (rows) of a tile are BF16 and the others INT8 with one binary32 scale per
+// row: the tile is [hi_rows, d_v] BF16 | [d_k - hi_rows, d_v] int8 codes |
+// [d_k - hi_rows] scales.  A row is read as code * scale; on store it is
+// requantised against its own largest magnitude (code = rne(x * 127 / rowmax),
+// scale = rowmax / 127), the maximum taken across the LPR lanes of the row.
+// hi_rows is a multiple of 8 and RPT divides 8, so each thread's rows are all
+// BF16 or all INT8.
+//
 // Work split (gfx950, wave64): every column j of the update is independent
 // given k, q and v, so a lane owns VEC consecutive columns (one 16-byte
 // vector per row) and RPT consecutive rows; LPR lanes cover one row, so each
@@ -50,6 +60,25 @@ __device__ __forceinline__ void stream_store(uint4 *p, const uint4 &v) {
   u32x4_t w = {v.x, v.y, v.z, v.w};
   __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(p));
 }
+// the same for the 8-byte pieces of INT8 rows
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 stream_load8(const uint2 *p) {
+  const u32x2_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_t *>(p));
+  return make_uint2(v.x, v.y);
+}
+__device__ __forceinline__ void stream_store8(uint2 *p, uint32_t lo, uint32_t hi) {
+  u32x2_t w = {lo, hi};
+  __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t *>(p));
+}
+
+// eight INT8 codes (the low 8 bytes of m) times their row's scale
+__device__ __forceinline__ void unpack_i8(const uint4 &m, float sc, float *f) {
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const uint32_t w = j < 4 ? m.x : m.y;
+    f[j] = (float)(int8_t)(w >> (8 * (j & 3))) * sc;
+  }
+}
 
 struct DecodeParams {
   int32_t B, H_qk, H_v, group;  // group = H_v / H_qk
@@ -62,6 +91,9 @@ struct DecodeParams {
   const int32_t *read_slot, *write_slot;
   void *o;
   uint32_t *status;
+  // 8-bit storage: BF16 rows at the head of each tile, and the tile's bytes
+  int32_t hi_rows;
+  int64_t tile_bytes;
 };
 
 template <bool SB, int DK, int DV, int NT>
@@ -81,7 +113,7 @@ struct DecodeShape {
 // the thread's runs of k, q (RPT rows) and v (VEC columns) are whole 16-byte
 // vectors they are kept packed as loaded (half the registers for BF16) and
 // unpacked in phase 2.
-template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false>
 struct DecodeTileRegs {
   using S = DecodeShape<SB, DK, DV, NT>;
   static constexpr int AV = Elem<AB>::kPer16B;  // activation elements per 16 bytes
@@ -94,6 +126,7 @@ struct DecodeTileRegs {
   float kr[PACKED ? 1 : S::RPT], qr[PACKED ? 1 : S::RPT], vv[PACKED ? 1 : S::VEC];
   float a, bw;                      // decay and write strength
   float ar[CW ? S::RPT : 1];        // CW: the decay of each of this thread's rows
+  float sc[Q8 ? S::RPT : 1];        // Q8: the scale of each of this thread's INT8 rows
   int64_t r, ws;                    // request, write slot
   int h;
   bool valid;                       // false: a bad slot (the tile is skipped)
@@ -105,10 +138,11 @@ struct DecodeTileRegs {
 // NT threads of a group call it with the same (r, h), each passing its index
 // in the group as `tid`: the workgroup, or one of its aligned NT-thread parts
 // (each with its own `red`).
-template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false>
 __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t r, int h,
-                                                 DecodeTileRegs<SB, AB, DK, DV, NT, CW> &t,
+                                                 DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8> &t,
                                                  int tid) {
+  static_assert(!Q8 || SB, "8-bit storage uses the BF16 tile shape");
   using S = DecodeShape<SB, DK, DV, NT>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT;
   constexpr bool ALL_LIVE = S::ALL_LIVE;
@@ -131,7 +165,7 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
   // this token's q, k (rows of this thread), v (its columns); issued before
   // the state tile: loads return in order, so waiting for these leaves the
   // state loads in flight
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW>;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8>;
   using AT = typename Elem<AB>::T;
   if constexpr (Regs::PACKED) {
     const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.k) +
@@ -154,8 +188,37 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
     load_run<AB, VEC>(p.v, (r * p.H_v + h) * DV + cv * VEC, t.vv);
   }
 
-  // the state tile: RPT 16-byte vectors per thread (a1)
-  if (rs >= 0) {
+  // the state tile: RPT 16-byte vectors per thread (a1); 8-byte pieces and
+  // one scale per row for the INT8 rows of an 8-bit tile
+  if constexpr (Q8) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      t.m[i] = make_uint4(0u, 0u, 0u, 0u);
+      t.sc[i] = 0.f;
+    }
+    if (rs >= 0) {
+      const char *tile = static_cast<const char *>(p.pool) + (rs * p.H_v + h) * p.tile_bytes;
+      if (row0 < p.hi_rows) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(tile);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+          if (ALL_LIVE || row0 + i < DK) t.m[i] = stream_load(src + (int64_t)(row0 + i) * LPR + cv);
+      } else {
+        const int lo = row0 - p.hi_rows;  // INT8 row index of the thread's first row
+        const int64_t hi_b = (int64_t)p.hi_rows * DV * 2;
+        const uint2 *src = reinterpret_cast<const uint2 *>(tile + hi_b);
+        const float *scl = reinterpret_cast<const float *>(tile + hi_b + (int64_t)(DK - p.hi_rows) * DV);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          if (ALL_LIVE || row0 + i < DK) {
+            const uint2 u = stream_load8(src + (int64_t)(lo + i) * LPR + cv);
+            t.m[i] = make_uint4(u.x, u.y, 0u, 0u);
+            t.sc[i] = scl[lo + i];
+          }
+        }
+      }
+    }
+  } else if (rs >= 0) {
     const uint4 *src = reinterpret_cast<const uint4 *>(
         static_cast<const typename SE::T *>(p.pool) + ((rs * p.H_v + h) * TILE));
 #pragma unroll
@@ -188,9 +251,9 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
 // and the store to the write slot (a5).  `red` is LDS of
 // DecodeShape::LDS_FLOATS floats.  For NW > 1 it has three barriers (the last
 // lets the caller reuse `red`); a skipped tile has none, uniformly.
-template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false>
 __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
-                                                   DecodeTileRegs<SB, AB, DK, DV, NT, CW> &t,
+                                                   DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8> &t,
                                                    float *red, int tid) {
   using S = DecodeShape<SB, DK, DV, NT>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT, NW = S::NW;
@@ -205,7 +268,18 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
   const int64_t r = t.r;
   const int h = t.h;
   constexpr int64_t TILE = (int64_t)DK * DV;
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW>;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8>;
+  // Q8: this thread's rows are BF16 (the tile's head) or INT8
+  const bool hi_run = !Q8 || row0 < p.hi_rows;
+  auto unpack_row = [&](int i, float *f) {
+    if constexpr (Q8) {
+      if (!hi_run) {
+        unpack_i8(t.m[i], t.sc[i], f);
+        return;
+      }
+    }
+    SE::unpack(t.m[i], f);
+  };
   float kr[RPT], qr[RPT], vv[VEC];
   if constexpr (Regs::PACKED) {
 #pragma unroll
@@ -230,7 +304,7 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     float f[VEC];
-    SE::unpack(t.m[i], f);
+    unpack_row(i, f);
     // CW: the decayed row a_i M_i is what k and q read
     const float kd = CW ? t.ar[i] * kr[i] : kr[i], qd = CW ? t.ar[i] * qr[i] : qr[i];
 #pragma unroll
@@ -297,14 +371,63 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
   }
 
   // ---- update and scatter to the write slot (a5) ----
-  if (t.ws >= 0 && rows_live) {
+  if constexpr (Q8) {
+    if (t.ws >= 0) {  // uniform over the tile: every lane takes part in the row maxima
+      char *tile = static_cast<char *>(p.pool) + (t.ws * p.H_v + h) * p.tile_bytes;
+      if (hi_run) {
+        uint4 *dst = reinterpret_cast<uint4 *>(tile);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          if (!ALL_LIVE && row0 + i >= DK) continue;
+          float f[VEC];
+          unpack_row(i, f);
+          const float ai = CW ? t.ar[i] : a;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) f[e] = fmaf(kr[i], d[e], ai * f[e]);
+          stream_store(dst + (int64_t)(row0 + i) * LPR + cv, SE::pack(f));
+        }
+      } else {
+        const int lo = row0 - p.hi_rows;
+        const int64_t hi_b = (int64_t)p.hi_rows * DV * 2;
+        uint2 *dst = reinterpret_cast<uint2 *>(tile + hi_b);
+        float *scl = reinterpret_cast<float *>(tile + hi_b + (int64_t)(DK - p.hi_rows) * DV);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const bool live = ALL_LIVE || row0 + i < DK;
+          float f[VEC];
+          unpack_row(i, f);
+          const float ai = CW ? t.ar[i] : a;
+          float m = 0.f;
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            f[e] = fmaf(kr[i], d[e], ai * f[e]);
+            m = fmaxf(m, fabsf(f[e]));
+          }
+          // the row's largest magnitude over its LPR lanes (an aligned lane group)
+#pragma unroll
+          for (int off = 1; off < LPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+          const float inv = m > 0.f ? 127.f / m : 0.f;
+          uint32_t w[2] = {0u, 0u};
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            const float y = fminf(fmaxf(f[e] * inv, -127.f), 127.f);
+            w[e >> 2] |= ((uint32_t)(int)rintf(y) & 0xffu) << (8 * (e & 3));
+          }
+          if (live) {
+            stream_store8(dst + (int64_t)(lo + i) * LPR + cv, w[0], w[1]);
+            if (cv == 0) scl[lo + i] = m / 127.f;
+          }
+        }
+      }
+    }
+  } else if (t.ws >= 0 && rows_live) {
     uint4 *dst = reinterpret_cast<uint4 *>(static_cast<typename SE::T *>(p.pool) +
                                            ((t.ws * p.H_v + h) * TILE));
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
       if (!ALL_LIVE && row0 + i >= DK) continue;
       float f[VEC];
-      SE::unpack(t.m[i], f);
+      unpack_row(i, f);
       const float ai = CW ? t.ar[i] : a;
 #pragma unroll
       for (int e = 0; e < VEC; ++e) f[e] = fmaf(kr[i], d[e], ai * f[e]);

@@ -9,7 +9,7 @@
 
 namespace gdn {
 
-template <bool SB, bool AB, int DK, int DV, bool CW>
+template <bool SB, bool AB, int DK, int DV, bool CW, bool Q8>
 __global__ __launch_bounds__(kDecodeMaxThreads) void decode_kernel(DecodeParams p, int ordered) {
   constexpr int NT = decode_threads<SB, DK, DV>();
   __shared__ float red[DecodeShape<SB, DK, DV, NT>::LDS_FLOATS];
@@ -20,13 +20,13 @@ __global__ __launch_bounds__(kDecodeMaxThreads) void decode_kernel(DecodeParams 
   // flight during this tile's reduction and store) measured slower on MI355X
   // (196 against 191 us per B = 512 launch), its extra registers costing more
   // occupancy than the overlap gains
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW>;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8>;
   for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int pos = (int)(t / p.H_v);
     Regs cur;
-    decode_tile_load<SB, AB, DK, DV, NT, CW>(p, ordered ? order_lds[pos] : pos, (int)(t % p.H_v),
-                                             cur, (int)threadIdx.x);
-    decode_tile_finish<SB, AB, DK, DV, NT, CW>(p, cur, red, (int)threadIdx.x);
+    decode_tile_load<SB, AB, DK, DV, NT, CW, Q8>(p, ordered ? order_lds[pos] : pos,
+                                                 (int)(t % p.H_v), cur, (int)threadIdx.x);
+    decode_tile_finish<SB, AB, DK, DV, NT, CW, Q8>(p, cur, red, (int)threadIdx.x);
   }
 }
 
@@ -37,17 +37,21 @@ DecodeParams make_decode_params(const gdn_decode_args &a) {
   p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta;
   p.pool = a.state_pool; p.read_slot = a.read_slot; p.write_slot = a.write_slot;
   p.o = a.o; p.status = a.status;
+  p.hi_rows = a.state_dtype == GDN_Q8 ? a.state_bf16_rows : 0;
+  p.tile_bytes = a.state_dtype == GDN_Q8
+                     ? (int64_t)gdn_state_q8_bytes(1, a.d_k, a.d_v, a.state_bf16_rows)
+                     : 0;
   return p;
 }
 
-template <bool SB, bool AB, int DK, int DV, bool CW>
+template <bool SB, bool AB, int DK, int DV, bool CW, bool Q8>
 static gdn_status launch_t(const DecodeParams &p, hipStream_t s) {
   constexpr int NT = decode_threads<SB, DK, DV>();
   const int64_t tiles = (int64_t)p.B * p.H_v;
   const int ordered =
       p.write_slot != nullptr && p.B <= kOrderMaxB && p.n_slots <= kOrderMaxSlots ? 1 : 0;
   const size_t lds = ordered ? slot_order_lds_bytes(p.B, p.n_slots, NT) : 0;
-  auto kern = decode_kernel<SB, AB, DK, DV, CW>;
+  auto kern = decode_kernel<SB, AB, DK, DV, CW, Q8>;
   // one resident wave of workgroups: CUs x workgroups per CU
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
@@ -60,40 +64,49 @@ static gdn_status launch_t(const DecodeParams &p, hipStream_t s) {
 }
 
 template <bool SB, bool AB, int DK, int DV>
-static gdn_status launch_cw(const DecodeParams &p, bool cw, hipStream_t s) {
-  return cw ? launch_t<SB, AB, DK, DV, true>(p, s) : launch_t<SB, AB, DK, DV, false>(p, s);
+static gdn_status launch_cw(const DecodeParams &p, bool cw, bool q8, hipStream_t s) {
+  if constexpr (SB) {
+    if (q8)
+      return cw ? launch_t<SB, AB, DK, DV, true, true>(p, s)
+                : launch_t<SB, AB, DK, DV, false, true>(p, s);
+  }
+  return cw ? launch_t<SB, AB, DK, DV, true, false>(p, s)
+            : launch_t<SB, AB, DK, DV, false, false>(p, s);
 }
 
 template <bool SB, bool AB, int DK>
-static gdn_status launch_dv(const DecodeParams &p, int dv, bool cw, hipStream_t s) {
+static gdn_status launch_dv(const DecodeParams &p, int dv, bool cw, bool q8, hipStream_t s) {
   switch (dv) {
-    case 16: return launch_cw<SB, AB, DK, 16>(p, cw, s);
-    case 32: return launch_cw<SB, AB, DK, 32>(p, cw, s);
-    case 64: return launch_cw<SB, AB, DK, 64>(p, cw, s);
-    case 128: return launch_cw<SB, AB, DK, 128>(p, cw, s);
+    case 16: return launch_cw<SB, AB, DK, 16>(p, cw, q8, s);
+    case 32: return launch_cw<SB, AB, DK, 32>(p, cw, q8, s);
+    case 64: return launch_cw<SB, AB, DK, 64>(p, cw, q8, s);
+    case 128: return launch_cw<SB, AB, DK, 128>(p, cw, q8, s);
   }
   return GDN_ERR_UNSUPPORTED;
 }
 
 template <bool SB, bool AB>
-static gdn_status launch_dk(const DecodeParams &p, int dk, int dv, bool cw, hipStream_t s) {
+static gdn_status launch_dk(const DecodeParams &p, int dk, int dv, bool cw, bool q8,
+                            hipStream_t s) {
   switch (dk) {
-    case 16: return launch_dv<SB, AB, 16>(p, dv, cw, s);
-    case 32: return launch_dv<SB, AB, 32>(p, dv, cw, s);
-    case 64: return launch_dv<SB, AB, 64>(p, dv, cw, s);
-    case 128: return launch_dv<SB, AB, 128>(p, dv, cw, s);
+    case 16: return launch_dv<SB, AB, 16>(p, dv, cw, q8, s);
+    case 32: return launch_dv<SB, AB, 32>(p, dv, cw, q8, s);
+    case 64: return launch_dv<SB, AB, 64>(p, dv, cw, q8, s);
+    case 128: return launch_dv<SB, AB, 128>(p, dv, cw, q8, s);
   }
   return GDN_ERR_UNSUPPORTED;
 }
 
 gdn_status launch_decode(const gdn_decode_args &a, hipStream_t s) {
   const DecodeParams p = make_decode_params(a);
-  const bool sb = a.state_dtype == GDN_BF16, ab = a.act_dtype == GDN_BF16;
+  // the 8-bit format runs the BF16 tile shape
+  const bool q8 = a.state_dtype == GDN_Q8;
+  const bool sb = a.state_dtype == GDN_BF16 || q8, ab = a.act_dtype == GDN_BF16;
   const bool cw = a.decay_mode == GDN_DECAY_CHANNEL;
-  if (sb && ab) return launch_dk<true, true>(p, a.d_k, a.d_v, cw, s);
-  if (sb && !ab) return launch_dk<true, false>(p, a.d_k, a.d_v, cw, s);
-  if (!sb && ab) return launch_dk<false, true>(p, a.d_k, a.d_v, cw, s);
-  return launch_dk<false, false>(p, a.d_k, a.d_v, cw, s);
+  if (sb && ab) return launch_dk<true, true>(p, a.d_k, a.d_v, cw, q8, s);
+  if (sb && !ab) return launch_dk<true, false>(p, a.d_k, a.d_v, cw, q8, s);
+  if (!sb && ab) return launch_dk<false, true>(p, a.d_k, a.d_v, cw, false, s);
+  return launch_dk<false, false>(p, a.d_k, a.d_v, cw, false, s);
 }
 
 }  // namespace gdn

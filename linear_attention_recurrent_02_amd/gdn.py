@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libgdn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "gdn.h")
 
 RULES = {"linear": 0, "gated": 1, "delta": 2, "gated_delta": 3}
-F32, BF16 = 0, 1
+F32, BF16, Q8 = 0, 1, 2
 DECAY_HEAD, DECAY_CHANNEL = 0, 1
 DEVICE_BAD_SLOT = 1
 DEVICE_BAD_SEQ = 2
@@ -34,7 +34,7 @@ class DecodeArgs(ctypes.Structure):
                 ("n_slots", _I64), ("scale", ctypes.c_float), ("decay_mode", _I32),
                 ("q", _P), ("k", _P), ("v", _P), ("g", _P), ("beta", _P),
                 ("state_pool", _P), ("read_slot", _P), ("write_slot", _P), ("o", _P),
-                ("status", _P)]
+                ("status", _P), ("state_bf16_rows", _I32), ("reserved0", _I32)]
 
 
 class PrefillArgs(ctypes.Structure):
@@ -82,6 +82,8 @@ def load_library() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     lib.gdn_state_bytes.restype = ctypes.c_size_t
     lib.gdn_state_bytes.argtypes = [_I32, _I32, _I32, _I32]
+    lib.gdn_state_q8_bytes.restype = ctypes.c_size_t
+    lib.gdn_state_q8_bytes.argtypes = [_I32, _I32, _I32, _I32]
     lib.gdn_prefill_workspace_size.restype = ctypes.c_size_t
     lib.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
     lib.gdn_parse_rule.restype = _I32
@@ -212,6 +214,11 @@ def gdn_state_bytes(H_v: int, d_k: int, d_v: int, state_dtype: int = BF16) -> in
     return int(load_library().gdn_state_bytes(H_v, d_k, d_v, state_dtype))
 
 
+def gdn_state_q8_bytes(H_v: int, d_k: int, d_v: int, bf16_rows: int) -> int:
+    """Bytes of one slot in the 8-bit state format (0 for invalid sizes)."""
+    return int(load_library().gdn_state_q8_bytes(H_v, d_k, d_v, bf16_rows))
+
+
 def gdn_parse_rule(name: str | None) -> int:
     out = _I32()
     code = load_library().gdn_parse_rule(None if name is None else name.encode(), ctypes.byref(out))
@@ -241,11 +248,13 @@ def gdn_validate_slots(read_slot, write_slot, n: int, n_slots: int) -> int:
 
 
 def make_decode_args(q, k, v, g, beta, state_pool, read_slot=None, write_slot=None, o=None, *,
-                     rule="gated_delta", scale=1.0, status=None):
+                     rule="gated_delta", scale=1.0, status=None, state_bf16_rows=None):
     """Build a DecodeArgs struct.  q, k: [B, H_qk, d_k]; v: [B, H_v, d_v];
     g: [B, H_v] float32, or [B, H_v, d_k] for a per-key-channel decay; beta:
-    [B, H_v] float32; state_pool: [n_slots, H_v, d_k, d_v];
-    read_slot / write_slot: [B] int32 or None.  Returns (args, o, keepalive)."""
+    [B, H_v] float32; state_pool: [n_slots, H_v, d_k, d_v] bfloat16 or
+    float32, or the 8-bit format as uint8 [n_slots, H_v, tile bytes] with
+    state_bf16_rows BF16 key channels per tile; read_slot / write_slot: [B]
+    int32 or None.  Returns (args, o, keepalive)."""
     _need(q, "q", dtypes=_ACT)
     if q.dim() != 3:
         raise ValueError(f"q must be [B, H_qk, d_k], got {tuple(q.shape)}")
@@ -260,10 +269,23 @@ def make_decode_args(q, k, v, g, beta, state_pool, read_slot=None, write_slot=No
     else:
         _need(g, "g", dtype=torch.float32, shape=(B, H_v))
     _need(beta, "beta", dtype=torch.float32, shape=(B, H_v))
-    _need(state_pool, "state_pool", dtypes=_ACT)
-    if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H_v, d_k, d_v):
-        raise ValueError(f"state_pool must be [n_slots, {H_v}, {d_k}, {d_v}], "
-                         f"got {tuple(state_pool.shape)}")
+    q8 = isinstance(state_pool, torch.Tensor) and state_pool.dtype == torch.uint8
+    if q8:
+        if state_bf16_rows is None:
+            raise ValueError("an 8-bit state pool (uint8) needs state_bf16_rows")
+        tb = gdn_state_q8_bytes(1, d_k, d_v, int(state_bf16_rows))
+        if tb == 0:
+            raise ValueError(f"state_bf16_rows must be a multiple of 8 in [0, {d_k}]")
+        if state_pool.dim() != 3 or tuple(state_pool.shape[1:]) != (H_v, tb):
+            raise ValueError(f"state_pool must be [n_slots, {H_v}, {tb}] bytes, "
+                             f"got {tuple(state_pool.shape)}")
+    else:
+        if state_bf16_rows:
+            raise ValueError("state_bf16_rows applies to an 8-bit (uint8) state pool only")
+        _need(state_pool, "state_pool", dtypes=_ACT)
+        if state_pool.dim() != 4 or tuple(state_pool.shape[1:]) != (H_v, d_k, d_v):
+            raise ValueError(f"state_pool must be [n_slots, {H_v}, {d_k}, {d_v}], "
+                             f"got {tuple(state_pool.shape)}")
     _need(read_slot, "read_slot", dtype=torch.int32, shape=(B,))
     _need(write_slot, "write_slot", dtype=torch.int32, shape=(B,))
     _need(o, "o", dtype=q.dtype, shape=(B, H_v, d_v))
@@ -277,7 +299,9 @@ def make_decode_args(q, k, v, g, beta, state_pool, read_slot=None, write_slot=No
     a = DecodeArgs()
     a.B, a.H_qk, a.H_v, a.d_k, a.d_v = B, H_qk, H_v, d_k, d_v
     a.rule = _rule(rule)
-    a.state_dtype = _dtype_code(state_pool)
+    a.state_dtype = Q8 if q8 else _dtype_code(state_pool)
+    a.state_bf16_rows = int(state_bf16_rows) if q8 else 0
+    a.reserved0 = 0
     a.act_dtype = _dtype_code(q)
     a.n_slots = state_pool.shape[0]
     a.scale = float(scale)
@@ -290,11 +314,12 @@ def make_decode_args(q, k, v, g, beta, state_pool, read_slot=None, write_slot=No
 
 
 def gdn_decode(q, k, v, g, beta, state_pool, read_slot=None, write_slot=None, o=None, *,
-               rule="gated_delta", scale=1.0, status=None, stream=None):
+               rule="gated_delta", scale=1.0, status=None, stream=None, state_bf16_rows=None):
     """One decode token for B requests; updates ``state_pool`` in place and
     returns o [B, H_v, d_v] (dtype of q)."""
     a, o, keep = make_decode_args(q, k, v, g, beta, state_pool, read_slot, write_slot, o,
-                                  rule=rule, scale=scale, status=status)
+                                  rule=rule, scale=scale, status=status,
+                                  state_bf16_rows=state_bf16_rows)
     code = load_library().gdn_decode(ctypes.byref(a), _stream(stream))
     if code:
         raise GdnError("gdn_decode", code)

@@ -28,7 +28,7 @@ def test_struct_layout_matches():
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
     assert lib.gdn_sizeof_conv_args() == ctypes.sizeof(B.ConvArgs)
-    assert gdn.gdn_abi_version() == 5
+    assert gdn.gdn_abi_version() == 6
 
 
 def test_state_bytes_against_the_pages():
@@ -76,7 +76,11 @@ def _call_decode(a):
 
 @pytest.mark.parametrize("over,code", [
     (dict(rule=4), RULE), (dict(rule=-1), RULE),
-    (dict(state_dtype=2), DTYPE), (dict(act_dtype=-1), DTYPE),
+    (dict(state_dtype=3), DTYPE), (dict(act_dtype=-1), DTYPE), (dict(act_dtype=2), DTYPE),
+    # the 8-bit state format: a multiple of 8 BF16 rows within d_k, none for other formats
+    (dict(state_dtype=2, state_bf16_rows=12), SHAPE), (dict(state_dtype=2, state_bf16_rows=136), SHAPE),
+    (dict(state_dtype=2, state_bf16_rows=-8), SHAPE), (dict(state_bf16_rows=8), SHAPE),
+    (dict(reserved0=1), UNSUP),
     (dict(B=-1), SHAPE), (dict(n_slots=-1), SHAPE), (dict(H_qk=0), SHAPE), (dict(d_k=0), SHAPE),
     (dict(H_qk=3), UNSUP), (dict(d_k=48), UNSUP), (dict(d_v=256), UNSUP), (dict(decay_mode=2), UNSUP), (dict(decay_mode=-1), UNSUP),
     (dict(q=None), NULL), (dict(state_pool=None), NULL), (dict(o=None), NULL),
@@ -87,6 +91,25 @@ def _call_decode(a):
 ])
 def test_decode_validation(over, code):
     assert _call_decode(_decode_args(**over)) == code
+
+
+def test_state_q8_bytes_and_q8_elsewhere():
+    """Slot bytes of the 8-bit format (the oracle's layout: BF16 head rows,
+    int8 codes, binary32 scales), and the calls that refuse it."""
+    import oracle
+    lib = gdn.load_library()
+    for dk, dv, n_hi in ((128, 128, 24), (128, 128, 0), (128, 128, 128), (64, 32, 16), (16, 16, 8)):
+        assert gdn.gdn_state_q8_bytes(32, dk, dv, n_hi) == 32 * oracle.q8_tile_bytes(dk, dv, n_hi)
+    assert gdn.gdn_state_q8_bytes(32, 128, 128, 12) == 0
+    assert gdn.gdn_state_q8_bytes(32, 128, 128, 136) == 0
+    # 24 BF16 rows at d = 128: 9.70 bits per value, 0.606 of the BF16 slot
+    assert gdn.gdn_state_q8_bytes(32, 128, 128, 24) == 32 * 19872
+    # an 8-bit pool passes the decode's checks (stops at B = 0); mixed and prefill refuse it
+    assert _call_decode(_decode_args(B=0, state_dtype=2, state_bf16_rows=24)) == OK
+    a = _decode_args(state_dtype=2, state_bf16_rows=24)
+    p = _prefill_args(state_dtype=2)
+    assert lib.gdn_mixed(ctypes.byref(a), ctypes.byref(_prefill_args()), None) == UNSUP
+    assert lib.gdn_prefill(ctypes.byref(p), None) == UNSUP
 
 
 def test_decode_rule_specific_pointers_and_empty_batch():
