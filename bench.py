@@ -343,6 +343,67 @@ def run_decode_cw(args, torch, gdn, syn, layers):
                 algorithmic_GBps=round(gbps, 1), hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
 
 
+def run_decode_q8(args, torch, gdn, syn, layers, n_hi=32):
+    """The same 48-layer B=512 decode on state pools in the 8-bit format (the
+    first n_hi key channels of each tile in BF16, the others INT8 with a
+    scale per channel: 10.19 bits per value at n_hi = 32, d = 128; 8.25 with
+    none), one HIP graph of 48 launches on 48 separate 8-bit pools."""
+    wl = syn.WORKLOADS["decode_b512_x48"]
+    B, Hqk, Hv, dk, dv, n = wl["B"], wl["H_qk"], wl["H_v"], wl["d_k"], wl["d_v"], wl["n_slots"]
+    calls = []
+    for l, (a, keep) in enumerate(layers):
+        q, k, v, g, beta, pool, rs, ws = keep[:8]
+        qpool = syn.state_pool_q8_bytes(wl["index"], l, n, Hv, dk, dv, n_hi)
+        qa, _, qkeep = gdn.make_decode_args(q, k, v, g, beta, qpool, rs, ws, state_bf16_rows=n_hi)
+        calls.append((qa, qkeep))
+    torch.cuda.synchronize()
+    lib = gdn.load_library()
+
+    def step():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for qa, _ in calls:
+            code = lib.gdn_decode(ctypes.byref(qa), s)
+            if code:
+                raise gdn.GdnError("gdn_decode", code)
+
+    step()
+    torch.cuda.synchronize()
+    run = step
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        run = graph.replay
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    slot = gdn.gdn_state_q8_bytes(Hv, dk, dv, n_hi)
+    # algorithmic: the rows, codes and scales each tile holds (not its padding)
+    used = Hv * (n_hi * dv * 2 + (dk - n_hi) * (dv + 4))
+    state_b = 2 * B * used
+    _, other_b = decode_bytes_per_launch(B, Hqk, Hv, dk, dv)
+    per_launch = state_b + other_b
+    us = ms * 1e3 / len(calls)
+    gbps = per_launch / (us / 1e6) / 1e9
+    del calls
+    return dict(workload="decode_b512_x48, 8-bit state", n_hi=n_hi,
+                bits_per_value=round(8 * used / (Hv * dk * dv), 3),
+                stored_bits_per_value=round(8 * slot / (Hv * dk * dv), 3),
+                state_bytes_vs_bf16=round(slot / (Hv * dk * dv * 2), 4),
+                kernel="decode_kernel<q8 state, bf16 act, 128, 128>",
+                ms_per_step=round(ms, 4), tokens_per_s=round(B / (ms / 1e3), 1),
+                avg_launch_us=round(us, 2), per_launch_bytes=per_launch,
+                algorithmic_GBps=round(gbps, 1), hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
+
+
 def prefill_useful_flops(lengths, H_v, d_k, d_v, C=64):
     """Useful flops of the chunked recurrence (per chunk of n tokens and head):
     K K^T and Q K^T (lower triangle incl. diagonal), the triangular solve,
@@ -565,6 +626,7 @@ def main():
     ap.add_argument("--no-conv", action="store_true",
                     help="skip the decode-side conv and the channel-wise decay measurements")
     ap.add_argument("--no-b64", action="store_true", help="skip the B=64 decode leg")
+    ap.add_argument("--no-q8", action="store_true", help="skip the 8-bit state decode leg")
     ap.add_argument("--prefill-reps", type=int, default=20)
     ap.add_argument("--prefill-warmup", type=int, default=10,
                     help="untimed calls before the prefill and mixed timings")
@@ -620,6 +682,11 @@ def main():
     if not args.no_conv:
         decode_cw = run_decode_cw(args, torch, gdn, syn, layers)
         log(f"decode, channel-wise decay: {decode_cw}")
+    decode_q8 = None
+    if not args.no_q8:
+        decode_q8 = [run_decode_q8(args, torch, gdn, syn, layers, n_hi) for n_hi in (32, 0)]
+        log(f"decode, 8-bit state: {decode_q8}")
+        torch.cuda.empty_cache()
     prefill = None
     if not args.no_prefill:
         del layers[:]
@@ -664,6 +731,7 @@ def main():
         "decode_b64": decode_b64,
         "conv_decode": conv,
         "decode_channel_decay": decode_cw,
+        "decode_q8_state": decode_q8,
         "prefill": prefill,
         "mixed": mixed,
     }

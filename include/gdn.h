@@ -84,8 +84,8 @@ typedef enum gdn_rule {
  * Each (slot, head) tile stores its first state_bf16_rows key channels (rows)
  * in BF16 and every other row in INT8 with one binary32 scale per row:
  *   [state_bf16_rows, d_v] BF16 | [d_k - state_bf16_rows, d_v] int8 codes |
- *   [d_k - state_bf16_rows] binary32 scales
- * (gdn_state_q8_bytes per head).  An INT8 row represents code * scale; when
+ *   [d_k - state_bf16_rows] binary32 scales | zero padding to a multiple of
+ *   256 bytes (gdn_state_q8_bytes per head; tiles start on 256-byte lines).  An INT8 row represents code * scale; when
  * stored it is requantised against its own largest magnitude rowmax:
  * code = round-to-nearest-even(x * (127 / rowmax)) within [-127, 127] and
  * scale = rowmax / 127, in binary32 (an all-zero row: codes and scale 0).
@@ -154,7 +154,8 @@ typedef struct gdn_decode_args {
   void *o;             /* [B, H_v, d_v] act_dtype */
   uint32_t *status;    /* optional device word; bits are OR-ed in, never cleared */
   int32_t state_bf16_rows; /* state_dtype GDN_Q8: key channels per tile kept in BF16, a
-                              multiple of 8 in [0, d_k]; must be 0 otherwise */
+                              multiple of gdn_state_q8_row_quantum(d_k, d_v) in [0, d_k]
+                              (32 at d_k = d_v = 128); must be 0 otherwise */
   int32_t reserved0;   /* must be 0 */
 } gdn_decode_args;
 
@@ -262,10 +263,18 @@ typedef struct gdn_conv_args {
  * 128 x 128 at 16 bits as 2 MB per request. */
 size_t gdn_state_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t state_dtype);
 
+/* The step of valid BF16-row counts of the 8-bit format at these head sizes
+ * (the rows one wavefront of the decode kernel holds, at least 8, at most
+ * d_k: 32 at d_k = d_v = 128), so that each wavefront's rows are of one
+ * kind; 0 for unsupported sizes.  Host-only. */
+int32_t gdn_state_q8_row_quantum(int32_t d_k, int32_t d_v);
+
 /* Bytes of one slot in the 8-bit format (GDN_Q8): per head
- * bf16_rows * d_v * 2 + (d_k - bf16_rows) * (d_v + 4); 0 for invalid sizes
- * (bf16_rows must be a multiple of 8 in [0, d_k]).  At d_k = d_v = 128 with
- * 24 BF16 rows that is 19,872 bytes per head, 9.70 bits per value. */
+ * bf16_rows * d_v * 2 + (d_k - bf16_rows) * (d_v + 4) rounded up to a
+ * multiple of 256; 0 for invalid sizes (bf16_rows must be a multiple of
+ * gdn_state_q8_row_quantum in [0, d_k]).  At d_k = d_v = 128 with 32 BF16
+ * rows: 20,992 bytes per head (10.25 bits per value, 0.64 of BF16); with
+ * none, 16,896 (8.25 bits). */
 size_t gdn_state_q8_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t bf16_rows);
 
 /* Workspace that gdn_prefill / gdn_mixed need for these arguments (host-only

@@ -5,6 +5,7 @@
 #include <mutex>
 #include <new>
 
+#include "decode.cuh"
 #include "internal.h"
 
 // The workspace of gdn_prefill_noalloc: a fixed device array of this file, one
@@ -36,13 +37,12 @@ gdn_status check_decode(const gdn_decode_args *a) {
   const bool q8 = a->state_dtype == GDN_Q8;
   if ((!valid_dtype(a->state_dtype) && !q8) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
   if (a->reserved0 != 0) return GDN_ERR_UNSUPPORTED;
-  if (q8 ? (a->state_bf16_rows < 0 || a->state_bf16_rows > a->d_k || a->state_bf16_rows % 8 != 0)
-         : a->state_bf16_rows != 0)
-    return GDN_ERR_SHAPE;
+  if (!q8 && a->state_bf16_rows != 0) return GDN_ERR_SHAPE;
   if (a->decay_mode != GDN_DECAY_HEAD && a->decay_mode != GDN_DECAY_CHANNEL)
     return GDN_ERR_UNSUPPORTED;
   gdn_status st = check_heads(a->H_qk, a->H_v, a->d_k, a->d_v);
   if (st != GDN_OK) return st;
+  if (q8 && gdn_state_q8_bytes(1, a->d_k, a->d_v, a->state_bf16_rows) == 0) return GDN_ERR_SHAPE;
   if ((int64_t)a->B * a->H_v > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;  // grid size
   if (a->B == 0) return GDN_OK;
   if (!a->q || !a->k || !a->v || !a->state_pool || !a->o) return GDN_ERR_NULL;
@@ -165,11 +165,18 @@ size_t gdn_state_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t state_dtyp
   return (size_t)H_v * (size_t)d_k * (size_t)d_v * (state_dtype == GDN_BF16 ? 2u : 4u);
 }
 
+int32_t gdn_state_q8_row_quantum(int32_t d_k, int32_t d_v) {
+  if (!supported_d(d_k) || !supported_d(d_v)) return 0;
+  return gdn::q8_row_quantum(d_k, d_v);
+}
+
 size_t gdn_state_q8_bytes(int32_t H_v, int32_t d_k, int32_t d_v, int32_t bf16_rows) {
-  if (H_v <= 0 || d_k <= 0 || d_v <= 0 || bf16_rows < 0 || bf16_rows > d_k || bf16_rows % 8)
+  const int32_t quantum = gdn_state_q8_row_quantum(d_k, d_v);
+  if (H_v <= 0 || quantum == 0 || bf16_rows < 0 || bf16_rows > d_k || bf16_rows % quantum)
     return 0;
   const size_t lo = (size_t)(d_k - bf16_rows);
-  return (size_t)H_v * ((size_t)bf16_rows * d_v * 2 + lo * d_v + lo * 4);
+  const size_t tile = (size_t)bf16_rows * d_v * 2 + lo * d_v + lo * 4;
+  return (size_t)H_v * ((tile + 255) / 256 * 256);  // tiles start on 256-byte boundaries
 }
 
 size_t gdn_prefill_workspace_size(const gdn_prefill_args *args) {

@@ -28,8 +28,9 @@
 // [d_k - hi_rows] scales.  A row is read as code * scale; on store it is
 // requantised against its own largest magnitude (code = rne(x * 127 / rowmax),
 // scale = rowmax / 127), the maximum taken across the LPR lanes of the row.
-// hi_rows is a multiple of 8 and RPT divides 8, so each thread's rows are all
-// BF16 or all INT8.
+// hi_rows is a multiple of the rows one wave holds (or 0 or d_k), so a wave's
+// rows are all BF16 or all INT8: the kernel branches once per wave and runs
+// an instance of one row kind (I8), which keeps the registers of one kind.
 //
 // Work split (gfx950, wave64): every column j of the update is independent
 // given k, q and v, so a lane owns VEC consecutive columns (one 16-byte
@@ -38,6 +39,8 @@
 // cross-lane work is the sum over rows: a butterfly across the lanes of a
 // wave that share columns, then NW partials through LDS.
 #pragma once
+
+#include <type_traits>
 
 #include "device.h"
 #include "internal.h"
@@ -71,8 +74,26 @@ __device__ __forceinline__ void stream_store8(uint2 *p, uint32_t lo, uint32_t hi
   __builtin_nontemporal_store(w, reinterpret_cast<u32x2_t *>(p));
 }
 
+// The largest value over each aligned group of L lanes (L = 2, 4, 8, 16: the
+// lanes of one state row), left in every lane of the group: DPP moves inside
+// a 16-lane row, no LDS round trip -- swap neighbours, swap pairs, mirror each
+// half-row, mirror the row.
+template <int L>
+__device__ __forceinline__ float lane_group_max(float m) {
+  static_assert(L == 1 || L == 2 || L == 4 || L == 8 || L == 16, "a row spans 1..16 lanes");
+  auto mv = [](float x, auto ctrl) {
+    return __int_as_float(
+        __builtin_amdgcn_mov_dpp(__float_as_int(x), decltype(ctrl)::value, 0xf, 0xf, false));
+  };
+  if constexpr (L >= 2) m = fmaxf(m, mv(m, std::integral_constant<int, 0xB1>()));   // quad_perm 1,0,3,2
+  if constexpr (L >= 4) m = fmaxf(m, mv(m, std::integral_constant<int, 0x4E>()));   // quad_perm 2,3,0,1
+  if constexpr (L >= 8) m = fmaxf(m, mv(m, std::integral_constant<int, 0x141>()));  // row_half_mirror
+  if constexpr (L >= 16) m = fmaxf(m, mv(m, std::integral_constant<int, 0x140>()));  // row_mirror
+  return m;
+}
+
 // eight INT8 codes (the low 8 bytes of m) times their row's scale
-__device__ __forceinline__ void unpack_i8(const uint4 &m, float sc, float *f) {
+__device__ __forceinline__ void unpack_i8(const uint2 &m, float sc, float *f) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     const uint32_t w = j < 4 ? m.x : m.y;
@@ -113,7 +134,8 @@ struct DecodeShape {
 // the thread's runs of k, q (RPT rows) and v (VEC columns) are whole 16-byte
 // vectors they are kept packed as loaded (half the registers for BF16) and
 // unpacked in phase 2.
-template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false,
+          bool I8 = false>
 struct DecodeTileRegs {
   using S = DecodeShape<SB, DK, DV, NT>;
   static constexpr int AV = Elem<AB>::kPer16B;  // activation elements per 16 bytes
@@ -121,12 +143,14 @@ struct DecodeTileRegs {
       S::ALL_LIVE && DK % S::RPT == 0 && S::RPT % AV == 0 && S::VEC % AV == 0;
   static constexpr int KN = PACKED ? S::RPT / AV : 1;
   static constexpr int VN = PACKED ? S::VEC / AV : 1;
-  uint4 m[S::RPT];                  // the packed state rows of this thread
+  // the packed state rows of this thread: 16-byte pieces, or the 8-byte
+  // pieces of INT8 rows
+  std::conditional_t<I8, uint2, uint4> m[S::RPT];
   uint4 kp[KN], qp[KN], vp[VN];     // packed k, q, v (PACKED)
   float kr[PACKED ? 1 : S::RPT], qr[PACKED ? 1 : S::RPT], vv[PACKED ? 1 : S::VEC];
   float a, bw;                      // decay and write strength
   float ar[CW ? S::RPT : 1];        // CW: the decay of each of this thread's rows
-  float sc[Q8 ? S::RPT : 1];        // Q8: the scale of each of this thread's INT8 rows
+  float sc[I8 ? S::RPT : 1];        // INT8 rows: the scale of each
   int64_t r, ws;                    // request, write slot
   int h;
   bool valid;                       // false: a bad slot (the tile is skipped)
@@ -138,11 +162,13 @@ struct DecodeTileRegs {
 // NT threads of a group call it with the same (r, h), each passing its index
 // in the group as `tid`: the workgroup, or one of its aligned NT-thread parts
 // (each with its own `red`).
-template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false,
+          bool I8 = false>
 __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t r, int h,
-                                                 DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8> &t,
+                                                 DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8, I8> &t,
                                                  int tid) {
   static_assert(!Q8 || SB, "8-bit storage uses the BF16 tile shape");
+  static_assert(Q8 || !I8, "INT8 rows exist in the 8-bit format only");
   using S = DecodeShape<SB, DK, DV, NT>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT;
   constexpr bool ALL_LIVE = S::ALL_LIVE;
@@ -165,7 +191,7 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
   // this token's q, k (rows of this thread), v (its columns); issued before
   // the state tile: loads return in order, so waiting for these leaves the
   // state loads in flight
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8>;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8, I8>;
   using AT = typename Elem<AB>::T;
   if constexpr (Regs::PACKED) {
     const uint4 *kp = reinterpret_cast<const uint4 *>(static_cast<const AT *>(p.k) +
@@ -193,12 +219,12 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
   if constexpr (Q8) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      t.m[i] = make_uint4(0u, 0u, 0u, 0u);
-      t.sc[i] = 0.f;
+      t.m[i] = {};
+      if constexpr (I8) t.sc[i] = 0.f;
     }
     if (rs >= 0) {
       const char *tile = static_cast<const char *>(p.pool) + (rs * p.H_v + h) * p.tile_bytes;
-      if (row0 < p.hi_rows) {
+      if constexpr (!I8) {
         const uint4 *src = reinterpret_cast<const uint4 *>(tile);
 #pragma unroll
         for (int i = 0; i < RPT; ++i)
@@ -210,11 +236,20 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
         const float *scl = reinterpret_cast<const float *>(tile + hi_b + (int64_t)(DK - p.hi_rows) * DV);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-          if (ALL_LIVE || row0 + i < DK) {
-            const uint2 u = stream_load8(src + (int64_t)(lo + i) * LPR + cv);
-            t.m[i] = make_uint4(u.x, u.y, 0u, 0u);
-            t.sc[i] = scl[lo + i];
+          if (ALL_LIVE || row0 + i < DK) t.m[i] = stream_load8(src + (int64_t)(lo + i) * LPR + cv);
+        }
+        // the run's scales: contiguous, and 16-byte aligned when RPT is a
+        // multiple of 4 (lo is a multiple of RPT, the scale area of 16)
+        if constexpr (ALL_LIVE && RPT % 4 == 0) {
+#pragma unroll
+          for (int i = 0; i < RPT; i += 4) {
+            const float4 s4 = *reinterpret_cast<const float4 *>(scl + lo + i);
+            t.sc[i] = s4.x; t.sc[i + 1] = s4.y; t.sc[i + 2] = s4.z; t.sc[i + 3] = s4.w;
           }
+        } else {
+#pragma unroll
+          for (int i = 0; i < RPT; ++i)
+            if (ALL_LIVE || row0 + i < DK) t.sc[i] = scl[lo + i];
         }
       }
     }
@@ -251,9 +286,10 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
 // and the store to the write slot (a5).  `red` is LDS of
 // DecodeShape::LDS_FLOATS floats.  For NW > 1 it has three barriers (the last
 // lets the caller reuse `red`); a skipped tile has none, uniformly.
-template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false>
+template <bool SB, bool AB, int DK, int DV, int NT, bool CW = false, bool Q8 = false,
+          bool I8 = false>
 __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
-                                                   DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8> &t,
+                                                   DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8, I8> &t,
                                                    float *red, int tid) {
   using S = DecodeShape<SB, DK, DV, NT>;
   constexpr int VEC = S::VEC, LPR = S::LPR, RPT = S::RPT, NW = S::NW;
@@ -268,17 +304,12 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
   const int64_t r = t.r;
   const int h = t.h;
   constexpr int64_t TILE = (int64_t)DK * DV;
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8>;
-  // Q8: this thread's rows are BF16 (the tile's head) or INT8
-  const bool hi_run = !Q8 || row0 < p.hi_rows;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8, I8>;
+  // Q8: the thread's rows are INT8 (I8) or BF16 (the tile's head); the kind
+  // is fixed per wave (the caller's branch), so each instance has one kind
   auto unpack_row = [&](int i, float *f) {
-    if constexpr (Q8) {
-      if (!hi_run) {
-        unpack_i8(t.m[i], t.sc[i], f);
-        return;
-      }
-    }
-    SE::unpack(t.m[i], f);
+    if constexpr (I8) unpack_i8(t.m[i], t.sc[i], f);
+    else SE::unpack(t.m[i], f);
   };
   float kr[RPT], qr[RPT], vv[VEC];
   if constexpr (Regs::PACKED) {
@@ -301,19 +332,22 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
   float kq = 0.f;
 #pragma unroll
   for (int e = 0; e < VEC; ++e) u[e] = w[e] = 0.f;
+  auto partials = [&]() {
 #pragma unroll
-  for (int i = 0; i < RPT; ++i) {
-    float f[VEC];
-    unpack_row(i, f);
-    // CW: the decayed row a_i M_i is what k and q read
-    const float kd = CW ? t.ar[i] * kr[i] : kr[i], qd = CW ? t.ar[i] * qr[i] : qr[i];
+    for (int i = 0; i < RPT; ++i) {
+      float f[VEC];
+      unpack_row(i, f);
+      // CW: the decayed row a_i M_i is what k and q read
+      const float kd = CW ? t.ar[i] * kr[i] : kr[i], qd = CW ? t.ar[i] * qr[i] : qr[i];
 #pragma unroll
-    for (int e = 0; e < VEC; ++e) {
-      u[e] = fmaf(f[e], kd, u[e]);
-      w[e] = fmaf(f[e], qd, w[e]);
+      for (int e = 0; e < VEC; ++e) {
+        u[e] = fmaf(f[e], kd, u[e]);
+        w[e] = fmaf(f[e], qd, w[e]);
+      }
+      kq = fmaf(kr[i], qr[i], kq);
     }
-    kq = fmaf(kr[i], qr[i], kq);
-  }
+  };
+  partials();
   // butterfly over the lanes of this wave that share column vector cv
 #pragma unroll
   for (int off = LPR; off < 64; off <<= 1) {
@@ -374,7 +408,7 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
   if constexpr (Q8) {
     if (t.ws >= 0) {  // uniform over the tile: every lane takes part in the row maxima
       char *tile = static_cast<char *>(p.pool) + (t.ws * p.H_v + h) * p.tile_bytes;
-      if (hi_run) {
+      if constexpr (!I8) {
         uint4 *dst = reinterpret_cast<uint4 *>(tile);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
@@ -404,8 +438,7 @@ __device__ __forceinline__ void decode_tile_finish(const DecodeParams &p,
             m = fmaxf(m, fabsf(f[e]));
           }
           // the row's largest magnitude over its LPR lanes (an aligned lane group)
-#pragma unroll
-          for (int off = 1; off < LPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off));
+          m = lane_group_max<LPR>(m);
           const float inv = m > 0.f ? 127.f / m : 0.f;
           uint32_t w[2] = {0u, 0u};
 #pragma unroll
@@ -445,14 +478,25 @@ __device__ __forceinline__ void decode_tile(const DecodeParams &p, int64_t r, in
   decode_tile_finish<SB, AB, DK, DV, NT>(p, t, red, (int)threadIdx.x);
 }
 
-// Threads per workgroup for a (state dtype, d_k, d_v) instance: enough lanes
-// for every row group to own at least one row, at most 256.
+// Threads per workgroup for a tile of d_k rows of lpr lanes each: enough
+// lanes for every row group to own at least one row, at most 256.
+__host__ __device__ constexpr int decode_threads_for(int lpr, int dk) {
+  return lpr * dk >= kDecodeMaxThreads ? kDecodeMaxThreads : (lpr * dk <= 64 ? 64 : lpr * dk);
+}
 template <bool SB, int DK, int DV>
 constexpr int decode_threads() {
-  constexpr int lpr = DV / Elem<SB>::kPer16B;
-  constexpr int full = lpr * DK;  // one row per thread
-  constexpr int cap = kDecodeMaxThreads;
-  return full >= cap ? cap : (full <= 64 ? 64 : full);
+  return decode_threads_for(DV / Elem<SB>::kPer16B, DK);
+}
+
+// The rows one wave of the BF16-shaped tile holds (64 / LPR row groups of RPT
+// rows), capped at d_k.  The 8-bit format's BF16 head must be a multiple of
+// it (and of 8) so that every wave's rows are of one kind: 32 at d_k = d_v =
+// 128.
+__host__ __device__ constexpr int q8_row_quantum(int dk, int dv) {
+  const int lpr = dv / 8, nt = decode_threads_for(lpr, dk), rg = nt / lpr;
+  const int rows = (64 / lpr) * ((dk + rg - 1) / rg);
+  const int q = rows < dk ? rows : dk;
+  return q < 8 ? 8 : q;
 }
 
 }  // namespace gdn

@@ -9,25 +9,57 @@
 
 namespace gdn {
 
+extern __shared__ int order_lds[];  // the slot order (dynamic LDS)
+
 template <bool SB, bool AB, int DK, int DV, bool CW, bool Q8>
-__global__ __launch_bounds__(kDecodeMaxThreads) void decode_kernel(DecodeParams p, int ordered) {
+__device__ __forceinline__ void decode_walk(const DecodeParams &p, int ordered, float *red) {
   constexpr int NT = decode_threads<SB, DK, DV>();
-  __shared__ float red[DecodeShape<SB, DK, DV, NT>::LDS_FLOATS];
-  extern __shared__ int order_lds[];
   if (ordered) build_slot_order<NT>(p.write_slot, p.B, p.n_slots, order_lds);
   const int64_t n_tiles = (int64_t)p.B * p.H_v;
   // one tile at a time: a software-pipelined loop (the next tile's loads in
   // flight during this tile's reduction and store) measured slower on MI355X
   // (196 against 191 us per B = 512 launch), its extra registers costing more
   // occupancy than the overlap gains
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8>;
-  for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const int pos = (int)(t / p.H_v);
-    Regs cur;
-    decode_tile_load<SB, AB, DK, DV, NT, CW, Q8>(p, ordered ? order_lds[pos] : pos,
-                                                 (int)(t % p.H_v), cur, (int)threadIdx.x);
-    decode_tile_finish<SB, AB, DK, DV, NT, CW, Q8>(p, cur, red, (int)threadIdx.x);
+  auto walk = [&](auto i8) {
+    constexpr bool I8 = decltype(i8)::value;
+    using Regs = DecodeTileRegs<SB, AB, DK, DV, NT, CW, Q8, I8>;
+    for (int64_t t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+      const int pos = (int)(t / p.H_v);
+      Regs cur;
+      decode_tile_load<SB, AB, DK, DV, NT, CW, Q8, I8>(p, ordered ? order_lds[pos] : pos,
+                                                       (int)(t % p.H_v), cur, (int)threadIdx.x);
+      decode_tile_finish<SB, AB, DK, DV, NT, CW, Q8, I8>(p, cur, red, (int)threadIdx.x);
+    }
+  };
+  if constexpr (Q8) {
+    // the wave's rows are all BF16 or all INT8 (host validation: hi_rows is a
+    // multiple of q8_row_quantum), so the branch is uniform per wave and every
+    // wave meets the same barriers in either instance
+    using S = DecodeShape<SB, DK, DV, NT>;
+    const int wave_row0 = (int)(threadIdx.x >> 6) * (64 / S::LPR) * S::RPT;
+    if (wave_row0 < p.hi_rows) walk(std::false_type());
+    else walk(std::true_type());
+  } else {
+    walk(std::false_type());
   }
+}
+
+template <bool SB, bool AB, int DK, int DV, bool CW, bool Q8>
+__global__ __launch_bounds__(kDecodeMaxThreads) void decode_kernel(DecodeParams p, int ordered) {
+  __shared__ float red[DecodeShape<SB, DK, DV, decode_threads<SB, DK, DV>()>::LDS_FLOATS];
+  decode_walk<SB, AB, DK, DV, CW, Q8>(p, ordered, red);
+}
+
+// The 8-bit format with a per-head decay at four waves per SIMD: its INT8
+// instance needs 129 registers and would otherwise run three.  The forced 128
+// spill 12 bytes per lane and still win (B = 512 x 48 layers, d = 128, 32
+// BF16 rows: 169 against 188 us per launch); each tile's pass is latency
+// bound, so waves in flight count more than the bytes of a tile.
+template <bool AB, int DK, int DV>
+__global__ __launch_bounds__(kDecodeMaxThreads) __attribute__((amdgpu_waves_per_eu(4)))
+void decode_q8_kernel(DecodeParams p, int ordered) {
+  __shared__ float red[DecodeShape<true, DK, DV, decode_threads<true, DK, DV>()>::LDS_FLOATS];
+  decode_walk<true, AB, DK, DV, false, true>(p, ordered, red);
 }
 
 DecodeParams make_decode_params(const gdn_decode_args &a) {
@@ -52,6 +84,7 @@ static gdn_status launch_t(const DecodeParams &p, hipStream_t s) {
       p.write_slot != nullptr && p.B <= kOrderMaxB && p.n_slots <= kOrderMaxSlots ? 1 : 0;
   const size_t lds = ordered ? slot_order_lds_bytes(p.B, p.n_slots, NT) : 0;
   auto kern = decode_kernel<SB, AB, DK, DV, CW, Q8>;
+  if constexpr (Q8 && !CW) kern = decode_q8_kernel<AB, DK, DV>;
   // one resident wave of workgroups: CUs x workgroups per CU
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

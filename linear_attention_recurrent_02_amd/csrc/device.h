@@ -27,6 +27,7 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 __device__ __forceinline__ void opaque(uint4 &v) {
   asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
+__device__ __forceinline__ void opaque(uint2 &v) { asm volatile("" : "+v"(v.x), "+v"(v.y)); }
 
 // 16-byte loads and stores marked non-temporal (streamed once: no reason to
 // keep the line in the caches).

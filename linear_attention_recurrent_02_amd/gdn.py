@@ -84,6 +84,8 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_state_bytes.argtypes = [_I32, _I32, _I32, _I32]
     lib.gdn_state_q8_bytes.restype = ctypes.c_size_t
     lib.gdn_state_q8_bytes.argtypes = [_I32, _I32, _I32, _I32]
+    lib.gdn_state_q8_row_quantum.restype = _I32
+    lib.gdn_state_q8_row_quantum.argtypes = [_I32, _I32]
     lib.gdn_prefill_workspace_size.restype = ctypes.c_size_t
     lib.gdn_prefill_workspace_size.argtypes = [ctypes.POINTER(PrefillArgs)]
     lib.gdn_parse_rule.restype = _I32
@@ -275,7 +277,8 @@ def make_decode_args(q, k, v, g, beta, state_pool, read_slot=None, write_slot=No
             raise ValueError("an 8-bit state pool (uint8) needs state_bf16_rows")
         tb = gdn_state_q8_bytes(1, d_k, d_v, int(state_bf16_rows))
         if tb == 0:
-            raise ValueError(f"state_bf16_rows must be a multiple of 8 in [0, {d_k}]")
+            step = int(load_library().gdn_state_q8_row_quantum(d_k, d_v))
+            raise ValueError(f"state_bf16_rows must be a multiple of {step} in [0, {d_k}]")
         if state_pool.dim() != 3 or tuple(state_pool.shape[1:]) != (H_v, tb):
             raise ValueError(f"state_pool must be [n_slots, {H_v}, {tb}] bytes, "
                              f"got {tuple(state_pool.shape)}")

@@ -107,6 +107,33 @@ def state_pool(wl: int, layer: int, n_slots: int, H_v: int, d_k: int, d_v: int,
     return _cast(a, state_dtype)
 
 
+def state_pool_q8_bytes(wl: int, layer: int, n_slots: int, H_v: int, d_k: int, d_v: int,
+                        n_hi: int, std: float = 0.02) -> torch.Tensor:
+    """A stored pool in the 8-bit state layout, drawn on the current CUDA device
+    (uint8 [n_slots, H_v, tile bytes], tile = [n_hi, d_v] BF16 | [d_k - n_hi,
+    d_v] int8 | [d_k - n_hi] float32 | zero padding to 256 bytes): BF16 rows ~ N(0, std^2), codes drawn as
+    integers spread over [-127, 127] (N(0, 36^2) rounded and clipped) and every
+    scale 3.5 std / 127, i.e. random states of the scale of ``state_pool``.
+    Benchmark-sized pools; tests encode their pools with the oracle instead."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3_000_017 * (int(wl) + 1) + 7901 * int(layer) + 41)
+    lo = d_k - n_hi
+    used = n_hi * d_v * 2 + lo * d_v + 4 * lo
+    tile = (used + 255) // 256 * 256  # tiles are padded to 256-byte lines
+    out = torch.zeros((n_slots, H_v, tile), dtype=torch.uint8, device="cuda")
+    step = max(1, (1 << 22) // max(1, H_v * d_k * d_v))  # slots per chunk of the draw
+    for s in range(0, n_slots, step):
+        e = min(n_slots, s + step)
+        n = (e - s) * H_v
+        hi = (torch.randn((n, n_hi * d_v), generator=gen, device="cuda") * std).to(torch.bfloat16)
+        codes = torch.randn((n, lo * d_v), generator=gen, device="cuda").mul_(36.0).round_()
+        codes = codes.clamp_(-127, 127).to(torch.int8)
+        scales = torch.full((n, lo), 3.5 * std / 127.0, dtype=torch.float32, device="cuda")
+        out[s:e, :, :used] = torch.cat([hi.view(torch.uint8), codes.view(torch.uint8),
+                                        scales.view(torch.uint8)], dim=1).view(e - s, H_v, used)
+    return out
+
+
 def distinct_slots(wl: int, layer: int, n_slots: int, B: int, in_place: bool):
     """Read / write slot indices (int32).
 

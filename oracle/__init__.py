@@ -262,10 +262,15 @@ def conv_tail(cu_seqlens, q_raw, k_raw, v_raw, K=4):
 # BF16, the other rows INT8 with one binary32 scale each (oracle.c states the
 # quantisation).  A stored tile is laid out as
 #   [n_hi, dv] BF16 bits | [dk - n_hi, dv] int8 codes | [dk - n_hi] binary32 scales
-# (little endian), one tile per (slot, head).
+# (little endian) followed by zero padding up to a multiple of 256 bytes, one
+# tile per (slot, head).
+
+Q8_TILE_ALIGN = 256
+
 
 def q8_tile_bytes(dk: int, dv: int, n_hi: int) -> int:
-    return n_hi * dv * 2 + (dk - n_hi) * dv + 4 * (dk - n_hi)
+    raw = n_hi * dv * 2 + (dk - n_hi) * dv + 4 * (dk - n_hi)
+    return (raw + Q8_TILE_ALIGN - 1) // Q8_TILE_ALIGN * Q8_TILE_ALIGN
 
 
 def q8_encode(values, n_hi: int):
@@ -294,11 +299,11 @@ def q8_pack(values, n_hi: int) -> np.ndarray:
     lead = v.shape[:-2]
     n = int(np.prod(lead)) if lead else 1
     bits = (hi.reshape(n, -1).astype(np.float32).view(np.uint32) >> 16).astype("<u2")
-    out = np.concatenate([bits.view(np.uint8).reshape(n, -1),
-                          codes.reshape(n, -1).view(np.uint8),
-                          scales.reshape(n, -1).astype("<f4").view(np.uint8).reshape(n, -1)],
-                         axis=1)
-    assert out.shape[1] == q8_tile_bytes(dk, dv, n_hi)
+    body = [bits.view(np.uint8).reshape(n, -1), codes.reshape(n, -1).view(np.uint8),
+            scales.reshape(n, -1).astype("<f4").view(np.uint8).reshape(n, -1)]
+    used = sum(b.shape[1] for b in body)
+    pad = np.zeros((n, q8_tile_bytes(dk, dv, n_hi) - used), np.uint8)
+    out = np.concatenate(body + [pad], axis=1)
     return out.reshape(*lead, out.shape[1])
 
 
@@ -313,9 +318,10 @@ def q8_unpack(raw, dk: int, dv: int, n_hi: int) -> np.ndarray:
     n = int(np.prod(lead)) if lead else 1
     r = raw.reshape(n, tb)
     a, b = n_hi * dv * 2, n_hi * dv * 2 + (dk - n_hi) * dv
+    c = b + 4 * (dk - n_hi)
     hi = (r[:, :a].copy().view("<u2").astype(np.uint32) << 16).view(np.float32)
     codes = r[:, a:b].copy().view(np.int8).astype(np.float32).reshape(n, dk - n_hi, dv)
-    scales = r[:, b:].copy().view("<f4").reshape(n, dk - n_hi, 1)
+    scales = r[:, b:c].copy().view("<f4").reshape(n, dk - n_hi, 1)
     lo = (codes * scales).astype(np.float32)
     out = np.concatenate([hi.reshape(n, n_hi, dv), lo], axis=1).astype(np.float64)
     return out.reshape(*lead, dk, dv)

@@ -77,7 +77,9 @@
  *    precision of the stored scale: x, rowmax, 127 / rowmax, the product and
  *    code * s are binary32 values.  Which channels are high-risk is a
  *    calibration result the pages leave to DAMP; here they are the first
- *    n_hi (a model orders its key channels so).
+ *    n_hi (a model orders its key channels so).  A stored tile is the BF16
+ *    rows, the codes and the scales, zero-padded to a multiple of 256 bytes
+ *    (the packing is in oracle/__init__.py).
  */
 #include <math.h>
 #include <pthread.h>

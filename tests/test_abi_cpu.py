@@ -79,6 +79,7 @@ def _call_decode(a):
     (dict(state_dtype=3), DTYPE), (dict(act_dtype=-1), DTYPE), (dict(act_dtype=2), DTYPE),
     # the 8-bit state format: a multiple of 8 BF16 rows within d_k, none for other formats
     (dict(state_dtype=2, state_bf16_rows=12), SHAPE), (dict(state_dtype=2, state_bf16_rows=136), SHAPE),
+    (dict(state_dtype=2, state_bf16_rows=24), SHAPE),
     (dict(state_dtype=2, state_bf16_rows=-8), SHAPE), (dict(state_bf16_rows=8), SHAPE),
     (dict(reserved0=1), UNSUP),
     (dict(B=-1), SHAPE), (dict(n_slots=-1), SHAPE), (dict(H_qk=0), SHAPE), (dict(d_k=0), SHAPE),
@@ -98,15 +99,24 @@ def test_state_q8_bytes_and_q8_elsewhere():
     int8 codes, binary32 scales), and the calls that refuse it."""
     import oracle
     lib = gdn.load_library()
-    for dk, dv, n_hi in ((128, 128, 24), (128, 128, 0), (128, 128, 128), (64, 32, 16), (16, 16, 8)):
+    for dk, dv, n_hi in ((128, 128, 32), (128, 128, 0), (128, 128, 128), (64, 32, 16),
+                         (16, 16, 16), (16, 128, 8)):
         assert gdn.gdn_state_q8_bytes(32, dk, dv, n_hi) == 32 * oracle.q8_tile_bytes(dk, dv, n_hi)
-    assert gdn.gdn_state_q8_bytes(32, 128, 128, 12) == 0
-    assert gdn.gdn_state_q8_bytes(32, 128, 128, 136) == 0
-    # 24 BF16 rows at d = 128: 9.70 bits per value, 0.606 of the BF16 slot
-    assert gdn.gdn_state_q8_bytes(32, 128, 128, 24) == 32 * 19872
+    # the BF16 head comes in steps of the rows one decode wavefront holds
+    lib = gdn.load_library()
+    quanta = {(128, 128): 32, (128, 64): 32, (128, 16): 32, (64, 128): 16, (64, 64): 16,
+              (64, 32): 16, (32, 64): 8, (32, 32): 16, (16, 128): 8, (16, 16): 16}
+    for (dk, dv), q in quanta.items():
+        assert lib.gdn_state_q8_row_quantum(dk, dv) == q, (dk, dv)
+    assert lib.gdn_state_q8_row_quantum(48, 128) == 0
+    for bad in (8, 12, 24, 136):
+        assert gdn.gdn_state_q8_bytes(32, 128, 128, bad) == 0, bad
+    # 32 BF16 rows at d = 128: 10.25 bits per value, 0.64 of the BF16 slot
+    assert gdn.gdn_state_q8_bytes(32, 128, 128, 32) == 32 * 20992
     # an 8-bit pool passes the decode's checks (stops at B = 0); mixed and prefill refuse it
-    assert _call_decode(_decode_args(B=0, state_dtype=2, state_bf16_rows=24)) == OK
-    a = _decode_args(state_dtype=2, state_bf16_rows=24)
+    assert _call_decode(_decode_args(B=0, state_dtype=2, state_bf16_rows=32)) == OK
+    assert _call_decode(_decode_args(B=0, state_dtype=2, state_bf16_rows=24)) == SHAPE
+    a = _decode_args(state_dtype=2, state_bf16_rows=32)
     p = _prefill_args(state_dtype=2)
     assert lib.gdn_mixed(ctypes.byref(a), ctypes.byref(_prefill_args()), None) == UNSUP
     assert lib.gdn_prefill(ctypes.byref(p), None) == UNSUP

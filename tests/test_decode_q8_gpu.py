@@ -54,21 +54,23 @@ def got_vals(r, dk, dv, n_hi):
 
 @pytest.mark.parametrize("rule", RULES)
 def test_q8_decode_b64(rule):
-    """B = 64, H_qk = 16, H_v = 32, d = 128, 24 BF16 rows of 128 (9.70 bits per
+    """B = 64, H_qk = 16, H_v = 32, d = 128, 32 BF16 rows of 128 (10.25 bits per
     value), 64 live slots of a 256-slot pool, distinct read and write slots."""
     say("q8 decode b64", rule)
-    r = run(61, 64, 16, 32, 128, 128, 256, 24, torch.bfloat16, rule=rule)
+    r = run(61, 64, 16, 32, 128, 128, 256, 32, torch.bfloat16, rule=rule)
     assert r["code"] == 0
     w = r["ws"].numpy()
     assert scaled_err(f64(r["o"]), r["ro"], 2) < BAR
-    assert scaled_err(got_vals(r, 128, 128, 24)[w], r["rvals"][w], 2) < BAR
+    assert scaled_err(got_vals(r, 128, 128, 32)[w], r["rvals"][w], 2) < BAR
     others = np.setdiff1d(np.arange(256), w)
     assert torch.equal(r["dpool"][others], r["raw"][others])  # bytes of unwritten slots
 
 
-@pytest.mark.parametrize("dk,dv,n_hi", [(16, 16, 8), (32, 64, 0), (64, 32, 16), (128, 16, 128),
-                                        (16, 128, 8), (64, 64, 32), (128, 128, 0),
-                                        (128, 64, 56)])
+# BF16 heads in steps of gdn_state_q8_row_quantum: 16 at (16, 16), 8 at
+# (32, 64) and (16, 128), 16 at (64, 32) and (64, 64), 32 at d_k = 128
+@pytest.mark.parametrize("dk,dv,n_hi", [(16, 16, 16), (16, 16, 0), (32, 64, 8), (64, 32, 16),
+                                        (128, 16, 32), (16, 128, 8), (64, 64, 48),
+                                        (128, 128, 0), (128, 64, 96)])
 @pytest.mark.parametrize("adt", [torch.bfloat16, torch.float32])
 def test_q8_decode_shapes(dk, dv, n_hi, adt):
     say("q8 decode shapes", dk, dv, n_hi, adt)
@@ -98,7 +100,7 @@ def test_q8_slot_rules_and_bad_slot():
 
 def test_q8_in_place_equals_out_of_place_and_frozen_state():
     say("q8 decode in place / frozen")
-    B, Hqk, Hv, d, n_hi = 16, 2, 4, 128, 24
+    B, Hqk, Hv, d, n_hi = 16, 2, 4, 128, 32
     q, k, v, g, beta = syn.token_inputs(64, 0, B, Hqk, Hv, d, d)
     raw, vals = q8_pool(64, 40, Hv, d, d, n_hi)
     rs, ws = syn.distinct_slots(64, 0, 40, B, in_place=False)
@@ -128,7 +130,7 @@ def test_q8_steps_accumulate():
     """Eight decode tokens in place on one 8-bit pool (each stores and reloads
     the quantised state) against the oracle stepping the same way."""
     say("q8 decode 8 steps")
-    B, Hqk, Hv, d, n_hi, T = 16, 2, 4, 128, 24, 8
+    B, Hqk, Hv, d, n_hi, T = 16, 2, 4, 128, 32, 8
     raw, vals = q8_pool(65, B, Hv, d, d, n_hi, std=0.05)
     own = torch.arange(B, dtype=torch.int32)
     dpool = raw.to(DEV)
@@ -148,7 +150,7 @@ def test_q8_steps_accumulate():
 def test_q8_channel_decay():
     """The per-key-channel decay (g [B, H_v, d_k]) on an 8-bit pool."""
     say("q8 decode channel decay")
-    B, Hqk, Hv, d, n_hi = 8, 2, 4, 128, 24
+    B, Hqk, Hv, d, n_hi = 8, 2, 4, 128, 32
     gen = torch.Generator().manual_seed(66)
     gcw = -torch.nn.functional.softplus(torch.randn((B, Hv, d), generator=gen))
     for rule in ("gated", "gated_delta"):
@@ -159,10 +161,10 @@ def test_q8_channel_decay():
 
 
 def test_q8_decode_b512_full_size():
-    """Batch 512 at the benchmark's shapes with 24 BF16 rows per 128 (one layer:
+    """Batch 512 at the benchmark's shapes with 32 BF16 rows per 128 (one layer:
     a 512-slot 8-bit pool, in place), every request against the oracle."""
     say("q8 decode b512")
-    B, Hqk, Hv, d, n, n_hi = 512, 16, 32, 128, 512, 24
+    B, Hqk, Hv, d, n, n_hi = 512, 16, 32, 128, 512, 32
     assert gdn_state_q8_bytes(Hv, d, d, n_hi) == Hv * oracle.q8_tile_bytes(d, d, n_hi)
     r = run(67, B, Hqk, Hv, d, d, n, n_hi, torch.bfloat16, in_place=True)
     w = r["ws"].numpy()

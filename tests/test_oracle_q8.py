@@ -88,20 +88,23 @@ def test_bf16_head_rows():
 
 def test_byte_layout():
     """Tile bytes: n_hi rows of BF16 bits, then the codes, then the binary32
-    scales; the sizes of the pages' DAMP-like point (d = 128, 24 BF16 rows:
-    9.70 bits per value)."""
-    dk, dv, n_hi = 128, 128, 24
-    assert oracle.q8_tile_bytes(dk, dv, n_hi) == 24 * 128 * 2 + 104 * 128 + 104 * 4
-    bits = 8 * oracle.q8_tile_bytes(dk, dv, n_hi) / (dk * dv)
-    assert abs(bits - 9.703) < 1e-3
+    scales, zero-padded to a multiple of 256 bytes; the sizes of the pages'
+    DAMP-like points (d = 128 with 24 or 32 BF16 rows: 9.75 and 10.25 bits
+    per value)."""
+    dk, dv = 128, 128
+    assert oracle.q8_tile_bytes(dk, dv, 24) == 19968  # 24*256 + 104*128 + 104*4 = 19872, padded
+    assert oracle.q8_tile_bytes(dk, dv, 32) == 20992  # 20864, padded
+    assert oracle.q8_tile_bytes(dk, dv, 0) == 16896   # 16384 + 512, already a multiple of 256
+    assert abs(8 * oracle.q8_tile_bytes(dk, dv, 24) / (dk * dv) - 9.75) < 1e-9
     row = np.zeros((1, 2, 16))
     row[0, 0, 0] = 1.0          # BF16 row: 1.0 = 0x3F80
     row[0, 1, :2] = [127 * U, -U]  # INT8 row: codes 127, -1, scale 2^-10
     raw = oracle.q8_pack(row, 1)[0]
-    assert raw.size == 16 * 2 + 16 + 4
+    assert raw.size == 256  # 16 * 2 + 16 + 4 = 52 bytes used
     assert raw[0] == 0x80 and raw[1] == 0x3F
     assert raw[32] == 127 and raw[33] == 0xFF and not raw[34:48].any()
     assert np.frombuffer(raw[48:52].tobytes(), "<f4")[0] == np.float32(U)
+    assert not raw[52:].any()
 
 
 def test_decode_all_bf16_rows_equals_bf16_decode():
