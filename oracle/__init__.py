@@ -73,6 +73,9 @@ def _load():
         lib.oracle_decode_cw_q8.restype = i32
         lib.oracle_decode_cw_q8.argtypes = [i32, i32, i32, i32, i32, i64, i32, f64, i32,
                                             P, P, P, P, P, P, P, P, P, i32]
+        lib.oracle_sequences_cw.restype = i32
+        lib.oracle_sequences_cw.argtypes = [i32, P, i32, i32, i32, i32, i64, i32, f64, i32,
+                                            P, P, P, P, P, P, P, P, P, i32]
         lib.oracle_version.restype = i32
         _lib = lib
     return _lib
@@ -176,6 +179,30 @@ def sequences(cu_seqlens, q, k, v, g, beta, pool, read_slot=None, write_slot=Non
                                     n_threads or default_threads())
     if code < 0:
         raise ValueError("oracle_sequences rejected its arguments")
+    return o, pool, code
+
+
+def sequences_cw(cu_seqlens, q, k, v, g, beta, pool, read_slot=None, write_slot=None, *,
+                 rule="gated_delta", scale=1.0, round_state=False, n_threads=None):
+    """``sequences`` with a per-key-channel decay: g is [N, Hv, dk] (Kimi Delta
+    Attention's gate, the Kimi Linear section).  Returns ``(o, pool_after,
+    code)``."""
+    q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    pool = _f64(pool).copy()
+    cu = _i32(cu_seqlens)
+    n_seq = cu.shape[0] - 1
+    N, Hqk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    if g.shape != (N, Hv, dk):
+        raise ValueError("g must be [N, Hv, dk]")
+    rs, ws = _i32(read_slot), _i32(write_slot)
+    o = np.zeros((N, Hv, dv), np.float64)
+    code = _load().oracle_sequences_cw(n_seq, _p(cu), Hqk, Hv, dk, dv, pool.shape[0],
+                                       _rule(rule), float(scale), int(bool(round_state)), _p(q),
+                                       _p(k), _p(v), _p(g), _p(beta), _p(pool), _p(rs), _p(ws),
+                                       _p(o), n_threads or default_threads())
+    if code < 0:
+        raise ValueError("oracle_sequences_cw rejected its arguments")
     return o, pool, code
 
 

@@ -87,7 +87,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_VERSION 4
+#define ORACLE_VERSION 5
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -472,25 +472,14 @@ typedef struct {
 
 static void q8_store(double *M, int dk, int dv, int n_hi, int8_t *codes, float *scales);
 
-static void decode_cw_unit(void *p, int64_t unit, double *work) {
-  decode_cw_ctx *c = (decode_cw_ctx *)p;
-  int64_t r = unit / c->Hv;
-  int h = (int)(unit % c->Hv);
-  int hq = (int)((int64_t)h * c->Hqk / c->Hv);
-  int64_t rs, ws;
-  if (!resolve_slots(c->read_slot, c->write_slot, r, c->n_slots, &rs, &ws)) {
-    *c->bad = 1;
-    return;
-  }
-  const int dk = c->dk, dv = c->dv;
-  int64_t tile = (int64_t)dk * dv;
-  double *S = work, *rd = work + tile;
-  if (rs >= 0) memcpy(S, c->pool + (rs * c->Hv + h) * tile, tile * sizeof(double));
-  else memset(S, 0, tile * sizeof(double));
-  const double *q = c->q + (r * c->Hqk + hq) * dk, *k = c->k + (r * c->Hqk + hq) * dk;
-  const double *v = c->v + (r * c->Hv + h) * dv, *g = c->g + (r * c->Hv + h) * dk;
-  const double beta = c->beta ? c->beta[r * c->Hv + h] : 1.0;
-  const int decay = c->rule == 1 || c->rule == 3, erase = c->rule >= 2;
+/* One token of the channel-wise decay recurrence on one head's state S
+ * (d_k x d_v, updated in place): row i decays by alpha_i = exp(g[i]), then
+ * the write beta k (v - S~^T k)^T reads the decayed state S~ (without erase:
+ * k v^T), then o = scale S^T q.  rd: d_v scratch. */
+static void cw_step(double *S, int dk, int dv, int rule, double scale, const double *q,
+                    const double *k, const double *v, const double *g, double beta, double *rd,
+                    double *o) {
+  const int decay = rule == 1 || rule == 3, erase = rule >= 2;
   /* decay row i (key channel i) by its own alpha_i */
   if (decay)
     for (int i = 0; i < dk; ++i) {
@@ -507,12 +496,32 @@ static void decode_cw_unit(void *p, int64_t unit, double *work) {
   for (int i = 0; i < dk; ++i)
     for (int j = 0; j < dv; ++j) S[(int64_t)i * dv + j] += k[i] * rd[j];
   /* read-out from the new state */
-  double *o = c->o + (r * c->Hv + h) * dv;
   for (int j = 0; j < dv; ++j) {
     double acc = 0.0;
     for (int i = 0; i < dk; ++i) acc += S[(int64_t)i * dv + j] * q[i];
-    o[j] = c->scale * acc;
+    o[j] = scale * acc;
   }
+}
+
+static void decode_cw_unit(void *p, int64_t unit, double *work) {
+  decode_cw_ctx *c = (decode_cw_ctx *)p;
+  int64_t r = unit / c->Hv;
+  int h = (int)(unit % c->Hv);
+  int hq = (int)((int64_t)h * c->Hqk / c->Hv);
+  int64_t rs, ws;
+  if (!resolve_slots(c->read_slot, c->write_slot, r, c->n_slots, &rs, &ws)) {
+    *c->bad = 1;
+    return;
+  }
+  const int dk = c->dk, dv = c->dv;
+  int64_t tile = (int64_t)dk * dv;
+  double *S = work, *rd = work + tile;
+  if (rs >= 0) memcpy(S, c->pool + (rs * c->Hv + h) * tile, tile * sizeof(double));
+  else memset(S, 0, tile * sizeof(double));
+  cw_step(S, dk, dv, c->rule, c->scale, c->q + (r * c->Hqk + hq) * dk,
+          c->k + (r * c->Hqk + hq) * dk, c->v + (r * c->Hv + h) * dv,
+          c->g + (r * c->Hv + h) * dk, c->beta ? c->beta[r * c->Hv + h] : 1.0, rd,
+          c->o + (r * c->Hv + h) * dv);
   if (ws >= 0) {
     double *dst = c->pool + (ws * c->Hv + h) * tile;
     if (c->n_hi >= 0) {
@@ -658,5 +667,53 @@ int oracle_decode_q8(int B, int Hqk, int Hv, int dk, int dv, int64_t n_slots, in
   decode_q8_ctx c = {B, Hqk, Hv, dk, dv, rule, n_hi, n_slots, scale, q, k, v, g, beta,
                      pool, read_slot, write_slot, o, &bad};
   if (run_units(decode_q8_unit, &c, (int64_t)B * Hv, (size_t)dk * dv + dv, n_threads)) return -1;
+  return bad ? 1 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* sequences with a channel-wise decay (the prefill recurrence of KDA)       */
+
+static void seq_cw_unit(void *p, int64_t unit, double *work) {
+  seq_ctx *c = (seq_ctx *)p;
+  int64_t s = unit / c->Hv;
+  int h = (int)(unit % c->Hv);
+  int hq = (int)((int64_t)h * c->Hqk / c->Hv);
+  int64_t rs, ws;
+  if (!resolve_slots(c->read_slot, c->write_slot, s, c->n_slots, &rs, &ws)) {
+    *c->bad = 1;
+    return;
+  }
+  const int dk = c->dk, dv = c->dv;
+  int64_t tile = (int64_t)dk * dv;
+  double *S = work, *rd = work + tile;
+  if (rs >= 0) memcpy(S, c->pool + (rs * c->Hv + h) * tile, tile * sizeof(double));
+  else memset(S, 0, tile * sizeof(double));
+  for (int64_t t = c->cu[s]; t < c->cu[s + 1]; ++t)
+    cw_step(S, dk, dv, c->rule, c->scale, c->q + (t * c->Hqk + hq) * dk,
+            c->k + (t * c->Hqk + hq) * dk, c->v + (t * c->Hv + h) * dv,
+            c->g + (t * c->Hv + h) * dk, c->beta ? c->beta[t * c->Hv + h] : 1.0, rd,
+            c->o + (t * c->Hv + h) * dv);
+  if (ws >= 0) {
+    double *dst = c->pool + (ws * c->Hv + h) * tile;
+    for (int64_t e = 0; e < tile; ++e) dst[e] = c->round_state ? oracle_round_bf16(S[e]) : S[e];
+  }
+}
+
+/* The channel-wise decay recurrence (Kimi Delta Attention, Kimi Linear
+ * section) over n_seq variable-length sequences: as oracle_sequences, except
+ * g is [N, Hv, dk], one log-decay per key channel of each state head. */
+int oracle_sequences_cw(int n_seq, const int32_t *cu, int Hqk, int Hv, int dk, int dv,
+                        int64_t n_slots, int rule, double scale, int round_state,
+                        const double *q, const double *k, const double *v, const double *g,
+                        const double *beta, double *pool, const int32_t *read_slot,
+                        const int32_t *write_slot, double *o, int n_threads) {
+  if (n_seq < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || rule < 0 || rule > 3) return -1;
+  if (Hv % Hqk != 0) return -1;
+  for (int s = 0; s < n_seq; ++s)
+    if (cu[s + 1] < cu[s]) return -1;
+  volatile int bad = 0;
+  seq_ctx c = {n_seq, Hqk, Hv, dk, dv, rule, round_state, n_slots, scale, cu, q, k, v, g, beta,
+               pool, read_slot, write_slot, o, &bad};
+  if (run_units(seq_cw_unit, &c, (int64_t)n_seq * Hv, (size_t)dk * dv + dv, n_threads)) return -1;
   return bad ? 1 : 0;
 }
