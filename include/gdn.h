@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 6
+#define GDN_ABI_VERSION 7
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -186,7 +186,8 @@ typedef struct gdn_prefill_args {
   const void *q;       /* [n_tokens, H_qk * d_k] act_dtype (raw or final) */
   const void *k;       /* [n_tokens, H_qk * d_k] act_dtype */
   const void *v;       /* [n_tokens, H_v * d_v] act_dtype */
-  const float *g;      /* [n_tokens, H_v] log-decay when use_frontend = 0 */
+  const float *g;      /* [n_tokens, H_v] log-decay when use_frontend = 0 ([n_tokens, H_v, d_k]
+                          with GDN_DECAY_CHANNEL) */
   const float *beta;   /* [n_tokens, H_v] write strength when use_frontend = 0 */
   const float *a_raw;  /* [n_tokens, H_v] when use_frontend = 1: g = -softplus(a_raw) */
   const float *b_raw;  /* [n_tokens, H_v] when use_frontend = 1: beta = sigmoid(b_raw) */
@@ -212,7 +213,10 @@ typedef struct gdn_prefill_args {
    * (unique, no other request's read slot).  Ignored when ckpt_interval = 0. */
   const int32_t *ckpt_slot; /* [n_seq, ckpt_per_seq] device */
   int32_t ckpt_per_seq;
-  int32_t reserved1;   /* must be 0 */
+  int32_t decay_mode;  /* gdn_decay_mode.  GDN_DECAY_CHANNEL: g is [n_tokens, H_v, d_k], one
+                          log-decay per key channel (Kimi Delta Attention), with use_frontend = 0
+                          (q, k, v, g, beta given); FP32 state or activations then need
+                          d_k <= 64 */
 } gdn_prefill_args;
 
 /* The front-end's conv window across calls.  The short conv is part of the

@@ -62,8 +62,12 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
   if (!valid_rule(a->rule)) return GDN_ERR_RULE;
   if (a->state_dtype == GDN_Q8) return GDN_ERR_UNSUPPORTED;  // the 8-bit format is decode-only
   if (!valid_dtype(a->state_dtype) || !valid_dtype(a->act_dtype)) return GDN_ERR_DTYPE;
-  if (a->reserved1 != 0) return GDN_ERR_UNSUPPORTED;
+  if (a->decay_mode != GDN_DECAY_HEAD && a->decay_mode != GDN_DECAY_CHANNEL)
+    return GDN_ERR_UNSUPPORTED;
   if (a->use_frontend != 0 && a->use_frontend != 1) return GDN_ERR_UNSUPPORTED;
+  // the front-end produces one decay per (token, head): the channel-wise
+  // decay takes q, k, v, g and beta as given
+  if (a->decay_mode == GDN_DECAY_CHANNEL && a->use_frontend) return GDN_ERR_UNSUPPORTED;
   gdn_status st = check_heads(a->H_qk, a->H_v, a->d_k, a->d_v);
   if (st != GDN_OK) return st;
   if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;

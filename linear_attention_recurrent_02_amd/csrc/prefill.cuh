@@ -69,6 +69,7 @@ struct PrefillParams {
   // state goes to ckpt_slot[seq * ckpt_per_seq + j]
   int32_t ckpt_chunks, ckpt_per_seq;
   const int32_t *ckpt_slot;
+  int32_t channel_decay;  // g is [N, H_v, d_k]: one log-decay per key channel
 };
 
 // LDS layout of the chain kernel (byte offsets).  IT is the storage type of

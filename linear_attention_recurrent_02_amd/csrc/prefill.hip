@@ -5,6 +5,7 @@
 // inputs are raw, then the chains.
 #include <algorithm>
 
+#include "prefill_cw.cuh"
 #include "prefill_pipe.cuh"
 
 namespace gdn {
@@ -15,6 +16,14 @@ __global__ __launch_bounds__((64 * kPrefillWaves<DK, DV, F32>)) void prefill_ker
   __shared__ __align__(16) char smem[kChainLds<DK, DV, F32, AB>];
   const int chain = chain_of_block(blockIdx.x);
   if (chain < n_chains) run_chain<SB, AB, DK, DV, F32, CK>(p, chain, smem);
+}
+
+// one (sequence, state head) chain per workgroup with a per-key-channel decay
+template <bool SB, bool AB, int DK, int DV, bool F32, bool CK>
+__global__ __launch_bounds__(256) void prefill_cw_kernel(PrefillParams p, int n_chains) {
+  __shared__ __align__(16) char smem[kCwChainLds<DK, DV, F32, AB>];
+  const int chain = chain_of_block(blockIdx.x);
+  if (chain < n_chains) prefill_chain_cw<SB, AB, DK, DV, F32, CK>(p, chain, smem);
 }
 
 // ---- launcher --------------------------------------------------------------
@@ -30,6 +39,7 @@ PrefillParams make_prefill_params(const gdn_prefill_args &a, const void *q, cons
   p.ckpt_chunks = a.ckpt_interval > 0 ? a.ckpt_interval / a.chunk : 0;
   p.ckpt_per_seq = a.ckpt_per_seq;
   p.ckpt_slot = a.ckpt_slot;
+  p.channel_decay = a.decay_mode == GDN_DECAY_CHANNEL ? 1 : 0;
   return p;
 }
 
@@ -38,6 +48,21 @@ static gdn_status launch_chains(const PrefillParams &p, hipStream_t s) {
   // FP32 arithmetic (FP32 MFMA operands) for an FP32 state or FP32
   // activations; BF16 MFMA operands only when both are BF16
   constexpr bool F32 = !AB || !SB;
+  if (p.channel_decay) {
+    if constexpr (kCwChainLds<DK, DV, F32, AB> > 160 * 1024) {
+      return GDN_ERR_UNSUPPORTED;  // FP32 operands of the channel-wise chain at d_k = 128
+    } else {
+      const int n_chains = p.n_seq * p.H_v;
+      const int blocks = (n_chains + 15) / 16 * 16;
+      if (p.ckpt_chunks > 0)
+        hipLaunchKernelGGL((prefill_cw_kernel<SB, AB, DK, DV, F32, true>), dim3(blocks), dim3(256),
+                           0, s, p, n_chains);
+      else
+        hipLaunchKernelGGL((prefill_cw_kernel<SB, AB, DK, DV, F32, false>), dim3(blocks), dim3(256),
+                           0, s, p, n_chains);
+      return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+    }
+  }
   if constexpr (kChainLds<DK, DV, F32, AB> > 160 * 1024) {
     return GDN_ERR_UNSUPPORTED;  // FP32 activation tiles at d = 128 do not fit in LDS
   } else {

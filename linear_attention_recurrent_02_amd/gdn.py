@@ -48,7 +48,7 @@ class PrefillArgs(ctypes.Structure):
                 ("conv_wk", _P), ("conv_wv", _P), ("state_pool", _P), ("read_slot", _P),
                 ("write_slot", _P), ("o", _P), ("workspace", _P),
                 ("workspace_bytes", ctypes.c_size_t), ("status", _P), ("ckpt_slot", _P),
-                ("ckpt_per_seq", _I32), ("reserved1", _I32)]
+                ("ckpt_per_seq", _I32), ("decay_mode", _I32)]
 
 
 class ConvArgs(ctypes.Structure):
@@ -360,7 +360,11 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
     _need(read_slot, "read_slot", dtype=torch.int32, shape=(n_seq,))
     _need(write_slot, "write_slot", dtype=torch.int32, shape=(n_seq,))
     _need(o, "o", dtype=q.dtype, shape=(N, H_v, d_v))
-    for name, t in (("g", g), ("beta", beta), ("a_raw", a_raw), ("b_raw", b_raw)):
+    channel = g is not None and g.dim() == 3  # one log-decay per key channel
+    if channel:
+        _need(g, "g", dtype=torch.float32, shape=(N, H_v, d_k))
+    for name, t in ((("g", g),) if not channel else ()) + (("beta", beta), ("a_raw", a_raw),
+                                                           ("b_raw", b_raw)):
         _need(t, name, dtype=torch.float32, shape=(N, H_v))
     use_fe = conv_wq is not None
     K = conv_wq.shape[-1] if use_fe and conv_wq.dim() == 2 else 4
@@ -402,7 +406,8 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
     a.o, a.status = _ptr(o), _ptr(status)
     a.ckpt_slot = _ptr(ckpt_slot)
     a.ckpt_per_seq = 0 if ckpt_slot is None else int(ckpt_slot.shape[-1])
-    a.reserved1 = 0
+    # g [N, H_v]: one decay per state head; [N, H_v, d_k]: one per key channel
+    a.decay_mode = DECAY_CHANNEL if channel else DECAY_HEAD
     need = int(load_library().gdn_prefill_workspace_size(ctypes.byref(a)))
     if need and workspace is None and alloc_workspace:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -475,6 +480,7 @@ def gdn_frontend(cu_seqlens, q_raw, k_raw, v_raw, *, H_qk, H_v, conv_wq, conv_wk
     a.state_dtype = F32
     a.act_dtype = _dtype_code(q_raw)
     a.use_frontend, a.conv_k, a.chunk, a.ckpt_interval = 1, K, 64, 0
+    a.decay_mode = DECAY_HEAD
     a.n_tokens, a.n_slots = N, 0
     a.scale, a.eps = 1.0, float(eps)
     a.cu_seqlens, a.q, a.k, a.v = _ptr(cu_seqlens), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw)

@@ -14,6 +14,8 @@ Distributions (the workload descriptions of the task):
   v      ~ N(0, 1)
   beta   = sigmoid(N(0, 1))          (write strength)
   g      = -softplus(N(0, 1))        (log of the decay a = exp(g))
+  channel-wise g = -softplus(N(0, 1) + b), b ~ U(-5, 1) fixed per (head,
+           key channel): one head's channels forget at different rates
   state  ~ N(0, 0.02^2)  (0.02 is the standard deviation)
   raw q/k/v for the front-end ~ N(0, 1); conv weights ~ N(0, 0.5^2);
   a_raw, b_raw ~ N(0, 1)
@@ -24,7 +26,8 @@ import numpy as np
 import torch
 
 # stream ids keep independent draws independent
-_S_Q, _S_K, _S_V, _S_G, _S_B, _S_STATE, _S_SLOTS, _S_LEN, _S_W, _S_RAW, _S_CONV = range(11)
+(_S_Q, _S_K, _S_V, _S_G, _S_B, _S_STATE, _S_SLOTS, _S_LEN, _S_W, _S_RAW, _S_CONV, _S_GC,
+ _S_GCB) = range(13)
 
 WORKLOADS = {
     # tiny FP32 recurrence: B=1, H=2, d=16, T=32, zero initial state
@@ -77,6 +80,18 @@ def token_inputs(wl: int, layer: int, n_tok: int, H_qk: int, H_v: int, d_k: int,
     beta = _sigmoid(rng(wl, layer, _S_B).standard_normal((n_tok, H_v)))
     return (_cast(q, act_dtype), _cast(k, act_dtype), _cast(v, act_dtype),
             _cast(g, torch.float32), _cast(beta, torch.float32))
+
+
+def channel_gates(wl: int, layer: int, n_tok: int, H_v: int, d_k: int, lo: float = -5.0,
+                  hi: float = 1.0) -> torch.Tensor:
+    """Per-key-channel log-decays g [n_tok, H_v, d_k] float32 (Kimi Delta
+    Attention's channel-wise gate): -softplus(x + b) with x ~ N(0, 1) per
+    (token, head, channel) and a bias b ~ U(lo, hi) fixed per (head, channel),
+    so the mean decay per token ranges from about e^-0.01 to e^-1.3 across
+    one head's channels."""
+    b = rng(wl, layer, _S_GCB).uniform(lo, hi, size=(1, H_v, d_k))
+    x = rng(wl, layer, _S_GC).standard_normal((n_tok, H_v, d_k))
+    return _cast(_neg_softplus(x + b), torch.float32)
 
 
 def state_pool(wl: int, layer: int, n_slots: int, H_v: int, d_k: int, d_v: int,

@@ -28,7 +28,7 @@ def test_struct_layout_matches():
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
     assert lib.gdn_sizeof_conv_args() == ctypes.sizeof(B.ConvArgs)
-    assert gdn.gdn_abi_version() == 6
+    assert gdn.gdn_abi_version() == 7
 
 
 def test_state_bytes_against_the_pages():
@@ -156,10 +156,13 @@ def _prefill_args(**over):
     (dict(q=FAKE + 2), ALIGN), (dict(v=FAKE + 8), ALIGN), (dict(conv_wv=FAKE + 4), ALIGN),
     (dict(o=FAKE + 2), ALIGN), (dict(state_pool=FAKE + 8), ALIGN),
     (dict(workspace=FAKE + 8, workspace_bytes=1 << 40), ALIGN),
-    # intermediate checkpoints: a positive multiple of the chunk, a slot matrix, reserved1 = 0
+    # intermediate checkpoints: a positive multiple of the chunk, a slot matrix; decay modes
     (dict(ckpt_interval=32), SHAPE), (dict(ckpt_interval=-64), SHAPE),
     (dict(ckpt_interval=64), SHAPE), (dict(ckpt_interval=64, ckpt_per_seq=2), NULL),
-    (dict(reserved1=1), UNSUP),
+    (dict(decay_mode=2), UNSUP), (dict(decay_mode=-1), UNSUP),
+    (dict(decay_mode=1), UNSUP),  # the channel-wise decay takes final q/k/v/g (no front-end)
+    # the channel-wise checks pass (an empty batch launches nothing)
+    (dict(decay_mode=1, use_frontend=0, n_seq=0, n_tokens=0), OK),
     (dict(ckpt_interval=128, ckpt_per_seq=2, ckpt_slot=FAKE), WORKSPACE),  # the checks pass
 ])
 def test_prefill_validation(over, code):
@@ -172,7 +175,7 @@ NOALLOC_SAME = [
     (dict(chunk=32), UNSUP), (dict(rule=9), RULE), (dict(act_dtype=3), DTYPE),
     (dict(n_seq=-1), SHAPE), (dict(cu_seqlens=None), NULL), (dict(conv_wk=None), NULL),
     (dict(H_v=5), UNSUP), (dict(n_slots=1), SHAPE), (dict(q=FAKE + 2), ALIGN),
-    (dict(ckpt_interval=32), SHAPE), (dict(reserved1=1), UNSUP),
+    (dict(ckpt_interval=32), SHAPE), (dict(decay_mode=3), UNSUP),
 ]
 
 
