@@ -502,6 +502,64 @@ def run_prefill(args, torch, gdn, syn):
                 ckpt_every_1024_ms=round(ms_ck, 3), ckpt_count=n_ck)
 
 
+def run_prefill_cw(args, torch, gdn, syn):
+    """The chunked-prefill workload's sequences and shapes (8 ragged sequences,
+    H_qk=16, H_v=32, d=128, BF16, fresh requests into 8 slots of a 64-slot
+    pool) with one decay per key channel (g [N, H_v, d_k] float32, Kimi Delta
+    Attention's gate), gated_delta, from final q, k, v, g, beta; beside it the
+    scalar-gate chain on the same q, k, v, beta (no front-end in either)."""
+    import numpy as np
+    wl = syn.WORKLOADS["prefill_varlen"]
+    Hqk, Hv, d = wl["H_qk"], wl["H_v"], wl["d_k"]
+    lengths = syn.seq_lengths(wl["index"], 0, wl["n_seq"], wl["min_len"], wl["max_len"])
+    cu = syn.cu_from_lengths(lengths).cuda()
+    N = int(lengths.sum())
+    q, k, v, g, beta = syn.token_inputs(wl["index"], 0, N, Hqk, Hv, d, d, on_device=True)
+    gcw = syn.channel_gates(wl["index"], 0, N, Hv, d, on_device=True)
+    pool = torch.zeros((wl["n_slots"], Hv, d, d), dtype=torch.bfloat16, device="cuda")
+    rs = torch.full((len(lengths),), -1, dtype=torch.int32, device="cuda")
+    ws = torch.from_numpy(np.random.default_rng(3).permutation(wl["n_slots"])[:len(lengths)]
+                          .astype(np.int32)).cuda()
+    lib = gdn.load_library()
+    s = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    a_cw, _, keep_cw = gdn.make_prefill_args(cu, q, k, v, pool, rs, ws, H_qk=Hqk, H_v=Hv, g=gcw,
+                                             beta=beta, scale=d ** -0.5)
+    a_sc, _, keep_sc = gdn.make_prefill_args(cu, q, k, v, pool, rs, ws, H_qk=Hqk, H_v=Hv, g=g,
+                                             beta=beta, scale=d ** -0.5)
+    assert a_cw.decay_mode == gdn.DECAY_CHANNEL and a_sc.decay_mode == gdn.DECAY_HEAD
+
+    def call(a):
+        code = lib.gdn_prefill(ctypes.byref(a), s())
+        if code:
+            raise gdn.GdnError("gdn_prefill", code)
+
+    def timed(a, reps):
+        for _ in range(args.prefill_warmup):  # untimed: the first calls run slower
+            call(a)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            call(a)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ms = timed(a_cw, args.prefill_reps)
+    ms_sc = timed(a_sc, args.prefill_reps)
+    flops = prefill_useful_flops(lengths, Hv, d, d)
+    algo_bytes = (N * ((2 * Hqk * d + Hv * d) * 2 + Hv * d * 2 + Hv * d * 4 + Hv * 4)
+                  + len(lengths) * Hv * d * d * 2)
+    return dict(workload="prefill_varlen, channel-wise decay", tokens=N, rule="gated_delta",
+                kernel="prefill_cw_kernel<bf16 state, bf16 act, 128, 128>",
+                ms=round(ms, 3), tokens_per_s=round(N / (ms / 1e3), 1),
+                scalar_gate_ms=round(ms_sc, 3), vs_scalar_gate=round(ms_sc / ms, 3),
+                useful_tflops=round(flops / (ms / 1e3) / 1e12, 2),
+                mfma_frac=round(flops / (ms / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                algorithmic_GBps=round(algo_bytes / (ms / 1e3) / 1e9, 1),
+                hbm_frac=round(algo_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4))
+
+
 def run_mixed(args, torch, gdn, syn):
     """448 decode requests plus 4 prefills of 8192 tokens (fused front-end) on
     one 1024-slot BF16 pool, 25% of requests reading a checkpoint slot, decode
@@ -700,6 +758,11 @@ def main():
         torch.cuda.empty_cache()
         prefill = run_prefill(args, torch, gdn, syn)
         log(f"prefill: {prefill}")
+    prefill_cw = None
+    if not args.no_prefill:
+        torch.cuda.empty_cache()
+        prefill_cw = run_prefill_cw(args, torch, gdn, syn)
+        log(f"prefill, channel-wise decay: {prefill_cw}")
     mixed = None
     if not args.no_prefill:
         torch.cuda.empty_cache()
@@ -733,6 +796,7 @@ def main():
         "decode_channel_decay": decode_cw,
         "decode_q8_state": decode_q8,
         "prefill": prefill,
+        "prefill_channel_decay": prefill_cw,
         "mixed": mixed,
     }
     print(json.dumps(out), flush=True)

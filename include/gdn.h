@@ -140,8 +140,8 @@ typedef struct gdn_decode_args {
   int32_t act_dtype;   /* gdn_dtype of q, k, v and o */
   int64_t n_slots;     /* pool capacity in slots */
   float scale;         /* read-out scale (1.0 for none) */
-  int32_t decay_mode;  /* gdn_decay_mode: the shape of g (gdn_decode only; gdn_mixed takes
-                          GDN_DECAY_HEAD) */
+  int32_t decay_mode;  /* gdn_decay_mode: the shape of g (gdn_mixed: the prefill half's
+                          decay_mode when both halves are present) */
   const void *q;       /* [B, H_qk, d_k] act_dtype; normalised by the caller */
   const void *k;       /* [B, H_qk, d_k] act_dtype */
   const void *v;       /* [B, H_v, d_v] act_dtype */
@@ -347,7 +347,9 @@ size_t gdn_noalloc_workspace_bytes(void);
  * own rule and slot arrays; they may share a pool).  The halves' results are
  * those of gdn_decode and gdn_prefill called separately; either half may be
  * empty (B = 0 or n_seq = 0).  The caller contract on slots applies across
- * both halves. */
+ * both halves.  Both halves describe one layer: the same heads, d_k, d_v,
+ * state and activation dtypes and decay_mode, else GDN_ERR_UNSUPPORTED; the
+ * 8-bit state format (GDN_Q8) is not taken (GDN_ERR_UNSUPPORTED). */
 gdn_status gdn_mixed(const gdn_decode_args *decode, const gdn_prefill_args *prefill,
                      void *stream);
 

@@ -266,9 +266,8 @@ gdn_status gdn_mixed(const gdn_decode_args *decode, const gdn_prefill_args *pref
                      void *stream) {
   gdn_status st = check_decode(decode);
   if (st != GDN_OK) return st;
-  // one decode instance: the per-head decay on a BF16 or FP32 state
-  if (decode->decay_mode != GDN_DECAY_HEAD || decode->state_dtype == GDN_Q8)
-    return GDN_ERR_UNSUPPORTED;
+  // decode tiles on a BF16 or FP32 state (not the 8-bit format)
+  if (decode->state_dtype == GDN_Q8) return GDN_ERR_UNSUPPORTED;
   st = check_prefill(prefill, true);
   if (st != GDN_OK) return st;
   if (decode->B == 0 && prefill->n_seq == 0) return GDN_OK;

@@ -18,31 +18,36 @@
 // of one another's barriers.
 //
 // Both halves must describe the same layer shape (heads, d_k, d_v, state and
-// activation dtypes).  With raw prefill inputs the front-end kernel runs
-// first, then the single mixed launch.
+// activation dtypes) and the same decay (one per head, or one per key
+// channel: then the chains are gdn_prefill's channel-wise chain and the
+// decode tiles its channel-wise decode).  With raw prefill inputs the
+// front-end kernel runs first, then the single mixed launch.
 #include <algorithm>
 
 #include "decode.cuh"
 #include "order.cuh"
+#include "prefill_cw.cuh"
 #include "prefill_pipe.cuh"
 
 namespace gdn {
 
 DecodeParams make_decode_params(const gdn_decode_args &a);
 
-template <bool SB, bool AB, int DK, int DV, bool F32>
+template <bool SB, bool AB, int DK, int DV, bool F32, bool CW>
 struct MixedLayout {
   // the chain's waves, except with FP32 state: a worker's two FP32 tiles in
-  // flight need more registers than a wave of a 512-thread block gets
-  static constexpr int NW = SB ? kPrefillWaves<DK, DV, F32> : 4;
+  // flight need more registers than a wave of a 512-thread block gets (the
+  // channel-wise chain has four waves)
+  static constexpr int NW = CW ? 4 : SB ? kPrefillWaves<DK, DV, F32> : 4;
   static constexpr int NT = 64 * NW;                          // threads per block
   static constexpr int DT = 256;                              // threads per decode worker
   static constexpr int NH = NT / DT;                          // decode workers per block
   static_assert(NT % DT == 0, "whole decode workers per block");
   // with the chain's own wave count the block runs gdn_prefill's chain
-  static constexpr bool OWN_CHAIN = NW == kPrefillWaves<DK, DV, F32>;
+  static constexpr bool OWN_CHAIN = !CW && NW == kPrefillWaves<DK, DV, F32>;
   static constexpr size_t PREFILL =
-      OWN_CHAIN ? kChainLds<DK, DV, F32, AB> : PrefillLayout<DK, DV, F32, AB>::BYTES;
+      CW ? kCwChainLds<DK, DV, F32, AB>
+         : OWN_CHAIN ? kChainLds<DK, DV, F32, AB> : PrefillLayout<DK, DV, F32, AB>::BYTES;
   // one worker's reduction area, rounded to 16 bytes so every worker's is aligned alike
   static constexpr size_t RED = (sizeof(float) * DecodeShape<SB, DK, DV, DT>::LDS_FLOATS + 15) / 16 * 16;
   static constexpr size_t ORDER = slot_order_lds_bytes(kOrderMaxB, kOrderMaxSlots, NT);
@@ -50,16 +55,17 @@ struct MixedLayout {
   static constexpr size_t BYTES = PREFILL > DECODE ? PREFILL : DECODE;
 };
 
-template <bool SB, bool AB, int DK, int DV, bool F32, bool CK>
-__global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32>::NT)) void mixed_kernel(
+template <bool SB, bool AB, int DK, int DV, bool F32, bool CW, bool CK>
+__global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32, CW>::NT)) void mixed_kernel(
     DecodeParams dp, PrefillParams pp, int n_chains, int prefill_blocks, int ordered) {
-  using L = MixedLayout<SB, AB, DK, DV, F32>;
+  using L = MixedLayout<SB, AB, DK, DV, F32, CW>;
   constexpr int NT = L::NT, DT = L::DT;
   __shared__ __align__(16) char smem[L::BYTES];
   if ((int)blockIdx.x < prefill_blocks) {
     const int chain = chain_of_block(blockIdx.x);
     if (chain < n_chains) {
-      if constexpr (L::OWN_CHAIN) run_chain<SB, AB, DK, DV, F32, CK>(pp, chain, smem);
+      if constexpr (CW) prefill_chain_cw<SB, AB, DK, DV, F32, CK>(pp, chain, smem);
+      else if constexpr (L::OWN_CHAIN) run_chain<SB, AB, DK, DV, F32, CK>(pp, chain, smem);
       else prefill_chain<SB, AB, DK, DV, F32, L::NW, CK>(pp, chain, smem);
     }
     return;
@@ -74,11 +80,11 @@ __global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32>::NT)) void mixed_
   const int64_t workers = ((int64_t)gridDim.x - prefill_blocks) * L::NH;
   int64_t t = ((int64_t)blockIdx.x - prefill_blocks) * L::NH + part;
   if (t >= n_tiles) return;
-  using Regs = DecodeTileRegs<SB, AB, DK, DV, DT>;
+  using Regs = DecodeTileRegs<SB, AB, DK, DV, DT, CW>;
   auto load = [&](int64_t tile, Regs &dst) {
     const int pos = (int)(tile / dp.H_v);
-    decode_tile_load<SB, AB, DK, DV, DT>(dp, ordered ? order[pos] : pos, (int)(tile % dp.H_v), dst,
-                                         tid);
+    decode_tile_load<SB, AB, DK, DV, DT, CW>(dp, ordered ? order[pos] : pos,
+                                             (int)(tile % dp.H_v), dst, tid);
   };
   Regs cur, nxt;
   load(t, cur);
@@ -86,17 +92,17 @@ __global__ __launch_bounds__((MixedLayout<SB, AB, DK, DV, F32>::NT)) void mixed_
     const int64_t tn = t + workers;
     const bool more = tn < n_tiles;
     if (more) load(tn, nxt);
-    decode_tile_finish<SB, AB, DK, DV, DT>(dp, cur, red, tid);
+    decode_tile_finish<SB, AB, DK, DV, DT, CW>(dp, cur, red, tid);
     if (!more) break;
     cur = nxt;
     t = tn;
   }
 }
 
-template <bool SB, bool AB, int DK, int DV>
+template <bool SB, bool AB, int DK, int DV, bool CW>
 static gdn_status launch_mixed_t(const DecodeParams &dp, const PrefillParams &pp, hipStream_t s) {
   constexpr bool F32 = !AB || !SB;  // the prefill chain's arithmetic, as in gdn_prefill
-  using L = MixedLayout<SB, AB, DK, DV, F32>;
+  using L = MixedLayout<SB, AB, DK, DV, F32, CW>;
   if constexpr (L::BYTES > 160 * 1024) {
     return GDN_ERR_UNSUPPORTED;
   } else {
@@ -116,36 +122,44 @@ static gdn_status launch_mixed_t(const DecodeParams &dp, const PrefillParams &pp
     if (grid == 0) return GDN_OK;
     // the instance with intermediate checkpoints only when they are asked for
     if (pp.ckpt_chunks > 0)
-      hipLaunchKernelGGL((mixed_kernel<SB, AB, DK, DV, F32, true>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((mixed_kernel<SB, AB, DK, DV, F32, CW, true>), dim3((unsigned)grid),
                          dim3(L::NT), 0, s, dp, pp, n_chains,
                          n_chains > 0 ? prefill_blocks : 0, ordered);
     else
-      hipLaunchKernelGGL((mixed_kernel<SB, AB, DK, DV, F32, false>), dim3((unsigned)grid),
+      hipLaunchKernelGGL((mixed_kernel<SB, AB, DK, DV, F32, CW, false>), dim3((unsigned)grid),
                          dim3(L::NT), 0, s, dp, pp, n_chains,
                          n_chains > 0 ? prefill_blocks : 0, ordered);
     return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
   }
 }
 
+template <bool SB, bool AB, int DK, int DV>
+static gdn_status mixed_cw(const DecodeParams &dp, const PrefillParams &pp, bool cw,
+                           hipStream_t s) {
+  return cw ? launch_mixed_t<SB, AB, DK, DV, true>(dp, pp, s)
+            : launch_mixed_t<SB, AB, DK, DV, false>(dp, pp, s);
+}
+
 template <bool SB, bool AB, int DK>
-static gdn_status mixed_dv(const DecodeParams &dp, const PrefillParams &pp, int dv, hipStream_t s) {
+static gdn_status mixed_dv(const DecodeParams &dp, const PrefillParams &pp, int dv, bool cw,
+                           hipStream_t s) {
   switch (dv) {
-    case 16: return launch_mixed_t<SB, AB, DK, 16>(dp, pp, s);
-    case 32: return launch_mixed_t<SB, AB, DK, 32>(dp, pp, s);
-    case 64: return launch_mixed_t<SB, AB, DK, 64>(dp, pp, s);
-    case 128: return launch_mixed_t<SB, AB, DK, 128>(dp, pp, s);
+    case 16: return mixed_cw<SB, AB, DK, 16>(dp, pp, cw, s);
+    case 32: return mixed_cw<SB, AB, DK, 32>(dp, pp, cw, s);
+    case 64: return mixed_cw<SB, AB, DK, 64>(dp, pp, cw, s);
+    case 128: return mixed_cw<SB, AB, DK, 128>(dp, pp, cw, s);
   }
   return GDN_ERR_UNSUPPORTED;
 }
 
 template <bool SB, bool AB>
 static gdn_status mixed_dk(const DecodeParams &dp, const PrefillParams &pp, int dk, int dv,
-                           hipStream_t s) {
+                           bool cw, hipStream_t s) {
   switch (dk) {
-    case 16: return mixed_dv<SB, AB, 16>(dp, pp, dv, s);
-    case 32: return mixed_dv<SB, AB, 32>(dp, pp, dv, s);
-    case 64: return mixed_dv<SB, AB, 64>(dp, pp, dv, s);
-    case 128: return mixed_dv<SB, AB, 128>(dp, pp, dv, s);
+    case 16: return mixed_dv<SB, AB, 16>(dp, pp, dv, cw, s);
+    case 32: return mixed_dv<SB, AB, 32>(dp, pp, dv, cw, s);
+    case 64: return mixed_dv<SB, AB, 64>(dp, pp, dv, cw, s);
+    case 128: return mixed_dv<SB, AB, 128>(dp, pp, dv, cw, s);
   }
   return GDN_ERR_UNSUPPORTED;
 }
@@ -153,13 +167,15 @@ static gdn_status mixed_dk(const DecodeParams &dp, const PrefillParams &pp, int 
 gdn_status launch_mixed(const gdn_decode_args &d, const gdn_prefill_args &p, hipStream_t stream) {
   if (d.B > 0 && p.n_seq > 0 &&
       (d.H_qk != p.H_qk || d.H_v != p.H_v || d.d_k != p.d_k || d.d_v != p.d_v ||
-       d.state_dtype != p.state_dtype || d.act_dtype != p.act_dtype))
+       d.state_dtype != p.state_dtype || d.act_dtype != p.act_dtype ||
+       d.decay_mode != p.decay_mode))
     return GDN_ERR_UNSUPPORTED;
   // shapes come from whichever half is present
   const gdn_prefill_args &shape = p;
   const int dk = d.B > 0 ? d.d_k : shape.d_k, dv = d.B > 0 ? d.d_v : shape.d_v;
   const int sdt = d.B > 0 ? d.state_dtype : shape.state_dtype;
   const int adt = d.B > 0 ? d.act_dtype : shape.act_dtype;
+  const bool cw = (d.B > 0 ? d.decay_mode : shape.decay_mode) == GDN_DECAY_CHANNEL;
   PrefillParams pp = {};
   if (p.n_seq > 0) {
     const gdn_status st = prepare_prefill(p, stream, &pp);
@@ -167,10 +183,10 @@ gdn_status launch_mixed(const gdn_decode_args &d, const gdn_prefill_args &p, hip
   }
   const DecodeParams dp = d.B > 0 ? make_decode_params(d) : DecodeParams{};
   const bool sb = sdt == GDN_BF16, ab = adt == GDN_BF16;
-  if (sb && ab) return mixed_dk<true, true>(dp, pp, dk, dv, stream);
-  if (sb && !ab) return mixed_dk<true, false>(dp, pp, dk, dv, stream);
-  if (!sb && ab) return mixed_dk<false, true>(dp, pp, dk, dv, stream);
-  return mixed_dk<false, false>(dp, pp, dk, dv, stream);
+  if (sb && ab) return mixed_dk<true, true>(dp, pp, dk, dv, cw, stream);
+  if (sb && !ab) return mixed_dk<true, false>(dp, pp, dk, dv, cw, stream);
+  if (!sb && ab) return mixed_dk<false, true>(dp, pp, dk, dv, cw, stream);
+  return mixed_dk<false, false>(dp, pp, dk, dv, cw, stream);
 }
 
 }  // namespace gdn

@@ -14,13 +14,18 @@
 //   R = beta (V - K_g M)  (delta rules; V otherwise),  U = (I + A)^-1 R
 //   O = scale (Q_g M + P U),   M <- Diag(e^(G_last)) M + K_e^T U
 //
-// A and P are formed per 16 x 16 tile.  Below the diagonal, tile (I, J)
-// factors each weight through the last token m of column tile J:
-// e^(G_r - G_s) = e^(G_r - G_m) e^(G_m - G_s), both factors <= 1 for
-// r > m >= s, so the tile is one MFMA product of on-the-fly scaled K / Q
-// fragments that neither overflows nor loses an O(1) weight.  A diagonal
-// tile has no such reference (any single one overflows for strong gates), so
-// its weights are taken entry by entry on the vector ALUs.  Everything else
+// A and P are formed per 16 x 16 tile, each one MFMA product of K / Q
+// fragments scaled on the fly through a reference token m:
+// e^(G_r - G_s) = e^(G_r - G_m) e^(G_m - G_s).  Below the diagonal, tile
+// (I, J) takes m = the last token of column tile J: both factors are <= 1
+// for r > m >= s, so nothing overflows and no O(1) weight is lost.  A
+// diagonal tile takes m = its first token: the row factors are <= 1 and the
+// column factors at most 2^span, span being the tile's largest cumulative
+// log2-decay over a channel; while span <= kCwDiagSpan the products stay far
+// inside FP32 / BF16 range (the entries above the diagonal, at most 2^span,
+// are discarded).  A diagonal tile with a larger span (a channel that
+// forgets nearly everything within 16 tokens) takes its weights entry by
+// entry on the vector ALUs instead, each e^(G_r - G_s) <= 1.  Everything else
 // -- the block substitution for U, the read-out, the state update, state in
 // and out, checkpoints -- is the 4-wave plain chain's (prefill_chain.cuh),
 // with the chunk's inputs in one LDS set (the per-channel decays take the
@@ -142,10 +147,16 @@ __device__ __forceinline__ void put_row16(T *p, const float *x) {
   put_row8(p + 8, x + 8);
 }
 
-// The chunk-local tiles below the diagonal that wave w forms: (I, J) pairs,
-// two for waves 0 and 1, one for waves 2 and 3.
-constexpr int kCwTiles[4][2][2] = {{{1, 0}, {2, 1}}, {{2, 0}, {3, 2}}, {{3, 0}, {0, 0}}, {{3, 1}, {0, 0}}};
-constexpr int kCwTileCount[4] = {2, 2, 1, 1};
+// The chunk-local tiles that wave w forms: (I, J) pairs, its diagonal tile
+// (w, w) first, then two (waves 0, 1) or one (waves 2, 3) below the diagonal.
+constexpr int kCwTiles[4][3][2] = {{{0, 0}, {1, 0}, {2, 1}},
+                                   {{1, 1}, {2, 0}, {3, 2}},
+                                   {{2, 2}, {3, 0}, {0, 0}},
+                                   {{3, 3}, {3, 1}, {0, 0}}};
+constexpr int kCwTileCount[4] = {3, 3, 2, 2};
+// Largest decay span (log2 units) of a diagonal tile formed by MFMA: column
+// factors up to 2^100, products of unit-norm rows far below FP32's 2^128.
+constexpr float kCwDiagSpan = 100.f;
 
 template <bool SB, bool AB, int DK, int DV, bool F32, bool CK = false>
 __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int chain, char *smem) {
@@ -375,12 +386,22 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
     // the last token on the last chunk: no branch around the loads)
     fetch(t1);
 
-    // 2: chunk-local products below the diagonal, one MFMA product per tile
-    // from fragments scaled through the column tile's last token m
+    // 2: chunk-local products, one MFMA product per tile from fragments
+    // scaled through the tile's reference token m; the wave's diagonal tile
+    // only while its decay span allows (a wave-uniform decision)
+    float span = 0.f;
+    for (int c = lane; c < DK; c += 64)
+      span = fmaxf(span, Gc[(16 * wave) * LDG + c] - Gc[(16 * wave + 15) * LDG + c]);
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti) {
+    for (int off = 32; off >= 1; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
+    const bool diag_mfma = span <= kCwDiagSpan;
+#pragma unroll
+    for (int ti = 0; ti < 3; ++ti) {
       if (ti >= kCwTileCount[wave]) break;
-      const int I = kCwTiles[wave][ti][0], J = kCwTiles[wave][ti][1], m = 16 * J + 15;
+      const int I = kCwTiles[wave][ti][0], J = kCwTiles[wave][ti][1];
+      const bool dg = I == J;
+      if (dg && !diag_mfma) continue;
+      const int m = dg ? 16 * J : 16 * J + 15;
       const int rl = 16 * I + (lane & 15), rr = 16 * J + (lane & 15);
       f32x4_t sa, pa;
 #pragma unroll
@@ -392,8 +413,8 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
         load8f(Gc + m * LDG + ch, gm);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          fl[e] = fast_exp2(gl[e] - gm[e]);  // <= 1: r after m
-          fr[e] = fast_exp2(gm[e] - gr[e]);  // <= 1: s up to m
+          fl[e] = fast_exp2(gl[e] - gm[e]);  // <= 1: r at or after m
+          fr[e] = fast_exp2(gm[e] - gr[e]);  // <= 1 below the diagonal, <= 2^span on it
         }
         const Frag<F32> fkl = scaled_frag<F32>(Kh + rl * LDK + ch, fl);
         const Frag<F32> fql = scaled_frag<F32>(Qh + rl * LDK + ch, fl);
@@ -405,13 +426,22 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * I + rq + e, s = 16 * J + col;
-        put(Ab + r * L::LDAB + s, -(ef * br[e]) * sa[e]);
-        put(Sq + r * LDC + s, p.scale * pa[e]);
+        if (dg) {
+          // strictly lower entries of A, lower entries and the diagonal of P
+          const float a = s < r ? ef * br[e] * sa[e] : 0.f;
+          put(Ab + r * L::LDAB + s, -a);
+          put(Sq + r * LDC + s, s <= r ? p.scale * pa[e] : 0.f);
+          Ad[r * L::LDD + col] = a;
+        } else {
+          put(Ab + r * L::LDAB + s, -(ef * br[e]) * sa[e]);
+          put(Sq + r * LDC + s, p.scale * pa[e]);
+        }
       }
     }
-    // 3: diagonal tile b = wave, entry by entry: lane (r, cg) sums channels
-    // cg*8 + 32 j .. +8 of every column s; the four cg lanes of a row then add
-    {
+    // 3: a diagonal tile whose span is too wide for the scaled product,
+    // entry by entry: lane (r, cg) sums channels cg*8 + 32 j .. +8 of every
+    // column s; the four cg lanes of a row then add
+    if (!diag_mfma) {
       const int b = wave, r = lane & 15, cg = lane >> 4;
       float accA[16], accP[16];
 #pragma unroll

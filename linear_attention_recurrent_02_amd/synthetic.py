@@ -66,13 +66,32 @@ def _cast(a: np.ndarray, dtype: torch.dtype) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).to(dtype)
 
 
+def _device_gen(wl: int, layer: int, stream: int) -> torch.Generator:
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1_000_003 * (int(wl) + 1) + 7919 * int(layer) + 101 * int(stream) + 17)
+    return gen
+
+
 def token_inputs(wl: int, layer: int, n_tok: int, H_qk: int, H_v: int, d_k: int, d_v: int,
-                 act_dtype: torch.dtype = torch.bfloat16):
+                 act_dtype: torch.dtype = torch.bfloat16, on_device: bool = False):
     """Per-token q, k (unit norm), v, g, beta for ``n_tok`` tokens (CPU tensors).
 
     q, k: [n_tok, H_qk, d_k] act_dtype; v: [n_tok, H_v, d_v] act_dtype;
-    g, beta: [n_tok, H_v] float32.
+    g, beta: [n_tok, H_v] float32.  ``on_device`` draws the same
+    distributions on the current CUDA device in float32 with seeded torch
+    generators (for benchmark-sized batches; other values than the host draw).
     """
+    if on_device:
+        def normal(stream, shape):
+            return torch.randn(shape, generator=_device_gen(wl, layer, stream), device="cuda")
+        q = normal(_S_Q, (n_tok, H_qk, d_k))
+        k = normal(_S_K, (n_tok, H_qk, d_k))
+        q = q / q.norm(dim=-1, keepdim=True)
+        k = k / k.norm(dim=-1, keepdim=True)
+        v = normal(_S_V, (n_tok, H_v, d_v))
+        g = -torch.nn.functional.softplus(normal(_S_G, (n_tok, H_v)))
+        beta = torch.sigmoid(normal(_S_B, (n_tok, H_v)))
+        return q.to(act_dtype), k.to(act_dtype), v.to(act_dtype), g, beta
     q = _unit_rows(rng(wl, layer, _S_Q).standard_normal((n_tok, H_qk, d_k)))
     k = _unit_rows(rng(wl, layer, _S_K).standard_normal((n_tok, H_qk, d_k)))
     v = rng(wl, layer, _S_V).standard_normal((n_tok, H_v, d_v))
@@ -83,12 +102,17 @@ def token_inputs(wl: int, layer: int, n_tok: int, H_qk: int, H_v: int, d_k: int,
 
 
 def channel_gates(wl: int, layer: int, n_tok: int, H_v: int, d_k: int, lo: float = -5.0,
-                  hi: float = 1.0) -> torch.Tensor:
+                  hi: float = 1.0, on_device: bool = False) -> torch.Tensor:
     """Per-key-channel log-decays g [n_tok, H_v, d_k] float32 (Kimi Delta
     Attention's channel-wise gate): -softplus(x + b) with x ~ N(0, 1) per
     (token, head, channel) and a bias b ~ U(lo, hi) fixed per (head, channel),
     so the mean decay per token ranges from about e^-0.01 to e^-1.3 across
-    one head's channels."""
+    one head's channels.  ``on_device``: drawn on the current CUDA device."""
+    if on_device:
+        b = torch.rand((1, H_v, d_k), generator=_device_gen(wl, layer, _S_GCB),
+                       device="cuda") * (hi - lo) + lo
+        x = torch.randn((n_tok, H_v, d_k), generator=_device_gen(wl, layer, _S_GC), device="cuda")
+        return -torch.nn.functional.softplus(x + b)
     b = rng(wl, layer, _S_GCB).uniform(lo, hi, size=(1, H_v, d_k))
     x = rng(wl, layer, _S_GC).standard_normal((n_tok, H_v, d_k))
     return _cast(_neg_softplus(x + b), torch.float32)

@@ -236,6 +236,21 @@ def test_prefill_conv_width_ignored_without_frontend_and_empty_batch():
     assert lib.gdn_mixed(ctypes.byref(bad), ctypes.byref(a), None) == RULE
 
 
+def test_mixed_halves_must_share_the_decay_mode():
+    """One layer per launch: a per-head decode half with a channel-wise
+    prefill half (or the reverse) is refused before any launch."""
+    lib = gdn.load_library()
+    p = _prefill_args(use_frontend=0, decay_mode=1)
+    d = _decode_args(decay_mode=0)
+    assert lib.gdn_mixed(ctypes.byref(d), ctypes.byref(p), None) == UNSUP
+    p = _prefill_args(use_frontend=0, decay_mode=0)
+    d = _decode_args(decay_mode=1)
+    assert lib.gdn_mixed(ctypes.byref(d), ctypes.byref(p), None) == UNSUP
+    # the channel-wise prefill takes no fused front-end, in gdn_mixed as in gdn_prefill
+    p = _prefill_args(decay_mode=1)
+    assert lib.gdn_mixed(ctypes.byref(d), ctypes.byref(p), None) == UNSUP
+
+
 def test_validate_slots():
     v = gdn.gdn_validate_slots
     assert v([0, 1, 2], [3, 4, 5], 3, 8) == OK

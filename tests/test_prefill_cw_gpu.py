@@ -294,3 +294,25 @@ def test_cw_prefill_varlen_full_size():
     assert seq_err(f64(o), ro, cu) < 2e-2
     w = ws.numpy()
     assert scaled_err(f64(pool.cpu()[w]), rpool[w], 2) < 2e-2
+
+
+@pytest.mark.parametrize("d,sdt,bar", [(128, torch.bfloat16, 2e-2), (64, torch.float32, 1e-4)])
+@pytest.mark.parametrize("g_fast", [-4.5, -4.7])
+def test_cw_prefill_diagonal_span_at_the_limit(d, sdt, bar, g_fast):
+    """Diagonal tiles whose decay span sits just inside (g = -4.5 per token:
+    15 * 4.5 * log2(e) = 97.4 < 100, column factors up to 2^97 in the scaled
+    product) or just outside (g = -4.7: 101.7, the entry-by-entry form) the
+    limit of the scaled MFMA product, beside channels that do not decay."""
+    say("cw prefill diagonal span", d, g_fast)
+    lengths = [130, 64]
+    N = sum(lengths)
+    g = np.zeros((N, 2, d))
+    g[:, :, 0::3] = g_fast
+    g[:, :, 1::3] = -np.logaddexp(0.0, np.random.default_rng(311).standard_normal((N, 2, d))[:, :, 1::3])
+    case = cw_case(311, lengths, 1, 2, d, d, 6, sdt, sdt, std=0.3,
+                   gates=torch.from_numpy(g).float())
+    o, pool, ro, rpool = run_both(case, "gated_delta")
+    ws = case[8].numpy()
+    assert np.all(np.isfinite(f64(o)))
+    assert seq_err(f64(o), ro, case[0]) < bar
+    assert scaled_err(f64(pool)[ws], rpool[ws], 2) < bar
