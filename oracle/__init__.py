@@ -58,7 +58,7 @@ def _load():
                                          P, P, P, P, P, P, P, P, P, i32]
         lib.oracle_frontend.restype = i32
         lib.oracle_frontend.argtypes = [i32, P, i32, i32, i32, i32, i32, f64,
-                                        P, P, P, P, P, P, P, P, P, P, P, P, P]
+                                        P, P, P, P, P, P, P, P, P, P, P, P, P, P]
         lib.oracle_decode_cw.restype = i32
         lib.oracle_decode_cw.argtypes = [i32, i32, i32, i32, i32, i64, i32, f64, i32,
                                          P, P, P, P, P, P, P, P, P, i32]
@@ -206,11 +206,14 @@ def sequences_cw(cu_seqlens, q, k, v, g, beta, pool, read_slot=None, write_slot=
     return o, pool, code
 
 
-def frontend(cu_seqlens, q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw, *, Hqk, Hv, eps=1e-6):
+def frontend(cu_seqlens, q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw, *, Hqk, Hv, eps=1e-6,
+             conv_init=None):
     """Causal depthwise conv + SiLU, L2 norm of q/k per head, gates.
 
     q_raw, k_raw: [N, Hqk*dk]; v_raw: [N, Hv*dv]; w*: [channels, K];
-    a_raw, b_raw: [N, Hv].  Returns (q, k, v, g, beta) with q, k as
+    a_raw, b_raw: [N, Hv]; conv_init: None (empty windows) or
+    [n_seq, K-1, 2*Hqk*dk + Hv*dv], the raw inputs of the K-1 tokens before
+    each sequence (oldest first).  Returns (q, k, v, g, beta) with q, k as
     [N, Hqk, dk], v as [N, Hv, dv], g and beta as [N, Hv].
     """
     q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw = map(
@@ -220,12 +223,19 @@ def frontend(cu_seqlens, q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw, *, Hqk, 
     dk = q_raw.shape[1] // Hqk
     dv = v_raw.shape[1] // Hv
     K = wq.shape[1]
+    C = 2 * Hqk * dk + Hv * dv
+    init = None
+    if conv_init is not None:
+        init = _f64(conv_init)
+        if init.shape != (cu.shape[0] - 1, K - 1, C):
+            raise ValueError("conv_init must be [n_seq, K-1, 2*Hqk*dk + Hv*dv]")
     qo, ko, vo = np.zeros_like(q_raw), np.zeros_like(k_raw), np.zeros_like(v_raw)
     g = np.zeros((N, Hv), np.float64)
     beta = np.zeros((N, Hv), np.float64)
     code = _load().oracle_frontend(cu.shape[0] - 1, _p(cu), Hqk, Hv, dk, dv, K, float(eps),
                                    _p(q_raw), _p(k_raw), _p(v_raw), _p(wq), _p(wk), _p(wv),
-                                   _p(a_raw), _p(b_raw), _p(qo), _p(ko), _p(vo), _p(g), _p(beta))
+                                   _p(a_raw), _p(b_raw), _p(init), _p(qo), _p(ko), _p(vo), _p(g),
+                                   _p(beta))
     if code != 0:
         raise ValueError("oracle_frontend rejected its arguments")
     return qo.reshape(N, Hqk, dk), ko.reshape(N, Hqk, dk), vo.reshape(N, Hv, dv), g, beta
@@ -264,23 +274,28 @@ def conv_decode(q_raw, k_raw, v_raw, wq, wk, wv, a_raw, b_raw, conv_pool, read_s
             pool, code)
 
 
-def conv_tail(cu_seqlens, q_raw, k_raw, v_raw, K=4):
+def conv_tail(cu_seqlens, q_raw, k_raw, v_raw, K=4, conv_init=None):
     """The conv window each sequence leaves behind: its last K-1 raw inputs.
 
     Returns [n_seq, K-1, 2*Hqk*dk + Hv*dv] (q|k|v channels, oldest token
-    first), zero where a sequence has fewer than K-1 tokens: the history a
-    decode step of that sequence continues from.
+    first): the history a decode step or a resumed prefill of that sequence
+    continues from.  Where a sequence has fewer than K-1 tokens the older
+    rows are those of the window it started from (conv_init, as for
+    ``frontend``), or zero without one.
     """
     q_raw, k_raw, v_raw = map(_f64, (q_raw, k_raw, v_raw))
     cu = _i32(cu_seqlens)
     rows = np.concatenate([q_raw, k_raw, v_raw], axis=1)
     out = np.zeros((cu.shape[0] - 1, K - 1, rows.shape[1]), np.float64)
+    init = None if conv_init is None else _f64(conv_init)
     for s in range(cu.shape[0] - 1):
         t0, t1 = int(cu[s]), int(cu[s + 1])
         for j in range(K - 1):
             t = t1 - (K - 1) + j
             if t >= t0:
                 out[s, j] = rows[t]
+            elif init is not None:
+                out[s, j] = init[s, t - t0 + K - 1]
     return out
 
 

@@ -47,8 +47,9 @@
  *  - BF16 state storage: wherever the state is stored, it is rounded from
  *    FP64 to the nearest BF16 value, ties to even (round_state != 0).
  *  - Front-end: per-channel causal conv of width conv_k (tap j multiplies
- *    x[t-(conv_k-1)+j], zero before the sequence's first token, never across
- *    a sequence boundary), then SiLU; q and k are then L2-normalised per
+ *    x[t-(conv_k-1)+j], never across a sequence boundary; before the
+ *    sequence's first token x is the stored window the sequence resumes, the
+ *    raw inputs of the conv_k-1 tokens before it, else zero), then SiLU; q and k are then L2-normalised per
  *    (token, head) as y / sqrt(sum y^2 + eps); g = -softplus(a_raw) and
  *    beta = sigmoid(b_raw).
  *  - Channel-wise decay (Kimi Delta Attention, "Seven Architectures ...",
@@ -87,7 +88,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-#define ORACLE_VERSION 5
+#define ORACLE_VERSION 6
 
 int oracle_version(void) { return ORACLE_VERSION; }
 
@@ -332,14 +333,20 @@ int oracle_sequences(int n_seq, const int32_t *cu, int Hqk, int Hv, int dk, int 
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
 
-/* causal conv + SiLU of one channel column over one sequence */
+/* causal conv + SiLU of one channel column over one sequence.  Inputs
+ * before the sequence's first token come from `init` (the K-1 raw tokens
+ * that precede it, oldest first, row length C, this channel at column cw of
+ * a row), or are 0 when init is NULL: the conv window a resumed sequence
+ * continues from. */
 static void conv_silu(const double *x, int64_t ld, int64_t c, int64_t t0, int64_t t1,
-                      const double *w, int K, double *y) {
+                      const double *w, int K, const double *init, int64_t C, int64_t cw,
+                      double *y) {
   for (int64_t t = t0; t < t1; ++t) {
     double s = 0.0;
     for (int j = 0; j < K; ++j) {
       int64_t src = t - (K - 1) + j;
       if (src >= t0) s += w[j] * x[src * ld + c];
+      else if (init) s += w[j] * init[(src - t0 + K - 1) * C + cw];
     }
     y[t * ld + c] = s * sigmoid(s);
   }
@@ -348,23 +355,29 @@ static void conv_silu(const double *x, int64_t ld, int64_t c, int64_t t0, int64_
 /* Front-end of one layer for n_seq sequences (conv fused with the layer per
  * the Gated DeltaNet glossary, Engineering details).  q_raw, k_raw:
  * [N, Hqk*dk]; v_raw: [N, Hv*dv]; wq, wk: [Hqk*dk, K]; wv: [Hv*dv, K];
- * a_raw, b_raw: [N, Hv].  Outputs have the input shapes; g_out, beta_out:
- * [N, Hv]. */
+ * a_raw, b_raw: [N, Hv].  init: NULL (every sequence starts from an empty
+ * window) or [n_seq, K-1, C] with C = 2*Hqk*dk + Hv*dv, the raw q|k|v
+ * inputs of the K-1 tokens before each sequence (oldest first): a sequence
+ * resumed from a stored window, as a checkpoint is resumed (Recurrent state
+ * glossary, Why it matters).  Outputs have the input shapes; g_out,
+ * beta_out: [N, Hv]. */
 int oracle_frontend(int n_seq, const int32_t *cu, int Hqk, int Hv, int dk, int dv, int K,
                     double eps, const double *q_raw, const double *k_raw, const double *v_raw,
                     const double *wq, const double *wk, const double *wv, const double *a_raw,
-                    const double *b_raw, double *q_out, double *k_out, double *v_out,
-                    double *g_out, double *beta_out) {
+                    const double *b_raw, const double *init, double *q_out, double *k_out,
+                    double *v_out, double *g_out, double *beta_out) {
   if (n_seq < 0 || Hqk <= 0 || Hv <= 0 || dk <= 0 || dv <= 0 || K <= 0) return -1;
-  int64_t cq = (int64_t)Hqk * dk, cv = (int64_t)Hv * dv;
+  int64_t cq = (int64_t)Hqk * dk, cv = (int64_t)Hv * dv, C = 2 * cq + cv;
   for (int s = 0; s < n_seq; ++s) {
     int64_t t0 = cu[s], t1 = cu[s + 1];
     if (t1 < t0) return -1;
+    const double *win = init ? init + (int64_t)s * (K - 1) * C : NULL;
     for (int64_t c = 0; c < cq; ++c) {
-      conv_silu(q_raw, cq, c, t0, t1, wq + c * K, K, q_out);
-      conv_silu(k_raw, cq, c, t0, t1, wk + c * K, K, k_out);
+      conv_silu(q_raw, cq, c, t0, t1, wq + c * K, K, win, C, c, q_out);
+      conv_silu(k_raw, cq, c, t0, t1, wk + c * K, K, win, C, cq + c, k_out);
     }
-    for (int64_t c = 0; c < cv; ++c) conv_silu(v_raw, cv, c, t0, t1, wv + c * K, K, v_out);
+    for (int64_t c = 0; c < cv; ++c)
+      conv_silu(v_raw, cv, c, t0, t1, wv + c * K, K, win, C, 2 * cq + c, v_out);
     for (int64_t t = t0; t < t1; ++t) {
       for (int h = 0; h < Hqk; ++h) {
         double *yq = q_out + t * cq + (int64_t)h * dk, *yk = k_out + t * cq + (int64_t)h * dk;

@@ -130,3 +130,99 @@ def test_batch_routes_slots_and_skips_bad_requests():
     assert not bad[0][2].any() and not bad[2][2].any()
     np.testing.assert_array_equal(bad[0][0], out[0][0])
     np.testing.assert_array_equal(bad[5][3], out[5][3])
+
+
+def frontend_of(x, cu, Hqk, Hv, init=None):
+    return oracle.frontend(cu, x["q_raw"], x["k_raw"], x["v_raw"], x["wq"], x["wk"], x["wv"],
+                           x["a_raw"], x["b_raw"], Hqk=Hqk, Hv=Hv, conv_init=init)
+
+
+def part(x, a, b):
+    return {n: (x[n][a:b] if n not in ("wq", "wk", "wv") else x[n]) for n in x}
+
+
+def test_resumed_frontend_equals_the_whole_sequence():
+    """A sequence cut into three parts, each resumed from the window the
+    previous one left (the middle part shorter than K-1 tokens, so its window
+    keeps rows of the first part's), gives the whole sequence's front-end
+    bit for bit."""
+    Hqk, Hv, dk, dv = 2, 2, 3, 2
+    T, T1, T2 = 11, 5, 7
+    x = raw(9, T, Hqk, Hv, dk, dv)
+    whole = frontend_of(x, np.array([0, T], np.int32), Hqk, Hv)
+    init = None
+    outs = []
+    for a, b in ((0, T1), (T1, T2), (T2, T)):
+        xp = part(x, a, b)
+        cu = np.array([0, b - a], np.int32)
+        outs.append(frontend_of(xp, cu, Hqk, Hv, init))
+        init = oracle.conv_tail(cu, xp["q_raw"], xp["k_raw"], xp["v_raw"], K, conv_init=init)
+    for i in range(5):
+        np.testing.assert_array_equal(np.concatenate([o[i] for o in outs]), whole[i])
+    # the last window is the whole sequence's tail
+    np.testing.assert_array_equal(init, oracle.conv_tail(np.array([0, T], np.int32), x["q_raw"],
+                                                         x["k_raw"], x["v_raw"], K))
+
+
+def test_resumed_frontend_equals_decode_steps():
+    """T tokens from a stored window W through the front-end equal T
+    conv-decode steps starting from a slot holding W."""
+    Hqk, Hv, dk, dv = 1, 2, 4, 3
+    T = 6
+    x = raw(10, T, Hqk, Hv, dk, dv)
+    C = 2 * Hqk * dk + Hv * dv
+    W = np.random.default_rng(11).standard_normal((1, K - 1, C))
+    q, k, v, g, beta = frontend_of(x, np.array([0, T], np.int32), Hqk, Hv, W)
+    pool = W.copy()
+    for t in range(T):
+        qd, kd, vd, gd, bd, pool, code = step(x, [t], pool, [0], [0], Hqk, Hv)
+        assert code == 0
+        np.testing.assert_allclose(qd[0], q[t], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(kd[0], k[t], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(vd[0], v[t], rtol=1e-13, atol=1e-15)
+    np.testing.assert_array_equal(pool[0], oracle.conv_tail(np.array([0, T], np.int32),
+                                                            x["q_raw"], x["k_raw"], x["v_raw"],
+                                                            K, conv_init=W)[0])
+
+
+def test_oldest_tap_reads_the_stored_window():
+    """With only the oldest tap set, output t of a resumed sequence is SiLU of
+    the raw input three tokens back: window rows 0, 1, 2 for its first three
+    tokens, then its own inputs."""
+    Hqk, Hv, dk, dv = 1, 1, 2, 2
+    T = 5
+    x = raw(12, T, Hqk, Hv, dk, dv)
+    for n in ("wq", "wk", "wv"):
+        x[n] = np.zeros_like(x[n])
+        x[n][:, 0] = 1.0
+    C = 2 * Hqk * dk + Hv * dv
+    W = np.random.default_rng(13).standard_normal((1, K - 1, C))
+    _, _, v, _, _ = frontend_of(x, np.array([0, T], np.int32), Hqk, Hv, W)
+    silu = lambda s: s / (1.0 + np.exp(-s))
+    vch = slice(2 * Hqk * dk, C)
+    for t in range(T):
+        src = W[0, t, vch] if t < K - 1 else x["v_raw"][t - (K - 1)]
+        np.testing.assert_allclose(v[t].reshape(-1), silu(src), rtol=1e-15)
+
+
+def test_windows_stay_with_their_sequences():
+    """A batch of sequences (one empty, one shorter than the window) with
+    windows of their own equals each sequence run alone with its window; the
+    windows left behind keep the older rows of short sequences."""
+    Hqk, Hv, dk, dv = 1, 2, 2, 2
+    lengths = [4, 0, 2, 6]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    N = int(cu[-1])
+    x = raw(14, N, Hqk, Hv, dk, dv)
+    C = 2 * Hqk * dk + Hv * dv
+    W = np.random.default_rng(15).standard_normal((len(lengths), K - 1, C))
+    got = frontend_of(x, cu, Hqk, Hv, W)
+    tail = oracle.conv_tail(cu, x["q_raw"], x["k_raw"], x["v_raw"], K, conv_init=W)
+    for s, L in enumerate(lengths):
+        a, b = int(cu[s]), int(cu[s + 1])
+        xs = part(x, a, b)
+        one = frontend_of(xs, np.array([0, L], np.int32), Hqk, Hv, W[s:s + 1])
+        for i in range(5):
+            np.testing.assert_array_equal(got[i][a:b], one[i])
+        rows = np.concatenate([W[s], np.concatenate([xs["q_raw"], xs["k_raw"], xs["v_raw"]], 1)])
+        np.testing.assert_array_equal(tail[s], rows[-(K - 1):])
