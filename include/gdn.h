@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 7
+#define GDN_ABI_VERSION 8
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -217,6 +217,33 @@ typedef struct gdn_prefill_args {
                           log-decay per key channel (Kimi Delta Attention), with use_frontend = 0
                           (q, k, v, g, beta given); FP32 state or activations then need
                           d_k <= 64 */
+  /* The front-end's conv window across calls (use_frontend = 1; with
+   * use_frontend = 0 the three slot arrays must be NULL).  conv_pool is the
+   * conv-state pool of gdn_conv_args: [conv_n_slots, conv_k - 1, C]
+   * act_dtype, C = 2 * H_qk * d_k + H_v * d_v raw channels in q|k|v order,
+   * oldest token first.  A sequence that resumes a stored state resumes its
+   * conv window too (the conv is part of the layer, "Gated DeltaNet"
+   * glossary entry, Engineering details; checkpoints are resumed, "Recurrent
+   * state" glossary entry, Why it matters):
+   *  - conv_read_slot[s]: the window before sequence s's first token (its
+   *    conv_k - 1 previous raw inputs); -1 or a NULL array = an empty window
+   *    (zeros), as a fresh request starts.
+   *  - conv_write_slot[s]: receives the window sequence s leaves (its last
+   *    conv_k - 1 raw inputs; when it has fewer tokens, the older rows come
+   *    from the window it resumed), what gdn_conv_decode continues from.
+   *  - conv_ckpt_slot[s * ckpt_per_seq + j]: the window at intermediate
+   *    checkpoint j (the raw inputs of the conv_k - 1 tokens before token
+   *    (j + 1) * ckpt_interval of the sequence), stored beside ckpt_slot's
+   *    state under the same conditions.
+   * -1 stores nothing; an index outside [-1, conv_n_slots) is read as an
+   * empty window or stores nothing, and sets GDN_DEVICE_BAD_SLOT.  Conv slots
+   * follow the write-slot contract among themselves (a sequence may write
+   * the slot it reads).  The windows are raw inputs: copied bit for bit. */
+  void *conv_pool;
+  int64_t conv_n_slots;
+  const int32_t *conv_read_slot;  /* [n_seq] device or NULL */
+  const int32_t *conv_write_slot; /* [n_seq] device or NULL */
+  const int32_t *conv_ckpt_slot;  /* [n_seq, ckpt_per_seq] device or NULL */
 } gdn_prefill_args;
 
 /* The front-end's conv window across calls.  The short conv is part of the
@@ -228,7 +255,8 @@ typedef struct gdn_prefill_args {
  * recurrent state's read/write rules ("Recurrent state" glossary entry, Why
  * it matters).  gdn_conv_decode runs the front-end for one token per request
  * and slides the window; gdn_conv_store fills slots from prefilled
- * sequences.  A prefill itself starts from an empty window. */
+ * sequences.  A prefill reads and stores windows through gdn_prefill_args'
+ * conv fields. */
 typedef struct gdn_conv_args {
   int32_t B;           /* requests (gdn_conv_decode) or sequences (gdn_conv_store), >= 0 */
   int32_t H_qk, H_v, d_k, d_v;
@@ -248,7 +276,10 @@ typedef struct gdn_conv_args {
   const float *conv_wk;  /* decode: [H_qk * d_k, conv_k] */
   const float *conv_wv;  /* decode: [H_v * d_v, conv_k] */
   void *conv_pool;     /* [n_slots, conv_k - 1, C] act_dtype, read and written in place */
-  const int32_t *read_slot;  /* decode: [B] or NULL (-1 = empty window, a fresh request) */
+  const int32_t *read_slot;  /* [B] or NULL (-1 = empty window, a fresh request): decode, the
+                                window before this token; store, the window each sequence
+                                resumed (the older rows of a sequence shorter than
+                                conv_k - 1 tokens) */
   const int32_t *write_slot; /* [B] or NULL (-1 = not stored) */
   const int32_t *cu_seqlens; /* store: [B + 1] device offsets into q/k/v; a sequence with
                                 cu[s] < 0, cu[s+1] < cu[s] or cu[s+1] > n_tokens is skipped
@@ -309,8 +340,11 @@ gdn_status gdn_frontend(const gdn_prefill_args *args, void *q_out, void *k_out, 
 gdn_status gdn_conv_decode(const gdn_conv_args *args, void *stream);
 
 /* After a prefill of B sequences packed by cu_seqlens: store each sequence's
- * last conv_k - 1 raw inputs (zeros before its first token) into
- * conv_pool[write_slot[s]], so that decode continues its conv window. */
+ * last conv_k - 1 raw inputs into conv_pool[write_slot[s]], so that decode
+ * continues its conv window.  Rows before a sequence's first token come from
+ * conv_pool[read_slot[s]] (zeros for -1 or a NULL array); a sequence may
+ * write the slot it read.  gdn_prefill stores the same windows itself when
+ * given conv_write_slot. */
 gdn_status gdn_conv_store(const gdn_conv_args *args, void *stream);
 
 /* Bytes of one conv-state slot. */

@@ -73,6 +73,12 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
   if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;
   if (a->use_frontend && a->conv_k != 4) return GDN_ERR_UNSUPPORTED;
   if (a->use_frontend && !(a->eps >= 0.0f)) return GDN_ERR_SHAPE;
+  // conv windows across calls belong to the front-end
+  const bool conv = a->conv_read_slot || a->conv_write_slot || a->conv_ckpt_slot;
+  if (conv && !a->use_frontend) return GDN_ERR_UNSUPPORTED;
+  if (conv && !a->conv_pool) return GDN_ERR_NULL;
+  if (a->conv_n_slots < 0) return GDN_ERR_SHAPE;
+  if (!al16(a->conv_pool)) return GDN_ERR_ALIGN;
   if ((int64_t)a->n_seq * a->H_v > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;
   if (a->n_tokens > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;  // token index fits int32
   if (a->n_seq == 0) return a->n_tokens == 0 ? GDN_OK : GDN_ERR_SHAPE;

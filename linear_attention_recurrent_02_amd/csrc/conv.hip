@@ -14,7 +14,9 @@
 //    the outputs are bitwise those of the prefill front-end for the same
 //    token and window.
 //  - conv_store_kernel: the window a prefilled sequence leaves behind (its
-//    last three raw inputs, zeros before its first token) into a slot.
+//    last three raw inputs; before its first token, the rows of the window
+//    it resumed, or zeros) into a slot, and for gdn_prefill also the window
+//    at each intermediate checkpoint.
 //
 // HBM-bound and tiny next to the recurrent state (48 KiB of window per
 // request against 1 MiB of state at 32 heads of 128 x 128 BF16): one thread
@@ -48,6 +50,11 @@ struct ConvParams {
   char *q_out, *k_out, *v_out;
   float *g_out, *beta_out;
   uint32_t *status;
+  // store: a NULL write_slot means slot s (gdn_conv_store) or none (gdn_prefill)
+  int32_t write_identity;
+  // store from gdn_prefill: windows at intermediate checkpoints
+  int32_t ckpt_per_seq, ckpt_interval;
+  const int32_t *ckpt_slot;
 };
 
 // which of q, k, v a piece of the concatenated row belongs to, and where
@@ -158,26 +165,57 @@ __global__ __launch_bounds__(kConvThreads) void conv_decode_kernel(ConvParams p)
 __global__ __launch_bounds__(kConvThreads) void conv_store_kernel(ConvParams p) {
   const int s = blockIdx.x;
   const int P = 2 * p.pq + p.pv;
+  const bool reporter = blockIdx.y == 0 && threadIdx.x == 0;  // reports a bad index once
   const int64_t t0 = p.cu[s], t1 = p.cu[s + 1];
   if (t0 < 0 || t1 < t0 || t1 > p.n_tokens) {
-    if (blockIdx.y == 0 && threadIdx.x == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SEQ);
-    return;
-  }
-  const int64_t ws = p.write_slot ? p.write_slot[s] : s;
-  if (ws < -1 || ws >= p.n_slots) {
-    if (blockIdx.y == 0 && threadIdx.x == 0 && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+    if (reporter && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SEQ);
     return;
   }
   const int piece = blockIdx.y * kConvThreads + threadIdx.x;
-  if (ws < 0 || piece >= P) return;
+  if (piece >= P) return;
   const PieceOf at = piece_of(p, piece);
   const char *raw = (at.region == 0 ? p.q : at.region == 1 ? p.k : p.v) + (int64_t)at.local * 16;
-  char *dst = p.pool + ws * (int64_t)kConvHist * P * 16 + (int64_t)piece * 16;
+  const int64_t slot_b = (int64_t)kConvHist * P * 16;
+  auto bad = [&](int64_t slot) { return slot < -1 || slot >= p.n_slots; };
+  const int64_t rs = p.read_slot ? p.read_slot[s] : -1;
+  if (bad(rs) && reporter && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+  const bool resumed = rs >= 0 && !bad(rs);
+  // this piece of token t's raw input, t >= t0 - 3: the input row, or before
+  // the first token the resumed window's row t - t0 + 3 (zeros without one)
+  auto row = [&](int64_t t) {
+    if (t >= t0) return nt_load16(raw + t * at.row_b);
+    if (resumed)
+      return *reinterpret_cast<const uint4 *>(p.pool + rs * slot_b + (t - t0 + kConvHist) * P * 16 +
+                                              (int64_t)piece * 16);
+    return make_uint4(0, 0, 0, 0);
+  };
+  // the window of the kConvHist tokens before token `end`, into `slot`; all
+  // loads first, so a sequence may write the slot it read
+  auto store_window = [&](int64_t end, int64_t slot) {
+    uint4 x[kConvHist];
 #pragma unroll
-  for (int j = 0; j < kConvHist; ++j) {
-    const int64_t t = t1 - kConvHist + j;
-    const uint4 x = t >= t0 ? nt_load16(raw + t * at.row_b) : make_uint4(0, 0, 0, 0);
-    nt_store16(dst + (int64_t)j * P * 16, x);
+    for (int j = 0; j < kConvHist; ++j) x[j] = row(end - kConvHist + j);
+    char *dst = p.pool + slot * slot_b + (int64_t)piece * 16;
+#pragma unroll
+    for (int j = 0; j < kConvHist; ++j) nt_store16(dst + (int64_t)j * P * 16, x[j]);
+  };
+  const int64_t ws = p.write_slot ? p.write_slot[s] : p.write_identity ? s : -1;
+  if (bad(ws)) {
+    if (reporter && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+  } else if (ws >= 0) {
+    store_window(t1, ws);
+  }
+  if (p.ckpt_slot) {
+    for (int j = 0; j < p.ckpt_per_seq; ++j) {
+      const int64_t tc = t0 + (int64_t)(j + 1) * p.ckpt_interval;
+      if (tc > t1) break;
+      const int64_t cs = p.ckpt_slot[(int64_t)s * p.ckpt_per_seq + j];
+      if (bad(cs)) {
+        if (reporter && p.status) atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+      } else if (cs >= 0) {
+        store_window(tc, cs);
+      }
+    }
   }
 }
 
@@ -196,6 +234,8 @@ static ConvParams make_conv_params(const gdn_conv_args &a) {
   p.q_out = static_cast<char *>(a.q_out); p.k_out = static_cast<char *>(a.k_out);
   p.v_out = static_cast<char *>(a.v_out);
   p.g_out = a.g_out; p.beta_out = a.beta_out; p.status = a.status;
+  p.write_identity = 1;
+  p.ckpt_per_seq = 0; p.ckpt_interval = 0; p.ckpt_slot = nullptr;
   return p;
 }
 
@@ -234,6 +274,30 @@ gdn_status launch_conv_decode(const gdn_conv_args &a, hipStream_t s) {
 
 gdn_status launch_conv_store(const gdn_conv_args &a, hipStream_t s) {
   const ConvParams p = make_conv_params(a);
+  hipLaunchKernelGGL(conv_store_kernel, conv_grid(p, 1), dim3(kConvThreads), 0, s, p);
+  return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
+}
+
+// The windows a prefill leaves (conv_write_slot) and those at its
+// intermediate checkpoints (conv_ckpt_slot), after its front-end has read
+// the windows it resumes (stream order).
+gdn_status launch_prefill_conv_store(const gdn_prefill_args &a, hipStream_t s) {
+  const bool ckpt = a.conv_ckpt_slot && a.ckpt_interval > 0 && a.ckpt_per_seq > 0;
+  if (a.n_seq == 0 || (!a.conv_write_slot && !ckpt)) return GDN_OK;
+  const int per = a.act_dtype == GDN_BF16 ? 8 : 4;
+  ConvParams p = {};
+  p.n = a.n_seq; p.H_v = a.H_v;
+  p.pq = a.H_qk * a.d_k / per; p.pv = a.H_v * a.d_v / per;
+  p.n_slots = a.conv_n_slots; p.n_tokens = a.n_tokens;
+  p.q = static_cast<const char *>(a.q); p.k = static_cast<const char *>(a.k);
+  p.v = static_cast<const char *>(a.v);
+  p.pool = static_cast<char *>(a.conv_pool);
+  p.read_slot = a.conv_read_slot; p.write_slot = a.conv_write_slot; p.cu = a.cu_seqlens;
+  p.status = a.status;
+  p.write_identity = 0;
+  p.ckpt_slot = ckpt ? a.conv_ckpt_slot : nullptr;
+  p.ckpt_per_seq = ckpt ? a.ckpt_per_seq : 0;
+  p.ckpt_interval = ckpt ? a.ckpt_interval : 0;
   hipLaunchKernelGGL(conv_store_kernel, conv_grid(p, 1), dim3(kConvThreads), 0, s, p);
   return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
 }

@@ -5,7 +5,9 @@
 // The "Gated DeltaNet" glossary entry (Engineering details) lists fusing the
 // short Conv1D with the layer among the optimisations; the width, SiLU and
 // the q/k normalisation follow the prefill workload description.  Tap j
-// multiplies x[t - 3 + j]; tokens before a sequence's first token count as 0.
+// multiplies x[t - 3 + j]; tokens before a sequence's first token are the
+// rows of the conv window it resumes (a conv-state slot: the raw inputs of
+// the three tokens before it), or 0 without one.
 //
 // HBM-bound elementwise work, laid out so that every raw byte is read once
 // and every load and store is a whole-row stream.  A thread owns one 16-byte
@@ -51,6 +53,7 @@ struct FeTensor {
   int32_t pieces;    // 16-byte pieces per row = H * D / channels-per-piece
   int32_t lpr_log2;  // log2 of the lanes per row group
   int32_t chunks;    // ceil(pieces / lanes per row group)
+  int32_t win_off;   // first piece of this tensor in a conv-window row (q|k|v order)
 };
 
 struct FrontendParams {
@@ -64,6 +67,13 @@ struct FrontendParams {
   int32_t runs_per[3];  // 64-token runs per row group
   const float *a_raw, *b_raw;
   float *g_out, *beta_out;
+  // the conv windows the sequences resume: [win_slots, 3, win_pieces] 16-byte
+  // pieces, win_read[s] the slot of sequence s (NULL: none)
+  const char *win;
+  int64_t win_slots;
+  const int32_t *win_read;
+  int32_t win_pieces;
+  uint32_t *status;
 };
 
 // index of the sequence holding token t: the last s with cu[s] <= t
@@ -127,6 +137,21 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
   // the sequence holding ts, and the offsets of the sequences that follow
   int s = seq_of(cu, p.n_seq, ts);
   const int64_t s_start = cu[s];
+  // this piece of the raw input of token t, t before the first token `start`
+  // of sequence sq (t >= start - 3): row t - start + 3 of the window the
+  // sequence resumes, or 0
+  auto before = [&](int sq, int64_t start, int64_t t) {
+    uint4 x = make_uint4(0, 0, 0, 0);
+    if (p.win_read) {
+      const int64_t slot = p.win_read[sq];
+      if (slot >= 0 && slot < p.win_slots)
+        x = *reinterpret_cast<const uint4 *>(
+            p.win + ((slot * 3 + (t - start + 3)) * p.win_pieces + T.win_off + piece) * 16);
+      else if (slot != -1 && p.status)
+        atomicOr(p.status, GDN_DEVICE_BAD_SLOT);
+    }
+    return x;
+  };
   // bit i of the mask is set when token r0 + i opens a sequence (equals an
   // offset cu[j], j >= 1): the conv window is cleared there
   auto starts_mask = [&](int64_t r0, int64_t r1) {
@@ -143,22 +168,27 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
   // The conv window is a ring of four token slots: token ts + j lives in slot
   // j % 4 (runs and the unrolled steps are multiples of 4 tokens, so every
   // slot index is a constant and the window slides without register copies).
-  // Slots 3, 2, 1 start as tokens ts - 1, ts - 2, ts - 3 (0 before the sequence).
+  // Slots 3, 2, 1 start as tokens ts - 1, ts - 2, ts - 3 (before the
+  // sequence: its resumed window, or 0).
   float xw[4][CH];
-  if (ts - 1 < s_start) h1 = make_uint4(0, 0, 0, 0);
-  if (ts - 2 < s_start) h2 = make_uint4(0, 0, 0, 0);
-  if (ts - 3 < s_start) h3 = make_uint4(0, 0, 0, 0);
+  if (ts - 1 < s_start) h1 = before(s, s_start, ts - 1);
+  if (ts - 2 < s_start) h2 = before(s, s_start, ts - 2);
+  if (ts - 3 < s_start) h3 = before(s, s_start, ts - 3);
   E::unpack(h1, xw[3]); E::unpack(h2, xw[2]); E::unpack(h3, xw[1]);
 
-  // one token, slot u % 4: conv + SiLU (+ L2 norm) of x0 given the window;
-  // `check` = the run holds a sequence start (bit i of resets clears the window)
-  auto step = [&](const float (&x0)[CH], bool check, uint64_t resets, int i, int u, float (&y)[CH]) {
+  // one token t, slot u % 4: conv + SiLU (+ L2 norm) of x0 given the window;
+  // `check` = the run holds a sequence start (bit i of resets: token t opens
+  // a sequence, whose window replaces the previous tokens)
+  auto step = [&](const float (&x0)[CH], bool check, uint64_t resets, int i, int u, int64_t t,
+                  float (&y)[CH]) {
     float(&x1)[CH] = xw[(u + 3) & 3];
     float(&x2)[CH] = xw[(u + 2) & 3];
     float(&x3)[CH] = xw[(u + 1) & 3];
     if (check && ((resets >> i) & 1ull)) {
-#pragma unroll
-      for (int c = 0; c < CH; ++c) { x1[c] = 0.f; x2[c] = 0.f; x3[c] = 0.f; }
+      const int sq = seq_of(cu, p.n_seq, t);
+      E::unpack(before(sq, t, t - 1), x1);
+      E::unpack(before(sq, t, t - 2), x2);
+      E::unpack(before(sq, t, t - 3), x3);
     }
 #pragma unroll
     for (int c = 0; c < CH; ++c) {
@@ -184,7 +214,7 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
         // refill the slot only after it has been unpacked, so the load can
         // land in the slot's own registers (no copies, no early waits)
         ring[u] = ld(ordered_after(x0, min(t + kFeDepth, tl)));
-        step(x0, check, resets, b0 + u, u, y);
+        step(x0, check, resets, b0 + u, u, t, y);
         nt_store16(dst + t * row_bytes, E::pack(y));
       }
     }
@@ -206,7 +236,7 @@ __device__ __forceinline__ void fe_run(const FrontendParams &p, const FeTensor &
         float x0[CH], y[CH];
         E::unpack(ring[u], x0);
         ring[u] = ld(min(t + kFeDepth, tl));
-        step(x0, true, resets, b0 + u, u, y);
+        step(x0, true, resets, b0 + u, u, t, y);
         if (t < te) nt_store16(dst + t * row_bytes, E::pack(y));
       }
     }
@@ -274,6 +304,14 @@ gdn_status launch_frontend(const gdn_prefill_args &a, void *q_out, void *k_out, 
   p.t[1] = make_tensor(a.k, k_out, a.conv_wk, a.H_qk, a.d_k, ab);
   p.t[2] = make_tensor(a.v, v_out, a.conv_wv, a.H_v, a.d_v, ab);
   p.a_raw = a.a_raw; p.b_raw = a.b_raw; p.g_out = g_out; p.beta_out = beta_out;
+  p.t[0].win_off = 0;
+  p.t[1].win_off = p.t[0].pieces;
+  p.t[2].win_off = 2 * p.t[0].pieces;
+  p.win = static_cast<const char *>(a.conv_pool);
+  p.win_slots = a.conv_n_slots;
+  p.win_read = a.conv_pool ? a.conv_read_slot : nullptr;
+  p.win_pieces = 2 * p.t[0].pieces + p.t[2].pieces;
+  p.status = a.status;
   p.y0[0] = 0;
   for (int i = 0; i < 3; ++i) p.y0[i + 1] = p.y0[i] + p.t[i].chunks;
   // about kFeBlocksPerCU workgroups per CU in all, the runs of a tensor dealt

@@ -21,6 +21,7 @@ gdn_status launch_mixed(const gdn_decode_args &d, const gdn_prefill_args &p, hip
 size_t prefill_workspace_bytes(const gdn_prefill_args &a);
 gdn_status launch_conv_decode(const gdn_conv_args &a, hipStream_t stream);
 gdn_status launch_conv_store(const gdn_conv_args &a, hipStream_t stream);
+gdn_status launch_prefill_conv_store(const gdn_prefill_args &a, hipStream_t stream);
 int64_t conv_grid_rows(const gdn_conv_args &a);  // blockIdx.y extent of the conv kernels
 
 struct PrefillParams;

@@ -140,6 +140,12 @@ gdn_status prepare_prefill(const gdn_prefill_args &a, hipStream_t stream, Prefil
     g = reinterpret_cast<const float *>(base + w.g);
     beta = reinterpret_cast<const float *>(base + w.beta);
   }
+  if (a.use_frontend) {
+    // the conv windows the sequences leave, once the front-end has read the
+    // ones they resume (an empty sequence leaves the window it resumed)
+    const gdn_status st = launch_prefill_conv_store(a, stream);
+    if (st != GDN_OK) return st;
+  }
   *out = make_prefill_params(a, q, k, v, g, beta);
   return GDN_OK;
 }

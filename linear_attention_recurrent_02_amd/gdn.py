@@ -48,7 +48,9 @@ class PrefillArgs(ctypes.Structure):
                 ("conv_wk", _P), ("conv_wv", _P), ("state_pool", _P), ("read_slot", _P),
                 ("write_slot", _P), ("o", _P), ("workspace", _P),
                 ("workspace_bytes", ctypes.c_size_t), ("status", _P), ("ckpt_slot", _P),
-                ("ckpt_per_seq", _I32), ("decay_mode", _I32)]
+                ("ckpt_per_seq", _I32), ("decay_mode", _I32), ("conv_pool", _P),
+                ("conv_n_slots", _I64), ("conv_read_slot", _P), ("conv_write_slot", _P),
+                ("conv_ckpt_slot", _P)]
 
 
 class ConvArgs(ctypes.Structure):
@@ -333,12 +335,16 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
                       H_qk, H_v, g=None, beta=None, a_raw=None, b_raw=None, conv_wq=None,
                       conv_wk=None, conv_wv=None, rule="gated_delta", scale=1.0, eps=1e-6,
                       chunk=64, workspace=None, status=None, ckpt_interval=0, ckpt_slot=None,
-                      alloc_workspace=True):
+                      conv_pool=None, conv_read_slot=None, conv_write_slot=None,
+                      conv_ckpt_slot=None, alloc_workspace=True):
     """Build a PrefillArgs struct.  q, k: [N, H_qk*d_k] (or [N, H_qk, d_k]);
     v: [N, H_v*d_v]; with conv weights given the front-end runs (a_raw,
     b_raw are the gate logits), otherwise g, beta are used as given.  With
     ckpt_interval > 0 (a multiple of chunk), ckpt_slot [n_seq, per_seq] int32
-    names the slots of the intermediate checkpoints.
+    names the slots of the intermediate checkpoints.  With the front-end,
+    conv_pool [n, conv_k-1, 2*H_qk*d_k + H_v*d_v] holds conv windows:
+    conv_read_slot / conv_write_slot [n_seq] and conv_ckpt_slot (shaped as
+    ckpt_slot) name the windows each sequence resumes and leaves.
     Returns (args, o, keepalive); allocates the workspace when needed unless
     alloc_workspace is False."""
     _need(cu_seqlens, "cu_seqlens", dtype=torch.int32)
@@ -375,6 +381,8 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
         _need(ckpt_slot, "ckpt_slot", dtype=torch.int32)
         if ckpt_slot.dim() != 2 or ckpt_slot.shape[0] != n_seq:
             raise ValueError(f"ckpt_slot must be [{n_seq}, per_seq], got {tuple(ckpt_slot.shape)}")
+    _conv_slots(conv_pool, conv_read_slot, conv_write_slot, conv_ckpt_slot, ckpt_slot, q, n_seq,
+                H_qk, H_v, d_k, d_v, K, use_fe)
     _need(workspace, "workspace", dtype=torch.uint8)
     _status(status)
     for name, t in (("cu_seqlens", cu_seqlens), ("q", q), ("k", k), ("v", v),
@@ -382,7 +390,9 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
                     ("write_slot", write_slot), ("o", o), ("g", g), ("beta", beta),
                     ("a_raw", a_raw), ("b_raw", b_raw), ("conv_wq", conv_wq),
                     ("conv_wk", conv_wk), ("conv_wv", conv_wv), ("status", status),
-                    ("ckpt_slot", ckpt_slot), ("workspace", workspace)):
+                    ("ckpt_slot", ckpt_slot), ("workspace", workspace), ("conv_pool", conv_pool),
+                    ("conv_read_slot", conv_read_slot), ("conv_write_slot", conv_write_slot),
+                    ("conv_ckpt_slot", conv_ckpt_slot)):
         _dev(t, name)
     if o is None:
         o = torch.empty((N, H_v, d_v), dtype=q.dtype, device=q.device)
@@ -408,14 +418,41 @@ def make_prefill_args(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slo
     a.ckpt_per_seq = 0 if ckpt_slot is None else int(ckpt_slot.shape[-1])
     # g [N, H_v]: one decay per state head; [N, H_v, d_k]: one per key channel
     a.decay_mode = DECAY_CHANNEL if channel else DECAY_HEAD
+    a.conv_pool = _ptr(conv_pool)
+    a.conv_n_slots = 0 if conv_pool is None else conv_pool.shape[0]
+    a.conv_read_slot, a.conv_write_slot = _ptr(conv_read_slot), _ptr(conv_write_slot)
+    a.conv_ckpt_slot = _ptr(conv_ckpt_slot)
     need = int(load_library().gdn_prefill_workspace_size(ctypes.byref(a)))
     if need and workspace is None and alloc_workspace:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a.workspace = _ptr(workspace)
     a.workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     keep = (cu_seqlens, q, k, v, state_pool, read_slot, write_slot, o, g, beta, a_raw, b_raw,
-            conv_wq, conv_wk, conv_wv, workspace, status, ckpt_slot)
+            conv_wq, conv_wk, conv_wv, workspace, status, ckpt_slot, conv_pool, conv_read_slot,
+            conv_write_slot, conv_ckpt_slot)
     return a, o, keep
+
+
+def _conv_slots(conv_pool, read_slot, write_slot, ckpt_slot, state_ckpt_slot, q, n_seq, H_qk,
+                H_v, d_k, d_v, K, use_fe):
+    """Checks of a prefill's conv-window arguments (see gdn_prefill_args)."""
+    given = [t is not None for t in (read_slot, write_slot, ckpt_slot)]
+    if any(given) and not use_fe:
+        raise ValueError("conv slots need the front-end (conv weights)")
+    if any(given) and conv_pool is None:
+        raise ValueError("conv slots need conv_pool")
+    if conv_pool is not None:
+        C = 2 * H_qk * d_k + H_v * d_v
+        _need(conv_pool, "conv_pool", dtype=q.dtype)
+        if conv_pool.dim() != 3 or tuple(conv_pool.shape[1:]) != (K - 1, C):
+            raise ValueError(f"conv_pool must be [n_slots, {K - 1}, {C}], "
+                             f"got {tuple(conv_pool.shape)}")
+    _need(read_slot, "conv_read_slot", dtype=torch.int32, shape=(n_seq,))
+    _need(write_slot, "conv_write_slot", dtype=torch.int32, shape=(n_seq,))
+    if ckpt_slot is not None:
+        if state_ckpt_slot is None:
+            raise ValueError("conv_ckpt_slot goes with ckpt_slot")
+        _need(ckpt_slot, "conv_ckpt_slot", dtype=torch.int32, shape=tuple(state_ckpt_slot.shape))
 
 
 def gdn_prefill(cu_seqlens, q, k, v, state_pool, read_slot=None, write_slot=None, o=None, *,
@@ -450,8 +487,10 @@ def gdn_noalloc_workspace_bytes() -> int:
 
 
 def gdn_frontend(cu_seqlens, q_raw, k_raw, v_raw, *, H_qk, H_v, conv_wq, conv_wk, conv_wv,
-                 a_raw, b_raw, eps=1e-6, stream=None):
-    """The front-end alone: returns (q [N,H_qk,d_k], k, v [N,H_v,d_v], g, beta)."""
+                 a_raw, b_raw, eps=1e-6, conv_pool=None, conv_read_slot=None, stream=None):
+    """The front-end alone: returns (q [N,H_qk,d_k], k, v [N,H_v,d_v], g, beta).
+    conv_pool / conv_read_slot: the windows the sequences resume, as for
+    make_prefill_args."""
     _need(cu_seqlens, "cu_seqlens", dtype=torch.int32)
     if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 1:
         raise ValueError("cu_seqlens must be [n_seq + 1]")
@@ -469,9 +508,12 @@ def gdn_frontend(cu_seqlens, q_raw, k_raw, v_raw, *, H_qk, H_v, conv_wq, conv_wk
     _need(conv_wv, "conv_wv", dtype=torch.float32, shape=(H_v * d_v, K))
     _need(a_raw, "a_raw", dtype=torch.float32, shape=(N, H_v))
     _need(b_raw, "b_raw", dtype=torch.float32, shape=(N, H_v))
+    _conv_slots(conv_pool, conv_read_slot, None, None, None, q_raw, cu_seqlens.shape[0] - 1,
+                H_qk, H_v, d_k, d_v, K, True)
     for name, t in (("cu_seqlens", cu_seqlens), ("q_raw", q_raw), ("k_raw", k_raw),
                     ("v_raw", v_raw), ("conv_wq", conv_wq), ("conv_wk", conv_wk),
-                    ("conv_wv", conv_wv), ("a_raw", a_raw), ("b_raw", b_raw)):
+                    ("conv_wv", conv_wv), ("a_raw", a_raw), ("b_raw", b_raw),
+                    ("conv_pool", conv_pool), ("conv_read_slot", conv_read_slot)):
         _dev(t, name)
     a = PrefillArgs()
     a.n_seq = cu_seqlens.shape[0] - 1
@@ -486,6 +528,9 @@ def gdn_frontend(cu_seqlens, q_raw, k_raw, v_raw, *, H_qk, H_v, conv_wq, conv_wk
     a.cu_seqlens, a.q, a.k, a.v = _ptr(cu_seqlens), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw)
     a.a_raw, a.b_raw = _ptr(a_raw), _ptr(b_raw)
     a.conv_wq, a.conv_wk, a.conv_wv = _ptr(conv_wq), _ptr(conv_wk), _ptr(conv_wv)
+    a.conv_pool = _ptr(conv_pool)
+    a.conv_n_slots = 0 if conv_pool is None else conv_pool.shape[0]
+    a.conv_read_slot = _ptr(conv_read_slot)
     q = torch.empty((N, H_qk, d_k), dtype=q_raw.dtype, device=q_raw.device)
     k = torch.empty_like(q)
     v = torch.empty((N, H_v, d_v), dtype=v_raw.dtype, device=q_raw.device)
@@ -610,11 +655,13 @@ def gdn_conv_decode(q_raw, k_raw, v_raw, conv_pool, read_slot=None, write_slot=N
 
 
 def gdn_conv_store(cu_seqlens, q_raw, k_raw, v_raw, conv_pool, write_slot=None, *, H_qk, H_v,
-                   status=None, stream=None):
+                   read_slot=None, status=None, stream=None):
     """Store each prefilled sequence's last conv_k-1 raw inputs into
-    conv_pool[write_slot[s]]."""
+    conv_pool[write_slot[s]]; rows before a sequence's first token come from
+    conv_pool[read_slot[s]] (zeros for -1 or None)."""
     a, keep = make_conv_args(q_raw, k_raw, v_raw, conv_pool, H_qk=H_qk, H_v=H_v,
-                             write_slot=write_slot, cu_seqlens=cu_seqlens, status=status)
+                             read_slot=read_slot, write_slot=write_slot, cu_seqlens=cu_seqlens,
+                             status=status)
     code = load_library().gdn_conv_store(ctypes.byref(a), _stream(stream))
     if code:
         raise GdnError("gdn_conv_store", code)

@@ -28,7 +28,7 @@ def test_struct_layout_matches():
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
     assert lib.gdn_sizeof_conv_args() == ctypes.sizeof(B.ConvArgs)
-    assert gdn.gdn_abi_version() == 7
+    assert gdn.gdn_abi_version() == 8
 
 
 def test_state_bytes_against_the_pages():
@@ -234,6 +234,23 @@ def test_prefill_conv_width_ignored_without_frontend_and_empty_batch():
     assert lib.gdn_mixed(ctypes.byref(d), ctypes.byref(a), None) == OK
     bad = _decode_args(rule=11)
     assert lib.gdn_mixed(ctypes.byref(bad), ctypes.byref(a), None) == RULE
+
+
+@pytest.mark.parametrize("over,code", [
+    # conv windows belong to the front-end
+    (dict(use_frontend=0, conv_pool=FAKE, conv_n_slots=4, conv_read_slot=FAKE), UNSUP),
+    (dict(use_frontend=0, conv_pool=FAKE, conv_n_slots=4, conv_write_slot=FAKE), UNSUP),
+    (dict(conv_write_slot=FAKE, conv_n_slots=4), NULL),      # slots without a pool
+    (dict(conv_ckpt_slot=FAKE, conv_n_slots=4), NULL),
+    (dict(conv_pool=FAKE, conv_n_slots=-1, conv_read_slot=FAKE), SHAPE),
+    (dict(conv_pool=FAKE + 8, conv_n_slots=4, conv_read_slot=FAKE), ALIGN),
+    (dict(conv_pool=FAKE, conv_n_slots=4, conv_read_slot=FAKE, conv_write_slot=FAKE),
+     WORKSPACE),  # valid conv fields: the call reaches the workspace check
+])
+def test_prefill_conv_window_fields(over, code):
+    lib = gdn.load_library()
+    a = _prefill_args(**over)
+    assert lib.gdn_prefill(ctypes.byref(a), None) == code
 
 
 def test_mixed_halves_must_share_the_decay_mode():
