@@ -562,8 +562,10 @@ def run_prefill_cw(args, torch, gdn, syn):
 
 def run_mixed(args, torch, gdn, syn):
     """448 decode requests plus 4 prefills of 8192 tokens (fused front-end) on
-    one 1024-slot BF16 pool, 25% of requests reading a checkpoint slot, decode
-    rule gated_delta: one gdn_mixed call vs gdn_decode + gdn_prefill."""
+    one 1024-slot BF16 pool, 25% of requests reading a checkpoint slot (the
+    prefills resume the conv window of their read slot and store the one they
+    leave, in a conv pool of the same slots), decode rule gated_delta: one
+    gdn_mixed call vs gdn_decode + gdn_prefill."""
     wl = syn.WORKLOADS["mixed"]
     Hqk, Hv, d = wl["H_qk"], wl["H_v"], wl["d_k"]
     nd, npf, L = wl["n_decode"], wl["n_prefill"], wl["prefill_len"]
@@ -574,10 +576,13 @@ def run_mixed(args, torch, gdn, syn):
     x = {kk: vv.cuda() for kk, vv in syn.frontend_inputs(wl["index"], 2, L * npf, Hqk, Hv, d, d, 4).items()}
     decs = {rule: gdn.make_decode_args(q, k, v, g, beta, pool, drs, dws, rule=rule)
             for rule in ("linear", "gated", "delta", "gated_delta")}
+    cpool = syn.conv_pool(wl["index"], 0, wl["n_slots"], 2 * Hqk * d + Hv * d, 4, torch.bfloat16,
+                          on_device=True)
     pa, po, pkeep = gdn.make_prefill_args(cu, x["q_raw"], x["k_raw"], x["v_raw"], pool, prs, pws,
                                           H_qk=Hqk, H_v=Hv, a_raw=x["a_raw"], b_raw=x["b_raw"],
                                           conv_wq=x["conv_wq"], conv_wk=x["conv_wk"],
-                                          conv_wv=x["conv_wv"])
+                                          conv_wv=x["conv_wv"], conv_pool=cpool,
+                                          conv_read_slot=prs, conv_write_slot=pws)
     lib = gdn.load_library()
     s = lambda: ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 

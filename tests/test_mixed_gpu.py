@@ -38,13 +38,24 @@ def build(wl, n_dec, lengths, Hqk, Hv, d, n_slots, frontend, std=0.02, sdt=torch
                 pin=pin, Hqk=Hqk, Hv=Hv)
 
 
+def conv_kw(c):
+    """With a conv pool in the case, the prefills resume the windows of their
+    read slots and store the ones they leave (a fresh copy of the pool per
+    run, kept in c["cpool_out"])."""
+    if "cpool" not in c:
+        return {}
+    c["cpool_out"] = dev(c["cpool"])
+    return dict(conv_pool=c["cpool_out"], conv_read_slot=dev(c["prs"]),
+                conv_write_slot=dev(c["pws"]))
+
+
 def run_mixed(c, rule):
     pool = dev(c["pool"])
     q, k, v, g, beta = c["dec"]
     da, do, dkeep = make_decode_args(q, k, v, g, beta, pool, dev(c["drs"]), dev(c["dws"]), rule=rule)
     pa, po, pkeep = make_prefill_args(dev(c["cu"]), dev(c["pin"]["q"]), dev(c["pin"]["k"]),
                                       dev(c["pin"]["v"]), pool, dev(c["prs"]), dev(c["pws"]),
-                                      H_qk=c["Hqk"], H_v=c["Hv"], **c["pin"]["kw"])
+                                      H_qk=c["Hqk"], H_v=c["Hv"], **c["pin"]["kw"], **conv_kw(c))
     gdn_mixed(da, pa)
     torch.cuda.synchronize()
     return do, po, pool
@@ -56,7 +67,7 @@ def run_separate(c, rule):
     do = gdn_decode(q, k, v, g, beta, pool, dev(c["drs"]), dev(c["dws"]), rule=rule)
     po = gdn_prefill(dev(c["cu"]), dev(c["pin"]["q"]), dev(c["pin"]["k"]), dev(c["pin"]["v"]),
                      pool, dev(c["prs"]), dev(c["pws"]), H_qk=c["Hqk"], H_v=c["Hv"],
-                     **c["pin"]["kw"])
+                     **c["pin"]["kw"], **conv_kw(c))
     torch.cuda.synchronize()
     return do, po, pool
 
@@ -172,14 +183,18 @@ def test_mixed_uneven_workers():
 def test_mixed_full_size():
     """448 decode requests (each update rule in turn, every rule from the same
     pool state) plus 4 prefills of 8192 tokens through the fused front-end, one
-    1024-slot BF16 pool, 25% of the requests reading a checkpoint slot.  Mixed =
-    separate bit for bit; every decode request's o and written state against
-    the oracle, and eight state heads of every prefill."""
+    1024-slot BF16 pool, 25% of the requests reading a checkpoint slot; the
+    prefills resume the conv windows of their read slots and store theirs.
+    Mixed = separate bit for bit (windows too); every decode request's o and
+    written state against the oracle, and eight state heads of every
+    prefill."""
     wl = syn.WORKLOADS["mixed"]
     Hqk, Hv, d = wl["H_qk"], wl["H_v"], wl["d_k"]
     nd = wl["n_decode"]
     lengths = [wl["prefill_len"]] * wl["n_prefill"]
     c = build(wl["index"], nd, lengths, Hqk, Hv, d, wl["n_slots"], frontend=True)
+    C = 2 * Hqk * d + Hv * d
+    c["cpool"] = syn.conv_pool(wl["index"], 0, wl["n_slots"], C, 4, torch.bfloat16)
     # the decode half's initial states, one per request (zero for a fresh one)
     rs_all = c["drs"].numpy()
     start = np.zeros((nd, Hv, d, d))
@@ -191,9 +206,11 @@ def test_mixed_full_size():
     for rule in RULES:
         say("mixed full size", rule)
         do, po, pool = run_mixed(c, rule)
+        cpool = c["cpool_out"]
         so, spo, spool = run_separate(c, rule)
         assert torch.equal(do, so) and torch.equal(po, spo), rule
         assert torch.equal(pool.view(torch.int16), spool.view(torch.int16)), rule
+        assert torch.equal(cpool.view(torch.int16), c["cpool_out"].view(torch.int16)), rule
         ro, rpool, _ = oracle.decode(f64(q), f64(k), f64(v), f64(g), f64(beta), start,
                                      np.where(live, own, -1).astype(np.int32), own, rule=rule,
                                      round_state=True)
@@ -204,14 +221,23 @@ def test_mixed_full_size():
     cu = c["cu"]
     pc = po.cpu()
     pool_after = pool.cpu()
+    # the windows the prefills resumed (zeros for fresh requests), q|k|v channels
+    prs = c["prs"].numpy()
+    init = np.zeros((len(prs), 3, C))
+    for s_, r in enumerate(prs):
+        if r >= 0:
+            init[s_] = f64(c["cpool"][int(r)])
     for j in (0, 5, 9, 15):
         hs = [2 * j, 2 * j + 1]
         qs, vs = slice(j * d, (j + 1) * d), slice(2 * j * d, (2 * j + 2) * d)
+        sub = np.concatenate([init[:, :, qs], init[:, :, Hqk * d + j * d:Hqk * d + (j + 1) * d],
+                              init[:, :, 2 * Hqk * d + 2 * j * d:2 * Hqk * d + (2 * j + 2) * d]],
+                             axis=2)
         rq, rk, rv, rg, rb = oracle.frontend(cu.numpy(), f64(x["q_raw"][:, qs]),
                                              f64(x["k_raw"][:, qs]), f64(x["v_raw"][:, vs]),
                                              f64(x["conv_wq"][qs]), f64(x["conv_wk"][qs]),
                                              f64(x["conv_wv"][vs]), f64(x["a_raw"][:, hs]),
-                                             f64(x["b_raw"][:, hs]), Hqk=1, Hv=2)
+                                             f64(x["b_raw"][:, hs]), Hqk=1, Hv=2, conv_init=sub)
         rq, rk, rv = (oracle.round_bf16(t) for t in (rq, rk, rv))
         sub_pool = f64(c["pool"][:, hs])
         rpo, rpool, _ = oracle.sequences(cu.numpy(), rq, rk, rv, rg, rb, sub_pool,
