@@ -68,6 +68,8 @@ gdn_status check_prefill(const gdn_prefill_args *a, bool need_state) {
   // the front-end produces one decay per (token, head): the channel-wise
   // decay takes q, k, v, g and beta as given
   if (a->decay_mode == GDN_DECAY_CHANNEL && a->use_frontend) return GDN_ERR_UNSUPPORTED;
+  // channel-wise decays are read four channels (16 bytes) at a time
+  if (a->decay_mode == GDN_DECAY_CHANNEL && !al16(a->g)) return GDN_ERR_ALIGN;
   gdn_status st = check_heads(a->H_qk, a->H_v, a->d_k, a->d_v);
   if (st != GDN_OK) return st;
   if (a->chunk != 64) return GDN_ERR_UNSUPPORTED;

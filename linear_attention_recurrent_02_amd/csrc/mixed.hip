@@ -37,8 +37,8 @@ template <bool SB, bool AB, int DK, int DV, bool F32, bool CW>
 struct MixedLayout {
   // the chain's waves, except with FP32 state: a worker's two FP32 tiles in
   // flight need more registers than a wave of a 512-thread block gets (the
-  // channel-wise chain has four waves)
-  static constexpr int NW = CW ? 4 : SB ? kPrefillWaves<DK, DV, F32> : 4;
+  // channel-wise chain has its own wave count)
+  static constexpr int NW = CW ? kCwWaves<DK, DV, F32> : SB ? kPrefillWaves<DK, DV, F32> : 4;
   static constexpr int NT = 64 * NW;                          // threads per block
   static constexpr int DT = 256;                              // threads per decode worker
   static constexpr int NH = NT / DT;                          // decode workers per block

@@ -20,7 +20,8 @@ __global__ __launch_bounds__((64 * kPrefillWaves<DK, DV, F32>)) void prefill_ker
 
 // one (sequence, state head) chain per workgroup with a per-key-channel decay
 template <bool SB, bool AB, int DK, int DV, bool F32, bool CK>
-__global__ __launch_bounds__(256) void prefill_cw_kernel(PrefillParams p, int n_chains) {
+__global__ __launch_bounds__((64 * kCwWaves<DK, DV, F32>)) void prefill_cw_kernel(PrefillParams p,
+                                                                                 int n_chains) {
   __shared__ __align__(16) char smem[kCwChainLds<DK, DV, F32, AB>];
   const int chain = chain_of_block(blockIdx.x);
   if (chain < n_chains) prefill_chain_cw<SB, AB, DK, DV, F32, CK>(p, chain, smem);
@@ -54,12 +55,13 @@ static gdn_status launch_chains(const PrefillParams &p, hipStream_t s) {
     } else {
       const int n_chains = p.n_seq * p.H_v;
       const int blocks = (n_chains + 15) / 16 * 16;
+      const dim3 block(64 * kCwWaves<DK, DV, F32>);
       if (p.ckpt_chunks > 0)
-        hipLaunchKernelGGL((prefill_cw_kernel<SB, AB, DK, DV, F32, true>), dim3(blocks), dim3(256),
-                           0, s, p, n_chains);
+        hipLaunchKernelGGL((prefill_cw_kernel<SB, AB, DK, DV, F32, true>), dim3(blocks), block, 0,
+                           s, p, n_chains);
       else
-        hipLaunchKernelGGL((prefill_cw_kernel<SB, AB, DK, DV, F32, false>), dim3(blocks), dim3(256),
-                           0, s, p, n_chains);
+        hipLaunchKernelGGL((prefill_cw_kernel<SB, AB, DK, DV, F32, false>), dim3(blocks), block, 0,
+                           s, p, n_chains);
       return hipGetLastError() == hipSuccess ? GDN_OK : GDN_ERR_LAUNCH;
     }
   }

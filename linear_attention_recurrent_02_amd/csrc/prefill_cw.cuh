@@ -27,9 +27,12 @@
 // forgets nearly everything within 16 tokens) takes its weights entry by
 // entry on the vector ALUs instead, each e^(G_r - G_s) <= 1.  Everything else
 // -- the block substitution for U, the read-out, the state update, state in
-// and out, checkpoints -- is the 4-wave plain chain's (prefill_chain.cuh),
-// with the chunk's inputs in one LDS set (the per-channel decays take the
-// room of the second).
+// and out, checkpoints -- follows the plain chain (prefill_chain.cuh), with
+// the chunk's inputs in one LDS set (the per-channel decays take the room of
+// the second).  The chain runs NW = 4 or 8 waves: with 8, two waves share
+// each SIMD, so one's LDS and exp latencies hide behind the other's work;
+// waves 0-3 form the diagonal tiles and waves 4-7 the six below, and each
+// wave owns d_v / 8 state columns.
 #pragma once
 
 #include <algorithm>
@@ -67,8 +70,8 @@ struct CwLayout {
   static constexpr size_t KE = ALIAS ? VH + (size_t)C * LDV * sizeof(IT) : QG + (size_t)C * LDKO * sizeof(OT);
   static constexpr size_t GC = KE + (size_t)C * LDKO * sizeof(OT);
   static constexpr size_t BETA = GC + (size_t)C * LDG * 4;
-  static constexpr size_t TOT = BETA + C * 4;  // 256 floats: the scan's partial sums
-  static constexpr size_t SQ = TOT + 256 * 4;
+  static constexpr size_t TOT = BETA + C * 4;  // 512 floats: the scan's partial sums
+  static constexpr size_t SQ = TOT + 512 * 4;
   static constexpr size_t AB_ = SQ + (size_t)C * LDC * sizeof(OT);
   static constexpr size_t TB = AB_ + (size_t)C * LDAB * sizeof(OT);
   static constexpr size_t AD = TB + (size_t)C * LDT * sizeof(OT);
@@ -147,20 +150,35 @@ __device__ __forceinline__ void put_row16(T *p, const float *x) {
   put_row8(p + 8, x + 8);
 }
 
-// The chunk-local tiles that wave w forms: (I, J) pairs, its diagonal tile
-// (w, w) first, then two (waves 0, 1) or one (waves 2, 3) below the diagonal.
-constexpr int kCwTiles[4][3][2] = {{{0, 0}, {1, 0}, {2, 1}},
-                                   {{1, 1}, {2, 0}, {3, 2}},
-                                   {{2, 2}, {3, 0}, {0, 0}},
-                                   {{3, 3}, {3, 1}, {0, 0}}};
-constexpr int kCwTileCount[4] = {3, 3, 2, 2};
+// The chunk-local tiles that wave w forms: (I, J) pairs, a diagonal tile
+// (I = J) first.  Four waves: wave w its diagonal tile (w, w) and two (waves
+// 0, 1) or one (waves 2, 3) below the diagonal.  Eight waves: waves 0-3 the
+// diagonal tiles, waves 4-7 the six below.
+struct CwTiles {
+  int n;
+  int ij[3][2];
+};
+constexpr CwTiles kCwTiles4[4] = {{3, {{0, 0}, {1, 0}, {2, 1}}},
+                                  {3, {{1, 1}, {2, 0}, {3, 2}}},
+                                  {2, {{2, 2}, {3, 0}, {0, 0}}},
+                                  {2, {{3, 3}, {3, 1}, {0, 0}}}};
+constexpr CwTiles kCwTiles8[8] = {{1, {{0, 0}, {0, 0}, {0, 0}}}, {1, {{1, 1}, {0, 0}, {0, 0}}},
+                                  {1, {{2, 2}, {0, 0}, {0, 0}}}, {1, {{3, 3}, {0, 0}, {0, 0}}},
+                                  {2, {{1, 0}, {2, 1}, {0, 0}}}, {2, {{2, 0}, {3, 2}, {0, 0}}},
+                                  {1, {{3, 0}, {0, 0}, {0, 0}}}, {1, {{3, 1}, {0, 0}, {0, 0}}}};
 // Largest decay span (log2 units) of a diagonal tile formed by MFMA: column
 // factors up to 2^100, products of unit-norm rows far below FP32's 2^128.
 constexpr float kCwDiagSpan = 100.f;
 
+// Waves of the channel-wise chain: 8 (two per SIMD) where each wave's
+// registers fit in half a SIMD's file, else 4.
+template <int DK, int DV, bool F32>
+constexpr int kCwWaves = 8;
+
 template <bool SB, bool AB, int DK, int DV, bool F32, bool CK = false>
 __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int chain, char *smem) {
-  constexpr int NW = 4, NT = 256;
+  constexpr int NW = kCwWaves<DK, DV, F32>, NT = 64 * NW;
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   using L = CwLayout<DK, DV, F32, AB>;
   using IT = typename L::IT;
   using OT = typename L::OT;
@@ -177,6 +195,8 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
   constexpr int KQ_GROUPS = C * (DK / 8), KQ_PER = (KQ_GROUPS + NT - 1) / NT;
   constexpr int V_GROUPS = C * (DV / 8), V_PER = (V_GROUPS + NT - 1) / NT;
   constexpr int TPC = NT / DK, TOK = C / TPC;  // decay scan: threads per channel, tokens each
+  constexpr int G_GROUPS = C * (DK / 4), G_PER = (G_GROUPS + NT - 1) / NT;  // decays, 4 per load
+  static_assert(TPC * DK == NT && TPC * TOK == C, "whole channel columns per scan thread");
   constexpr float LOG2E = 1.4426950408889634f;
 
   IT *const Kh = reinterpret_cast<IT *>(smem + L::KH);
@@ -215,7 +235,7 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
   // Rows past the sequence's end re-read its last token; staging gives them
   // beta = 0 and no decay, so they reach neither M nor a stored O row.
   u32x4_t pk[KQ_PER][EW], pq[KQ_PER][EW], pv[V_PER][EW];
-  float pgc[TOK];             // log-decays of channel gch over this thread's tokens
+  float4 pg4[G_PER];          // log-decays, 4 channels of a token per entry
   float pb = 0.f;             // wave 0: write strength of token `lane`
   const int gch = tid % DK, gpart = tid / DK;
   const int64_t kq_row = (int64_t)p.H_qk * DK, v_row = (int64_t)p.H_v * DV;
@@ -245,9 +265,12 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
       for (int e = 0; e < EW; ++e) pv[i][e] = sv[e];
     }
 #pragma unroll
-    for (int j = 0; j < TOK; ++j) {
-      const int64_t t = std::min<int64_t>(t0 + gpart * TOK + j, last);
-      pgc[j] = decay ? p.g[(t * p.H_v + h) * DK + gch] : 0.f;
+    for (int i = 0; i < G_PER; ++i) {
+      const int gi = tid + NT * i;
+      if (G_GROUPS % NT != 0 && gi >= G_GROUPS) continue;
+      const int64_t t = std::min<int64_t>(t0 + gi / (DK / 4), last);
+      pg4[i] = decay ? *reinterpret_cast<const float4 *>(p.g + (t * p.H_v + h) * DK + (gi % (DK / 4)) * 4)
+                     : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     if (wave == 0) {
       const int64_t t = std::min<int64_t>(t0 + lane, last);
@@ -277,20 +300,32 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
       for (int e = 0; e < EW; ++e) dv[e] = pv[i][e];
     }
     if (wave == 0) bet[lane] = lane < n ? pb : 0.f;
-    // inclusive scan of the log2 decays of channel gch over this thread's
-    // tokens (rows past the end add nothing), and the part's total
+    // the log2 decays into G's rows (rows past the end decay nothing), then
+    // per channel an inclusive scan down the column: each thread its TOK
+    // tokens, then the totals of the parts above it
+#pragma unroll
+    for (int i = 0; i < G_PER; ++i) {
+      const int gi = tid + NT * i;
+      if (G_GROUPS % NT != 0 && gi >= G_GROUPS) continue;
+      const int r = gi / (DK / 4);
+      const float m = r < n ? LOG2E : 0.f;
+      reinterpret_cast<float4 *>(Gc + r * LDG)[gi % (DK / 4)] =
+          make_float4(pg4[i].x * m, pg4[i].y * m, pg4[i].z * m, pg4[i].w * m);
+    }
+    __syncthreads();
+    float part[TOK];
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < TOK; ++j) {
-      acc += gpart * TOK + j < n ? pgc[j] * LOG2E : 0.f;
-      pgc[j] = acc;
+      acc += Gc[(gpart * TOK + j) * LDG + gch];
+      part[j] = acc;
     }
     tot[gpart * DK + gch] = acc;
     __syncthreads();
     float pre = 0.f;
     for (int pp = 0; pp < gpart; ++pp) pre += tot[pp * DK + gch];
 #pragma unroll
-    for (int j = 0; j < TOK; ++j) Gc[(gpart * TOK + j) * LDG + gch] = pre + pgc[j];
+    for (int j = 0; j < TOK; ++j) Gc[(gpart * TOK + j) * LDG + gch] = pre + part[j];
   };
 
   // O rows of the chunk from the accumulator layout (the plain chain's store)
@@ -389,16 +424,19 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
     // 2: chunk-local products, one MFMA product per tile from fragments
     // scaled through the tile's reference token m; the wave's diagonal tile
     // only while its decay span allows (a wave-uniform decision)
+    const bool dwave = wave < 4;  // owns diagonal tile `wave`
     float span = 0.f;
-    for (int c = lane; c < DK; c += 64)
-      span = fmaxf(span, Gc[(16 * wave) * LDG + c] - Gc[(16 * wave + 15) * LDG + c]);
+    if (dwave)
+      for (int c = lane; c < DK; c += 64)
+        span = fmaxf(span, Gc[(16 * wave) * LDG + c] - Gc[(16 * wave + 15) * LDG + c]);
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) span = fmaxf(span, __shfl_xor(span, off));
     const bool diag_mfma = span <= kCwDiagSpan;
+    const CwTiles &tw = NW == 8 ? kCwTiles8[wave] : kCwTiles4[wave];
 #pragma unroll
     for (int ti = 0; ti < 3; ++ti) {
-      if (ti >= kCwTileCount[wave]) break;
-      const int I = kCwTiles[wave][ti][0], J = kCwTiles[wave][ti][1];
+      if (ti >= tw.n) break;
+      const int I = tw.ij[ti][0], J = tw.ij[ti][1];
       const bool dg = I == J;
       if (dg && !diag_mfma) continue;
       const int m = dg ? 16 * J : 16 * J + 15;
@@ -441,7 +479,7 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
     // 3: a diagonal tile whose span is too wide for the scaled product,
     // entry by entry: lane (r, cg) sums channels cg*8 + 32 j .. +8 of every
     // column s; the four cg lanes of a row then add
-    if (!diag_mfma) {
+    if (dwave && !diag_mfma) {
       const int b = wave, r = lane & 15, cg = lane >> 4;
       float accA[16], accP[16];
 #pragma unroll
@@ -494,7 +532,7 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
     // 16: column c); then the per-channel scalings of K and Q
     {
       const int b = wave, c = lane;
-      if (c < 16) {
+      if (dwave && c < 16) {
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
