@@ -146,7 +146,8 @@ typedef struct gdn_decode_args {
   const void *k;       /* [B, H_qk, d_k] act_dtype */
   const void *v;       /* [B, H_v, d_v] act_dtype */
   const float *g;      /* log-decay, [B, H_v] (GDN_DECAY_HEAD) or [B, H_v, d_k]
-                          (GDN_DECAY_CHANNEL); unused by linear and delta (may be NULL then) */
+                          (GDN_DECAY_CHANNEL, 16-byte aligned); unused by linear and delta
+                          (may be NULL then) */
   const float *beta;   /* [B, H_v] write strength (unused by linear and gated; may be NULL then) */
   void *state_pool;    /* [n_slots, H_v, d_k, d_v] state_dtype, read and written in place */
   const int32_t *read_slot;  /* [B] or NULL */

@@ -51,6 +51,8 @@ gdn_status check_decode(const gdn_decode_args *a) {
   if ((!a->read_slot || !a->write_slot) && a->n_slots < a->B) return GDN_ERR_SHAPE;
   if (!al16(a->q) || !al16(a->k) || !al16(a->v) || !al16(a->o) || !al16(a->state_pool))
     return GDN_ERR_ALIGN;
+  // channel-wise log-decays are read as 16-byte runs
+  if (a->decay_mode == GDN_DECAY_CHANNEL && !al16(a->g)) return GDN_ERR_ALIGN;
   return GDN_OK;
 }
 

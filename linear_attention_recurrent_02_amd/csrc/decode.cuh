@@ -214,6 +214,24 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
     load_run<AB, VEC>(p.v, (r * p.H_v + h) * DV + cv * VEC, t.vv);
   }
 
+  // the gates, issued before the state tile like q, k, v, so their
+  // exponentials overlap the state's loads: g per head, or (CW, g is
+  // [B, H_v, d_k]) the run of RPT log-decays as 16-byte loads (host-checked
+  // alignment), and beta
+  const bool decay = (p.rule & kRuleDecay) != 0;
+  const bool erase = (p.rule & kRuleErase) != 0;
+  constexpr int G4 = CW && ALL_LIVE && RPT % 4 == 0 ? RPT / 4 : 1;
+  float4 g4s[G4];
+  float g1 = 0.f;
+  if constexpr (CW && ALL_LIVE && RPT % 4 == 0) {
+    const float4 *gr4 = reinterpret_cast<const float4 *>(p.g + (r * p.H_v + h) * DK + row0);
+#pragma unroll
+    for (int i = 0; i < G4; ++i) g4s[i] = decay ? gr4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+  } else if constexpr (!CW) {
+    g1 = decay ? p.g[r * p.H_v + h] : 0.f;
+  }
+  const float b1 = erase ? p.beta[r * p.H_v + h] : 1.0f;
+
   // the state tile: RPT 16-byte vectors per thread (a1); 8-byte pieces and
   // one scale per row for the INT8 rows of an 8-bit tile
   if constexpr (Q8) {
@@ -265,21 +283,28 @@ __device__ __forceinline__ void decode_tile_load(const DecodeParams &p, int64_t 
 #pragma unroll
     for (int i = 0; i < RPT; ++i) t.m[i] = make_uint4(0u, 0u, 0u, 0u);
   }
-  const bool decay = (p.rule & kRuleDecay) != 0;
-  const bool erase = (p.rule & kRuleErase) != 0;
   if constexpr (CW) {
-    // g is [B, H_v, d_k]: this thread's rows' log-decays, through the
-    // hardware exponential (RPT of them per thread; expf measured 0.8%
-    // slower per B=512 launch)
+    // this thread's rows' decays, through the hardware exponential (expf
+    // measured 0.8% slower per B=512 launch); their loads were issued with
+    // q, k, v, ahead of the state
     t.a = 1.0f;
+    if constexpr (ALL_LIVE && RPT % 4 == 0) {
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      t.ar[i] = decay && (ALL_LIVE || row0 + i < DK)
-                    ? __expf(p.g[(r * p.H_v + h) * DK + row0 + i]) : 1.0f;
+      for (int i = 0; i < RPT; i += 4) {
+        const float4 g4 = g4s[i / 4];
+        t.ar[i] = __expf(g4.x); t.ar[i + 1] = __expf(g4.y);
+        t.ar[i + 2] = __expf(g4.z); t.ar[i + 3] = __expf(g4.w);
+      }
+    } else {
+      const float *gr = p.g + (r * p.H_v + h) * DK + row0;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        t.ar[i] = decay && (ALL_LIVE || row0 + i < DK) ? __expf(gr[i]) : 1.0f;
+    }
   } else {
-    t.a = decay ? expf(p.g[r * p.H_v + h]) : 1.0f;
+    t.a = decay ? expf(g1) : 1.0f;
   }
-  t.bw = erase ? p.beta[r * p.H_v + h] : 1.0f;
+  t.bw = b1;
 }
 
 // Phase 2 of a tile: the reductions over rows, the read-out (a4), the update

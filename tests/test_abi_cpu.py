@@ -78,6 +78,7 @@ def _call_decode(a):
     (dict(rule=4), RULE), (dict(rule=-1), RULE),
     (dict(state_dtype=3), DTYPE), (dict(act_dtype=-1), DTYPE), (dict(act_dtype=2), DTYPE),
     # the 8-bit state format: a multiple of 8 BF16 rows within d_k, none for other formats
+    (dict(decay_mode=1, g=FAKE + 4), ALIGN),  # channel-wise decays are read 16 bytes at a time
     (dict(state_dtype=2, state_bf16_rows=12), SHAPE), (dict(state_dtype=2, state_bf16_rows=136), SHAPE),
     (dict(state_dtype=2, state_bf16_rows=24), SHAPE),
     (dict(state_dtype=2, state_bf16_rows=-8), SHAPE), (dict(state_bf16_rows=8), SHAPE),

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from linear_attention_recurrent_02_amd import GdnError, gdn_decode, synthetic as syn
+from linear_attention_recurrent_02_amd import gdn_decode, synthetic as syn
 from gpu_util import f64, say, scaled_err, tol
 
 pytestmark = pytest.mark.gpu
@@ -67,18 +67,25 @@ def test_decode_cw_in_place_full_size():
            in_place=True)
 
 
-def test_mixed_refuses_channel_decay():
+def test_mixed_decode_half_with_channel_decay_equals_gdn_decode():
+    """gdn_mixed with a channel-wise decode half and an empty prefill half
+    runs gdn_decode's channel-wise tiles: the same outputs and state, bit
+    for bit."""
     from linear_attention_recurrent_02_amd import gdn as B
     q, k, v, _, beta = syn.token_inputs(504, 0, 2, 1, 1, 16, 16, torch.bfloat16)
     g = cw_gates(504, 2, 1, 16)
-    pool = torch.zeros((4, 1, 16, 16), dtype=torch.bfloat16, device=DEV)
-    da, _, dkeep = B.make_decode_args(q.to(DEV), k.to(DEV), v.to(DEV), g.to(DEV), beta.to(DEV),
-                                      pool)
+    pool0 = syn.state_pool(504, 0, 4, 1, 16, 16, torch.bfloat16, std=0.3)
+    p1, p2 = pool0.to(DEV), pool0.to(DEV)
+    args = [t.to(DEV) for t in (q, k, v, g, beta)]
+    da, o1, dkeep = B.make_decode_args(*args, p1)
     cu = torch.zeros(1, dtype=torch.int32, device=DEV)
     e = torch.zeros((0, 16), dtype=torch.bfloat16, device=DEV)
-    pa, _, pkeep = B.make_prefill_args(cu, e, e, e, pool, H_qk=1, H_v=1,
+    pa, _, pkeep = B.make_prefill_args(cu, e, e, e, p1, H_qk=1, H_v=1,
                                        g=torch.zeros((0, 1), device=DEV),
                                        beta=torch.zeros((0, 1), device=DEV))
     assert da.decay_mode == B.DECAY_CHANNEL
-    with pytest.raises(GdnError):
-        B.gdn_mixed(da, pa)
+    B.gdn_mixed(da, pa)
+    o2 = gdn_decode(*args, p2)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    assert torch.equal(p1.view(torch.int16), p2.view(torch.int16))
