@@ -368,6 +368,83 @@ __device__ __forceinline__ float wave_inclusive_sum(float x) {
 }
 
 // store a float into an operand buffer
+// BF16 rows of a K, Q or V tile in LDS (W values each), in one of three
+// layouts.  The chains read these tiles in three shapes: 8-byte row reads
+// (16 rows x 2 groups of 8 bytes per 32 lanes: Q M, K M), transposing 8-byte
+// reads (8 rows x 4 groups per 32 lanes: V, and K^T for the update of M) and
+// 16-byte row reads (S and P).
+//  - kRowsPadded: rows padded by 16 bytes.
+//  - kRowsXor (128-value rows): unpadded, 8-byte group j of row r at group
+//    j ^ sw(r), sw(r) = 4 (r mod 8) + 2 ((r / 8) mod 2).  sw's bits 1-4 are a
+//    bijection of r mod 16 and its bits 2-4 one of r mod 8, so both 8-byte
+//    shapes meet 64 distinct banks; sw is even, so a 16-byte piece stays
+//    whole.  The permutation reaches the bits that slab offsets change, so
+//    each read computes its own address.
+//  - kRowsSwap (128-value rows): padded by 32 bytes (a row starts 8 banks
+//    after the one before it, so eight rows cover the 64 banks) and, on
+//    every other block of 8 rows, the 16-byte pieces swapped in pairs (group
+//    j at j ^ 2), giving rows r and r + 8 the other half of their 8-bank
+//    window: both 8-byte shapes again meet 64 distinct banks.  The swap
+//    flips one bit that no slab or half-row offset touches, so a lane's reads
+//    are one base plus constant offsets.
+// Measured on gfx950 (one CU, 8 waves), LDS clocks per 512 bytes read, padded
+// / xor / swap: row 8.5 / 3.4 / 3.3, transposing 4.5 / 3.3 / 3.35, 16-byte
+// 9.1 / 8.4 / 8.5 per 1 KB.  In the chains, the pipelined one ran faster
+// with kRowsXor (0.770 against 0.786 ms for the varlen prefill), the
+// channel-wise one with kRowsSwap (1.483 against 1.525 ms padded; with
+// kRowsXor its per-read addresses spilled 248 bytes per lane).
+constexpr int kRowsPadded = 0, kRowsXor = 1, kRowsSwap = 2;
+template <int W, int KIND>
+struct LdsRows {
+  static_assert(KIND == kRowsPadded || W == 128, "the permuted layouts are of 128-value rows");
+  static constexpr int LD = KIND == kRowsSwap ? W + 16 : KIND == kRowsXor ? W : W + 8;  // elements
+  // element offset of (r, c), c a multiple of 4
+  __device__ static __forceinline__ int at(int r, int c) {
+    if constexpr (KIND == kRowsXor) return r * LD + (((c >> 2) ^ (4 * (r & 7) + 2 * ((r >> 3) & 1))) << 2) + (c & 3);
+    else if constexpr (KIND == kRowsSwap) return r * LD + (c ^ (8 * ((r >> 3) & 1)));
+    else return r * LD + c;
+  }
+  // (r0 + r, k0 + c) with r0 and k0 multiples of 16 and r < 16, c < 16
+  __device__ static __forceinline__ int at(int r0, int k0, int r, int c) {
+    if constexpr (KIND == kRowsXor) return at(r0 + r, k0 + c);
+    else return r0 * LD + k0 + at(r, c);  // only the lane's part is permuted
+  }
+};
+
+// BF16 operand fragments from LdsRows rows (R), in the layouts of load_frag,
+// load_afrag, load_afrag_t and load_col4.
+template <class R>
+__device__ __forceinline__ Frag<false> rows_frag(const uint16_t *base, int r0, int k0) {
+  const int l = threadIdx.x & 63;
+  return frag_of_bf16<false>(*reinterpret_cast<const uint4 *>(base + R::at(r0, k0, l & 15, 8 * (l >> 4))));
+}
+template <class R>
+__device__ __forceinline__ Frag<false> rows_afrag(const uint16_t *base, int r0, int k0) {
+  const int l = threadIdx.x & 63;
+  const uint2 a = *reinterpret_cast<const uint2 *>(base + R::at(r0, k0, l & 15, 4 * (l >> 4)));
+  const uint2 b = *reinterpret_cast<const uint2 *>(base + R::at(r0, k0 + 16, l & 15, 4 * (l >> 4)));
+  return frag_of_bf16<false>(make_uint4(a.x, a.y, b.x, b.y));
+}
+template <class R>
+__device__ __forceinline__ Frag<false> rows_afrag_t(const uint16_t *base, int r0, int k0) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
+  const uint16_t *const p = base + R::at(k0, r0, 4 * g + (s >> 2), 4 * (s & 3));
+  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * R::LD));
+  const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
+  return frag_of_bf16<false>(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
+}
+template <class R>
+__device__ __forceinline__ void rows_col4(const uint16_t *base, int r0, int c0, float *x) {
+  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
+  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4 *)(base + R::at(r0, c0, 4 * g + (s >> 2), 4 * (s & 3))));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) x[e] = bf16_to_f32((uint16_t)v[e]);
+}
+
 __device__ __forceinline__ void put(uint16_t *p, float x) { *p = f32_to_bf16(x); }
 __device__ __forceinline__ void put(float *p, float x) { *p = x; }
 __device__ __forceinline__ float get(const uint16_t *p) { return bf16_to_f32(*p); }

@@ -54,9 +54,28 @@ struct CwLayout {
   static constexpr int C = 64;
   static constexpr int DKP = DK < 32 ? 32 : DK;  // MFMA K-steps are 32 wide
   static constexpr int PADI = 16 / (int)sizeof(IT), PADO = 16 / (int)sizeof(OT);
-  static constexpr int LDK = DKP + PADI;   // K, Q rows (IT)
-  static constexpr int LDKO = DKP + PADO;  // K_g, Q_g, K_e rows (OT)
-  static constexpr int LDV = DV + PADI;    // V rows (IT)
+  // BF16 rows of 128 values (K, Q, K_g, Q_g, K_e at d_k = 128, V at d_v =
+  // 128) in the layout of LdsRows; other rows padded by 16 bytes
+  static constexpr bool SWK = !F32 && DKP == 128;
+  static constexpr bool SWV = !F32 && DV == 128;
+  using RS = LdsRows<128, kRowsSwap>;
+  static constexpr int LDK = SWK ? RS::LD : DKP + PADI;   // K, Q rows (IT)
+  static constexpr int LDKO = SWK ? RS::LD : DKP + PADO;  // K_g, Q_g, K_e rows (OT)
+  static constexpr int LDV = SWV ? RS::LD : DV + PADI;    // V rows (IT)
+  // element offsets of (r, c) in those rows, c a multiple of 4
+  __device__ static __forceinline__ int ak(int r, int c) {
+    if constexpr (SWK) return RS::at(r, c); else return r * LDK + c;
+  }
+  __device__ static __forceinline__ int ako(int r, int c) {
+    if constexpr (SWK) return RS::at(r, c); else return r * LDKO + c;
+  }
+  // (r0 + r, k0 + c) of K and Q rows, r0 and k0 multiples of 16
+  __device__ static __forceinline__ int ak(int r0, int k0, int r, int c) {
+    if constexpr (SWK) return RS::at(r0, k0, r, c); else return (r0 + r) * LDK + k0 + c;
+  }
+  __device__ static __forceinline__ int av(int r, int c) {
+    if constexpr (SWV) return RS::at(r, c); else return r * LDV + c;
+  }
   static constexpr int LDG = DKP + 4;      // G rows (float)
   static constexpr int LDC = C + PADO;     // L o P rows (OT)
   static constexpr int LDAB = C + PADO;    // -A rows (OT)
@@ -285,8 +304,8 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
       const int gi = tid + NT * i;
       if (KQ_GROUPS % NT != 0 && gi >= KQ_GROUPS) continue;
       const int r = gi / (DK / 8), d = (gi % (DK / 8)) * 8;
-      u32x4_t *dk = reinterpret_cast<u32x4_t *>(Kh + r * LDK + d);
-      u32x4_t *dq = reinterpret_cast<u32x4_t *>(Qh + r * LDK + d);
+      u32x4_t *dk = reinterpret_cast<u32x4_t *>(Kh + L::ak(r, d));
+      u32x4_t *dq = reinterpret_cast<u32x4_t *>(Qh + L::ak(r, d));
 #pragma unroll
       for (int e = 0; e < EW; ++e) { dk[e] = pk[i][e]; dq[e] = pq[i][e]; }
     }
@@ -295,7 +314,7 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
       const int gi = tid + NT * i;
       if (V_GROUPS % NT != 0 && gi >= V_GROUPS) continue;
       const int r = gi / (DV / 8), c = (gi % (DV / 8)) * 8;
-      u32x4_t *dv = reinterpret_cast<u32x4_t *>(Vh + r * LDV + c);
+      u32x4_t *dv = reinterpret_cast<u32x4_t *>(Vh + L::av(r, c));
 #pragma unroll
       for (int e = 0; e < EW; ++e) dv[e] = pv[i][e];
     }
@@ -362,8 +381,8 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
   if constexpr (DKP > DK) {
     for (int i = tid; i < C * (DKP - DK); i += NT) {
       const int r = i / (DKP - DK), c = DK + i % (DKP - DK);
-      put(Kh + r * LDK + c, 0.f);
-      put(Qh + r * LDK + c, 0.f);
+      put(Kh + L::ak(r, c), 0.f);
+      put(Qh + L::ak(r, c), 0.f);
       Gc[r * LDG + c] = 0.f;
     }
   }
@@ -454,9 +473,9 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
           fl[e] = fast_exp2(gl[e] - gm[e]);  // <= 1: r at or after m
           fr[e] = fast_exp2(gm[e] - gr[e]);  // <= 1 below the diagonal, <= 2^span on it
         }
-        const Frag<F32> fkl = scaled_frag<F32>(Kh + rl * LDK + ch, fl);
-        const Frag<F32> fql = scaled_frag<F32>(Qh + rl * LDK + ch, fl);
-        const Frag<F32> fkr = scaled_frag<F32>(Kh + rr * LDK + ch, fr);
+        const Frag<F32> fkl = scaled_frag<F32>(Kh + L::ak(16 * I, 32 * kk, lane & 15, 8 * (lane >> 4)), fl);
+        const Frag<F32> fql = scaled_frag<F32>(Qh + L::ak(16 * I, 32 * kk, lane & 15, 8 * (lane >> 4)), fl);
+        const Frag<F32> fkr = scaled_frag<F32>(Kh + L::ak(16 * J, 32 * kk, lane & 15, 8 * (lane >> 4)), fr);
         sa = mma<F32>(kk == 0 ? z : sa, fkl, fkr);
         pa = mma<F32>(kk == 0 ? z : pa, fql, fkr);
       }
@@ -486,13 +505,13 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
       for (int s = 0; s < 16; ++s) accA[s] = accP[s] = 0.f;
       for (int c0 = 8 * cg; c0 < DK; c0 += 32) {
         float kr[8], qr[8], gr[8];
-        load8(Kh + (16 * b + r) * LDK + c0, kr);
-        load8(Qh + (16 * b + r) * LDK + c0, qr);
+        load8(Kh + L::ak(16 * b + r, c0), kr);
+        load8(Qh + L::ak(16 * b + r, c0), qr);
         load8f(Gc + (16 * b + r) * LDG + c0, gr);
 #pragma unroll
         for (int s = 0; s < 16; ++s) {
           float ks[8], gs[8];
-          load8(Kh + (16 * b + s) * LDK + c0, ks);
+          load8(Kh + L::ak(16 * b + s, c0), ks);
           load8f(Gc + (16 * b + s) * LDG + c0, gs);
           float ta = 0.f, tp = 0.f;
 #pragma unroll
@@ -548,8 +567,8 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
     for (int i = tid; i < C * (DKP / 8); i += NT) {
       const int r = i / (DKP / 8), c = (i % (DKP / 8)) * 8;
       float kx[8], qx[8], g8[8], gl8[8];
-      load8(Kh + r * LDK + c, kx);
-      load8(Qh + r * LDK + c, qx);
+      load8(Kh + L::ak(r, c), kx);
+      load8(Qh + L::ak(r, c), qx);
       load8f(Gc + r * LDG + c, g8);
       load8f(Gc + (C - 1) * LDG + c, gl8);
       float kg[8], qg[8], ke[8];
@@ -560,9 +579,9 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
         qg[e] = qx[e] * eg;
         ke[e] = kx[e] * fast_exp2(gl8[e] - g8[e]);
       }
-      put_row8(Kg + r * LDKO + c, kg);
-      put_row8(Qg + r * LDKO + c, qg);
-      put_row8(Ke + r * LDKO + c, ke);
+      put_row8(Kg + L::ako(r, c), kg);
+      put_row8(Qg + L::ako(r, c), qg);
+      put_row8(Ke + L::ako(r, c), ke);
     }
     __syncthreads();
 
@@ -573,7 +592,8 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
       Frag<F32> fa[RING];
       Frag<F32> fm[NA];
       auto load_a = [&](int f) {
-        return load_afrag<F32>((f & 1) ? Kg : Qg, LDKO, 16 * ((f >> 1) & 3), 32 * (f >> 3));
+        if constexpr (L::SWK) return rows_afrag<typename L::RS>((f & 1) ? Kg : Qg, 16 * ((f >> 1) & 3), 32 * (f >> 3));
+        else return load_afrag<F32>((f & 1) ? Kg : Qg, LDKO, 16 * ((f >> 1) & 3), 32 * (f >> 3));
       };
 #pragma unroll
       for (int f = 0; f < RING - 1; ++f) fa[f] = load_a(f);
@@ -599,7 +619,10 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
       for (int tb = 0; tb < 4; ++tb) {
         float vv[NA][4];
 #pragma unroll
-        for (int ia = 0; ia < NA; ++ia) load_col4(Vh, LDV, 16 * tb, 16 * (wave * NA + ia), vv[ia]);
+        for (int ia = 0; ia < NA; ++ia) {
+          if constexpr (L::SWV) rows_col4<typename L::RS>(Vh, 16 * tb, 16 * (wave * NA + ia), vv[ia]);
+          else load_col4(Vh, LDV, 16 * tb, 16 * (wave * NA + ia), vv[ia]);
+        }
         const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * tb + rq);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
@@ -679,7 +702,10 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
         constexpr int NF = DKB * 2;  // (d_k block, token slab)
         constexpr int RK = RING < NF ? RING : NF;
         Frag<F32> fk[RK];
-        auto load_k = [&](int f) { return load_afrag_t<F32>(Ke, LDKO, 16 * (f >> 1), 32 * (f & 1)); };
+        auto load_k = [&](int f) {
+          if constexpr (L::SWK) return rows_afrag_t<typename L::RS>(Ke, 16 * (f >> 1), 32 * (f & 1));
+          else return load_afrag_t<F32>(Ke, LDKO, 16 * (f >> 1), 32 * (f & 1));
+        };
 #pragma unroll
         for (int f = 0; f < RK - 1; ++f) fk[f] = load_k(f);
 #pragma unroll

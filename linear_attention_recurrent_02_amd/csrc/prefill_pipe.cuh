@@ -28,37 +28,15 @@
 
 namespace gdn {
 
-// Rows of the chain's K, Q and V tiles in LDS.  A row of 128 BF16 values is
-// stored unpadded, its 8-byte column groups permuted per row: group j of row
-// r sits at group j ^ sw(r), sw(r) = 4 (r mod 8) + 2 ((r / 8) mod 2).  The
-// chain reads these tiles in three shapes: 8-byte row reads (16 rows x 2
-// groups per 32 lanes: Q M, K M), transposing 8-byte reads (8 rows x 4
-// groups per 32 lanes: V, and K^T for the update of M) and 16-byte row reads
-// (the producers' S and P).  With the permutation the first two meet 64
-// distinct banks (sw's bits 1-4 are a bijection of r mod 16, its bits 2-4
-// one of r mod 8); sw is even, so a 16-byte piece stays whole.  Measured on
-// gfx950 against 16-byte row padding, LDS clocks per 512 bytes read: 8.5 ->
-// 3.4 (row), 4.5 -> 3.3 (transposing), 9.1 -> 8.4 per 1 KB (16-byte).
-// Narrower rows keep the 16-byte padding.
-template <int W>
-struct PipeRows {
-  static constexpr bool SW = W == 128;
-  static constexpr int LD = SW ? W : W + 8;  // elements between rows
-  // element offset of (r, c), c a multiple of 4
-  __device__ static __forceinline__ int at(int r, int c) {
-    if constexpr (SW) return r * LD + (((c >> 2) ^ (4 * (r & 7) + 2 * ((r >> 3) & 1))) << 2) + (c & 3);
-    else return r * LD + c;
-  }
-};
-
 // LDS layout of the pipelined chain (byte offsets): two input sets (K, Q, V
 // rows and the six per-token gate arrays), two chunk-local sets of BF16 L o P
 // (scaled), -A and T_ii, and one FP32 diagonal block of A per producer wave.
 template <int DK, int DV>
 struct PipeLayout {
   using B = PrefillLayout<DK, DV, false>;
-  using RK = PipeRows<DK>;  // K and Q rows (the pipelined chain has d_k >= 32)
-  using RV = PipeRows<DV>;
+  // K and Q rows (the pipelined chain has d_k >= 32), V rows
+  using RK = LdsRows<DK, DK == 128 ? kRowsXor : kRowsPadded>;
+  using RV = LdsRows<DV, DV == 128 ? kRowsXor : kRowsPadded>;
   static constexpr int C = B::C;
   static constexpr size_t KH = 0;
   static constexpr size_t QH = KH + (size_t)C * RK::LD * 2;
@@ -78,41 +56,6 @@ struct PipeLayout {
   static constexpr size_t BYTES = ADIAG + 4 * ADIAG_WAVE;
   static_assert(SET % 16 == 0 && LOC % 16 == 0, "16-byte aligned sets");
 };
-
-// The pipelined chain's BF16 operand fragments from swizzled rows (R: a
-// PipeRows), in the layouts of prefill.cuh's load_frag, load_afrag,
-// load_afrag_t and load_col4.
-template <class R>
-__device__ __forceinline__ Frag<false> pipe_frag(const uint16_t *base, int r0, int k0) {
-  const int l = threadIdx.x & 63;
-  return frag_of_bf16<false>(*reinterpret_cast<const uint4 *>(base + R::at(r0 + (l & 15), k0 + 8 * (l >> 4))));
-}
-template <class R>
-__device__ __forceinline__ Frag<false> pipe_afrag(const uint16_t *base, int r0, int k0) {
-  const int l = threadIdx.x & 63, r = r0 + (l & 15), c = k0 + 4 * (l >> 4);
-  const uint2 a = *reinterpret_cast<const uint2 *>(base + R::at(r, c));
-  const uint2 b = *reinterpret_cast<const uint2 *>(base + R::at(r, c + 16));
-  return frag_of_bf16<false>(make_uint4(a.x, a.y, b.x, b.y));
-}
-template <class R>
-__device__ __forceinline__ Frag<false> pipe_afrag_t(const uint16_t *base, int r0, int k0) {
-  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
-  const int r = k0 + 4 * g + (s >> 2), c = r0 + 4 * (s & 3);
-  const s16x4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + R::at(r, c)));
-  const s16x4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + R::at(r + 16, c)));
-  const uint2 ulo = __builtin_bit_cast(uint2, lo), uhi = __builtin_bit_cast(uint2, hi);
-  return frag_of_bf16<false>(make_uint4(ulo.x, ulo.y, uhi.x, uhi.y));
-}
-template <class R>
-__device__ __forceinline__ void pipe_col4(const uint16_t *base, int r0, int c0, float *x) {
-  typedef __attribute__((address_space(3))) s16x4_t lds_s16x4;
-  const int l = threadIdx.x & 63, g = l >> 4, s = l & 15;
-  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (lds_s16x4 *)(base + R::at(r0 + 4 * g + (s >> 2), c0 + 4 * (s & 3))));
-#pragma unroll
-  for (int e = 0; e < 4; ++e) x[e] = bf16_to_f32((uint16_t)v[e]);
-}
 
 // Chunk-local tiles of producer wave b (waves 4 + b): its diagonal block b
 // (S_bb for A_bb and T_bb, and P_bb) and some tiles below the diagonal, from
@@ -303,7 +246,7 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
 #pragma unroll
       for (int f = 0; f < c.nf; ++f) {
         const int id = c.frag[f];
-        dst[f] = pipe_frag<RowK>((id & 1) ? Qh : Kh, 16 * (id >> 1), 32 * kk);
+        dst[f] = rows_frag<RowK>((id & 1) ? Qh : Kh, 16 * (id >> 1), 32 * kk);
       }
     };
     load_slab(0, fr[0]);
@@ -476,7 +419,7 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
         Frag<F32> fa[RING];
         Frag<F32> fm[NA];
         auto load_a = [&](int f) {
-          return pipe_afrag<RowK>((f & 1) ? Kh : Qh, 16 * ((f >> 1) & 3), 32 * (f >> 3));
+          return rows_afrag<RowK>((f & 1) ? Kh : Qh, 16 * ((f >> 1) & 3), 32 * (f >> 3));
         };
 #pragma unroll
         for (int f = 0; f < RING - 1; ++f) fa[f] = load_a(f);
@@ -508,7 +451,7 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
       for (int tb = 0; tb < 4; ++tb) {
         float vv[NA][4];
 #pragma unroll
-        for (int ia = 0; ia < NA; ++ia) pipe_col4<RowV>(Vh, 16 * tb, 16 * (cw * NA + ia), vv[ia]);
+        for (int ia = 0; ia < NA; ++ia) rows_col4<RowV>(Vh, 16 * tb, 16 * (cw * NA + ia), vv[ia]);
         const f32x4_t br = *reinterpret_cast<const f32x4_t *>(bet + 16 * tb + rq);
         const f32x4_t gr = *reinterpret_cast<const f32x4_t *>(gme + 16 * tb + rq);
 #pragma unroll
@@ -610,7 +553,7 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
         constexpr int NF = DKB * 2;  // (d_k block, token slab)
         constexpr int RK = RING < NF ? RING : NF;
         Frag<F32> fk[RK];
-        auto load_k = [&](int f) { return pipe_afrag_t<RowK>(Kh, 16 * (f >> 1), 32 * (f & 1)); };
+        auto load_k = [&](int f) { return rows_afrag_t<RowK>(Kh, 16 * (f >> 1), 32 * (f & 1)); };
 #pragma unroll
         for (int f = 0; f < RK - 1; ++f) fk[f] = load_k(f);
 #pragma unroll
