@@ -216,6 +216,17 @@ def conv_bytes_per_launch(B, H_qk, H_v, d_k, d_v, act_bytes=2):
     return B * C * act_bytes * (1 + 1 + 3 + 3) + B * H_v * 4 * 4 + C * 4 * 4
 
 
+def fused_bytes_per_launch(B, H_qk, H_v, d_k, d_v, act_bytes=2, state_bytes=2):
+    """Algorithmic bytes of one fused conv + decode launch: per (request, state
+    head) the state tile read and written and o written; per request the raw
+    q|k|v row in, the 3-token conv window read and written, a and b in; the
+    taps (FP32, 4 per channel) once."""
+    C = 2 * H_qk * d_k + H_v * d_v
+    state = 2 * B * H_v * d_k * d_v * state_bytes
+    return (state + B * H_v * d_v * act_bytes + B * C * act_bytes * (1 + 3 + 3)
+            + B * H_v * 2 * 4 + C * 4 * 4)
+
+
 def run_conv(args, torch, gdn, syn, layers):
     """The decode-side front-end for the same 48-layer B=512 batch: one
     gdn_conv_decode launch per layer (a 512-slot BF16 conv pool per layer, the
@@ -254,6 +265,23 @@ def run_conv(args, torch, gdn, syn, layers):
             if code:
                 raise gdn.GdnError("conv + decode", code)
 
+    # the same layers through the fused call: the decode's token inputs and
+    # the conv step's outputs left NULL
+    fused = []
+    for ca, _, da in convs:
+        fd = gdn.DecodeArgs.from_buffer_copy(da)
+        fd.q = fd.k = fd.v = fd.g = fd.beta = None
+        fc = gdn.ConvArgs.from_buffer_copy(ca)
+        fc.q_out = fc.k_out = fc.v_out = fc.g_out = fc.beta_out = None
+        fused.append((fd, fc))
+
+    def fused_step():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for fd, fc in fused:
+            code = lib.gdn_decode_conv(ctypes.byref(fd), ctypes.byref(fc), s)
+            if code:
+                raise gdn.GdnError("gdn_decode_conv", code)
+
     def timed(fn):
         fn()
         torch.cuda.synchronize()
@@ -277,15 +305,99 @@ def run_conv(args, torch, gdn, syn, layers):
 
     ms_conv = timed(conv_only)
     ms_step = timed(conv_then_decode)
+    ms_fused = timed(fused_step)
     L = len(convs)
     per_launch = conv_bytes_per_launch(B, Hqk, Hv, dk, dv)
     us = ms_conv * 1e3 / L
     gbps = per_launch / (us / 1e6) / 1e9
+    f_bytes = fused_bytes_per_launch(B, Hqk, Hv, dk, dv)
+    f_us = ms_fused * 1e3 / L
+    f_gbps = f_bytes / (f_us / 1e6) / 1e9
     return dict(workload="decode_b512_x48 front-end", kernel="conv_decode_kernel<bf16, 128>",
                 avg_launch_us=round(us, 2), per_launch_bytes=per_launch,
                 algorithmic_GBps=round(gbps, 1), hbm_frac=round(gbps / HBM_PEAK_GBPS, 4),
                 decode_with_conv_ms_per_step=round(ms_step, 4),
-                decode_with_conv_tokens_per_s=round(B / (ms_step / 1e3), 1))
+                decode_with_conv_tokens_per_s=round(B / (ms_step / 1e3), 1),
+                fused=dict(kernel="decode_conv_bf16_kernel<128, 128>",
+                           ms_per_step=round(ms_fused, 4),
+                           tokens_per_s=round(B / (ms_fused / 1e3), 1),
+                           avg_launch_us=round(f_us, 2), per_launch_bytes=f_bytes,
+                           algorithmic_GBps=round(f_gbps, 1),
+                           hbm_frac=round(f_gbps / HBM_PEAK_GBPS, 4),
+                           vs_separate=round(ms_step / ms_fused, 4)))
+
+
+def run_conv_small(args, torch, gdn, syn, B=16):
+    """The conv + decode step at a small batch (B = 16 requests, the decode
+    workload's heads, 48 layers with a B-slot state and conv pool each,
+    in-place slots in a seeded permutation): the separate calls against the
+    fused gdn_decode_conv, each layer sequence captured in one HIP graph.  At
+    this size every launch is short, so the saved launch is what counts."""
+    wl = syn.WORKLOADS["decode_b512_x48"]
+    Hqk, Hv, d = wl["H_qk"], wl["H_v"], wl["d_k"]
+    lib = gdn.load_library()
+    sep, fus, keep = [], [], []
+    for l in range(args.layers):
+        x = {kk: vv.cuda() for kk, vv in syn.frontend_inputs(wl["index"], 200 + l, B, Hqk, Hv, d,
+                                                             d, 4).items()}
+        pool = syn.state_pool(wl["index"], 200 + l, B, Hv, d, d, torch.bfloat16, on_device=True)
+        cpool = syn.conv_pool(wl["index"], 200 + l, B, 2 * Hqk * d + Hv * d, 4, torch.bfloat16,
+                              on_device=True)
+        slots = syn.distinct_slots(wl["index"], 200 + l, B, B, True)[0].cuda()
+        q = torch.empty((B, Hqk, d), dtype=torch.bfloat16, device="cuda")
+        k = torch.empty_like(q)
+        v = torch.empty((B, Hv, d), dtype=torch.bfloat16, device="cuda")
+        g = torch.empty((B, Hv), dtype=torch.float32, device="cuda")
+        b = torch.empty_like(g)
+        ca, ck = gdn.make_conv_args(x["q_raw"], x["k_raw"], x["v_raw"], cpool, H_qk=Hqk, H_v=Hv,
+                                    read_slot=slots, write_slot=slots, a_raw=x["a_raw"],
+                                    b_raw=x["b_raw"], conv_wq=x["conv_wq"], conv_wk=x["conv_wk"],
+                                    conv_wv=x["conv_wv"], outputs=(q, k, v, g, b))
+        da, _, dk = gdn.make_decode_args(q, k, v, g, b, pool, slots, slots)
+        fd = gdn.DecodeArgs.from_buffer_copy(da)
+        fd.q = fd.k = fd.v = fd.g = fd.beta = None
+        fc = gdn.ConvArgs.from_buffer_copy(ca)
+        fc.q_out = fc.k_out = fc.v_out = fc.g_out = fc.beta_out = None
+        sep.append((ca, da))
+        fus.append((fd, fc))
+        keep.append((x, pool, cpool, slots, ck, dk))
+
+    def separate():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for ca, da in sep:
+            code = lib.gdn_conv_decode(ctypes.byref(ca), s) or lib.gdn_decode(ctypes.byref(da), s)
+            if code:
+                raise gdn.GdnError("conv + decode", code)
+
+    def fused():
+        s = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        for fd, fc in fus:
+            code = lib.gdn_decode_conv(ctypes.byref(fd), ctypes.byref(fc), s)
+            if code:
+                raise gdn.GdnError("gdn_decode_conv", code)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            fn()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps
+
+    ms_sep, ms_fused = timed(separate), timed(fused)
+    return dict(workload=f"decode_b{B}_x{len(sep)} with the conv step", B=B,
+                separate_ms_per_step=round(ms_sep, 4), fused_ms_per_step=round(ms_fused, 4),
+                fused_tokens_per_s=round(B / (ms_fused / 1e3), 1),
+                fused_vs_separate=round(ms_sep / ms_fused, 4))
 
 
 def run_decode_cw(args, torch, gdn, syn, layers):
@@ -740,6 +852,7 @@ def main():
     conv = None
     if not args.no_conv:
         conv = run_conv(args, torch, gdn, syn, layers)
+        conv["small_batch"] = run_conv_small(args, torch, gdn, syn)
         log(f"conv: {conv}")
     decode_cw = None
     if not args.no_conv:

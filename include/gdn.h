@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 8
+#define GDN_ABI_VERSION 9
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -339,6 +339,27 @@ gdn_status gdn_frontend(const gdn_prefill_args *args, void *q_out, void *k_out, 
  * window slid by one token (the last conv_k - 1 raw inputs) is stored into
  * the write slot.  The outputs feed gdn_decode. */
 gdn_status gdn_conv_decode(const gdn_conv_args *args, void *stream);
+
+/* One decode token with the layer's short conv fused into the state update,
+ * one kernel for both ("Gated DeltaNet" glossary entry, Engineering details:
+ * Conv1D and GDN fused for decode).  It computes what gdn_conv_decode
+ * followed by gdn_decode computes, bit for bit, without writing q, k, v, g
+ * and beta to memory:
+ *  - decode: gdn_decode's arguments, except that q, k, v, g and beta must be
+ *    NULL (they come from the conv step) and decay_mode must be
+ *    GDN_DECAY_HEAD (the front-end makes one decay per head); state_dtype
+ *    BF16 or F32 (not the 8-bit format);
+ *  - conv: gdn_conv_decode's arguments (raw q, k, v, a_raw, b_raw, taps,
+ *    conv_pool with its read and write slots), except that q_out, k_out,
+ *    v_out, g_out and beta_out must be NULL; B, H_qk, H_v, d_k, d_v and
+ *    act_dtype equal to decode's.
+ * A request whose state or conv slot index is outside [-1, n_slots) is
+ * skipped entirely (no o, state or window is written) and sets
+ * GDN_DEVICE_BAD_SLOT in decode->status.  H_v / H_qk is at most 8, else
+ * GDN_ERR_UNSUPPORTED.  The state and conv slot contracts are gdn_decode's
+ * and gdn_conv_decode's. */
+gdn_status gdn_decode_conv(const gdn_decode_args *decode, const gdn_conv_args *conv,
+                           void *stream);
 
 /* After a prefill of B sequences packed by cu_seqlens: store each sequence's
  * last conv_k - 1 raw inputs into conv_pool[write_slot[s]], so that decode

@@ -231,6 +231,43 @@ gdn_status gdn_conv_decode(const gdn_conv_args *args, void *stream) {
   return gdn::launch_conv_decode(*args, static_cast<hipStream_t>(stream));
 }
 
+gdn_status gdn_decode_conv(const gdn_decode_args *decode, const gdn_conv_args *conv,
+                           void *stream) {
+  if (!decode || !conv) return GDN_ERR_NULL;
+  // the token's inputs come from the conv step: none may be passed
+  if (decode->q || decode->k || decode->v || decode->g || decode->beta) return GDN_ERR_UNSUPPORTED;
+  if (conv->q_out || conv->k_out || conv->v_out || conv->g_out || conv->beta_out)
+    return GDN_ERR_UNSUPPORTED;
+  // every other check of the two calls, with the raw inputs standing in for
+  // the pointers the fused kernel does not take
+  gdn_decode_args d = *decode;
+  d.q = d.k = d.v = conv->q;
+  d.g = d.beta = conv->a_raw;
+  gdn_conv_args c = *conv;
+  c.q_out = c.k_out = c.v_out = const_cast<void *>(conv->q);
+  c.g_out = c.beta_out = const_cast<float *>(conv->a_raw);
+  gdn_status st = check_decode(&d);
+  if (st != GDN_OK) return st;
+  st = check_conv(&c, true);
+  if (st != GDN_OK) return st;
+  if (conv->B != decode->B || conv->H_qk != decode->H_qk || conv->H_v != decode->H_v ||
+      conv->d_k != decode->d_k || conv->d_v != decode->d_v)
+    return GDN_ERR_SHAPE;
+  if (conv->act_dtype != decode->act_dtype) return GDN_ERR_DTYPE;
+  if (decode->state_dtype == GDN_Q8 || decode->decay_mode != GDN_DECAY_HEAD)
+    return GDN_ERR_UNSUPPORTED;
+  const int group = decode->H_v / decode->H_qk;
+  if (group > gdn::decode_conv_max_group() ||
+      gdn::decode_conv_stage_threads(decode->d_k, decode->d_v, group,
+                                     decode->act_dtype == GDN_BF16) >
+          gdn::decode_conv_block_threads(decode->d_k, decode->d_v,
+                                         decode->state_dtype == GDN_BF16))
+    return GDN_ERR_UNSUPPORTED;
+  if ((int64_t)decode->B * decode->H_qk > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;
+  if (decode->B == 0) return GDN_OK;
+  return gdn::launch_decode_conv(*decode, *conv, static_cast<hipStream_t>(stream));
+}
+
 gdn_status gdn_conv_store(const gdn_conv_args *args, void *stream) {
   gdn_status st = check_conv(args, false);
   if (st != GDN_OK || args->B == 0) return st;

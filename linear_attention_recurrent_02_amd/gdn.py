@@ -108,6 +108,8 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_conv_decode.argtypes = [ctypes.POINTER(ConvArgs), _P]
     lib.gdn_conv_store.restype = _I32
     lib.gdn_conv_store.argtypes = [ctypes.POINTER(ConvArgs), _P]
+    lib.gdn_decode_conv.restype = _I32
+    lib.gdn_decode_conv.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ConvArgs), _P]
     lib.gdn_conv_slot_bytes.restype = ctypes.c_size_t
     lib.gdn_conv_slot_bytes.argtypes = [_I32, _I32, _I32, _I32, _I32, _I32]
     lib.gdn_validate_slots.restype = _I32
@@ -652,6 +654,51 @@ def gdn_conv_decode(q_raw, k_raw, v_raw, conv_pool, read_slot=None, write_slot=N
     if code:
         raise GdnError("gdn_conv_decode", code)
     return q, k, v, g, beta
+
+
+def make_decode_conv_args(q_raw, k_raw, v_raw, conv_pool, state_pool, *, H_qk, H_v, conv_wq,
+                          conv_wk, conv_wv, a_raw, b_raw, read_slot=None, write_slot=None,
+                          conv_read_slot=None, conv_write_slot=None, o=None,
+                          rule="gated_delta", scale=1.0, eps=1e-6, status=None):
+    """Build the (DecodeArgs, ConvArgs) pair of gdn_decode_conv: the decode's
+    token inputs are NULL (the conv step makes them) and so are the conv
+    step's outputs.  Returns (decode_args, conv_args, o, keepalive)."""
+    _need(q_raw, "q_raw", dtypes=_ACT)
+    B = q_raw.shape[0]
+    d_k = _row_dim(q_raw, "q_raw", B, H_qk)
+    d_v = _row_dim(v_raw, "v_raw", B, H_v)
+    _need(k_raw, "k_raw", dtype=q_raw.dtype, shape=q_raw.shape)
+    _need(v_raw, "v_raw", dtype=q_raw.dtype)
+    # the decode's checks, with views of the raw inputs and the raw gates standing in
+    d, o, keep_d = make_decode_args(q_raw.reshape(B, H_qk, d_k), k_raw.reshape(B, H_qk, d_k),
+                                    v_raw.reshape(B, H_v, d_v), a_raw, b_raw, state_pool,
+                                    read_slot, write_slot, o, rule=rule, scale=scale,
+                                    status=status)
+    d.q = d.k = d.v = d.g = d.beta = None
+    c, keep_c = make_conv_args(q_raw, k_raw, v_raw, conv_pool, H_qk=H_qk, H_v=H_v,
+                               read_slot=conv_read_slot, write_slot=conv_write_slot, a_raw=a_raw,
+                               b_raw=b_raw, conv_wq=conv_wq, conv_wk=conv_wk, conv_wv=conv_wv,
+                               eps=eps)
+    return d, c, o, (keep_d, keep_c)
+
+
+def gdn_decode_conv(q_raw, k_raw, v_raw, conv_pool, state_pool, *, H_qk, H_v, conv_wq, conv_wk,
+                    conv_wv, a_raw, b_raw, read_slot=None, write_slot=None, conv_read_slot=None,
+                    conv_write_slot=None, o=None, rule="gated_delta", scale=1.0, eps=1e-6,
+                    status=None, stream=None):
+    """One decode token with the conv step fused in: raw q, k [B, H_qk*d_k]
+    and v [B, H_v*d_v], the conv window from conv_pool and the state from
+    state_pool (both updated through their slots).  Returns o [B, H_v, d_v];
+    bitwise gdn_conv_decode followed by gdn_decode."""
+    d, c, o, keep = make_decode_conv_args(
+        q_raw, k_raw, v_raw, conv_pool, state_pool, H_qk=H_qk, H_v=H_v, conv_wq=conv_wq,
+        conv_wk=conv_wk, conv_wv=conv_wv, a_raw=a_raw, b_raw=b_raw, read_slot=read_slot,
+        write_slot=write_slot, conv_read_slot=conv_read_slot, conv_write_slot=conv_write_slot,
+        o=o, rule=rule, scale=scale, eps=eps, status=status)
+    code = load_library().gdn_decode_conv(ctypes.byref(d), ctypes.byref(c), _stream(stream))
+    if code:
+        raise GdnError("gdn_decode_conv", code)
+    return o
 
 
 def gdn_conv_store(cu_seqlens, q_raw, k_raw, v_raw, conv_pool, write_slot=None, *, H_qk, H_v,

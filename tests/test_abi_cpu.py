@@ -28,7 +28,7 @@ def test_struct_layout_matches():
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
     assert lib.gdn_sizeof_conv_args() == ctypes.sizeof(B.ConvArgs)
-    assert gdn.gdn_abi_version() == 8
+    assert gdn.gdn_abi_version() == 9
 
 
 def test_state_bytes_against_the_pages():
@@ -337,3 +337,44 @@ def test_conv_store_validation_and_empty():
     assert lib.gdn_conv_decode(ctypes.byref(_conv_args(B=0, q=None, conv_pool=None)), None) == OK
     assert lib.gdn_conv_store(ctypes.byref(_conv_args(B=0, cu_seqlens=None)), None) == OK
     assert lib.gdn_conv_store(ctypes.byref(_conv_args(B=0, n_tokens=5)), None) == SHAPE
+
+
+def _fused_args(dover=None, cover=None):
+    """gdn_decode_conv's pair: the decode's token inputs and the conv step's
+    outputs NULL, everything else as for the separate calls."""
+    d = _decode_args(**{"q": None, "k": None, "v": None, "g": None, "beta": None,
+                        "d_k": 64, "d_v": 64, **(dover or {})})
+    c = _conv_args(**{"q_out": None, "k_out": None, "v_out": None, "g_out": None,
+                      "beta_out": None, **(cover or {})})
+    return d, c
+
+
+@pytest.mark.parametrize("dover,cover,code", [
+    # the fused call takes no token inputs and writes no conv outputs
+    (dict(q=FAKE), None, UNSUP), (dict(beta=FAKE), None, UNSUP),
+    (None, dict(v_out=FAKE), UNSUP), (None, dict(g_out=FAKE), UNSUP),
+    # the halves must describe one layer
+    (dict(B=5), None, SHAPE), (None, dict(H_v=8), SHAPE), (None, dict(d_v=32), SHAPE),
+    (None, dict(act_dtype=0), DTYPE),
+    # per-head decay only (the front-end makes one decay per head); no 8-bit state
+    (dict(decay_mode=1), None, UNSUP), (dict(state_dtype=2, state_bf16_rows=32), None, UNSUP),
+    # every check of each separate call still applies
+    (dict(rule=7), None, RULE), (dict(state_pool=None), None, NULL), (dict(o=FAKE + 4), None, ALIGN),
+    (None, dict(conv_pool=None), NULL), (None, dict(a_raw=None), NULL),
+    (None, dict(conv_wq=FAKE + 4), ALIGN), (None, dict(eps=-1.0), SHAPE),
+    # more than 8 state heads per q/k head
+    (dict(H_qk=1, H_v=16), dict(H_qk=1, H_v=16), UNSUP),
+])
+def test_decode_conv_validation(dover, cover, code):
+    lib = gdn.load_library()
+    d, c = _fused_args(dover, cover)
+    assert lib.gdn_decode_conv(ctypes.byref(d), ctypes.byref(c), None) == code
+
+
+def test_decode_conv_null_and_empty():
+    lib = gdn.load_library()
+    d, c = _fused_args()
+    assert lib.gdn_decode_conv(None, ctypes.byref(c), None) == NULL
+    assert lib.gdn_decode_conv(ctypes.byref(d), None, None) == NULL
+    d, c = _fused_args(dict(B=0, state_pool=None, o=None), dict(B=0, q=None, conv_pool=None))
+    assert lib.gdn_decode_conv(ctypes.byref(d), ctypes.byref(c), None) == OK
