@@ -516,6 +516,40 @@ def run_decode_q8(args, torch, gdn, syn, layers, n_hi=32):
                 algorithmic_GBps=round(gbps, 1), hbm_frac=round(gbps / HBM_PEAK_GBPS, 4))
 
 
+def run_convert(args, torch, gdn, syn, layers, n_hi=32):
+    """gdn_state_convert on the decode workload's shape: the 512 BF16 slots of
+    a layer's pool stored into an 8-bit pool (n_hi BF16 rows of 128), and back
+    into BF16; each direction 20 calls timed with HIP events after 3."""
+    wl = syn.WORKLOADS["decode_b512_x48"]
+    Hv, dk, dv, n = wl["H_v"], wl["d_k"], wl["d_v"], wl["n_slots"]
+    src = layers[0][1][5]
+    q8 = torch.zeros((n, Hv, gdn.gdn_state_q8_bytes(1, dk, dv, n_hi)), dtype=torch.uint8,
+                     device="cuda")
+    b16 = torch.empty_like(src)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 20 * 1e3
+
+    us_in = timed(lambda: gdn.gdn_state_convert(src, q8, dst_bf16_rows=n_hi))
+    us_out = timed(lambda: gdn.gdn_state_convert(q8, b16, src_bf16_rows=n_hi))
+    bf16_b = n * Hv * dk * dv * 2
+    q8_b = n * Hv * (n_hi * dv * 2 + (dk - n_hi) * (dv + 4))
+    gb = lambda b, us: round(b / (us / 1e6) / 1e9, 1)
+    return dict(workload=f"{n} slots x {Hv} heads of {dk}x{dv}", n_hi=n_hi,
+                to_q8_us=round(us_in, 2), to_q8_GBps=gb(bf16_b + q8_b, us_in),
+                from_q8_us=round(us_out, 2), from_q8_GBps=gb(bf16_b + q8_b, us_out),
+                bytes_moved=bf16_b + q8_b)
+
+
 def prefill_useful_flops(lengths, H_v, d_k, d_v, C=64):
     """Useful flops of the chunked recurrence (per chunk of n tokens and head):
     K K^T and Q K^T (lower triangle incl. diagonal), the triangular solve,
@@ -858,10 +892,12 @@ def main():
     if not args.no_conv:
         decode_cw = run_decode_cw(args, torch, gdn, syn, layers)
         log(f"decode, channel-wise decay: {decode_cw}")
-    decode_q8 = None
+    decode_q8 = state_convert = None
     if not args.no_q8:
         decode_q8 = [run_decode_q8(args, torch, gdn, syn, layers, n_hi) for n_hi in (32, 0)]
         log(f"decode, 8-bit state: {decode_q8}")
+        state_convert = run_convert(args, torch, gdn, syn, layers)
+        log(f"state convert: {state_convert}")
         torch.cuda.empty_cache()
     prefill = None
     if not args.no_prefill:
@@ -913,6 +949,7 @@ def main():
         "conv_decode": conv,
         "decode_channel_decay": decode_cw,
         "decode_q8_state": decode_q8,
+        "state_convert": state_convert,
         "prefill": prefill,
         "prefill_channel_decay": prefill_cw,
         "mixed": mixed,

@@ -68,7 +68,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 9
+#define GDN_ABI_VERSION 10
 
 typedef enum gdn_rule {
   GDN_RULE_LINEAR = 0,
@@ -294,6 +294,34 @@ typedef struct gdn_conv_args {
                           request and set GDN_DEVICE_BAD_SLOT */
 } gdn_conv_args;
 
+/* State tiles copied from one pool to another whose storage format may
+ * differ: FP32, BF16, or the 8-bit format (GDN_Q8, the DAMP-like mixed
+ * precision of "Seven Architectures ...", ONNX LinearAttention / FlashInfer
+ * section).  A prefill stores BF16 or FP32 states, so a prefilled state
+ * enters an 8-bit decode pool through this call, and an 8-bit checkpoint is
+ * read back through it before a prefill resumes ("Recurrent state" glossary
+ * entry, Why it matters: checkpoint slots).  For each pair i and head h:
+ * dst_pool[dst_slot[i], h] = the tile src_pool[src_slot[i], h] represents,
+ * stored in dst_dtype: BF16 rounds to nearest even; an 8-bit tile keeps its
+ * first dst_bf16_rows rows in BF16 and stores every other row as INT8 codes
+ * rne(x * (127 / rowmax)) clamped to +-127 with scale rowmax / 127, each step
+ * in binary32 (the rule gdn_decode stores with); an 8-bit row is read as
+ * code * scale in binary32. */
+typedef struct gdn_convert_args {
+  int32_t n;                       /* slot pairs, >= 0 */
+  int32_t H_v, d_k, d_v;           /* heads per slot and tile shape (16, 32, 64 or 128) */
+  int32_t src_dtype, dst_dtype;    /* GDN_F32, GDN_BF16 or GDN_Q8 */
+  int32_t src_bf16_rows;           /* src GDN_Q8: BF16 rows per tile (gdn_state_q8_bytes rules), else 0 */
+  int32_t dst_bf16_rows;           /* dst GDN_Q8: the same for the destination, else 0 */
+  int64_t src_n_slots, dst_n_slots;
+  const void *src_pool;            /* [src_n_slots, H_v, tile], 16-byte aligned */
+  void *dst_pool;                  /* [dst_n_slots, H_v, tile], 16-byte aligned */
+  const int32_t *src_slot;         /* [n] device or NULL (pair i reads slot i); -1 = a zero state */
+  const int32_t *dst_slot;         /* [n] device or NULL (pair i writes slot i); -1 = not stored */
+  uint32_t *status;                /* optional device word: an index outside [-1, n_slots)
+                                      skips the pair and sets GDN_DEVICE_BAD_SLOT */
+} gdn_convert_args;
+
 /* Bytes of one slot (all H_v heads of one request, one layer).  The ONNX
  * LinearAttention section of "Seven Architectures ..." sizes 64 heads of
  * 128 x 128 at 16 bits as 2 MB per request. */
@@ -361,6 +389,14 @@ gdn_status gdn_conv_decode(const gdn_conv_args *args, void *stream);
 gdn_status gdn_decode_conv(const gdn_decode_args *decode, const gdn_conv_args *conv,
                            void *stream);
 
+/* gdn_convert_args' copy.  A pair may read and write the same slot of one
+ * pool; pairs follow the write-slot contract among themselves (no slot
+ * written by two pairs or read by one pair and written by another).  Host
+ * validation only: GDN_ERR_DTYPE, _SHAPE (an 8-bit BF16-row count that
+ * gdn_state_q8_bytes refuses, NULL slot arrays with fewer slots than pairs),
+ * _NULL, _ALIGN. */
+gdn_status gdn_state_convert(const gdn_convert_args *args, void *stream);
+
 /* After a prefill of B sequences packed by cu_seqlens: store each sequence's
  * last conv_k - 1 raw inputs into conv_pool[write_slot[s]], so that decode
  * continues its conv window.  Rows before a sequence's first token come from
@@ -423,6 +459,7 @@ int32_t gdn_abi_version(void);
 size_t gdn_sizeof_decode_args(void);
 size_t gdn_sizeof_prefill_args(void);
 size_t gdn_sizeof_conv_args(void);
+size_t gdn_sizeof_convert_args(void);
 
 #ifdef __cplusplus
 }

@@ -268,6 +268,28 @@ gdn_status gdn_decode_conv(const gdn_decode_args *decode, const gdn_conv_args *c
   return gdn::launch_decode_conv(*decode, *conv, static_cast<hipStream_t>(stream));
 }
 
+gdn_status gdn_state_convert(const gdn_convert_args *a, void *stream) {
+  if (!a) return GDN_ERR_NULL;
+  if (a->n < 0 || a->src_n_slots < 0 || a->dst_n_slots < 0) return GDN_ERR_SHAPE;
+  auto kind_ok = [](int32_t k) { return k == GDN_F32 || k == GDN_BF16 || k == GDN_Q8; };
+  if (!kind_ok(a->src_dtype) || !kind_ok(a->dst_dtype)) return GDN_ERR_DTYPE;
+  if (a->H_v <= 0 || a->d_k <= 0 || a->d_v <= 0) return GDN_ERR_SHAPE;
+  if (!supported_d(a->d_k) || !supported_d(a->d_v)) return GDN_ERR_UNSUPPORTED;
+  // BF16 rows: a valid count for an 8-bit side, none otherwise
+  auto rows_ok = [&](int32_t kind, int32_t rows) {
+    return kind == GDN_Q8 ? gdn_state_q8_bytes(1, a->d_k, a->d_v, rows) != 0 : rows == 0;
+  };
+  if (!rows_ok(a->src_dtype, a->src_bf16_rows) || !rows_ok(a->dst_dtype, a->dst_bf16_rows))
+    return GDN_ERR_SHAPE;
+  if ((int64_t)a->n * a->H_v > 0x7fffffffLL) return GDN_ERR_UNSUPPORTED;  // grid size
+  if (a->n == 0) return GDN_OK;
+  if ((!a->src_slot && a->src_n_slots < a->n) || (!a->dst_slot && a->dst_n_slots < a->n))
+    return GDN_ERR_SHAPE;
+  if (!a->src_pool || !a->dst_pool) return GDN_ERR_NULL;
+  if (!al16(a->src_pool) || !al16(a->dst_pool)) return GDN_ERR_ALIGN;
+  return gdn::launch_state_convert(*a, static_cast<hipStream_t>(stream));
+}
+
 gdn_status gdn_conv_store(const gdn_conv_args *args, void *stream) {
   gdn_status st = check_conv(args, false);
   if (st != GDN_OK || args->B == 0) return st;
@@ -367,5 +389,6 @@ int32_t gdn_abi_version(void) { return GDN_ABI_VERSION; }
 size_t gdn_sizeof_decode_args(void) { return sizeof(gdn_decode_args); }
 size_t gdn_sizeof_prefill_args(void) { return sizeof(gdn_prefill_args); }
 size_t gdn_sizeof_conv_args(void) { return sizeof(gdn_conv_args); }
+size_t gdn_sizeof_convert_args(void) { return sizeof(gdn_convert_args); }
 
 }  // extern "C"

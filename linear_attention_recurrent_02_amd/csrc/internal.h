@@ -25,6 +25,7 @@ gdn_status launch_decode_conv(const gdn_decode_args &d, const gdn_conv_args &c, 
 int decode_conv_stage_threads(int d_k, int d_v, int group, bool act_bf16);
 int decode_conv_max_group();
 int decode_conv_block_threads(int d_k, int d_v, bool state_bf16);
+gdn_status launch_state_convert(const gdn_convert_args &a, hipStream_t stream);
 gdn_status launch_prefill_conv_store(const gdn_prefill_args &a, hipStream_t stream);
 int64_t conv_grid_rows(const gdn_conv_args &a);  // blockIdx.y extent of the conv kernels
 

@@ -204,7 +204,7 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
   using AT = typename Elem<AB>::T;
   static_assert(sizeof(AT) == sizeof(IT), "inputs are staged in the activation dtype");
   constexpr int C = L::C, DKP = L::DKP;
-  constexpr int LDK = L::LDK, LDKO = L::LDKO, LDV = L::LDV, LDG = L::LDG, LDC = L::LDC;
+  constexpr int LDKO = L::LDKO, LDV = L::LDV, LDG = L::LDG, LDC = L::LDC;
   constexpr int NKB = DKP / 32;    // MFMA K-steps over d_k
   constexpr int DKB = DK / 16;     // 16-row blocks of d_k
   constexpr int DVB = DV / 16;     // 16-column blocks of d_v

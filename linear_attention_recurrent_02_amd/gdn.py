@@ -64,6 +64,14 @@ class ConvArgs(ctypes.Structure):
                 ("status", _P)]
 
 
+class ConvertArgs(ctypes.Structure):
+    _fields_ = [("n", _I32), ("H_v", _I32), ("d_k", _I32), ("d_v", _I32),
+                ("src_dtype", _I32), ("dst_dtype", _I32), ("src_bf16_rows", _I32),
+                ("dst_bf16_rows", _I32), ("src_n_slots", _I64), ("dst_n_slots", _I64),
+                ("src_pool", _P), ("dst_pool", _P), ("src_slot", _P), ("dst_slot", _P),
+                ("status", _P)]
+
+
 class GdnError(RuntimeError):
     def __init__(self, fn: str, code: int):
         self.code = code
@@ -108,6 +116,10 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_conv_decode.argtypes = [ctypes.POINTER(ConvArgs), _P]
     lib.gdn_conv_store.restype = _I32
     lib.gdn_conv_store.argtypes = [ctypes.POINTER(ConvArgs), _P]
+    lib.gdn_state_convert.restype = _I32
+    lib.gdn_state_convert.argtypes = [ctypes.POINTER(ConvertArgs), _P]
+    lib.gdn_sizeof_convert_args.restype = ctypes.c_size_t
+    lib.gdn_sizeof_convert_args.argtypes = []
     lib.gdn_decode_conv.restype = _I32
     lib.gdn_decode_conv.argtypes = [ctypes.POINTER(DecodeArgs), ctypes.POINTER(ConvArgs), _P]
     lib.gdn_conv_slot_bytes.restype = ctypes.c_size_t
@@ -123,7 +135,8 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_sizeof_conv_args.restype = ctypes.c_size_t
     if lib.gdn_sizeof_decode_args() != ctypes.sizeof(DecodeArgs) or \
             lib.gdn_sizeof_prefill_args() != ctypes.sizeof(PrefillArgs) or \
-            lib.gdn_sizeof_conv_args() != ctypes.sizeof(ConvArgs):
+            lib.gdn_sizeof_conv_args() != ctypes.sizeof(ConvArgs) or \
+            lib.gdn_sizeof_convert_args() != ctypes.sizeof(ConvertArgs):
         raise RuntimeError("libgdn.so argument-struct layout differs from this binding")
     _lib = lib
     return lib
@@ -699,6 +712,67 @@ def gdn_decode_conv(q_raw, k_raw, v_raw, conv_pool, state_pool, *, H_qk, H_v, co
     if code:
         raise GdnError("gdn_decode_conv", code)
     return o
+
+
+def _pool_kind(pool, name, bf16_rows):
+    """Storage format of a state pool tensor: BF16, FP32, or the 8-bit format
+    (uint8 [n_slots, H_v, tile bytes], which needs its BF16-row count)."""
+    if pool.dtype == torch.uint8:
+        if bf16_rows is None:
+            raise ValueError(f"an 8-bit {name} (uint8) needs its bf16_rows")
+        if pool.dim() != 3:
+            raise ValueError(f"{name} must be [n_slots, H_v, tile bytes], got {tuple(pool.shape)}")
+        return Q8, int(bf16_rows)
+    _need(pool, name, dtypes=_ACT)
+    if pool.dim() != 4:
+        raise ValueError(f"{name} must be [n_slots, H_v, d_k, d_v], got {tuple(pool.shape)}")
+    if bf16_rows:
+        raise ValueError(f"bf16_rows applies to an 8-bit (uint8) {name} only")
+    return _dtype_code(pool), 0
+
+
+def gdn_state_convert(src_pool, dst_pool, src_slot=None, dst_slot=None, *, d_k=None, d_v=None,
+                      src_bf16_rows=None, dst_bf16_rows=None, status=None, stream=None):
+    """dst_pool[dst_slot[i]] = the states src_pool[src_slot[i]] represents, in
+    dst_pool's format (torch.bfloat16 / torch.float32 [n, H_v, d_k, d_v], or
+    the 8-bit format as uint8 [n, H_v, tile bytes] with its bf16_rows)."""
+    sk, sh = _pool_kind(src_pool, "src_pool", src_bf16_rows)
+    dk_, dh = _pool_kind(dst_pool, "dst_pool", dst_bf16_rows)
+    for pool in (src_pool, dst_pool):
+        if pool.dim() == 4:
+            d_k = pool.shape[2] if d_k is None else d_k
+            d_v = pool.shape[3] if d_v is None else d_v
+    if d_k is None or d_v is None:
+        raise ValueError("two 8-bit pools need d_k and d_v")
+    H_v = src_pool.shape[1]
+    for pool, kind, rows, name in ((src_pool, sk, sh, "src_pool"), (dst_pool, dk_, dh, "dst_pool")):
+        want = (H_v, gdn_state_q8_bytes(1, d_k, d_v, rows)) if kind == Q8 else (H_v, d_k, d_v)
+        if tuple(pool.shape[1:]) != tuple(want):
+            raise ValueError(f"{name} must be [n_slots, {', '.join(map(str, want))}], "
+                             f"got {tuple(pool.shape)}")
+    n = None
+    for t, name in ((src_slot, "src_slot"), (dst_slot, "dst_slot")):
+        if t is not None:
+            _need(t, name, dtype=torch.int32)
+            if t.dim() != 1 or (n is not None and t.shape[0] != n):
+                raise ValueError("src_slot and dst_slot must be [n] int32 of one length")
+            n = t.shape[0]
+    if n is None:
+        n = min(src_pool.shape[0], dst_pool.shape[0])
+    _status(status)
+    for name, t in (("src_pool", src_pool), ("dst_pool", dst_pool), ("src_slot", src_slot),
+                    ("dst_slot", dst_slot), ("status", status)):
+        _dev(t, name)
+    a = ConvertArgs()
+    a.n, a.H_v, a.d_k, a.d_v = n, H_v, d_k, d_v
+    a.src_dtype, a.dst_dtype, a.src_bf16_rows, a.dst_bf16_rows = sk, dk_, sh, dh
+    a.src_n_slots, a.dst_n_slots = src_pool.shape[0], dst_pool.shape[0]
+    a.src_pool, a.dst_pool = _ptr(src_pool), _ptr(dst_pool)
+    a.src_slot, a.dst_slot, a.status = _ptr(src_slot), _ptr(dst_slot), _ptr(status)
+    code = load_library().gdn_state_convert(ctypes.byref(a), _stream(stream))
+    if code:
+        raise GdnError("gdn_state_convert", code)
+    return dst_pool
 
 
 def gdn_conv_store(cu_seqlens, q_raw, k_raw, v_raw, conv_pool, write_slot=None, *, H_qk, H_v,

@@ -28,7 +28,8 @@ def test_struct_layout_matches():
     assert lib.gdn_sizeof_decode_args() == ctypes.sizeof(B.DecodeArgs)
     assert lib.gdn_sizeof_prefill_args() == ctypes.sizeof(B.PrefillArgs)
     assert lib.gdn_sizeof_conv_args() == ctypes.sizeof(B.ConvArgs)
-    assert gdn.gdn_abi_version() == 9
+    assert gdn.gdn_abi_version() == 10
+    assert lib.gdn_sizeof_convert_args() == ctypes.sizeof(B.ConvertArgs)
 
 
 def test_state_bytes_against_the_pages():
@@ -378,3 +379,38 @@ def test_decode_conv_null_and_empty():
     assert lib.gdn_decode_conv(ctypes.byref(d), None, None) == NULL
     d, c = _fused_args(dict(B=0, state_pool=None, o=None), dict(B=0, q=None, conv_pool=None))
     assert lib.gdn_decode_conv(ctypes.byref(d), ctypes.byref(c), None) == OK
+
+
+def _convert_args(**over):
+    a = B.ConvertArgs()
+    a.n, a.H_v, a.d_k, a.d_v = 4, 2, 128, 128
+    a.src_dtype, a.dst_dtype, a.src_bf16_rows, a.dst_bf16_rows = B.BF16, B.Q8, 0, 32
+    a.src_n_slots = a.dst_n_slots = 8
+    a.src_pool = a.dst_pool = FAKE
+    for k, v in over.items():
+        setattr(a, k, v)
+    return a
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(n=-1), SHAPE), (dict(src_n_slots=-1), SHAPE), (dict(src_dtype=3), DTYPE),
+    (dict(dst_dtype=-1), DTYPE), (dict(H_v=0), SHAPE), (dict(d_k=48), UNSUP),
+    (dict(d_v=256), UNSUP),
+    # BF16-row counts: valid for an 8-bit side (multiples of the decode's row quantum), none else
+    (dict(dst_bf16_rows=12), SHAPE), (dict(dst_bf16_rows=136), SHAPE),
+    (dict(src_bf16_rows=32), SHAPE), (dict(src_dtype=B.Q8, src_bf16_rows=24), SHAPE),
+    (dict(n=9, src_slot=None), SHAPE),       # identity slots need n <= n_slots
+    (dict(src_pool=None), NULL), (dict(dst_pool=None), NULL),
+    (dict(src_pool=FAKE + 8), ALIGN), (dict(dst_pool=FAKE + 4), ALIGN),
+    (dict(n=1 << 30, H_v=4), UNSUP),         # grid size
+])
+def test_state_convert_validation(over, code):
+    a = _convert_args(**over)
+    assert gdn.load_library().gdn_state_convert(ctypes.byref(a), None) == code
+
+
+def test_state_convert_null_and_empty():
+    lib = gdn.load_library()
+    assert lib.gdn_state_convert(None, None) == NULL
+    a = _convert_args(n=0, src_pool=None, dst_pool=None)
+    assert lib.gdn_state_convert(ctypes.byref(a), None) == OK
