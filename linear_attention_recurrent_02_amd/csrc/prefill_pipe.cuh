@@ -48,8 +48,8 @@ struct PipeLayout {
   static constexpr size_t L_TB = L_AB + (size_t)C * B::LDAB * 2;
   static constexpr size_t LOC = L_TB + (size_t)C * B::LDTB * 2;  // one chunk-local set
   static constexpr size_t LOC0 = 2 * SET;
-  // per producer wave: its FP32 diagonal block of A, row-major (rows of LDA
-  // floats: the padding puts a wave's four row groups in different banks)
+  // per producer wave: its FP32 diagonal block of A, transposed (row c holds
+  // column c of A; rows of LDA floats, 16-byte aligned)
   static constexpr int LDA = 20;
   static constexpr size_t ADIAG = LOC0 + 2 * LOC;
   static constexpr size_t ADIAG_WAVE = 16 * LDA * 4;
@@ -295,25 +295,29 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
         put(Sq + r * LDC + s2, p.scale * (dec * pa[t][e]));
       }
     }
-    // T_bb column `col` by forward substitution, row r of A_bb read back as
-    // 16-byte broadcast loads (every lane reads the same row)
-    float *const Ar = reinterpret_cast<float *>(smem + L::ADIAG + b * L::ADIAG_WAVE);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) Ar[(rq + e) * L::LDA + col] = ab[e];
+    // T_bb column `col` by forward substitution in right-looking order: once
+    // x_s is final, every later row's sum takes its term -A[r][s] x_s, so a
+    // step waits on one FMA instead of a row's whole chain.  Each row still adds its terms
+    // in the order s = 0, 1, ..., so T is bitwise the row-by-row result.
+    // A_bb is written transposed to the wave's LDS area (one 16-byte store
+    // per lane: row c holds column c of A), and step s reads column s back as
+    // 16-byte broadcast loads (every lane reads the same row).
+    float *const At = reinterpret_cast<float *>(smem + L::ADIAG + b * L::ADIAG_WAVE);
+    *reinterpret_cast<f32x4_t *>(At + col * L::LDA + rq) = ab;
     float tc[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = r == col ? 1.f : 0.f;
-      float ar[16];
+    for (int r = 0; r < 16; ++r) tc[r] = r == col ? 1.f : 0.f;
 #pragma unroll
-      for (int q4 = 0; q4 < (r + 3) / 4; ++q4) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(Ar + r * L::LDA + 4 * q4);
+    for (int s2 = 0; s2 < 15; ++s2) {
+      float ac[16];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ar[4 * q4 + e] = v[e];
+      for (int q4 = (s2 + 1) / 4; q4 < 4; ++q4) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t *>(At + s2 * L::LDA + 4 * q4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ac[4 * q4 + e] = v[e];
       }
 #pragma unroll
-      for (int s2 = 0; s2 < r; ++s2) x = fmaf(-ar[s2], tc[s2], x);
-      tc[r] = x;
+      for (int r = s2 + 1; r < 16; ++r) tc[r] = fmaf(-ac[r], tc[s2], tc[r]);
     }
     if (lane < 16) {
 #pragma unroll
