@@ -363,9 +363,8 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
   // Both meet the same barriers: two in the prologue, two per chunk.
   const int n_chunks = (int)((t_end - t_begin + C - 1) / C);
   if (consumer) {
-    // the consumers are the chain's critical path (the producers finish their
-    // chunk with time to spare): when both waves of a SIMD can issue, they go
-    // first (measured: 0.6%)
+    // when both waves of a SIMD can issue, the consumer goes first, except
+    // while its producer stages the next chunk's inputs (see there)
     __builtin_amdgcn_s_setprio(1);
     // ---- consumers: initial state (a8), read slot -> FP32 accumulators ------
     // macc[b][ia]: rows 16b.. of d_k, columns 16 (cw NA + ia).. of d_v
@@ -602,7 +601,12 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
         // chunk c + 1 staged, chunk c + 2 fetched, then chunk
         // c + 1's chunk-local products (on the last iterations these run on
         // clamped rows that no consumer reads) ----
+        // staged above the consumers' issue priority: they wait for it at Y,
+        // and at their priority the staging trailed their QM and KM (cycle
+        // stamps, varlen workload: 8.25k-8.77k -> 8.11k-8.30k cycles per chunk)
+        __builtin_amdgcn_s_setprio(2);
         stage((c + 1) & 1);
+        __builtin_amdgcn_s_setprio(0);
         fetch(t0 + 2 * C);
         __syncthreads();  // Y: chunk c + 1's inputs are visible
         use_set((c + 1) & 1);
