@@ -548,18 +548,20 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
     __syncthreads();
 
     // 4: T_bb = (I + A_bb)^-1 by forward substitution (wave b, lane c <
-    // 16: column c); then the per-channel scalings of K and Q
+    // 16: column c) in right-looking order: once x_s is final, every later
+    // row takes its term -A[r][s] x_s, so a step waits on one FMA rather than
+    // on a row's chain, and each row still adds its terms in the order
+    // s = 0, 1, ...; then the per-channel scalings of K and Q
     {
       const int b = wave, c = lane;
       if (dwave && c < 16) {
         float x[16];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = r == c ? 1.f : 0.f;
+        for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
 #pragma unroll
-          for (int s = 0; s < r; ++s) v = fmaf(-Ad[(16 * b + r) * L::LDD + s], x[s], v);
-          x[r] = v;
-        }
+        for (int s = 0; s < 15; ++s)
+#pragma unroll
+          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-Ad[(16 * b + r) * L::LDD + s], x[s], x[r]);
 #pragma unroll
         for (int r = 0; r < 16; ++r) put(Tb + (16 * b + r) * L::LDT + c, x[r]);
       }
