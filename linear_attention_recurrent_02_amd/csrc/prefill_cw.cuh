@@ -566,7 +566,11 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
         for (int r = 0; r < 16; ++r) put(Tb + (16 * b + r) * L::LDT + c, x[r]);
       }
     }
-    for (int i = tid; i < C * (DKP / 8); i += NT) {
+    // with 8 waves the scalings run on waves 4-7 alone, beside waves 0-3's
+    // substitutions (0.4% faster than sharing them out over all eight)
+    constexpr int XT = NW == 8 ? NT - 256 : NT;  // threads that scale
+    for (int i = NW == 8 ? tid - 256 : tid; i < C * (DKP / 8); i += XT) {
+      if (i < 0) break;
       const int r = i / (DKP / 8), c = (i % (DKP / 8)) * 8;
       float kx[8], qx[8], g8[8], gl8[8];
       load8(Kh + L::ak(r, c), kx);
