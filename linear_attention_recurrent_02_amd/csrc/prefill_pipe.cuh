@@ -297,9 +297,9 @@ __device__ __forceinline__ void prefill_chain_pipe(const PrefillParams &p, int c
     }
     // T_bb column `col` by forward substitution in right-looking order: once
     // x_s is final, every later row's sum takes its term -A[r][s] x_s, so a
-    // step waits on one FMA instead of a row's whole chain.  Each row still adds its terms
-    // in the order s = 0, 1, ..., so T is bitwise the row-by-row result.
-    // A_bb is written transposed to the wave's LDS area (one 16-byte store
+    // step waits on one FMA instead of a row's whole chain.  Each row still
+    // adds its terms in the order s = 0, 1, ..., so T is bitwise the
+    // row-by-row result.  A_bb is written transposed to the wave's LDS area (one 16-byte store
     // per lane: row c holds column c of A), and step s reads column s back as
     // 16-byte broadcast loads (every lane reads the same row).
     float *const At = reinterpret_cast<float *>(smem + L::ADIAG + b * L::ADIAG_WAVE);
