@@ -80,7 +80,7 @@ struct CwLayout {
   static constexpr int LDC = C + PADO;     // L o P rows (OT)
   static constexpr int LDAB = C + PADO;    // -A rows (OT)
   static constexpr int LDT = 16 + PADO;    // T_ii rows (OT)
-  static constexpr int LDD = 20;           // diagonal blocks of A in float
+  static constexpr int LDD = 20;           // diagonal blocks of A in float, transposed
   static constexpr size_t KH = 0;
   static constexpr size_t QH = KH + (size_t)C * LDK * sizeof(IT);
   static constexpr size_t VH = QH + (size_t)C * LDK * sizeof(IT);
@@ -488,7 +488,7 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
           const float a = s < r ? ef * br[e] * sa[e] : 0.f;
           put(Ab + r * L::LDAB + s, -a);
           put(Sq + r * LDC + s, s <= r ? p.scale * pa[e] : 0.f);
-          Ad[r * L::LDD + col] = a;
+          Ad[(16 * I + col) * L::LDD + rq + e] = a;
         } else {
           put(Ab + r * L::LDAB + s, -(ef * br[e]) * sa[e]);
           put(Sq + r * LDC + s, p.scale * pa[e]);
@@ -539,7 +539,7 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
         for (int s = 0; s < 16; ++s) {
           a16[s] = s < r ? -bw * accA[s] : 0.f;   // -A
           p16[s] = s <= r ? p.scale * accP[s] : 0.f;
-          Ad[(16 * b + r) * L::LDD + s] = -a16[s];
+          Ad[(16 * b + s) * L::LDD + r] = -a16[s];
         }
         put_row16(Ab + (16 * b + r) * L::LDAB + 16 * b, a16);
         put_row16(Sq + (16 * b + r) * LDC + 16 * b, p16);
@@ -551,17 +551,28 @@ __device__ __forceinline__ void prefill_chain_cw(const PrefillParams &p, int cha
     // 16: column c) in right-looking order: once x_s is final, every later
     // row takes its term -A[r][s] x_s, so a step waits on one FMA rather than
     // on a row's chain, and each row still adds its terms in the order
-    // s = 0, 1, ...; then the per-channel scalings of K and Q
+    // s = 0, 1, ...  A_bb is stored transposed (row 16 b + s of Ad holds
+    // column s of the block), so step s reads its column as 16-byte loads.
+    // Then the per-channel scalings of K and Q.
     {
       const int b = wave, c = lane;
       if (dwave && c < 16) {
+        const float *const At = Ad + 16 * b * L::LDD;
         float x[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
 #pragma unroll
-        for (int s = 0; s < 15; ++s)
+        for (int s = 0; s < 15; ++s) {
+          float ac[16];
 #pragma unroll
-          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-Ad[(16 * b + r) * L::LDD + s], x[s], x[r]);
+          for (int q4 = (s + 1) / 4; q4 < 4; ++q4) {
+            const f32x4_t v = *reinterpret_cast<const f32x4_t *>(At + s * L::LDD + 4 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ac[4 * q4 + e] = v[e];
+          }
+#pragma unroll
+          for (int r = s + 1; r < 16; ++r) x[r] = fmaf(-ac[r], x[s], x[r]);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) put(Tb + (16 * b + r) * L::LDT + c, x[r]);
       }
